@@ -1,0 +1,129 @@
+"""Pins for oracle.planner.  The split policy is our reading (the pages give
+trade-offs, not an algorithm), so it is pinned by a hand-worked example and by
+the partition invariants the merge needs: page-aligned, disjoint chunks that
+cover every key a tile may see exactly once (Deep Dive - FlashInfer, 'A worked
+split-KV example': overlapping chunks double-count keys)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import planner as pl
+
+
+def test_hand_worked_decode_split():
+    """Two decode requests of 600 and 100 tokens, page 16 (38 and 7 pages).
+    Unforced with one CU and target 1: chunk = max(16, 45) = 45 pages, nothing
+    splits.  Forced to 16-page chunks: request 0 splits into keys [0,256),
+    [256,512), [512,600) with partial rows 0, 1, 2; request 1 stays direct.
+    Emission is by descending cost: 256, 256, 100, 88."""
+    args = dict(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4],
+                page_size=16, heads_y=1, rows=1, causal=True, num_cus=1, target_per_cu=1)
+    p = pl.plan(**args)
+    assert p["chunk_pages"] == 45 and not p["split"] and p["merges"] == []
+    assert p["items"] == [[0, 1, 0, 600, 599, 0, -1, 0], [1, 1, 0, 100, 99, 38, -1, 1]]
+    p = pl.plan(**args, fixed_split_pages=16)
+    assert p["split"] and p["num_partial_rows"] == 3
+    assert p["merges"] == [[0, 1, 0, 3]]
+    assert p["items"] == [[0, 1, 0, 256, 599, 0, 0, 0], [0, 1, 256, 512, 599, 0, 1, 0],
+                          [1, 1, 0, 100, 99, 38, -1, 1], [0, 1, 512, 600, 599, 0, 2, 0]]
+
+
+def test_hand_worked_causal_pruning():
+    """One prefill request, 6 new rows after a 26-token prefix (K = 32), page 4,
+    tiles of 4 rows, 2-page (8-key) chunks.  Tile 0 (rows 0..3, diag 26) sees
+    keys < 30: chunks [0,8) [8,16) [16,24) [24,30).  Tile 1 (rows 4,5, diag 30)
+    sees keys < 32: chunks up to [24,32)."""
+    p = pl.plan(mode="prefill", qo_indptr=[0, 6], kv_indptr=[0, 8], kv_last_page_len=[4],
+                page_size=4, heads_y=1, rows=4, causal=True, num_cus=1, fixed_split_pages=2)
+    t0 = sorted(i for i in p["items"] if i[0] == 0)
+    t1 = sorted(i for i in p["items"] if i[0] == 4)
+    assert [(i[2], i[3]) for i in t0] == [(0, 8), (8, 16), (16, 24), (24, 30)]
+    assert [(i[2], i[3]) for i in t1] == [(0, 8), (8, 16), (16, 24), (24, 32)]
+    assert all(i[4] == 26 and i[1] == 4 for i in t0) and all(i[4] == 30 and i[1] == 2 for i in t1)
+    assert p["merges"] == [[0, 4, 0, 4], [4, 2, 16, 4]]
+    assert p["num_partial_rows"] == 24
+
+
+def _random_case(rng, mode):
+    b = int(rng.integers(1, 9))
+    page = int(rng.choice([1, 3, 4, 16]))
+    if mode == "prefill":
+        q = [int(x) for x in rng.integers(0, 40, size=b)]
+        k = [qi + int(rng.integers(0, 90)) for qi in q]
+        k = [max(1, x) for x in k]
+        qo = list(np.cumsum([0] + q))
+    else:
+        k = [int(x) for x in rng.integers(1, 700, size=b)]
+        qo = None
+    n = [math.ceil(x / page) for x in k]
+    last = [x - (m - 1) * page for x, m in zip(k, n)]
+    return dict(qo_indptr=qo, kv_indptr=list(np.cumsum([0] + n)), kv_last_page_len=last, page_size=page,
+                k=k)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill", "mla"])
+def test_partition_invariants(mode):
+    rng = np.random.default_rng(21)
+    for trial in range(60):
+        c = _random_case(rng, mode)
+        rows = int(rng.choice([1, 2, 4, 32])) if mode == "prefill" else 1
+        causal = bool(rng.integers(2)) if mode == "prefill" else True
+        fixed = int(rng.choice([0, 0, 1, 2, 7]))
+        p = pl.plan(mode=mode, qo_indptr=c["qo_indptr"], kv_indptr=c["kv_indptr"],
+                    kv_last_page_len=c["kv_last_page_len"], page_size=c["page_size"],
+                    heads_y=int(rng.integers(1, 9)), rows=rows, causal=causal,
+                    num_cus=int(rng.integers(1, 300)), fixed_split_pages=fixed)
+        chunk_tok = p["chunk_pages"] * c["page_size"]
+        qo = c["qo_indptr"] or list(range(len(c["k"]) + 1))
+        by_tile = {}
+        for it in p["items"]:
+            q_row0, n_rows, lo, hi, diag, page_base, slot, b = it
+            assert lo % chunk_tok == 0 and 0 <= lo < hi and hi - lo <= chunk_tok
+            assert page_base == c["kv_indptr"][b] and qo[b] <= q_row0 < qo[b + 1]
+            assert q_row0 + n_rows <= qo[b + 1] and n_rows >= 1
+            by_tile.setdefault((b, q_row0), []).append(it)
+        # every query row is covered by exactly one tile
+        covered = sorted(r for (b, r0), its in by_tile.items() for r in range(r0, r0 + its[0][1]))
+        assert covered == list(range(qo[-1]))
+        for (b, r0), its in by_tile.items():
+            k_len, q_len = c["k"][b], qo[b + 1] - qo[b]
+            l0 = r0 - qo[b]
+            diag = (k_len - q_len + l0) if causal else k_len
+            limit = min(k_len, diag + its[0][1])
+            spans = sorted((i[2], i[3]) for i in its)
+            # chunks tile [0, limit) exactly once
+            assert spans[0][0] == 0 and spans[-1][1] == limit
+            assert all(a[1] == b_[0] for a, b_ in zip(spans, spans[1:]))
+            assert all(i[4] == diag for i in its)
+            if len(its) == 1:
+                assert its[0][6] == -1
+            else:
+                m = [x for x in p["merges"] if x[0] == r0]
+                assert len(m) == 1 and m[0][1] == its[0][1] and m[0][3] == len(its)
+                slots = sorted(i[6] for i in its)
+                assert slots == [m[0][2] + c_ * its[0][1] for c_ in range(len(its))]
+        total = sum(m[1] * m[3] for m in p["merges"])
+        assert total == p["num_partial_rows"]
+        costs = [(i[3] - i[2]) * i[1] for i in p["items"]]
+        assert costs == sorted(costs, reverse=True)
+        if fixed == 1:
+            assert all(i[3] - i[2] <= c["page_size"] for i in p["items"])
+
+
+def test_rows_per_tile_rule():
+    assert pl.rows_per_tile("decode", 4, "bf16") == 1
+    assert pl.rows_per_tile("prefill", 4, "f32") == 1
+    assert pl.rows_per_tile("prefill", 4, "bf16") == 32
+    assert pl.rows_per_tile("prefill", 1, "bf16") == 128
+    assert pl.rows_per_tile("prefill", 256, "bf16") == 1
+
+
+def test_empty_batch_and_empty_requests():
+    p = pl.plan(mode="prefill", qo_indptr=[0], kv_indptr=[0], kv_last_page_len=[], page_size=4,
+                heads_y=2, rows=4, causal=True, num_cus=8)
+    assert p["items"] == [] and p["merges"] == []
+    p = pl.plan(mode="prefill", qo_indptr=[0, 0, 2], kv_indptr=[0, 1, 2], kv_last_page_len=[3, 4],
+                page_size=4, heads_y=1, rows=4, causal=True, num_cus=8)
+    assert [i[7] for i in p["items"]] == [1]

@@ -1,0 +1,270 @@
+"""Seeded synthetic inputs for paged KV-cache attention.
+
+This module only draws inputs: request lengths, page permutations and
+N(0, 1) payloads, packed as CSR page-table metadata and caches.  It holds none
+of the attention arithmetic and is the one module that both the CPU oracle
+(tests, bench baseline) and the HIP path (tests, bench) import.
+
+Draw order per workload (one ``numpy.random.default_rng(seed)``): lengths,
+page permutation, Q, K pool, V pool, new K, new V.  A pool draws values only
+for the pages some request owns, in ascending page id, 2048 pages at a time.  bfloat16 payloads are
+drawn as float32 N(0, 1) and rounded to nearest-even bfloat16 here, so the GPU
+and the oracle see the same bits.  With ``poison=True`` every pool slot that
+no request owns (unused pages, page tails past last_page_len, and the slots
+an append is about to fill) holds NaN, so any read of them shows.
+
+Workloads (sizes follow the pages' worked example and the serving mixes
+described there; see the design doc for the recipe):
+  worked    3 requests, qo 3/1/4, kv 6/2/9, page 4, pool 16, heads 4/2, dim
+            64, float32, NHD, causal, sm_scale 1/8.  ``literal_pages=True``
+            uses the pages' own page ids 7,2 | 11 | 3,14,6.
+  decode    64 requests, qo 1, kv U[512, 4096], page 16, pool 20000 pages,
+            heads 32/8, dim 128, bfloat16, NHD.
+  skewed    16 requests, qo 1, one kv 32768 and 15 kv U[256, 1024], page 1,
+            pool = exactly the tokens used, heads 32/8, dim 128, bfloat16, NHD.
+  prefill   8 requests, qo U[512, 2048], prefix U[0, 8192], kv = prefix + qo,
+            page 16, HND, heads 32/8, dim 128, bfloat16, causal; new K/V are
+            appended before attention.
+  mla       32 requests, qo 1, kv U[1024, 8192], page 64, latent cache
+            [pages, 64, 512 + 64] bfloat16, 128 heads, sm_scale 1/sqrt(576).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+WORKLOADS = ("worked", "decode", "skewed", "prefill", "mla")
+SEEDS = {"worked": 1000, "decode": 1001, "skewed": 1002, "prefill": 1003, "mla": 1004}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return the 16-bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def _payload(rng, shape, dtype: str):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _pool(rng, shape, dtype: str, owned_pages):
+    """A page pool whose owned pages (in ascending page id) get fresh N(0, 1)
+    draws; pages nobody owns stay zero (or NaN once poisoned)."""
+    pool = np.zeros(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    pages = np.unique(np.asarray(owned_pages, dtype=np.int64))
+    step = 2048
+    for i in range(0, len(pages), step):
+        sel = pages[i:i + step]
+        pool[sel] = _payload(rng, (len(sel),) + tuple(shape[1:]), dtype)
+    return pool
+
+
+@dataclass
+class Batch:
+    """One synthetic batch.  Arrays are numpy; metadata is int32."""
+    name: str
+    mode: str                      # "decode" | "prefill" | "mla"
+    dtype: str                     # "f32" | "bf16" (payload storage)
+    layout: str                    # "NHD" | "HND" (ignored for mla)
+    page_size: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    causal: bool
+    sm_scale: float
+    qo_lens: list
+    kv_lens: list
+    qo_indptr: np.ndarray
+    kv_indptr: np.ndarray
+    kv_indices: np.ndarray
+    kv_last_page_len: np.ndarray
+    max_num_pages: int
+    q: np.ndarray = None           # [nnz, Hq, D]             (mla: q_ckv [B, H, 512])
+    k_cache: np.ndarray = None     # tuple form, layout-shaped (mla: unified [pages, P, 576])
+    v_cache: np.ndarray = None
+    q_kpe: np.ndarray = None       # mla only: [B, H, 64]
+    k_new: np.ndarray = None       # [nnz, Hkv, D] appended tokens (prefill/worked)
+    v_new: np.ndarray = None
+    append_indptr: np.ndarray = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def batch_size(self) -> int:
+        return len(self.qo_lens)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.qo_indptr[-1])
+
+
+def _csr(kv_lens, page_size, pages_for_request):
+    n_pages = [max(1, math.ceil(k / page_size)) for k in kv_lens]
+    kv_indptr = np.zeros(len(kv_lens) + 1, dtype=np.int32)
+    kv_indptr[1:] = np.cumsum(n_pages)
+    kv_indices = np.concatenate([np.asarray(pages_for_request(b, n), dtype=np.int32)
+                                 for b, n in enumerate(n_pages)]) if kv_lens else np.zeros(0, np.int32)
+    last = np.asarray([k - (n - 1) * page_size for k, n in zip(kv_lens, n_pages)], dtype=np.int32)
+    return n_pages, kv_indptr, kv_indices.astype(np.int32), last
+
+
+def _cache_shape(layout, pages, page_size, heads, dim):
+    return (pages, page_size, heads, dim) if layout == "NHD" else (pages, heads, page_size, dim)
+
+
+def _poison(cache, layout, used_slots, dtype):
+    """Replace every (page, slot) not in ``used_slots`` by NaN."""
+    pages, page_size = cache.shape[0], (cache.shape[1] if layout == "NHD" else cache.shape[2])
+    keep = np.zeros((pages, page_size), dtype=bool)
+    if len(used_slots):
+        keep[used_slots[:, 0], used_slots[:, 1]] = True
+    nan = BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    if layout == "NHD":
+        cache[~keep] = nan
+    else:
+        cache.transpose(0, 2, 1, 3)[~keep] = nan
+
+
+def _slots(kv_indptr, kv_indices, page_size, b, lo, hi):
+    j = np.arange(lo, hi)
+    pages = kv_indices[kv_indptr[b]:kv_indptr[b + 1]]
+    return np.stack([pages[j // page_size], j % page_size], axis=1) if len(j) else np.zeros((0, 2), np.int64)
+
+
+def _gqa_batch(name, rng, *, mode, qo_lens, kv_lens, page_size, pool, pages_for_request, hq, hkv,
+               dim, dtype, layout, causal, sm_scale, with_append, poison):
+    n_pages, kv_indptr, kv_indices, last = _csr(kv_lens, page_size, pages_for_request)
+    qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    nnz = int(qo_indptr[-1])
+    q = _payload(rng, (nnz, hq, dim), dtype)
+    shape = _cache_shape(layout, pool, page_size, hkv, dim)
+    k_cache = _pool(rng, shape, dtype, kv_indices)
+    v_cache = _pool(rng, shape, dtype, kv_indices)
+    k_new = v_new = append_indptr = None
+    if with_append:
+        k_new = _payload(rng, (nnz, hkv, dim), dtype)
+        v_new = _payload(rng, (nnz, hkv, dim), dtype)
+        append_indptr = qo_indptr.copy()
+    if poison:
+        # Slots holding cached history keep their values; everything else
+        # (free pages, tails, and slots the append will fill) becomes NaN.
+        hist = [_slots(kv_indptr, kv_indices, page_size, b, 0,
+                       kv_lens[b] - (qo_lens[b] if with_append else 0)) for b in range(len(kv_lens))]
+        used = np.concatenate(hist) if hist else np.zeros((0, 2), np.int64)
+        _poison(k_cache, layout, used, dtype)
+        _poison(v_cache, layout, used, dtype)
+    return Batch(name=name, mode=mode, dtype=dtype, layout=layout, page_size=page_size,
+                 num_qo_heads=hq, num_kv_heads=hkv, head_dim=dim, causal=causal, sm_scale=sm_scale,
+                 qo_lens=list(qo_lens), kv_lens=list(kv_lens), qo_indptr=qo_indptr,
+                 kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+                 max_num_pages=pool, q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new,
+                 v_new=v_new, append_indptr=append_indptr)
+
+
+def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pages: bool = False,
+         scale: float = 1.0, **overrides) -> Batch:
+    """Build workload ``name`` (one of WORKLOADS).
+
+    ``scale`` < 1 shrinks lengths/batch for quick CPU tests while keeping the
+    workload's structure; ``overrides`` replace individual knobs (e.g.
+    ``layout="HND"``, ``page_size=1``, ``batch=4``).
+    """
+    rng = np.random.default_rng(SEEDS[name] if seed is None else seed)
+    o = dict(overrides)
+    if name == "worked":
+        qo_lens, kv_lens = o.get("qo_lens", [3, 1, 4]), o.get("kv_lens", [6, 2, 9])
+        page_size, pool = o.get("page_size", 4), o.get("pool", 16)
+        perm = rng.permutation(pool)
+        if literal_pages:
+            fixed = {0: [7, 2], 1: [11], 2: [3, 14, 6]}
+            pages_for = lambda b, n: fixed[b]
+        else:
+            starts = np.cumsum([0] + [math.ceil(k / page_size) for k in kv_lens])
+            pages_for = lambda b, n: perm[starts[b]:starts[b] + n]
+        return _gqa_batch("worked", rng, mode="prefill", qo_lens=qo_lens, kv_lens=kv_lens,
+                          page_size=page_size, pool=pool, pages_for_request=pages_for,
+                          hq=o.get("hq", 4), hkv=o.get("hkv", 2), dim=o.get("dim", 64),
+                          dtype=o.get("dtype", "f32"), layout=o.get("layout", "NHD"), causal=True,
+                          sm_scale=o.get("sm_scale", 1.0 / 8.0), with_append=True, poison=poison)
+    if name in ("decode", "skewed"):
+        if name == "decode":
+            batch = o.get("batch", max(1, int(round(64 * scale))))
+            lo, hi = o.get("kv_range", (max(1, int(512 * scale)), max(1, int(4096 * scale))))
+            kv_lens = [int(x) for x in rng.integers(lo, hi, size=batch, endpoint=True)]
+            page_size = o.get("page_size", 16)
+            pool = o.get("pool", max(int(20000 * scale), sum(math.ceil(k / page_size) for k in kv_lens)))
+            layout = o.get("layout", "NHD")
+        else:
+            batch = o.get("batch", 16)
+            long_len = o.get("long_len", max(1, int(32768 * scale)))
+            lo, hi = o.get("kv_range", (max(1, int(256 * scale)), max(1, int(1024 * scale))))
+            kv_lens = [long_len] + [int(x) for x in rng.integers(lo, hi, size=batch - 1, endpoint=True)]
+            page_size = o.get("page_size", 1)
+            pool = o.get("pool", sum(math.ceil(k / page_size) for k in kv_lens))
+            layout = o.get("layout", "NHD")
+        perm = rng.permutation(pool)
+        starts = np.cumsum([0] + [math.ceil(k / page_size) for k in kv_lens])
+        return _gqa_batch(name, rng, mode="decode", qo_lens=[1] * batch, kv_lens=kv_lens,
+                          page_size=page_size, pool=pool,
+                          pages_for_request=lambda b, n: perm[starts[b]:starts[b] + n],
+                          hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=o.get("dim", 128),
+                          dtype=o.get("dtype", "bf16"), layout=layout, causal=True,
+                          sm_scale=o.get("sm_scale", 1.0 / math.sqrt(o.get("dim", 128))),
+                          with_append=o.get("with_append", False), poison=poison)
+    if name == "prefill":
+        batch = o.get("batch", 8)
+        qlo, qhi = o.get("qo_range", (max(1, int(512 * scale)), max(1, int(2048 * scale))))
+        plo, phi = o.get("prefix_range", (0, int(8192 * scale)))
+        qo_lens = [int(x) for x in rng.integers(qlo, qhi, size=batch, endpoint=True)]
+        prefix = [int(x) for x in rng.integers(plo, phi, size=batch, endpoint=True)]
+        kv_lens = [p + q for p, q in zip(prefix, qo_lens)]
+        page_size = o.get("page_size", 16)
+        need = sum(math.ceil(k / page_size) for k in kv_lens)
+        pool = o.get("pool", need + need // 4 + 1)
+        perm = rng.permutation(pool)
+        starts = np.cumsum([0] + [math.ceil(k / page_size) for k in kv_lens])
+        dim = o.get("dim", 128)
+        return _gqa_batch("prefill", rng, mode="prefill", qo_lens=qo_lens, kv_lens=kv_lens,
+                          page_size=page_size, pool=pool,
+                          pages_for_request=lambda b, n: perm[starts[b]:starts[b] + n],
+                          hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=dim,
+                          dtype=o.get("dtype", "bf16"), layout=o.get("layout", "HND"),
+                          causal=o.get("causal", True), sm_scale=o.get("sm_scale", 1.0 / math.sqrt(dim)),
+                          with_append=True, poison=poison)
+    if name == "mla":
+        batch = o.get("batch", max(1, int(round(32 * scale))))
+        lo, hi = o.get("kv_range", (max(1, int(1024 * scale)), max(1, int(8192 * scale))))
+        kv_lens = [int(x) for x in rng.integers(lo, hi, size=batch, endpoint=True)]
+        page_size = o.get("page_size", 64)
+        need = sum(math.ceil(k / page_size) for k in kv_lens)
+        pool = o.get("pool", need + need // 4 + 1)
+        perm = rng.permutation(pool)
+        starts = np.cumsum([0] + [math.ceil(k / page_size) for k in kv_lens])
+        n_pages, kv_indptr, kv_indices, last = _csr(
+            kv_lens, page_size, lambda b, n: perm[starts[b]:starts[b] + n])
+        heads = o.get("heads", 128)
+        d_ckv, d_kpe = 512, 64
+        q_ckv = _payload(rng, (batch, heads, d_ckv), "bf16")
+        q_kpe = _payload(rng, (batch, heads, d_kpe), "bf16")
+        cache = _pool(rng, (pool, page_size, d_ckv + d_kpe), "bf16", kv_indices)
+        if poison:
+            used = np.concatenate([_slots(kv_indptr, kv_indices, page_size, b, 0, kv_lens[b])
+                                   for b in range(batch)])
+            keep = np.zeros((pool, page_size), dtype=bool)
+            keep[used[:, 0], used[:, 1]] = True
+            cache[~keep] = BF16_NAN
+        qo_indptr = np.arange(batch + 1, dtype=np.int32)
+        return Batch(name="mla", mode="mla", dtype="bf16", layout="NHD", page_size=page_size,
+                     num_qo_heads=heads, num_kv_heads=1, head_dim=d_ckv + d_kpe, causal=False,
+                     sm_scale=o.get("sm_scale", 1.0 / math.sqrt(d_ckv + d_kpe)),
+                     qo_lens=[1] * batch, kv_lens=kv_lens, qo_indptr=qo_indptr,
+                     kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+                     max_num_pages=pool, q=q_ckv, q_kpe=q_kpe, k_cache=cache, v_cache=None)
+    raise KeyError(name)
