@@ -1,0 +1,344 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache attention library for AMD MI355X (gfx950).
+ *
+ * Batched attention of ragged queries against a paged KV cache described by a
+ * CSR page table.  The calls follow the problem statement of three web pages:
+ *   [DD]  "Deep Dive - FlashInfer" (leetllm.com)
+ *   [KVL] "FlashInfer 中的 KV-Cache 布局" (KV-cache layouts, docs.flashinfer.cn)
+ *   [GAB] "GPU attention backends: FlashInfer and FlashAttention"
+ *         (mini-sglang from Scratch, Stage 4)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Plain C types only.  "host" pointers are ordinary CPU memory; "device"
+ *   pointers are HIP device memory of the current device.  `stream` is a
+ *   hipStream_t passed as void* (NULL = the null stream).
+ * - Every call returns a pkv_status; nothing throws across the ABI.  On error
+ *   pkv_last_error() returns a thread-local message; for PKV_ERR_METADATA,
+ *   pkv_last_meta_reason() names the broken rule (pkv_meta_reason).
+ * - All metadata arrays are int32 ([KVL] "Ragged Tensor" and "页表布局":
+ *   indptr, page-index and tail-length arrays are 32-bit).
+ * - Element strides are counted in elements of the payload dtype.
+ * - The library never allocates device memory: the caller owns the caches,
+ *   Q/O/LSE buffers, the plan workspace and the pinned staging buffer, and
+ *   keeps them alive until the last queued call that uses them has finished
+ *   ([DD] "Where FlashInfer sits in a serving stack": the engine owns pages
+ *   and their lifetime).
+ * - LSE values are base 2: lse = log2(sum_j exp(s_j)) with s_j the scaled
+ *   logits; the empty state is (zero vector, -inf) ([DD] "Core mechanism:
+ *   schedule work around state", "A worked split-KV example").
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride/alignment, plan/call mismatch */
+  PKV_ERR_METADATA = 2,     /* page-table metadata breaks a rule (see pkv_meta_reason) */
+  PKV_ERR_UNSUPPORTED = 3,  /* a head dim, group size, dtype or mode this build has no kernel for */
+  PKV_ERR_WORKSPACE = 4,    /* workspace or staging buffer too small */
+  PKV_ERR_STALE_PLAN = 5,   /* pkv_plan_check: metadata differs from what the plan was built on */
+  PKV_ERR_HIP = 6           /* a HIP runtime call failed (message has the HIP error string) */
+};
+
+/* Metadata rules.  [DD] "Why inference attention becomes irregular" (length
+ * contract and its rejections) and [KVL] "Ragged Tensor" / "页表布局" state
+ * the first ones; the ones marked "completion" are our plainest reading. */
+typedef enum {
+  PKV_META_NONE = 0,
+  PKV_META_BATCH_SIZE = 1,       /* batch_size < 0 */
+  PKV_META_PAGE_SIZE = 2,        /* page_size < 1 */
+  PKV_META_INDPTR_START = 3,     /* an indptr does not start at 0 */
+  PKV_META_INDPTR_ORDER = 4,     /* an indptr decreases */
+  PKV_META_EMPTY_PAGE_LIST = 5,  /* a request owns no page */
+  PKV_META_LAST_PAGE_LEN = 6,    /* last_page_len outside 1..page_size */
+  PKV_META_PAGE_INDEX = 7,       /* page id outside [0, max_num_pages) */
+  PKV_META_INDICES_LENGTH = 8,   /* kv_indptr[B] > number of kv_indices */
+  PKV_META_QO_EXCEEDS_KV = 9,    /* completion: qo_len > kv_len (kv_len counts the new tokens) */
+  PKV_META_HEAD_GROUP = 10,      /* completion: num_qo_heads not a multiple of num_kv_heads */
+  PKV_META_DECODE_QO_LEN = 11,   /* completion: decode mode needs qo_len == 1 */
+  PKV_META_APPEND_COLLISION = 12 /* completion: two appended tokens target one slot */
+} pkv_meta_reason;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* [KVL] "布局：NHD/HND": the last three dims of a page are
+ * (page_size, heads, head_dim) for NHD and (heads, page_size, head_dim) for HND. */
+typedef enum { PKV_NHD = 0, PKV_HND = 1 } pkv_layout;
+
+typedef enum {
+  PKV_MODE_DECODE = 0,     /* one query row per request; no qo_indptr ([DD] "Plan then run") */
+  PKV_MODE_PREFILL = 1,    /* ragged query rows (chunked prefill / append), optional causal mask */
+  PKV_MODE_MLA_DECODE = 2  /* MLA latent cache, one query row per request ([KVL] MLA page layout) */
+} pkv_mode;
+
+const char* pkv_version(void);
+const char* pkv_last_error(void);
+int32_t pkv_last_meta_reason(void);
+
+/* Number of compute units of the current device (HIP call). */
+pkv_status pkv_device_num_cus(int32_t* num_cus_out);
+
+/*
+ * Paged cache descriptor.  k and v point at element (page 0, slot 0, head 0,
+ * dim 0) of the K and V pools.  Element (page, slot, head, dim) of K is at
+ *   k + page*page_stride + slot*token_stride + head*head_stride + dim.
+ * The dim stride is 1.  This covers both storage forms of [KVL] "页表布局":
+ *   5-D single tensor [pages, 2, ...]: v = k + (page_stride / 2),
+ *                                      page_stride = 2 * page_size * heads * head_dim;
+ *   (k, v) tuple of 4-D tensors:       page_stride = page_size * heads * head_dim;
+ * and both layouts: NHD token_stride = heads*head_dim, head_stride = head_dim;
+ *                   HND token_stride = head_dim, head_stride = page_size*head_dim.
+ * `layout` is informational (the strides decide the addressing).
+ */
+typedef struct pkv_cache_desc {
+  void* k;
+  void* v;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t max_num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;   /* pkv_dtype */
+  int32_t layout;  /* pkv_layout */
+} pkv_cache_desc;
+
+/*
+ * Host-side metadata check.  [DD] "Why inference attention becomes
+ * irregular": kv_len = page_size*(num_pages-1) + last_page_len with
+ * 1 <= last_page_len <= page_size and a nonempty list of nonnegative page ids;
+ * [KVL] "Ragged Tensor": indptr arrays have B+1 entries starting at 0.
+ * Rules are checked in pkv_meta_reason order of the oracle's statement:
+ * batch, page size, heads, qo_indptr, kv_indptr, indices length, per-request
+ * pages and tail, then qo_len vs kv_len (and decode's qo_len == 1).
+ *   qo_indptr        host, B+1 entries, or NULL (one row per request)
+ *   kv_indptr        host, B+1 entries, counts pages
+ *   kv_indices       host, num_indices entries (page ids in logical order)
+ *   kv_last_page_len host, B entries
+ *   kv_len_out       host, B entries, or NULL
+ * Returns PKV_OK or PKV_ERR_METADATA (reason via pkv_last_meta_reason()).
+ */
+pkv_status pkv_validate(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, int64_t num_indices,
+                        const int32_t* kv_last_page_len, int32_t batch_size,
+                        int32_t page_size, int32_t max_num_pages, int32_t num_qo_heads,
+                        int32_t num_kv_heads, int32_t decode, int32_t* kv_len_out);
+
+/*
+ * Host-side check of an append batch: the metadata is valid, every request
+ * appends at most kv_len tokens, and no two appended tokens map to the same
+ * (page, slot) (which would be a write race).  All pointers host.
+ */
+pkv_status pkv_validate_append(const int32_t* append_indptr, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, int64_t num_indices,
+                               const int32_t* kv_last_page_len, int32_t batch_size,
+                               int32_t page_size, int32_t max_num_pages);
+
+/*
+ * append_paged_kv: scatter a ragged batch of new K/V rows into the paged
+ * cache.  [KVL], FlashInfer API note under the MLA page layout: the caller
+ * allocates the pages before appending.  The metadata is post-append: kv_len
+ * already counts the new tokens ([DD] "Why inference attention becomes
+ * irregular"), so the n_b new rows of request b land at logical positions
+ * kv_len_b - n_b + t, i.e. page kv_indices[kv_indptr[b] + pos / page_size],
+ * slot pos % page_size.  The copy is bit-exact.
+ *   k_new, v_new      device, [nnz, num_kv_heads, head_dim] with the given
+ *                     token / head strides (elements), dtype of the cache
+ *   d_append_indptr   device, B+1 entries (new rows per request, prefix sums)
+ *   d_kv_indptr, d_kv_indices, d_kv_last_page_len   device page table
+ *   cache             host descriptor of the pools being written
+ * Asynchronous on `stream`.  Shapes are checked on the host; the metadata
+ * itself is read only on the device (use pkv_validate_append on the host
+ * copy to check it).  Rows whose request lookup fails are skipped.
+ */
+pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new_stride_token,
+                               int64_t new_stride_head, const int32_t* d_append_indptr,
+                               const int32_t* d_kv_indptr, const int32_t* d_kv_indices,
+                               const int32_t* d_kv_last_page_len, int32_t batch_size, int32_t nnz,
+                               const pkv_cache_desc* cache, void* stream);
+
+/* ------------------------------------------------------------------ plan -- */
+
+/*
+ * plan(): the inspector half of plan/run ([DD] "Plan then run:
+ * inspector-executor for GPU kernels"; [GAB] "FlashInfer: plan and run").
+ * Runs once per batch on the host, turns the metadata into a work list of
+ * (query tile, key chunk) items plus a merge list for split tiles, and copies
+ * them to the caller's device workspace with one asynchronous copy through
+ * the caller's pinned staging buffer.  Every layer of the batch then calls
+ * run() with the same plan.
+ *
+ * Split policy ([DD] "Load balancing and split-KV decisions" gives the
+ * trade-off, not an algorithm; this is our rule): chunk pages
+ * C = fixed_split_pages if > 0, else max(ceil(256/page_size), ceil(W/T)) with
+ * W = sum_b tiles_b * pages_b * heads_y and T = target_per_cu * num_cus.
+ * Chunks are page-aligned and disjoint; causal tiles drop chunks they cannot
+ * see.  Items run longest first.
+ */
+typedef struct pkv_plan pkv_plan;
+
+typedef struct pkv_plan_params {
+  int32_t mode;              /* pkv_mode */
+  int32_t batch_size;
+  int32_t num_qo_heads;      /* MLA: query heads */
+  int32_t num_kv_heads;      /* MLA: must be 1 */
+  int32_t head_dim_qk;       /* MLA: 576 (512 ckv + 64 kpe) */
+  int32_t head_dim_vo;       /* MLA: 512 */
+  int32_t page_size;
+  int32_t causal;            /* prefill: bottom-right causal mask ([DD] "Causality uses
+                                logical positions, not page numbers"); ignored by decode */
+  int32_t q_dtype;           /* pkv_dtype; must equal kv_dtype */
+  int32_t kv_dtype;
+  int32_t num_cus;           /* 0: query the current device */
+  int32_t fixed_split_pages; /* > 0 forces this chunk size in pages */
+  int32_t target_per_cu;     /* 0: default (decode 4, prefill 4, MLA 1) */
+  int32_t mla_head_groups;   /* MLA only; 0: default */
+  int32_t max_num_pages;     /* pool size, for the page-id range check */
+} pkv_plan_params;
+
+typedef struct pkv_plan_info {
+  int32_t mode;
+  int32_t batch_size;
+  int32_t num_items;         /* work items (each replicated over heads_y on the device) */
+  int32_t num_merges;
+  int32_t num_partial_rows;
+  int32_t chunk_pages;
+  int32_t split;             /* 1 if any tile is split over several chunks */
+  int32_t rows_per_tile;
+  int32_t heads_y;           /* kv heads (decode/prefill) or head groups (MLA) */
+  int32_t num_cus;
+  int32_t target;            /* target_per_cu * num_cus */
+  int32_t total_rows;        /* query rows (nnz) */
+  int64_t workspace_bytes;   /* device workspace this plan needs */
+  int64_t staging_bytes;     /* pinned staging this plan needs */
+  uint64_t fingerprint;      /* hash of params + metadata (staleness check) */
+} pkv_plan_info;
+
+/* Work item / merge item sizes in int32 words (layout documented in the
+ * planner source; exposed for pkv_plan_compute's output buffers). */
+#define PKV_ITEM_WORDS 8
+#define PKV_MERGE_WORDS 4
+
+/*
+ * Host-only planning pass (no HIP call unless params->num_cus == 0): fills
+ * info and, when the buffers are large enough, the work list
+ * (info.num_items * PKV_ITEM_WORDS int32) and merge list
+ * (info.num_merges * PKV_MERGE_WORDS int32).  Pass NULL buffers to query
+ * sizes.  kv_indices may be NULL (the page-id range check is then skipped).
+ * Returns PKV_ERR_WORKSPACE if a non-NULL buffer is too small.
+ */
+pkv_status pkv_plan_compute(const pkv_plan_params* params, const int32_t* qo_indptr,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int64_t num_indices, const int32_t* kv_last_page_len,
+                            int32_t* items_out, int64_t items_capacity, int32_t* merges_out,
+                            int64_t merges_capacity, pkv_plan_info* info);
+
+/*
+ * Build a plan and upload it.  Host arrays as for pkv_validate (qo_indptr
+ * NULL in decode/MLA modes).  d_workspace: device buffer of ws_bytes >=
+ * info.workspace_bytes; h_staging: pinned host buffer (hipHostMalloc) of
+ * staging_bytes >= info.staging_bytes, or NULL for a synchronous upload.  If
+ * the same staging buffer was used by an earlier plan, this call first waits
+ * for that plan's copy to finish ([GAB] "FlashInfer: plan and run": pinned
+ * staging is reused, so the previous copy must complete first).  The plan
+ * (host memory, owned by the library) stays valid only for this exact batch
+ * ([DD] "Plan then run"; a plan reused after the page table changes gives
+ * plausible output for the wrong sequence) and until pkv_plan_destroy.
+ */
+pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t num_indices, const int32_t* kv_last_page_len,
+                           void* d_workspace, size_t ws_bytes, void* h_staging,
+                           size_t staging_bytes, void* stream, pkv_plan** plan_out);
+
+pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info);
+
+/* PKV_OK if the metadata hashes to the plan's fingerprint, else
+ * PKV_ERR_STALE_PLAN.  Host arrays as for pkv_plan_create. */
+pkv_status pkv_plan_check(const pkv_plan* plan, const int32_t* qo_indptr,
+                          const int32_t* kv_indptr, const int32_t* kv_indices,
+                          int64_t num_indices, const int32_t* kv_last_page_len);
+
+pkv_status pkv_plan_destroy(pkv_plan* plan);
+
+/* ------------------------------------------------------------------- run -- */
+
+/*
+ * run(): the executor half.  For every query row i of request b and query
+ * head h, attention over the keys that row sees: key j with j < kv_len_b and,
+ * when causal, j <= kv_len_b - qo_len_b + i ([DD] "Causality uses logical
+ * positions, not page numbers").  Head h reads kv head h / (Hq/Hkv) ([DD]
+ * "Plan then run", GQA grouping).  Key j of request b lives at page
+ * kv_indices[kv_indptr[b] + j / page_size], slot j % page_size.
+ *   q      device [nnz, Hq, head_dim_qk], strides in elements, dtype of the plan
+ *   cache  host descriptor; must match the plan (page size, heads, dim, dtype)
+ *   d_kv_indices device page ids (the same values the plan was built on)
+ *   o      device [nnz, Hq, head_dim_vo], dtype of q, strides in elements
+ *   lse    device float [nnz, Hq] (contiguous), base-2, or NULL
+ *   sm_scale  logit scale; <= 0 selects 1/sqrt(head_dim_qk)
+ * Enqueues one attention kernel and, if the plan split any tile, one merge
+ * kernel on `stream`.  No host synchronisation, no allocation, no host copy.
+ */
+pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token,
+                   int64_t q_stride_head, const pkv_cache_desc* cache,
+                   const int32_t* d_kv_indices, void* o, int64_t o_stride_token,
+                   int64_t o_stride_head, float* lse, float sm_scale, void* stream);
+
+/*
+ * MLA decode run ([KVL] "多头潜在注意力页布局"): one latent row per token,
+ * ckv (512) and kpe (64), shared by every query head; score =
+ * sm_scale * (q_ckv . ckv + q_kpe . kpe); output = softmax-weighted ckv.
+ *   q_ckv  device bf16 [B, H, 512] contiguous;  q_kpe device bf16 [B, H, 64] contiguous
+ *   ckv    device bf16, element (page, slot, d) at ckv + page*page_stride + slot*token_stride + d
+ *   kpe    device bf16, same strides (zero-copy slices of one [pages, P, 576] tensor work)
+ *   o      device bf16 [B, H, 512] contiguous; lse device float [B, H] or NULL
+ *   sm_scale <= 0 selects 1/sqrt(576)
+ */
+pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kpe,
+                       const void* ckv, const void* kpe, int64_t page_stride,
+                       int64_t token_stride, const int32_t* d_kv_indices, void* o, float* lse,
+                       float sm_scale, void* stream);
+
+/* ----------------------------------------------------------------- merge -- */
+
+/*
+ * merge_state ([DD] "A worked split-KV example"): combine two attention
+ * states over disjoint key sets, per (row, head):
+ *   m = max(s_a, s_b); w_x = 2^(s_x - m); v = (w_a v_a + w_b v_b)/(w_a + w_b);
+ *   s = m + log2(w_a + w_b); a -inf side passes the other side through.
+ *   v_a, v_b, v_out  device [num_rows, num_heads, head_dim], dtype f32 or bf16
+ *   s_a, s_b, s_out  device float [num_rows, num_heads]
+ * v_out may alias v_a or v_b (and s_out s_a or s_b): each element is read
+ * before it is written by the same thread.
+ */
+pkv_status pkv_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                           void* v_out, float* s_out, int64_t num_rows, int32_t num_heads,
+                           int32_t head_dim, int32_t dtype, void* stream);
+
+/*
+ * Merge num_states states per (row, head) (associative in exact arithmetic,
+ * [DD] "Core mechanism: schedule work around state").
+ *   v      device [num_rows, num_states, num_heads, head_dim] (f32 or bf16)
+ *   s      device float [num_rows, num_states, num_heads]
+ *   v_out  device [num_rows, num_heads, head_dim] (dtype of v); s_out float [num_rows, num_heads]
+ * num_states == 0 yields the empty state (0, -inf).
+ */
+pkv_status pkv_merge_states(const void* v, const float* s, void* v_out, float* s_out,
+                            int64_t num_rows, int32_t num_states, int32_t num_heads,
+                            int32_t head_dim, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -77,6 +77,8 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     batch = len(kv_last_page_len)
     if qo_indptr is None:
         qo_indptr = list(range(batch + 1))
+    if mode != PREFILL:
+        causal = True        # a single decode row sees every key; diag = K - 1
     if target_per_cu <= 0:
         target_per_cu = DEFAULT_TARGET_PER_CU[mode]
     n_pages = [kv_indptr[b + 1] - kv_indptr[b] for b in range(batch)]

@@ -1,0 +1,736 @@
+// Host half of the paged KV-cache attention library: error state, metadata
+// validation, the planner (inspector) and the argument checking of run /
+// append / merge before their kernels are launched.
+//
+// Sources: "Deep Dive - FlashInfer" (length contract, causal rule, plan/run,
+// split-KV trade-offs), "FlashInfer 中的 KV-Cache 布局" (CSR page table,
+// NHD/HND, MLA cache), "GPU attention backends: FlashInfer and
+// FlashAttention" (plan once per batch, pinned staging reuse).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "internal.h"
+
+using pkv::Item;
+using pkv::MergeItem;
+
+namespace {
+
+thread_local std::string g_error;
+thread_local int32_t g_reason = PKV_META_NONE;
+
+pkv_status fail(pkv_status code, const std::string& msg, int32_t reason = PKV_META_NONE) {
+  g_error = msg;
+  g_reason = reason;
+  return code;
+}
+
+pkv_status meta_fail(int32_t reason, const std::string& msg) {
+  return fail(PKV_ERR_METADATA, msg, reason);
+}
+
+pkv_status ok() {
+  g_error.clear();
+  g_reason = PKV_META_NONE;
+  return PKV_OK;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b, c);
+  return buf;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+int page_shift_of(int32_t p) {
+  if (p <= 0 || (p & (p - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < p) ++s;
+  return s;
+}
+
+size_t dtype_size(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
+
+// ------------------------------------------------------------- validation --
+
+// Checks one indptr: starts at 0, never decreases.
+pkv_status check_indptr(const char* name, const int32_t* indptr, int32_t batch) {
+  if (indptr[0] != 0)
+    return meta_fail(PKV_META_INDPTR_START, std::string(name) + fmt("[0] = %lld, expected 0", indptr[0]));
+  for (int32_t i = 0; i < batch; ++i)
+    if (indptr[i + 1] < indptr[i])
+      return meta_fail(PKV_META_INDPTR_ORDER, std::string(name) + fmt(" decreases at %lld", i));
+  return PKV_OK;
+}
+
+// The rule order mirrors the statement of the metadata contract: batch, page
+// size, heads, qo_indptr, kv_indptr, index count, then per request its pages
+// and tail, then per request qo_len against kv_len.
+pkv_status validate_impl(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, int64_t num_indices,
+                         const int32_t* last, int32_t batch, int32_t page_size,
+                         int32_t max_num_pages, int32_t hq, int32_t hkv, bool decode,
+                         std::vector<int32_t>* kv_len_out) {
+  if (batch < 0) return meta_fail(PKV_META_BATCH_SIZE, "negative batch size");
+  if (page_size < 1) return meta_fail(PKV_META_PAGE_SIZE, fmt("page_size %lld < 1", page_size));
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return meta_fail(PKV_META_HEAD_GROUP, fmt("%lld qo heads do not group over %lld kv heads", hq, hkv));
+  if (!kv_indptr || (batch > 0 && !last)) return fail(PKV_ERR_INVALID_ARG, "null metadata pointer");
+  if (qo_indptr) {
+    pkv_status s = check_indptr("qo_indptr", qo_indptr, batch);
+    if (s) return s;
+  }
+  pkv_status s = check_indptr("kv_indptr", kv_indptr, batch);
+  if (s) return s;
+  if (kv_indices && kv_indptr[batch] > num_indices)
+    return meta_fail(PKV_META_INDICES_LENGTH,
+                     fmt("kv_indptr[B] = %lld > %lld indices", kv_indptr[batch], num_indices));
+  if (kv_len_out) kv_len_out->assign(batch, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = kv_indptr[b + 1] - kv_indptr[b];
+    if (n < 1) return meta_fail(PKV_META_EMPTY_PAGE_LIST, fmt("request %lld owns no page", b));
+    if (kv_indices) {
+      for (int32_t i = kv_indptr[b]; i < kv_indptr[b + 1]; ++i) {
+        const int32_t p = kv_indices[i];
+        if (p < 0 || p >= max_num_pages)
+          return meta_fail(PKV_META_PAGE_INDEX,
+                           fmt("request %lld: page %lld outside [0, %lld)", b, p, max_num_pages));
+      }
+    }
+    if (last[b] < 1 || last[b] > page_size)
+      return meta_fail(PKV_META_LAST_PAGE_LEN,
+                       fmt("request %lld: tail %lld outside 1..%lld", b, last[b], page_size));
+    const int64_t len = int64_t(page_size) * (n - 1) + last[b];
+    if (len > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, fmt("request %lld: kv_len overflows int32", b));
+    if (kv_len_out) (*kv_len_out)[b] = int32_t(len);
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t q = qo_indptr ? int64_t(qo_indptr[b + 1]) - qo_indptr[b] : 1;
+    const int64_t len = int64_t(page_size) * (kv_indptr[b + 1] - kv_indptr[b] - 1) + last[b];
+    if (decode && q != 1)
+      return meta_fail(PKV_META_DECODE_QO_LEN, fmt("request %lld: decode needs qo_len 1, got %lld", b, q));
+    if (q > len)
+      return meta_fail(PKV_META_QO_EXCEEDS_KV, fmt("request %lld: qo_len %lld > kv_len %lld", b, q, len));
+  }
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------- planner --
+
+constexpr int32_t kMinSplitTokens = 256;
+constexpr int32_t kMfmaTileRows = 128;   // prefill tile height in (row, head) pairs
+
+int32_t default_target(int32_t mode) { return mode == PKV_MODE_MLA_DECODE ? 1 : 4; }
+constexpr int32_t kMlaHeadsPerGroup = 32;   // the MLA kernel's head-group width
+
+int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype) {
+  if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32) return 1;
+  return std::max<int32_t>(1, kMfmaTileRows / group);
+}
+
+struct PlanResult {
+  std::vector<Item> items;
+  std::vector<MergeItem> merges;
+  pkv_plan_info info;
+};
+
+uint64_t fnv1a(uint64_t h, const void* data, size_t bytes) {
+  const unsigned char* p = static_cast<const unsigned char*>(data);
+  for (size_t i = 0; i < bytes; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+uint64_t fingerprint(const pkv_plan_params& prm, const int32_t* qo, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, int64_t num_indices, const int32_t* last) {
+  uint64_t h = 1469598103934665603ull;
+  h = fnv1a(h, &prm, sizeof prm);
+  const int32_t b = prm.batch_size;
+  if (qo) h = fnv1a(h, qo, sizeof(int32_t) * (b + 1));
+  h = fnv1a(h, kv_indptr, sizeof(int32_t) * (b + 1));
+  if (b > 0) h = fnv1a(h, last, sizeof(int32_t) * b);
+  if (kv_indices) {
+    const int64_t n = std::min<int64_t>(num_indices, kv_indptr[b]);
+    h = fnv1a(h, kv_indices, sizeof(int32_t) * n);
+  }
+  return h;
+}
+
+pkv_status check_params(const pkv_plan_params* p) {
+  if (!p) return fail(PKV_ERR_INVALID_ARG, "null params");
+  if (p->mode < PKV_MODE_DECODE || p->mode > PKV_MODE_MLA_DECODE)
+    return fail(PKV_ERR_INVALID_ARG, fmt("unknown mode %lld", p->mode));
+  if (p->q_dtype != p->kv_dtype)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must equal kv_dtype");
+  if (p->kv_dtype != PKV_F32 && p->kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, fmt("dtype %lld", p->kv_dtype));
+  if (p->head_dim_qk < 1 || p->head_dim_vo < 1) return fail(PKV_ERR_INVALID_ARG, "head dims must be >= 1");
+  if (p->mode == PKV_MODE_MLA_DECODE) {
+    if (p->num_kv_heads != 1 || p->head_dim_qk != 576 || p->head_dim_vo != 512 || p->kv_dtype != PKV_BF16)
+      return fail(PKV_ERR_UNSUPPORTED, "MLA decode needs 1 kv head, dims 576/512, bf16");
+  } else if (p->head_dim_qk != p->head_dim_vo) {
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim_qk must equal head_dim_vo outside MLA");
+  }
+  if (p->fixed_split_pages < 0 || p->target_per_cu < 0 || p->mla_head_groups < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative planner knob");
+  return PKV_OK;
+}
+
+pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                     const int32_t* kv_indices, int64_t num_indices, const int32_t* last,
+                     PlanResult* out) {
+  pkv_status s = check_params(prm);
+  if (s) return s;
+  const bool prefill = prm->mode == PKV_MODE_PREFILL;
+  const bool mla = prm->mode == PKV_MODE_MLA_DECODE;
+  if (!prefill && qo_indptr) return fail(PKV_ERR_INVALID_ARG, "decode modes take no qo_indptr");
+  if (prefill && !qo_indptr) return fail(PKV_ERR_INVALID_ARG, "prefill needs qo_indptr");
+  const int32_t batch = prm->batch_size;
+  const int32_t max_pages = prm->max_num_pages > 0 ? prm->max_num_pages : INT32_MAX;
+  std::vector<int32_t> kv_len;
+  s = validate_impl(qo_indptr, kv_indptr, kv_indices, num_indices, last, batch, prm->page_size,
+                    max_pages, prm->num_qo_heads, prm->num_kv_heads, !prefill, &kv_len);
+  if (s) return s;
+
+  int32_t num_cus = prm->num_cus;
+  if (num_cus <= 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
+  }
+  const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
+  const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype);
+  int32_t heads_y = prm->num_kv_heads;
+  if (mla) {
+    heads_y = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
+    if (heads_y < 1 || prm->num_qo_heads != heads_y * kMlaHeadsPerGroup)
+      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 32 heads");
+  }
+  const int32_t target_per_cu = prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode);
+  const bool causal = prefill ? prm->causal != 0 : true;
+
+  // Step 1-3: tiles, page work, chunk size.
+  std::vector<int64_t> q_len(batch), n_pages(batch), tiles(batch);
+  int64_t work = 0;
+  int64_t total_rows = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    q_len[b] = prefill ? int64_t(qo_indptr[b + 1]) - qo_indptr[b] : 1;
+    n_pages[b] = kv_indptr[b + 1] - kv_indptr[b];
+    tiles[b] = cdiv(q_len[b], rows);
+    work += tiles[b] * n_pages[b] * heads_y;
+    total_rows += q_len[b];
+  }
+  const int64_t target = int64_t(target_per_cu) * num_cus;
+  int64_t chunk = prm->fixed_split_pages > 0
+                      ? prm->fixed_split_pages
+                      : std::max<int64_t>(cdiv(kMinSplitTokens, prm->page_size), cdiv(work, target));
+  const int64_t chunk_tokens = chunk * prm->page_size;
+
+  // Step 4-6: chunks per tile, causal pruning, partial-row assignment.
+  struct Raw {
+    int64_t cost;
+    int32_t b, t, c;
+    Item it;
+  };
+  std::vector<Raw> raw;
+  out->merges.clear();
+  int64_t slot = 0;
+  bool split_any = false;
+  std::vector<std::pair<int32_t, int32_t>> kept;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t k = kv_len[b];
+    for (int64_t t = 0; t < tiles[b]; ++t) {
+      const int64_t l0 = t * rows;
+      const int64_t n_rows = std::min<int64_t>(rows, q_len[b] - l0);
+      const int64_t diag = causal ? k - q_len[b] + l0 : k;
+      const int64_t limit = std::min<int64_t>(k, diag + n_rows);
+      kept.clear();
+      const int64_t n_chunks = cdiv(n_pages[b], chunk);
+      for (int64_t c = 0; c < n_chunks; ++c) {
+        const int64_t lo = c * chunk_tokens;
+        if (lo >= limit) break;
+        const int64_t hi = std::min<int64_t>(std::min<int64_t>(lo + chunk_tokens, k), limit);
+        kept.emplace_back(int32_t(lo), int32_t(hi));
+      }
+      const int32_t q_row0 = int32_t((prefill ? qo_indptr[b] : b) + l0);
+      if (kept.size() == 1) {
+        Item it{q_row0, int32_t(n_rows), kept[0].first, kept[0].second, int32_t(diag), kv_indptr[b], -1, b};
+        raw.push_back({int64_t(kept[0].second - kept[0].first) * n_rows, b, int32_t(t), 0, it});
+        continue;
+      }
+      split_any = true;
+      if (slot + int64_t(kept.size()) * n_rows > INT32_MAX)
+        return fail(PKV_ERR_INVALID_ARG, "too many partial rows");
+      out->merges.push_back({q_row0, int32_t(n_rows), int32_t(slot), int32_t(kept.size())});
+      for (size_t ci = 0; ci < kept.size(); ++ci) {
+        Item it{q_row0, int32_t(n_rows), kept[ci].first, kept[ci].second, int32_t(diag), kv_indptr[b],
+                int32_t(slot + int64_t(ci) * n_rows), b};
+        raw.push_back({int64_t(kept[ci].second - kept[ci].first) * n_rows, b, int32_t(t), int32_t(ci), it});
+      }
+      slot += int64_t(kept.size()) * n_rows;
+    }
+  }
+  // Step 7: longest first; (b, t, c) breaks ties, so the order is unique.
+  std::sort(raw.begin(), raw.end(), [](const Raw& x, const Raw& y) {
+    if (x.cost != y.cost) return x.cost > y.cost;
+    if (x.b != y.b) return x.b < y.b;
+    if (x.t != y.t) return x.t < y.t;
+    return x.c < y.c;
+  });
+  if (raw.size() > size_t(INT32_MAX)) return fail(PKV_ERR_INVALID_ARG, "too many work items");
+  out->items.resize(raw.size());
+  for (size_t i = 0; i < raw.size(); ++i) out->items[i] = raw[i].it;
+
+  pkv_plan_info& in = out->info;
+  std::memset(&in, 0, sizeof in);
+  in.mode = prm->mode;
+  in.batch_size = batch;
+  in.num_items = int32_t(out->items.size());
+  in.num_merges = int32_t(out->merges.size());
+  in.num_partial_rows = int32_t(slot);
+  in.chunk_pages = int32_t(std::min<int64_t>(chunk, INT32_MAX));
+  in.split = split_any ? 1 : 0;
+  in.rows_per_tile = rows;
+  in.heads_y = heads_y;
+  in.num_cus = num_cus;
+  in.target = int32_t(std::min<int64_t>(target, INT32_MAX));
+  in.total_rows = int32_t(total_rows);
+  const int64_t hq = prm->num_qo_heads;
+  const int64_t staging = align256(int64_t(out->items.size()) * sizeof(Item)) +
+                          align256(int64_t(out->merges.size()) * sizeof(MergeItem));
+  in.staging_bytes = staging;
+  in.workspace_bytes = staging + align256(slot * hq * 4) + align256(slot * hq * prm->head_dim_vo * 4);
+  in.fingerprint = fingerprint(*prm, qo_indptr, kv_indptr, kv_indices, num_indices, last);
+  return PKV_OK;
+}
+
+// Pinned staging buffers remember the event of the last upload made from
+// them, so a later plan does not overwrite bytes still being copied.
+std::mutex g_staging_mu;
+std::unordered_map<void*, hipEvent_t> g_staging_events;
+
+}  // namespace
+
+struct pkv_plan {
+  pkv_plan_params params;
+  pkv_plan_info info;
+  Item* d_items;
+  MergeItem* d_merges;
+  float* d_part_lse;
+  float* d_part_o;
+  int device;
+};
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+const char* pkv_last_error(void) { return g_error.c_str(); }
+int32_t pkv_last_meta_reason(void) { return g_reason; }
+
+pkv_status pkv_device_num_cus(int32_t* out) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "null output");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  return ok();
+}
+
+pkv_status pkv_validate(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                        int64_t num_indices, const int32_t* kv_last_page_len, int32_t batch_size,
+                        int32_t page_size, int32_t max_num_pages, int32_t num_qo_heads,
+                        int32_t num_kv_heads, int32_t decode, int32_t* kv_len_out) {
+  std::vector<int32_t> lens;
+  pkv_status s = validate_impl(qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len,
+                               batch_size, page_size, max_num_pages, num_qo_heads, num_kv_heads,
+                               decode != 0, &lens);
+  if (s) return s;
+  if (kv_len_out) std::copy(lens.begin(), lens.end(), kv_len_out);
+  return ok();
+}
+
+pkv_status pkv_validate_append(const int32_t* append_indptr, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, int64_t num_indices,
+                               const int32_t* kv_last_page_len, int32_t batch_size, int32_t page_size,
+                               int32_t max_num_pages) {
+  if (!append_indptr || !kv_indices) return fail(PKV_ERR_INVALID_ARG, "null metadata pointer");
+  std::vector<int32_t> lens;
+  pkv_status s = validate_impl(append_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len,
+                               batch_size, page_size, max_num_pages, 1, 1, false, &lens);
+  if (s) return s;
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < batch_size; ++b) {
+    const int32_t n = append_indptr[b + 1] - append_indptr[b];
+    for (int32_t t = 0; t < n; ++t) {
+      const int64_t pos = int64_t(lens[b]) - n + t;
+      const int64_t page = kv_indices[kv_indptr[b] + pos / page_size];
+      const int64_t key = page * page_size + pos % page_size;
+      if (!seen.insert(key).second)
+        return meta_fail(PKV_META_APPEND_COLLISION,
+                         fmt("page %lld slot %lld written twice", page, pos % page_size));
+    }
+  }
+  return ok();
+}
+
+pkv_status pkv_plan_compute(const pkv_plan_params* params, const int32_t* qo_indptr,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, int64_t num_indices,
+                            const int32_t* kv_last_page_len, int32_t* items_out, int64_t items_capacity,
+                            int32_t* merges_out, int64_t merges_capacity, pkv_plan_info* info) {
+  PlanResult r;
+  pkv_status s = plan_impl(params, qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len, &r);
+  if (s) return s;
+  if (info) *info = r.info;
+  if (items_out) {
+    if (items_capacity < int64_t(r.items.size()) * PKV_ITEM_WORDS)
+      return fail(PKV_ERR_WORKSPACE, "work-item buffer too small");
+    std::memcpy(items_out, r.items.data(), r.items.size() * sizeof(Item));
+  }
+  if (merges_out) {
+    if (merges_capacity < int64_t(r.merges.size()) * PKV_MERGE_WORDS)
+      return fail(PKV_ERR_WORKSPACE, "merge buffer too small");
+    std::memcpy(merges_out, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+  }
+  return ok();
+}
+
+pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, int64_t num_indices,
+                           const int32_t* kv_last_page_len, void* d_workspace, size_t ws_bytes,
+                           void* h_staging, size_t staging_bytes, void* stream, pkv_plan** plan_out) {
+  if (!plan_out) return fail(PKV_ERR_INVALID_ARG, "null plan_out");
+  *plan_out = nullptr;
+  PlanResult r;
+  pkv_status s = plan_impl(params, qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len, &r);
+  if (s) return s;
+  const pkv_plan_info& in = r.info;
+  if (in.workspace_bytes > 0 && (!d_workspace || int64_t(ws_bytes) < in.workspace_bytes))
+    return fail(PKV_ERR_WORKSPACE, fmt("workspace %lld bytes < %lld needed", int64_t(ws_bytes),
+                                       in.workspace_bytes));
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (h_staging && int64_t(staging_bytes) < in.staging_bytes)
+    return fail(PKV_ERR_WORKSPACE, fmt("staging %lld bytes < %lld needed", int64_t(staging_bytes),
+                                       in.staging_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(d_workspace);
+  const int64_t items_bytes = align256(int64_t(r.items.size()) * sizeof(Item));
+  const int64_t merges_bytes = align256(int64_t(r.merges.size()) * sizeof(MergeItem));
+  const int64_t lse_bytes = align256(int64_t(in.num_partial_rows) * params->num_qo_heads * 4);
+
+  pkv_plan* plan = new pkv_plan;
+  plan->params = *params;
+  plan->info = in;
+  plan->d_items = reinterpret_cast<Item*>(ws);
+  plan->d_merges = reinterpret_cast<MergeItem*>(ws + items_bytes);
+  plan->d_part_lse = reinterpret_cast<float*>(ws + items_bytes + merges_bytes);
+  plan->d_part_o = reinterpret_cast<float*>(ws + items_bytes + merges_bytes + lse_bytes);
+  hipError_t e = hipGetDevice(&plan->device);
+  if (e != hipSuccess) {
+    delete plan;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (in.staging_bytes > 0) {
+    if (h_staging) {
+      std::lock_guard<std::mutex> lock(g_staging_mu);
+      auto it = g_staging_events.find(h_staging);
+      if (it == g_staging_events.end()) {
+        hipEvent_t ev;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+          delete plan;
+          return hip_fail(e, "hipEventCreate");
+        }
+        it = g_staging_events.emplace(h_staging, ev).first;
+      } else {
+        e = hipEventSynchronize(it->second);   // the previous upload from this buffer
+        if (e != hipSuccess) {
+          delete plan;
+          return hip_fail(e, "waiting for the previous plan upload");
+        }
+      }
+      char* hs = static_cast<char*>(h_staging);
+      std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
+      std::memcpy(hs + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+      e = hipMemcpyAsync(ws, hs, size_t(in.staging_bytes), hipMemcpyHostToDevice, st);
+      if (e == hipSuccess) e = hipEventRecord(it->second, st);
+    } else {
+      std::vector<char> tmp(size_t(in.staging_bytes), 0);
+      std::memcpy(tmp.data(), r.items.data(), r.items.size() * sizeof(Item));
+      std::memcpy(tmp.data() + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+      e = hipMemcpyAsync(ws, tmp.data(), tmp.size(), hipMemcpyHostToDevice, st);
+      if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
+    if (e != hipSuccess) {
+      delete plan;
+      return hip_fail(e, "uploading the plan");
+    }
+  }
+  if (const char* lg = std::getenv("PKV_LOG")) {
+    if (lg[0] == '1')
+      std::fprintf(stderr, "[pkv] plan mode=%d B=%d items=%d merges=%d chunk_pages=%d split=%d ws=%lld\n",
+                   in.mode, in.batch_size, in.num_items, in.num_merges, in.chunk_pages, in.split,
+                   (long long)in.workspace_bytes);
+  }
+  *plan_out = plan;
+  return ok();
+}
+
+pkv_status pkv_plan_get_info(const pkv_plan* plan, pkv_plan_info* info) {
+  if (!plan || !info) return fail(PKV_ERR_INVALID_ARG, "null argument");
+  *info = plan->info;
+  return ok();
+}
+
+pkv_status pkv_plan_check(const pkv_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, int64_t num_indices,
+                          const int32_t* kv_last_page_len) {
+  if (!plan || !kv_indptr) return fail(PKV_ERR_INVALID_ARG, "null argument");
+  const uint64_t h = fingerprint(plan->params, qo_indptr, kv_indptr, kv_indices, num_indices,
+                                 kv_last_page_len);
+  if (h != plan->info.fingerprint)
+    return fail(PKV_ERR_STALE_PLAN, "metadata differs from the batch the plan was built for");
+  return ok();
+}
+
+pkv_status pkv_plan_destroy(pkv_plan* plan) {
+  delete plan;
+  return ok();
+}
+
+// ------------------------------------------------------------------- run --
+
+static pkv_status check_ptr16(const void* p, const char* what) {
+  if (!p) return fail(PKV_ERR_INVALID_ARG, std::string("null ") + what);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, std::string(what) + " must be 16-byte aligned");
+  return PKV_OK;
+}
+
+static bool stride_ok(int64_t stride, size_t esize) { return stride >= 0 && (stride * int64_t(esize)) % 16 == 0; }
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                   const pkv_cache_desc* cache, const int32_t* d_kv_indices, void* o,
+                   int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                   void* stream) {
+  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
+  const pkv_plan_params& p = plan->params;
+  if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
+  if (cache->page_size != p.page_size || cache->num_kv_heads != p.num_kv_heads ||
+      cache->head_dim != p.head_dim_qk || cache->dtype != p.kv_dtype)
+    return fail(PKV_ERR_INVALID_ARG, "cache descriptor does not match the plan");
+  if (p.max_num_pages > 0 && cache->max_num_pages != p.max_num_pages)
+    return fail(PKV_ERR_INVALID_ARG, "cache page count does not match the plan");
+  const size_t es = dtype_size(p.kv_dtype);
+  pkv_status s;
+  if ((s = check_ptr16(q, "q")) || (s = check_ptr16(o, "o")) || (s = check_ptr16(cache->k, "cache k")) ||
+      (s = check_ptr16(cache->v, "cache v")))
+    return s;
+  if (!d_kv_indices && plan->info.num_items > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
+  if (!stride_ok(q_stride_token, es) || !stride_ok(q_stride_head, es) || !stride_ok(o_stride_token, es) ||
+      !stride_ok(o_stride_head, es) || !stride_ok(cache->page_stride, es) ||
+      !stride_ok(cache->token_stride, es) || !stride_ok(cache->head_stride, es))
+    return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(PKV_ERR_INVALID_ARG, "plan was built on another device");
+  if (plan->info.num_items == 0) return ok();
+
+  pkv::AttnArgs a;
+  a.items = plan->d_items;
+  a.num_items = plan->info.num_items;
+  a.num_kv_heads = p.num_kv_heads;
+  a.num_qo_heads = p.num_qo_heads;
+  a.q = q;
+  a.q_stride_token = q_stride_token;
+  a.q_stride_head = q_stride_head;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.page_stride = cache->page_stride;
+  a.token_stride = cache->token_stride;
+  a.head_stride = cache->head_stride;
+  a.page_size = cache->page_size;
+  a.page_shift = page_shift_of(cache->page_size);
+  a.max_num_pages = cache->max_num_pages;
+  a.kv_indices = d_kv_indices;
+  a.o = o;
+  a.o_stride_token = o_stride_token;
+  a.o_stride_head = o_stride_head;
+  a.lse = lse;
+  a.part_o = plan->d_part_o;
+  a.part_lse = plan->d_part_lse;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(p.head_dim_qk));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const int32_t group = p.num_qo_heads / p.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bool supported = false;
+  hipError_t e;
+  if (p.mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
+    e = pkv::launch_prefill_mfma(p.head_dim_qk, group, a, st, &supported);
+  else
+    e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
+  if (!supported)
+    return fail(PKV_ERR_UNSUPPORTED, fmt("no kernel for head_dim %lld, group %lld, dtype %lld",
+                                         p.head_dim_qk, group, p.kv_dtype));
+  if (e != hipSuccess) return hip_fail(e, "launching attention");
+  if (plan->info.num_merges > 0) {
+    pkv::MergePartialArgs m;
+    m.merges = plan->d_merges;
+    m.num_merges = plan->info.num_merges;
+    m.num_heads = p.num_qo_heads;
+    m.head_dim = p.head_dim_vo;
+    m.part_o = plan->d_part_o;
+    m.part_lse = plan->d_part_lse;
+    m.o = o;
+    m.o_stride_token = o_stride_token;
+    m.o_stride_head = o_stride_head;
+    m.lse = lse;
+    e = pkv::launch_merge_partials(p.kv_dtype, m, st);
+    if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+  }
+  return ok();
+}
+
+pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kpe, const void* ckv,
+                       const void* kpe, int64_t page_stride, int64_t token_stride,
+                       const int32_t* d_kv_indices, void* o, float* lse, float sm_scale, void* stream) {
+  if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
+  const pkv_plan_params& p = plan->params;
+  if (p.mode != PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "not an MLA plan");
+  pkv_status s;
+  if ((s = check_ptr16(q_ckv, "q_ckv")) || (s = check_ptr16(q_kpe, "q_kpe")) || (s = check_ptr16(ckv, "ckv")) ||
+      (s = check_ptr16(kpe, "kpe")) || (s = check_ptr16(o, "o")))
+    return s;
+  if (!stride_ok(page_stride, 2) || !stride_ok(token_stride, 2))
+    return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (!d_kv_indices && plan->info.num_items > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+    return fail(PKV_ERR_INVALID_ARG, "plan was built on another device");
+  if (plan->info.num_items == 0) return ok();
+  pkv::MlaArgs a;
+  a.items = plan->d_items;
+  a.num_items = plan->info.num_items;
+  a.num_heads = p.num_qo_heads;
+  a.head_groups = plan->info.heads_y;
+  a.q_ckv = q_ckv;
+  a.q_kpe = q_kpe;
+  a.ckv = ckv;
+  a.kpe = kpe;
+  a.page_stride = page_stride;
+  a.token_stride = token_stride;
+  a.page_size = p.page_size;
+  a.page_shift = page_shift_of(p.page_size);
+  a.max_num_pages = p.max_num_pages > 0 ? p.max_num_pages : INT32_MAX;
+  a.kv_indices = d_kv_indices;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = plan->d_part_o;
+  a.part_lse = plan->d_part_lse;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(576.0f);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_mla_decode(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching MLA decode");
+  if (plan->info.num_merges > 0) {
+    pkv::MergePartialArgs m;
+    m.merges = plan->d_merges;
+    m.num_merges = plan->info.num_merges;
+    m.num_heads = p.num_qo_heads;
+    m.head_dim = 512;
+    m.part_o = plan->d_part_o;
+    m.part_lse = plan->d_part_lse;
+    m.o = o;
+    m.o_stride_token = int64_t(p.num_qo_heads) * 512;
+    m.o_stride_head = 512;
+    m.lse = lse;
+    e = pkv::launch_merge_partials(PKV_BF16, m, st);
+    if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+  }
+  return ok();
+}
+
+// --------------------------------------------------------- append, merge --
+
+pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new_stride_token,
+                               int64_t new_stride_head, const int32_t* d_append_indptr,
+                               const int32_t* d_kv_indptr, const int32_t* d_kv_indices,
+                               const int32_t* d_kv_last_page_len, int32_t batch_size, int32_t nnz,
+                               const pkv_cache_desc* cache, void* stream) {
+  if (!cache) return fail(PKV_ERR_INVALID_ARG, "null cache");
+  if (batch_size < 0 || nnz < 0) return fail(PKV_ERR_INVALID_ARG, "negative batch or nnz");
+  if (nnz == 0) return ok();
+  if (cache->dtype != PKV_F32 && cache->dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "cache dtype");
+  if (cache->page_size < 1 || cache->num_kv_heads < 1 || cache->head_dim < 1)
+    return fail(PKV_ERR_INVALID_ARG, "cache shape");
+  const size_t es = dtype_size(cache->dtype);
+  pkv_status s;
+  if ((s = check_ptr16(k_new, "k_new")) || (s = check_ptr16(v_new, "v_new")) ||
+      (s = check_ptr16(cache->k, "cache k")) || (s = check_ptr16(cache->v, "cache v")))
+    return s;
+  if (!d_append_indptr || !d_kv_indptr || !d_kv_indices || !d_kv_last_page_len || batch_size == 0)
+    return fail(PKV_ERR_INVALID_ARG, "null metadata pointer or empty batch");
+  if ((cache->head_dim * es) % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "head_dim * dtype size must be a multiple of 16 bytes");
+  if (!stride_ok(new_stride_token, es) || !stride_ok(new_stride_head, es) || !stride_ok(cache->page_stride, es) ||
+      !stride_ok(cache->token_stride, es) || !stride_ok(cache->head_stride, es))
+    return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  hipError_t e = pkv::launch_append(cache->dtype, k_new, v_new, new_stride_token, new_stride_head,
+                                    d_append_indptr, d_kv_indptr, d_kv_indices, d_kv_last_page_len,
+                                    batch_size, nnz, cache->k, cache->v, cache->page_stride,
+                                    cache->token_stride, cache->head_stride, cache->page_size,
+                                    cache->num_kv_heads, cache->head_dim, cache->max_num_pages,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching append");
+  return ok();
+}
+
+pkv_status pkv_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b, void* v_out,
+                           float* s_out, int64_t num_rows, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                           void* stream) {
+  if (num_rows < 0 || num_heads < 0 || head_dim < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype");
+  if (num_rows == 0 || num_heads == 0 || head_dim == 0) return ok();
+  if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  hipError_t e = pkv::launch_merge_pair(dtype, v_a, s_a, v_b, s_b, v_out, s_out, num_rows, num_heads, head_dim,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching merge_state");
+  return ok();
+}
+
+pkv_status pkv_merge_states(const void* v, const float* s, void* v_out, float* s_out, int64_t num_rows,
+                            int32_t num_states, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                            void* stream) {
+  if (num_rows < 0 || num_states < 0 || num_heads < 0 || head_dim < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype");
+  if (num_rows == 0 || num_heads == 0 || head_dim == 0) return ok();
+  if (!v_out || !s_out || (num_states > 0 && (!v || !s))) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  hipError_t e = pkv::launch_merge_many(dtype, v, s, v_out, s_out, num_rows, num_states, num_heads, head_dim,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching merge_states");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the host library and the HIP kernels.
+// Not part of the C ABI (include/pkv.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// One unit of attention work: a tile of query rows of one request against one
+// chunk of its keys.  The device replicates it over kv heads (or MLA head
+// groups).  Row r of the tile sees key j when kv_start <= j < kv_end and
+// j <= diag + r.
+struct Item {
+  int32_t q_row0;     // first global query row
+  int32_t num_rows;   // rows in the tile
+  int32_t kv_start;   // first key of the chunk
+  int32_t kv_end;     // one past the last key any row of the tile sees in the chunk
+  int32_t diag;       // causal limit of the tile's first row
+  int32_t page_base;  // kv_indptr[b]
+  int32_t out_slot;   // -1: final output; else first partial row
+  int32_t batch;      // request index
+};
+static_assert(sizeof(Item) == 32, "work item is eight int32");
+
+// One split tile: its chunks' partial states are rows slot0 + c*num_rows + r.
+struct MergeItem {
+  int32_t q_row0;
+  int32_t num_rows;
+  int32_t slot0;
+  int32_t num_chunks;
+};
+static_assert(sizeof(MergeItem) == 16, "merge item is four int32");
+
+enum DType : int32_t { kF32 = 0, kBF16 = 1 };
+
+struct AttnArgs {
+  const Item* items;
+  int32_t num_items;
+  int32_t num_kv_heads;
+  int32_t num_qo_heads;
+  const void* q;
+  int64_t q_stride_token, q_stride_head;
+  const void* k;
+  const void* v;
+  int64_t page_stride, token_stride, head_stride;
+  int32_t page_size;
+  int32_t page_shift;  // log2(page_size) if a power of two, else -1
+  int32_t max_num_pages;  // page ids outside [0, max_num_pages) are never dereferenced
+  const int32_t* kv_indices;
+  void* o;
+  int64_t o_stride_token, o_stride_head;
+  float* lse;          // [rows, Hq] or null
+  float* part_o;       // [partial rows, Hq, Dvo]
+  float* part_lse;     // [partial rows, Hq]
+  float scale_log2;    // sm_scale * log2(e)
+};
+
+struct MergePartialArgs {
+  const MergeItem* merges;
+  int32_t num_merges;
+  int32_t num_heads;
+  int32_t head_dim;
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  int64_t o_stride_token, o_stride_head;
+  float* lse;
+};
+
+struct MlaArgs {
+  const Item* items;
+  int32_t num_items;
+  int32_t num_heads;
+  int32_t head_groups;
+  const void* q_ckv;   // [B, H, 512]
+  const void* q_kpe;   // [B, H, 64]
+  const void* ckv;
+  const void* kpe;
+  int64_t page_stride, token_stride;
+  int32_t page_size;
+  int32_t page_shift;
+  int32_t max_num_pages;
+  const int32_t* kv_indices;
+  void* o;             // [B, H, 512]
+  float* lse;          // [B, H] or null
+  float* part_o;       // [partial rows, H, 512]
+  float* part_lse;     // [partial rows, H]
+  float scale_log2;
+};
+
+// Kernel launchers (each returns the launch error, if any).
+hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
+                            hipStream_t stream, bool* supported);
+hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& a, hipStream_t stream,
+                               bool* supported);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t stream);
+hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st,
+                         int64_t new_sh, const int32_t* append_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, const int32_t* last_page_len, int32_t batch,
+                         int32_t nnz, void* k, void* v, int64_t page_stride, int64_t token_stride,
+                         int64_t head_stride, int32_t page_size, int32_t num_heads, int32_t head_dim,
+                         int32_t max_num_pages, hipStream_t stream);
+hipError_t launch_merge_pair(int32_t dtype, const void* va, const float* sa, const void* vb,
+                             const float* sb, void* vo, float* so, int64_t rows, int32_t heads,
+                             int32_t dim, hipStream_t stream);
+hipError_t launch_merge_many(int32_t dtype, const void* v, const float* s, void* vo, float* so,
+                             int64_t rows, int32_t states, int32_t heads, int32_t dim,
+                             hipStream_t stream);
+
+}  // namespace pkv

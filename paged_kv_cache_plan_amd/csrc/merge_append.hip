@@ -1,0 +1,217 @@
+// Append (ragged -> paged scatter) and the attention-state merges.
+//
+// append_paged_kv: "FlashInfer 中的 KV-Cache 布局", FlashInfer API note under
+// the MLA page layout (pages are allocated by the caller first); the new rows
+// are the last n_b logical positions of each request because kv_len already
+// counts them ("Deep Dive - FlashInfer", "Why inference attention becomes
+// irregular").  A bit-exact copy, bound by HBM bandwidth.
+//
+// Merges: "Deep Dive - FlashInfer", "A worked split-KV example": shift by the
+// largest base-2 statistic, normalise the weights 2^(s - shift) to scales,
+// combine, and keep shift + log2(sum); an empty state (-inf) contributes
+// nothing and two empty states stay empty.
+
+#include "device.h"
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+// One workgroup per appended token: find its request by binary search over
+// append_indptr, locate (page, slot), copy K and V rows in 16-byte chunks.
+__global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new, int64_t new_st_b,
+                                                     int64_t new_sh_b, const int32_t* append_indptr,
+                                                     const int32_t* kv_indptr, const int32_t* kv_indices,
+                                                     const int32_t* last, int32_t batch, char* k, char* v,
+                                                     int64_t page_b, int64_t tok_b, int64_t head_b,
+                                                     int32_t page_size, int32_t heads, int32_t row_chunks,
+                                                     int32_t max_pages) {
+  const int32_t t = blockIdx.x;
+  if (t >= append_indptr[batch]) return;
+  int32_t lo = 0, hi = batch - 1;   // last request b with append_indptr[b] <= t
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (append_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int32_t b = lo;
+  const int32_t n_new = append_indptr[b + 1] - append_indptr[b];
+  const int32_t n_pages = kv_indptr[b + 1] - kv_indptr[b];
+  const int32_t kv_len = page_size * (n_pages - 1) + last[b];
+  const int32_t pos = kv_len - n_new + (t - append_indptr[b]);
+  if (n_pages < 1 || pos < 0 || pos >= kv_len) return;
+  const int32_t page = kv_indices[kv_indptr[b] + pos / page_size];
+  if (page < 0 || page >= max_pages) return;
+  const int64_t dst = int64_t(page) * page_b + int64_t(pos % page_size) * tok_b;
+  const int64_t src = int64_t(t) * new_st_b;
+  const int32_t per = heads * row_chunks;
+  for (int32_t i = threadIdx.x; i < 2 * per; i += blockDim.x) {
+    const int32_t which = i >= per;
+    const int32_t j = i - which * per;
+    const int32_t h = j / row_chunks, c = j - (j / row_chunks) * row_chunks;
+    const char* s = (which ? v_new : k_new) + src + int64_t(h) * new_sh_b + int64_t(c) * 16;
+    char* d = (which ? v : k) + dst + int64_t(h) * head_b + int64_t(c) * 16;
+    *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, int64_t i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+template <typename T>
+__device__ __forceinline__ void store_f(T* p, int64_t i, float x);
+template <>
+__device__ __forceinline__ void store_f<float>(float* p, int64_t i, float x) { p[i] = x; }
+template <>
+__device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float x) { p[i] = dev::f32_to_bf16(x); }
+
+// Split-KV merge: workgroup (merge item, head); the chunk states of row r are
+// partial rows slot0 + c*num_rows + r.
+template <typename T>
+__global__ __launch_bounds__(128) void merge_partials_kernel(const MergePartialArgs a) {
+  const MergeItem mi = a.merges[blockIdx.x];
+  const int32_t h = blockIdx.y;
+  const int32_t hq = a.num_heads, d_all = a.head_dim;
+  for (int32_t r = 0; r < mi.num_rows; ++r) {
+    float mx = -INFINITY;
+    for (int32_t c = 0; c < mi.num_chunks; ++c)
+      mx = fmaxf(mx, a.part_lse[int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h]);
+    float z = 0.f;
+    if (mx != -INFINITY)
+      for (int32_t c = 0; c < mi.num_chunks; ++c) {
+        const float s = a.part_lse[int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h];
+        if (s != -INFINITY) z += dev::fast_exp2(s - mx);
+      }
+    const int32_t row = mi.q_row0 + r;
+    T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
+    for (int32_t d = threadIdx.x; d < d_all; d += blockDim.x) {
+      float acc = 0.f;
+      if (z > 0.f)
+        for (int32_t c = 0; c < mi.num_chunks; ++c) {
+          const int64_t prow = int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h;
+          const float s = a.part_lse[prow];
+          if (s != -INFINITY) acc = fmaf(dev::fast_exp2(s - mx) / z, a.part_o[prow * d_all + d], acc);
+        }
+      store_f<T>(orow, d, acc);
+    }
+    if (threadIdx.x == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+  }
+}
+
+// Pairwise merge: one wave per (row, head).  Each wave reads both statistics
+// before any lane writes, so v_out / s_out may alias the inputs.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_pair_kernel(const T* va, const float* sa, const T* vb, const float* sb,
+                                                         T* vo, float* so, int64_t row_heads, int32_t dim) {
+  const int64_t rh = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (rh >= row_heads) return;
+  const float a_s = sa[rh], b_s = sb[rh];
+  const bool a_empty = a_s == -INFINITY, b_empty = b_s == -INFINITY;
+  const float mx = fmaxf(a_s, b_s);
+  const float wa = a_empty ? 0.f : dev::fast_exp2(a_s - mx);
+  const float wb = b_empty ? 0.f : dev::fast_exp2(b_s - mx);
+  const float z = wa + wb;
+  const float ca = z > 0.f ? wa / z : 0.f, cb = z > 0.f ? wb / z : 0.f;
+  for (int32_t d = lane; d < dim; d += 64) {
+    const int64_t i = rh * dim + d;
+    const float x = load_f<T>(va, i), y = load_f<T>(vb, i);
+    float out;
+    if (a_empty) out = y;
+    else if (b_empty) out = x;
+    else out = ca * x + cb * y;
+    store_f<T>(vo, i, out);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) so[rh] = a_empty ? b_s : (b_empty ? a_s : mx + __log2f(z));
+}
+
+// Many-way merge: one wave per (row, head) over num_states states.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_many_kernel(const T* v, const float* s, T* vo, float* so, int64_t rows,
+                                                         int32_t states, int32_t heads, int32_t dim) {
+  const int64_t rh = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (rh >= rows * heads) return;
+  const int64_t row = rh / heads;
+  const int32_t h = int32_t(rh - row * heads);
+  float mx = -INFINITY;
+  for (int32_t k = 0; k < states; ++k) mx = fmaxf(mx, s[(row * states + k) * heads + h]);
+  float z = 0.f;
+  if (mx != -INFINITY)
+    for (int32_t k = 0; k < states; ++k) {
+      const float sk = s[(row * states + k) * heads + h];
+      if (sk != -INFINITY) z += dev::fast_exp2(sk - mx);
+    }
+  for (int32_t d = lane; d < dim; d += 64) {
+    float acc = 0.f;
+    if (z > 0.f)
+      for (int32_t k = 0; k < states; ++k) {
+        const float sk = s[(row * states + k) * heads + h];
+        if (sk != -INFINITY)
+          acc = fmaf(dev::fast_exp2(sk - mx) / z, load_f<T>(v, ((row * states + k) * heads + h) * dim + d), acc);
+      }
+    store_f<T>(vo, rh * dim + d, acc);
+  }
+  if (lane == 0) so[rh] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st, int64_t new_sh,
+                         const int32_t* append_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* last_page_len, int32_t batch, int32_t nnz, void* k, void* v,
+                         int64_t page_stride, int64_t token_stride, int64_t head_stride, int32_t page_size,
+                         int32_t num_heads, int32_t head_dim, int32_t max_num_pages, hipStream_t st) {
+  const int64_t es = dtype == kF32 ? 4 : 2;
+  const int32_t row_chunks = int32_t(head_dim * es / 16);
+  hipLaunchKernelGGL(append_kernel, dim3(uint32_t(nnz)), dim3(256), 0, st, static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), new_st * es, new_sh * es, append_indptr, kv_indptr, kv_indices,
+                     last_page_len, batch, static_cast<char*>(k), static_cast<char*>(v), page_stride * es,
+                     token_stride * es, head_stride * es, page_size, num_heads, row_chunks, max_num_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t st) {
+  const dim3 grid(uint32_t(a.num_merges), uint32_t(a.num_heads));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, dim3(128), 0, st, a);
+  else
+    hipLaunchKernelGGL(merge_partials_kernel<float>, grid, dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_pair(int32_t dtype, const void* va, const float* sa, const void* vb, const float* sb,
+                             void* vo, float* so, int64_t rows, int32_t heads, int32_t dim, hipStream_t st) {
+  const int64_t rh = rows * heads;
+  const int64_t blocks = (rh + 3) / 4;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(merge_pair_kernel<uint16_t>, dim3(uint32_t(blocks)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(va), sa, static_cast<const uint16_t*>(vb), sb,
+                       static_cast<uint16_t*>(vo), so, rh, dim);
+  else
+    hipLaunchKernelGGL(merge_pair_kernel<float>, dim3(uint32_t(blocks)), dim3(256), 0, st,
+                       static_cast<const float*>(va), sa, static_cast<const float*>(vb), sb, static_cast<float*>(vo),
+                       so, rh, dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_many(int32_t dtype, const void* v, const float* s, void* vo, float* so, int64_t rows,
+                             int32_t states, int32_t heads, int32_t dim, hipStream_t st) {
+  const int64_t blocks = (rows * heads + 3) / 4;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(merge_many_kernel<uint16_t>, dim3(uint32_t(blocks)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(v), s, static_cast<uint16_t*>(vo), so, rows, states, heads, dim);
+  else
+    hipLaunchKernelGGL(merge_many_kernel<float>, dim3(uint32_t(blocks)), dim3(256), 0, st,
+                       static_cast<const float*>(v), s, static_cast<float*>(vo), so, rows, states, heads, dim);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

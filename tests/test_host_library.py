@@ -1,0 +1,192 @@
+"""CPU tests of the native host library (no kernel launches): the C ABI
+loads and exports everything include/pkv.h declares, the validator agrees with
+the oracle rule by rule, and the native planner matches the oracle's planner
+specification bit for bit."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import metadata as md
+from oracle import planner as pl
+
+pkv = pytest.importorskip("paged_kv_cache_plan_amd")
+from paged_kv_cache_plan_amd import _abi  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(lib, name), name
+    # and the binding declares exactly those
+    assert sorted(_abi.SIGNATURES) == declared
+
+
+def test_version_string():
+    assert "gfx950" in pkv.version()
+
+
+BASE = dict(qo_indptr=[0, 3, 4, 8], kv_indptr=[0, 2, 3, 6], kv_indices=[7, 2, 11, 3, 14, 6],
+            kv_last_page_len=[2, 2, 1], page_size=4, max_num_pages=16)
+
+CASES = [
+    dict(kv_indptr=[1, 2, 3, 6]),
+    dict(qo_indptr=[0, 3, 2, 8]),
+    dict(kv_indptr=[0, 2, 2, 6], kv_indices=[7, 2, 3, 14, 6, 1]),
+    dict(kv_last_page_len=[2, 0, 1]),
+    dict(kv_last_page_len=[2, 5, 1]),
+    dict(kv_indices=[7, 2, 11, 3, 16, 6]),
+    dict(kv_indices=[7, 2, 11, 3, -1, 6]),
+    dict(kv_indptr=[0, 2, 3, 7]),
+    dict(qo_indptr=[0, 3, 6, 10]),
+    dict(page_size=0),
+    dict(num_qo_heads=6, num_kv_heads=4),
+    dict(decode=True),
+    dict(qo_indptr=[0, 3, 3, 7]),
+    dict(),
+]
+
+
+@pytest.mark.parametrize("change", CASES)
+def test_validator_matches_oracle(change):
+    args = dict(BASE)
+    args.update(change)
+    try:
+        want = md.validate(**args)
+        want_reason = None
+    except md.MetadataError as e:
+        want_reason = e.reason
+    if want_reason is None:
+        got = pkv.validate(**args)
+        assert list(got) == want
+    else:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.validate(**args)
+        assert e.value.status == _abi.ERR_METADATA
+        assert e.value.reason == _abi.META_REASONS[want_reason]
+
+
+def test_validator_rejects_int64_metadata():
+    with pytest.raises(TypeError):
+        pkv.validate(**dict(BASE, kv_indptr=np.array([0, 2, 3, 6], dtype=np.int64)))
+
+
+def test_append_validation():
+    pkv.validate_append(append_indptr=[0, 3, 4, 8], kv_indptr=[0, 2, 3, 6], kv_indices=[7, 2, 11, 3, 14, 6],
+                        kv_last_page_len=[2, 2, 1], page_size=4, max_num_pages=16)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.validate_append(append_indptr=[0, 1, 2], kv_indptr=[0, 1, 2], kv_indices=[5, 5],
+                            kv_last_page_len=[4, 4], page_size=4, max_num_pages=8)
+    assert e.value.reason == _abi.META_REASONS["append_collision"]
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.validate_append(append_indptr=[0, 3], kv_indptr=[0, 1], kv_indices=[5], kv_last_page_len=[2],
+                            page_size=4, max_num_pages=8)
+    assert e.value.reason == _abi.META_REASONS["qo_exceeds_kv"]
+
+
+def _compare_plans(mode, qo_indptr, kv_indptr, kv_indices, last, page_size, hq, hkv, dtype, causal, num_cus,
+                   fixed=0, target=0, mla_groups=0):
+    params = pkv.plan_params(mode=mode, batch_size=len(last), num_qo_heads=hq, num_kv_heads=hkv,
+                             head_dim_qk=576 if mode == "mla" else 128, head_dim_vo=512 if mode == "mla" else 128,
+                             page_size=page_size, causal=causal, dtype=dtype, num_cus=num_cus,
+                             fixed_split_pages=fixed, target_per_cu=target, mla_head_groups=mla_groups)
+    info, items, merges = pkv.plan_compute(params, qo_indptr=qo_indptr if mode == "prefill" else None,
+                                           kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last)
+    rows = pl.rows_per_tile(mode, hq // hkv, dtype)
+    assert info["rows_per_tile"] == rows
+    spec = pl.plan(mode=mode, qo_indptr=list(qo_indptr) if mode == "prefill" else None,
+                   kv_indptr=list(kv_indptr), kv_last_page_len=list(last), page_size=page_size,
+                   heads_y=info["heads_y"], rows=rows, causal=causal, num_cus=num_cus, fixed_split_pages=fixed,
+                   target_per_cu=target)
+    assert items.tolist() == spec["items"]
+    assert merges.tolist() == spec["merges"]
+    assert info["num_partial_rows"] == spec["num_partial_rows"]
+    assert info["chunk_pages"] == spec["chunk_pages"]
+    assert bool(info["split"]) == spec["split"]
+    return info
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("worked", dict(literal_pages=True)),
+    ("decode", {}),
+    ("skewed", {}),
+    ("prefill", {}),
+    ("mla", {}),
+])
+def test_planner_matches_spec_on_workloads(name, kw):
+    b = wl.make(name, **kw, **({} if name == "worked" else {"scale": 1.0}))
+    mode = b.mode
+    hkv = b.num_kv_heads
+    for num_cus in (256, 80):
+        info = _compare_plans(mode, b.qo_indptr, b.kv_indptr, b.kv_indices, b.kv_last_page_len, b.page_size,
+                              b.num_qo_heads, hkv, b.dtype, b.causal, num_cus)
+        assert info["num_items"] > 0
+    if name == "skewed":
+        assert info["split"] == 1
+
+
+def test_planner_matches_spec_randomised():
+    rng = np.random.default_rng(33)
+    for trial in range(150):
+        mode = ["decode", "prefill", "mla"][trial % 3]
+        b = int(rng.integers(1, 12))
+        page = int(rng.choice([1, 4, 16, 64]))
+        if mode == "prefill":
+            q = [int(x) for x in rng.integers(0, 300, size=b)]
+            k = [max(1, qi + int(rng.integers(0, 3000))) for qi in q]
+        else:
+            q = [1] * b
+            k = [int(x) for x in rng.integers(1, 20000, size=b)]
+        n = [math.ceil(x / page) for x in k]
+        kv_indptr = np.array([0] + list(np.cumsum(n)), dtype=np.int32)
+        last = np.array([x - (m - 1) * page for x, m in zip(k, n)], dtype=np.int32)
+        qo = np.array([0] + list(np.cumsum(q)), dtype=np.int32)
+        hq, hkv = (128, 1) if mode == "mla" else [(32, 8), (8, 8), (16, 2), (64, 8)][trial % 4]
+        dtype = "bf16" if (mode == "mla" or trial % 5) else "f32"
+        _compare_plans(mode, qo, kv_indptr, None, last, page, hq, hkv, dtype, bool(trial % 2),
+                       int(rng.integers(1, 400)), fixed=int(rng.choice([0, 0, 0, 1, 3, 50])),
+                       target=int(rng.choice([0, 1, 2, 8])))
+
+
+def test_fingerprint_tracks_metadata():
+    params = pkv.plan_params(mode="decode", batch_size=3, num_qo_heads=4, num_kv_heads=2, head_dim_qk=128,
+                             page_size=4, num_cus=8)
+    base = dict(qo_indptr=None, kv_indptr=[0, 2, 3, 6], kv_indices=[7, 2, 11, 3, 14, 6], kv_last_page_len=[2, 2, 1])
+    f0 = pkv.plan_compute(params, **base)[0]["fingerprint"]
+    assert pkv.plan_compute(params, **base)[0]["fingerprint"] == f0
+    moved = dict(base, kv_indices=[7, 2, 11, 3, 14, 5])
+    assert pkv.plan_compute(params, **moved)[0]["fingerprint"] != f0
+    grown = dict(base, kv_last_page_len=[2, 2, 2])
+    assert pkv.plan_compute(params, **grown)[0]["fingerprint"] != f0
+
+
+def test_plan_rejects_bad_inputs():
+    params = pkv.plan_params(mode="prefill", batch_size=3, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                             page_size=4, num_cus=8, dtype="f32", max_num_pages=16)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_compute(params, qo_indptr=[0, 3, 4, 8], kv_indptr=[0, 2, 3, 6], kv_indices=[7, 2, 11, 3, 99, 6],
+                         kv_last_page_len=[2, 2, 1])
+    assert e.value.status == _abi.ERR_METADATA and e.value.reason == _abi.META_REASONS["page_index"]
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_compute(params, qo_indptr=None, kv_indptr=[0, 2, 3, 6], kv_indices=None, kv_last_page_len=[2, 2, 1])
+    assert e.value.status == _abi.ERR_INVALID_ARG
+    mla = pkv.plan_params(mode="mla", batch_size=1, num_qo_heads=100, num_kv_heads=1, head_dim_qk=576,
+                          head_dim_vo=512, page_size=64, num_cus=8)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_compute(mla, qo_indptr=None, kv_indptr=[0, 1], kv_indices=None, kv_last_page_len=[5])
+    assert e.value.status == _abi.ERR_UNSUPPORTED
