@@ -1,0 +1,370 @@
+"""Benchmark of the paged KV-cache attention hot path on one MI355X.
+
+A step is one batch through the whole path: validate + plan (host, once per
+batch) and then, for each of the model's layers, append the new K/V rows,
+run attention and merge split tiles ("Deep Dive - FlashInfer", "Plan then
+run": one plan serves every layer of a batch; "GPU attention backends",
+"FlashInfer: plan and run": 28 layers share one plan).  Every layer has its
+own KV pool, so the working set is far larger than the 256 MB MALL and the
+KV stream comes from HBM.
+
+Headline workload: batch paged decode, 64 requests, kv_len U[512, 4096],
+page 16, 20k-page pool, 32 query / 8 kv heads, head_dim 128, bf16, NHD.
+value = algorithmic bytes of all layers / step time (GB/s).  The same JSON
+line carries the roofline of the attention kernel (HIP events around each
+launch), the chunked-prefill TFLOP/s secondary, the skewed and MLA decode
+secondaries, and the CPU oracle baseline.
+
+    python bench.py [--steps K] [--warmup W] [--layers L] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6              # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
+METRIC = "paged decode KV-read GB/s + prefill TFLOP/s, each as fraction of MI355X peak"
+KERNEL_SOURCES = ["attn_rows.hip", "prefill_mfma.hip", "mla_decode.hip", "merge_append.hip", "device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ work counts --
+
+def decode_bytes(b) -> dict:
+    """Algorithmic HBM bytes of one decode layer: every K and V row read once
+    per kv head, Q read, O and LSE written, page ids read; append reads and
+    writes the new rows."""
+    es = 2 if b.dtype == "bf16" else 4
+    kv = sum(b.kv_lens) * b.num_kv_heads * b.head_dim * 2 * es
+    q = b.nnz * b.num_qo_heads * b.head_dim * es
+    o = q
+    lse = b.nnz * b.num_qo_heads * 4
+    idx = int(b.kv_indptr[-1]) * 4
+    append = 0 if b.k_new is None else 2 * 2 * b.k_new.size * es
+    return {"kv": kv, "attn": kv + q + o + lse + idx, "append": append, "layer": kv + q + o + lse + idx + append}
+
+
+def prefill_flops(b) -> int:
+    """2 * Hq * (d_qk + d_vo) per visible (row, key) pair; masked pairs are not counted."""
+    pairs = sum(q * (k - q) + q * (q + 1) // 2 for q, k in zip(b.qo_lens, b.kv_lens))
+    return 2 * b.num_qo_heads * (2 * b.head_dim) * pairs
+
+
+def mla_bytes(b) -> dict:
+    kv = sum(b.kv_lens) * 576 * 2
+    q = b.batch_size * 128 * 576 * 2
+    o = b.batch_size * 128 * 512 * 2
+    lse = b.batch_size * 128 * 4
+    idx = int(b.kv_indptr[-1]) * 4
+    flops = sum(b.kv_lens) * 128 * (576 + 512) * 2
+    return {"kv": kv, "attn": kv + q + o + lse + idx, "flops": flops}
+
+
+# ---------------------------------------------------------------- runners --
+
+class Runner:
+    """Device copies of one batch with ``layers`` independent KV pools."""
+
+    def __init__(self, b, layers: int):
+        import torch
+        import paged_kv_cache_plan_amd as pkv
+        self.b, self.torch, self.pkv = b, torch, pkv
+        dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+                             if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
+        bf = b.dtype == "bf16"
+        self.q = dev(b.q, bf)
+        self.kv_indices = dev(b.kv_indices, False)
+        if b.mode == "mla":
+            self.q_kpe = dev(b.q_kpe, True)
+            base = dev(b.k_cache, True)
+            self.pools = [base] + [base.clone() for _ in range(layers - 1)]
+            self.out = torch.empty((b.batch_size, 128, 512), dtype=torch.bfloat16, device="cuda")
+            self.lse = torch.empty((b.batch_size, 128), dtype=torch.float32, device="cuda")
+        else:
+            k0, v0 = dev(b.k_cache, bf), dev(b.v_cache, bf)
+            self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(layers - 1)]
+            self.out = torch.empty_like(self.q)
+            self.lse = torch.empty((b.nnz, b.num_qo_heads), dtype=torch.float32, device="cuda")
+            if b.k_new is not None:
+                self.k_new, self.v_new = dev(b.k_new, bf), dev(b.v_new, bf)
+                self.append_indptr = dev(b.append_indptr, False)
+                self.kv_indptr_d = dev(b.kv_indptr, False)
+                self.last_d = dev(b.kv_last_page_len, False)
+        self.params = pkv.plan_params(
+            mode=b.mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+            head_dim_qk=576 if b.mode == "mla" else b.head_dim, head_dim_vo=512 if b.mode == "mla" else b.head_dim,
+            page_size=b.page_size, causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages)
+        info, _, _ = pkv.plan_compute(self.params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None,
+                                      kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
+                                      kv_last_page_len=b.kv_last_page_len)
+        self.workspace = torch.empty(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+        self.staging = torch.empty(max(info["staging_bytes"], 256), dtype=torch.uint8, pin_memory=True)
+        self.plan = None
+
+    def make_plan(self):
+        b = self.b
+        self.plan = self.pkv.Plan(self.params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None,
+                                  kv_indptr=b.kv_indptr, kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len,
+                                  workspace=self.workspace, staging=self.staging)
+        return self.plan
+
+    def layer(self, i: int, ev=None):
+        """append + attention + merge for layer i; ev = (start, end) events around attention."""
+        b, plan = self.b, self.plan
+        if b.mode == "mla":
+            pool = self.pools[i % len(self.pools)]
+            if ev:
+                ev[0].record()
+            plan.run_mla(self.q, self.q_kpe, pool[..., :512], pool[..., 512:], self.kv_indices, self.out, self.lse,
+                         sm_scale=b.sm_scale)
+            if ev:
+                ev[1].record()
+            return
+        k, v = self.pools[i % len(self.pools)]
+        if b.k_new is not None:
+            self.pkv.append_paged_kv(self.k_new, self.v_new, self.append_indptr, self.kv_indptr_d, self.kv_indices,
+                                     self.last_d, k, v, layout=b.layout, page_size=b.page_size)
+        if ev:
+            ev[0].record()
+        plan.run_attention(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
+        if ev:
+            ev[1].record()
+        plan.run_merge(self.out, self.lse)
+
+
+def measure(runner: Runner, layers: int, steps: int, warmup: int) -> dict:
+    """Time `steps` steps (plan + `layers` layers each); attention timed per launch."""
+    torch = runner.torch
+    for _ in range(warmup):
+        runner.make_plan()
+        for i in range(layers):
+            runner.layer(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps * layers)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plan_host = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for s in range(steps):
+        p0 = time.perf_counter()
+        runner.make_plan()
+        plan_host.append(time.perf_counter() - p0)
+        for i in range(layers):
+            runner.layer(i, evs[s * layers + i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    return {"ms_per_step": step_ms, "wall_ms_per_step": wall * 1e3 / steps,
+            "attn_ms_mean": float(np.mean(attn_ms)), "attn_ms_median": float(np.median(attn_ms)),
+            "attn_ms_p10": float(np.percentile(attn_ms, 10)), "attn_ms_p90": float(np.percentile(attn_ms, 90)),
+            "plan_host_ms": float(np.median(plan_host)) * 1e3, "plan_info": runner.plan.info}
+
+
+def cpu_baseline(b, budget_s: float = 12.0) -> dict:
+    """The float64 oracle, as it stands, on one host thread over the decode batch."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oat
+    reqs = list(range(b.batch_size))
+    done_bytes = 0
+    t0 = time.perf_counter()
+    passes = 0
+    per_req = decode_bytes(b)["kv"] / max(1, sum(b.kv_lens))
+    with threadpool_limits(limits=1):
+        while True:
+            for r in reqs:
+                oat.paged_attention(b.q, b.k_cache, b.v_cache, qo_indptr=list(b.qo_indptr),
+                                    kv_indptr=list(b.kv_indptr), kv_indices=b.kv_indices,
+                                    kv_last_page_len=list(b.kv_last_page_len), page_size=b.page_size,
+                                    layout=b.layout, num_kv_heads=b.num_kv_heads, sm_scale=b.sm_scale,
+                                    q_dtype=b.dtype, kv_dtype=b.dtype, requests=[r])
+                done_bytes += per_req * b.kv_lens[r]
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            passes += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 numpy oracle over the decode batch's requests one at a time, "
+                      f"{passes} pass(es) in {el:.1f} s; KV bytes counted like the GPU's",
+            "host_cpus": os.cpu_count()}
+
+
+def read_traffic(kernel: str):
+    """Counter-measured HBM traffic per launch from profiles/, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--secondary-layers", type=int, default=4)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla"], default=None,
+                    help="time one workload (profiling runs)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_plan_amd as pkv
+    import workloads as wl
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    pkv.lib()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name}, CUs {props.multi_processor_count}")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read, {n} bytes written")
+
+    result = {}
+    which = [args.only] if args.only else ["decode"] + ([] if args.no_secondary else ["prefill", "skewed", "mla"])
+
+    if "decode" in which:
+        b = wl.make("decode", with_append=True)
+        r = Runner(b, args.layers)
+        m = measure(r, args.layers, args.steps, args.warmup)
+        nb = decode_bytes(b)
+        value = nb["layer"] * args.layers / (m["ms_per_step"] * 1e-3) / 1e9
+        achieved = nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9
+        traffic = read_traffic("decode")
+        result["decode"] = dict(m, value=value, bytes=nb, achieved=achieved)
+        log(f"decode: {value:.1f} GB/s per step, attention kernel {achieved:.1f} GB/s "
+            f"({m['attn_ms_mean'] * 1e3:.1f} us), plan {m['plan_host_ms']:.3f} ms host")
+        del r
+    if "prefill" in which:
+        b = wl.make("prefill")
+        layers = args.secondary_layers
+        r = Runner(b, layers)
+        m = measure(r, layers, max(1, min(args.steps, 5)), 1)
+        fl = prefill_flops(b)
+        tf = fl / (m["attn_ms_mean"] * 1e-3) / 1e12
+        step_tf = fl * layers / (m["ms_per_step"] * 1e-3) / 1e12
+        result["prefill"] = dict(m, tflops=tf, step_tflops=step_tf, flops=fl)
+        log(f"prefill: attention {tf:.1f} TFLOP/s ({m['attn_ms_mean']:.3f} ms), step {step_tf:.1f} TFLOP/s")
+        del r
+    if "skewed" in which:
+        b = wl.make("skewed")
+        layers = args.secondary_layers
+        r = Runner(b, layers)
+        m = measure(r, layers, args.steps, args.warmup)
+        nb = decode_bytes(b)
+        result["skewed"] = dict(m, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9, bytes=nb)
+        log(f"skewed: attention {result['skewed']['gbs']:.1f} GB/s ({m['attn_ms_mean'] * 1e3:.1f} us)")
+        del r
+    if "mla" in which:
+        b = wl.make("mla")
+        layers = args.secondary_layers
+        r = Runner(b, layers)
+        m = measure(r, layers, args.steps, args.warmup)
+        nb = mla_bytes(b)
+        result["mla"] = dict(m, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
+                             tflops=nb["flops"] / (m["attn_ms_mean"] * 1e-3) / 1e12, bytes=nb)
+        log(f"mla: run {result['mla']['gbs']:.1f} GB/s, {result['mla']['tflops']:.1f} TFLOP/s "
+            f"({m['attn_ms_mean'] * 1e3:.1f} us)")
+        del r
+
+    if args.only and args.only != "decode":
+        print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk != "plan_info"} for k, v in result.items()}))
+        return
+
+    d = result["decode"]
+    line = {
+        "metric": METRIC,
+        "value": round(d["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "batch paged decode: 64 requests, qo_len 1, kv_len U[512,4096], page_size 16, "
+                               "20000-page shuffled pool, 32 qo / 8 kv heads, head_dim 128, bf16, NHD; "
+                               f"step = plan + {args.layers} layers x (append + attention + merge)",
+                   "layers": args.layers, "batch": 64, "page_size": 16, "heads": [32, 8], "head_dim": 128},
+        "roofline": {"bound": "hbm", "achieved": round(d["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d["achieved"] / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode"),
+                     "kernel": "attention (decode)", "bytes_per_launch": d["bytes"]["attn"],
+                     "launch_us_mean": round(d["attn_ms_mean"] * 1e3, 2),
+                     "launch_us_p10_p90": [round(d["attn_ms_p10"] * 1e3, 2), round(d["attn_ms_p90"] * 1e3, 2)]},
+        "plan_host_ms": round(d["plan_host_ms"], 4),
+        "plan": {k: d["plan_info"][k] for k in ("num_items", "num_merges", "chunk_pages", "split")},
+        "kernel_source": source_hash(),
+    }
+    if "prefill" in result:
+        p = result["prefill"]
+        line["prefill"] = {"value": round(p["tflops"], 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                           "frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
+                           "launch_ms_mean": round(p["attn_ms_mean"], 4), "flops_per_launch": p["flops"],
+                           "step_tflops_incl_append": round(p["step_tflops"], 2),
+                           "workload": "chunked prefill/append: 8 requests, qo U[512,2048], prefix U[0,8192], "
+                                       "page 16, HND, 32/8 heads, d128, bf16, causal"}
+    if "skewed" in result:
+        s = result["skewed"]
+        line["skewed_decode"] = {"value": round(s["gbs"], 1), "unit": "GB/s", "frac": round(s["gbs"] / HBM_PEAK_GBS, 4),
+                                 "launch_us_mean": round(s["attn_ms_mean"] * 1e3, 2),
+                                 "merge_items": s["plan_info"]["num_merges"]}
+    if "mla" in result:
+        mm = result["mla"]
+        line["mla_decode"] = {"value": round(mm["gbs"], 1), "unit": "GB/s", "frac": round(mm["gbs"] / HBM_PEAK_GBS, 4),
+                              "tflops": round(mm["tflops"], 2), "launch_us_mean": round(mm["attn_ms_mean"] * 1e3, 2)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl.make("decode"))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -295,6 +295,24 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token,
                    int64_t o_stride_head, float* lse, float sm_scale, void* stream);
 
 /*
+ * The two launches of pkv_run, separately: pkv_run_attention enqueues only
+ * the attention kernel (rows of split tiles then hold fp32 partial states in
+ * the plan's workspace, not in o/lse); pkv_run_merge enqueues only the merge
+ * of those partial states into o/lse ([DD] "A worked split-KV example") and
+ * is a no-op for a plan without splits.  pkv_run == attention then merge on
+ * one stream.  Splitting them lets a caller place other work between the two
+ * (for instance an exchange of partial states across devices, which the same
+ * merge then combines, [DD] "Core mechanism: schedule work around state") or
+ * time each kernel.  Arguments as for pkv_run.
+ */
+pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stride_token,
+                             int64_t q_stride_head, const pkv_cache_desc* cache,
+                             const int32_t* d_kv_indices, void* o, int64_t o_stride_token,
+                             int64_t o_stride_head, float* lse, float sm_scale, void* stream);
+pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token,
+                         int64_t o_stride_head, float* lse, void* stream);
+
+/*
  * MLA decode run ([KVL] "多头潜在注意力页布局"): one latent row per token,
  * ckv (512) and kpe (64), shared by every query head; score =
  * sm_scale * (q_ckv . ckv + q_kpe . kpe); output = softmax-weighted ckv.

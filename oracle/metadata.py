@@ -76,13 +76,15 @@ def indptr_from_lengths(lengths) -> list[int]:
 
 
 def kv_lens(kv_indptr, kv_indices, kv_last_page_len, page_size: int) -> list[int]:
-    """Per-request KV lengths of a CSR page table (applies ``kv_len`` per row).
+    """Per-request KV lengths of a CSR page table (applies ``kv_len`` per row;
+    numpy integers are converted to Python ints first).
 
     "FlashInfer 中的 KV-Cache 布局", section "页表布局" (page-table layout):
     request i's pages are kv_indices[kv_indptr[i]:kv_indptr[i+1]].
     """
     b = len(kv_indptr) - 1
-    return [kv_len(list(kv_indices[kv_indptr[i]:kv_indptr[i + 1]]), kv_last_page_len[i], page_size)
+    ip = [int(x) for x in kv_indptr]
+    return [kv_len([int(p) for p in kv_indices[ip[i]:ip[i + 1]]], int(kv_last_page_len[i]), page_size)
             for i in range(b)]
 
 

@@ -255,7 +255,8 @@ class Plan:
         last, last_p = _host_i32(kv_last_page_len, "kv_last_page_len")
         _check(lib().pkv_plan_check(self._handle, qo_p, kvp_p, idx_p, 0 if idx is None else len(idx), last_p))
 
-    def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None):
+    def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None,
+            _entry="pkv_run"):
         """pkv_run.  q [nnz, Hq, D] and out [nnz, Hq, D] device tensors of the plan's dtype;
         k_cache/v_cache 4-D views (see ``cache_desc``); kv_indices device int32; lse float32 [nnz, Hq]."""
         import torch
@@ -265,10 +266,20 @@ class Plan:
             raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
             raise TypeError("lse must be contiguous float32")
-        _check(lib().pkv_run(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
-                             _dev(kv_indices, "kv_indices", torch.int32), _dev(out, "out", q.dtype), out.stride(0),
-                             out.stride(1), None if lse is None else _dev(lse, "lse"), ctypes.c_float(sm_scale),
-                             _stream(stream)))
+        _check(getattr(lib(), _entry)(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
+                                      _dev(kv_indices, "kv_indices", torch.int32), _dev(out, "out", q.dtype),
+                                      out.stride(0), out.stride(1), None if lse is None else _dev(lse, "lse"),
+                                      ctypes.c_float(sm_scale), _stream(stream)))
+
+    def run_attention(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None):
+        """pkv_run_attention: the attention kernel only (split tiles stay as partial states)."""
+        self.run(q, k_cache, v_cache, kv_indices, out, lse, layout=layout, sm_scale=sm_scale, stream=stream,
+                 _entry="pkv_run_attention")
+
+    def run_merge(self, out, lse=None, *, stream=None):
+        """pkv_run_merge: merge the split tiles' partial states into out / lse."""
+        _check(lib().pkv_run_merge(self._handle, _dev(out, "out"), out.stride(0), out.stride(1),
+                                   None if lse is None else _dev(lse, "lse"), _stream(stream)))
 
     def run_mla(self, q_ckv, q_kpe, ckv, kpe, kv_indices, out, lse=None, *, sm_scale=0.0, stream=None):
         """pkv_run_mla.  ckv/kpe are [pages, P, 512] / [pages, P, 64] views (same page/token strides)."""

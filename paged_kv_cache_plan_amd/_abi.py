@@ -71,6 +71,9 @@ SIGNATURES = {
     "pkv_plan_destroy": (_i32, [_vp]),
     "pkv_run": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp, ctypes.c_float,
                        _vp]),
+    "pkv_run_attention": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp,
+                                 ctypes.c_float, _vp]),
+    "pkv_run_merge": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "pkv_run_mla": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.c_float, _vp]),
     "pkv_merge_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "pkv_merge_states": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),

@@ -530,10 +530,10 @@ static pkv_status check_ptr16(const void* p, const char* what) {
 
 static bool stride_ok(int64_t stride, size_t esize) { return stride >= 0 && (stride * int64_t(esize)) % 16 == 0; }
 
-pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
-                   const pkv_cache_desc* cache, const int32_t* d_kv_indices, void* o,
-                   int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
-                   void* stream) {
+pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stride_token,
+                             int64_t q_stride_head, const pkv_cache_desc* cache, const int32_t* d_kv_indices,
+                             void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                             void* stream) {
   if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
   const pkv_plan_params& p = plan->params;
   if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
@@ -594,22 +594,44 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, 
     return fail(PKV_ERR_UNSUPPORTED, fmt("no kernel for head_dim %lld, group %lld, dtype %lld",
                                          p.head_dim_qk, group, p.kv_dtype));
   if (e != hipSuccess) return hip_fail(e, "launching attention");
-  if (plan->info.num_merges > 0) {
-    pkv::MergePartialArgs m;
-    m.merges = plan->d_merges;
-    m.num_merges = plan->info.num_merges;
-    m.num_heads = p.num_qo_heads;
-    m.head_dim = p.head_dim_vo;
-    m.part_o = plan->d_part_o;
-    m.part_lse = plan->d_part_lse;
-    m.o = o;
-    m.o_stride_token = o_stride_token;
-    m.o_stride_head = o_stride_head;
-    m.lse = lse;
-    e = pkv::launch_merge_partials(p.kv_dtype, m, st);
-    if (e != hipSuccess) return hip_fail(e, "launching the split merge");
-  }
   return ok();
+}
+
+pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, int64_t o_stride_head,
+                         float* lse, void* stream) {
+  if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
+  if (plan->info.num_merges == 0) return ok();
+  const pkv_plan_params& p = plan->params;
+  const size_t es = dtype_size(p.kv_dtype);
+  pkv_status s = check_ptr16(o, "o");
+  if (s) return s;
+  if (!stride_ok(o_stride_token, es) || !stride_ok(o_stride_head, es))
+    return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  pkv::MergePartialArgs m;
+  m.merges = plan->d_merges;
+  m.num_merges = plan->info.num_merges;
+  m.num_heads = p.num_qo_heads;
+  m.head_dim = p.head_dim_vo;
+  m.part_o = plan->d_part_o;
+  m.part_lse = plan->d_part_lse;
+  m.o = o;
+  m.o_stride_token = o_stride_token;
+  m.o_stride_head = o_stride_head;
+  m.lse = lse;
+  hipError_t e = pkv::launch_merge_partials(p.kv_dtype, m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+  return ok();
+}
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                   const pkv_cache_desc* cache, const int32_t* d_kv_indices, void* o,
+                   int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                   void* stream) {
+  pkv_status s = pkv_run_attention(plan, q, q_stride_token, q_stride_head, cache, d_kv_indices, o, o_stride_token,
+                                   o_stride_head, lse, sm_scale, stream);
+  if (s) return s;
+  if (plan->params.mode == PKV_MODE_MLA_DECODE) return ok();
+  return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
 }
 
 pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kpe, const void* ckv,
