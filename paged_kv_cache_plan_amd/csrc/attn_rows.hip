@@ -5,23 +5,34 @@
 // paged decode"): each workgroup takes one work item (a key chunk of one
 // request) for one kv head and all G query heads that share it (GQA: query head
 // h reads kv head h / G).  Every K and V row is fetched from HBM exactly once
-// per kv head and used for all G heads.
+// per kv head and used for all G heads.  The arithmetic is plain VALU work.
 //
 // Work split inside a workgroup (4 waves of 64 lanes): waves take interleaved
-// blocks of 16 keys.
+// blocks of 16 keys, and each wave keeps the loads of its next block in flight
+// while it computes the current one (two register sets).
 //   Score phase: a quad of 4 lanes owns one key; each lane loads a quarter of
 //     the key row with 16-byte loads (4 lanes x 16 B = 64 contiguous bytes per
 //     instruction) and forms partial dot products for the G heads (bf16 pairs
 //     through v_dot2c_f32_bf16); two DPP quad exchanges finish them.
-//   Softmax: block max over the wave's 16 keys by DPP row rotations and two
-//     cross-row shuffles, exp2 in the log2 domain (scores are pre-multiplied by
-//     sm_scale * log2 e), running max m and per-quad running sum l.
+//   Softmax: the wave is cut into softmax groups (a 16-lane row, or half a row
+//     for 64-wide heads).  A group's quads score exactly the keys its value
+//     lanes consume, so the running max m, the rescale factor and the weights
+//     stay inside the group: the block max is two DPP row rotations, with no
+//     cross-row traffic.  Scores are pre-multiplied by sm_scale * log2 e and
+//     exponentiated with exp2.
 //   Value phase: 16 lanes own one value row (each lane 16 bytes), 4 rows per
-//     load instruction; p comes from a per-wave LDS slot; the accumulator is
-//     rescaled once per block.
-// At the end the 4 waves' states are merged in LDS and written either as the
+//     load instruction.  For bf16, the weights of two keys are packed as a bf16
+//     pair in LDS and the values of the same two keys are paired with v_perm,
+//     so one v_dot2c accumulates two keys for one (head, dim).  The rescale of
+//     the accumulator is skipped when no lane's max moved.
+// At the end the groups and the 4 waves are merged and written either as the
 // final output (dtype of Q, plus base-2 LSE) or as an fp32 partial state for
 // the split merge ("Deep Dive - FlashInfer", "A worked split-KV example").
+//
+// Loads are branch-free: a key past the end of the row's range re-reads the
+// last valid key (its weight is zero), and a page id outside the pool is
+// replaced by page 0 so no access leaves the cache allocation (the host
+// validates page ids; such rows would give undefined values, never a fault).
 //
 // Multi-row tiles (float32 prefill) loop over their rows; row r sees key j iff
 // j <= diag + r ("Causality uses logical positions, not page numbers").
@@ -35,6 +46,11 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockKeys = 16;
+constexpr int kSegPages = 1024;   // page ids staged in LDS per segment
+// Minimum waves per SIMD the register allocation must allow (compile-time tunable).
+#ifndef PKV_ROWS_MIN_WAVES
+#define PKV_ROWS_MIN_WAVES 2
+#endif
 
 template <typename T>
 struct Elem {
@@ -60,27 +76,8 @@ __device__ __forceinline__ void dot_chunk<float>(const uint4& q, const uint4& k,
   acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
 }
 
-template <typename T>
-__device__ __forceinline__ void unpack_chunk(const uint4& v, float* out);
-
-template <>
-__device__ __forceinline__ void unpack_chunk<uint16_t>(const uint4& v, float* out) {
-  out[0] = dev::bf16_lo(v.x);
-  out[1] = dev::bf16_hi(v.x);
-  out[2] = dev::bf16_lo(v.y);
-  out[3] = dev::bf16_hi(v.y);
-  out[4] = dev::bf16_lo(v.z);
-  out[5] = dev::bf16_hi(v.z);
-  out[6] = dev::bf16_lo(v.w);
-  out[7] = dev::bf16_hi(v.w);
-}
-
-template <>
-__device__ __forceinline__ void unpack_chunk<float>(const uint4& v, float* out) {
-  out[0] = __uint_as_float(v.x);
-  out[1] = __uint_as_float(v.y);
-  out[2] = __uint_as_float(v.z);
-  out[3] = __uint_as_float(v.w);
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 template <typename T>
@@ -90,17 +87,36 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) { *p =
 template <>
 __device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void attn_rows_kernel(const AttnArgs a) {
+// Reductions over the QPG quads of one softmax group: 4 quads = a 16-lane
+// row, 2 quads = half a row.
+template <int QPG>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (QPG == 4) {
+    x = fmaxf(x, dev::dpp<dev::kRowRor4>(x));
+    x = fmaxf(x, dev::dpp<dev::kRowRor8>(x));
+  } else {
+    x = fmaxf(x, dev::dpp<dev::kRowHalfMirror>(x));
+  }
+  return x;
+}
+
+template <typename T, int D, int G, bool kAligned>
+__global__ __launch_bounds__(kThreads, PKV_ROWS_MIN_WAVES) void attn_rows_kernel(const AttnArgs a) {
+  constexpr bool kBF16 = sizeof(T) == 2;
   constexpr int E = Elem<T>::kPer16;   // elements per 16-byte chunk
   constexpr int NCH = D / E;           // chunks per row
   constexpr int KC = NCH / 4;          // score phase: chunks per lane (4 lanes per key)
   constexpr int VL = NCH < 16 ? NCH : 16;  // value phase: lanes per row
   constexpr int VC = NCH / VL;         // value phase: chunks per lane
-  constexpr int VT = 64 / VL;          // value phase: rows per load instruction
-  static_assert(NCH % 4 == 0 && NCH % VL == 0, "head_dim must split into 16-byte chunks");
+  constexpr int VT = 64 / VL;          // value phase: rows per load instruction = softmax groups
+  constexpr int NU = kBlockKeys / VT;  // value phase: passes per block = keys per group per block
+  constexpr int QPG = kBlockKeys / VT; // score phase: quads per softmax group
+  static_assert(NCH % 4 == 0 && NCH % VL == 0 && (QPG == 4 || QPG == 2), "unsupported head_dim");
+  static_assert(NU % 2 == 0, "value passes come in pairs");
 
-  __shared__ float s_p[kWaves][kBlockKeys][G];
+  __shared__ int32_t s_pages[kSegPages];
+  // Block weights: bf16 pairs (keys 2w*VT+g, (2w+1)*VT+g) per head, or fp32.
+  __shared__ uint32_t s_p[kWaves][NU][VT][G];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_acc[kWaves][G][D];
@@ -111,18 +127,28 @@ __global__ __launch_bounds__(kThreads) void attn_rows_kernel(const AttnArgs a) {
   const Item it = a.items[item_idx];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int qk = lane >> 2, qi = lane & 3;     // score phase: key in block, quarter of the row
-  const int vg = lane / VL, vi = lane % VL;    // value phase: row in pass, chunk column
+  // Score phase: quad qk scores key u*VT + g of the block, where g = qk / QPG
+  // is its softmax group and u = qk % QPG its pass in the value phase.
+  const int qk = lane >> 2, qi = lane & 3;
+  const int k_u = qk % QPG, k_g = qk / QPG;
+  const int key_in_block = k_u * VT + k_g;
+  const int vg = lane / VL, vi = lane % VL;    // value phase: group (= k_g of this lane), chunk column
 
   const T* kbase = static_cast<const T*>(a.k) + int64_t(kvh) * a.head_stride;
   const T* vbase = static_cast<const T*>(a.v) + int64_t(kvh) * a.head_stride;
   const int32_t* pages = a.kv_indices + it.page_base;
   const int32_t hq = a.num_qo_heads;
+  const int32_t psz = a.page_size, pshift = a.page_shift;
+  const uint32_t max_pages = uint32_t(a.max_num_pages);
+  auto page_of = [&](int32_t j) { return kAligned ? (j >> pshift) : (pshift >= 0 ? (j >> pshift) : (j / psz)); };
+  auto slot_of = [&](int32_t j) {
+    return kAligned ? (j & (psz - 1)) : (pshift >= 0 ? (j & (psz - 1)) : (j - (j / psz) * psz));
+  };
 
   for (int r = 0; r < it.num_rows; ++r) {
     const int32_t row = it.q_row0 + r;
-    const int32_t kv_end = min(it.kv_end, it.diag + r + 1);
-    const int32_t nkeys = kv_end - it.kv_start;
+    const int32_t lo = it.kv_start;
+    const int32_t hi = min(it.kv_end, it.diag + r + 1);
 
     uint4 qreg[G][KC];
     const T* qrow = static_cast<const T*>(a.q) + int64_t(row) * a.q_stride_token +
@@ -142,92 +168,151 @@ __global__ __launch_bounds__(kThreads) void attn_rows_kernel(const AttnArgs a) {
       for (int e = 0; e < VC * E; ++e) acc[h][e] = 0.f;
     }
 
-    for (int32_t blk = wave * kBlockKeys; blk < nkeys; blk += kWaves * kBlockKeys) {
-      // Score phase: one key per quad.
-      const int32_t kj = blk + qk;
-      uint4 kreg[KC];
-      bool kvalid = kj < nkeys;
-      if (kvalid) {
-        const int64_t off = dev::token_offset(pages, it.kv_start + kj, a.page_size, a.page_shift,
-                                              a.max_num_pages, a.page_stride, a.token_stride);
-        kvalid = off >= 0;
-        if (kvalid) {
-          const T* krow = kbase + off;
-#pragma unroll
-          for (int c = 0; c < KC; ++c) kreg[c] = *reinterpret_cast<const uint4*>(krow + (qi + 4 * c) * E);
-        }
+    const int32_t p_lo = lo < hi ? page_of(lo) : 0;
+    const int32_t p_hi = lo < hi ? page_of(hi - 1) + 1 : 0;
+    for (int32_t sp = p_lo; sp < p_hi; sp += kSegPages) {
+      // Stage this segment's page ids in LDS.
+      const int32_t np = min(kSegPages, p_hi - sp);
+      __syncthreads();
+      for (int i = threadIdx.x; i < np; i += kThreads) {
+        const int32_t pg = pages[sp + i];
+        s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;
       }
-      // Value rows of this block, issued before the score math so both are in flight.
-      uint4 vreg[kBlockKeys / VT][VC];
-      bool vvalid[kBlockKeys / VT];
-#pragma unroll
-      for (int u = 0; u < kBlockKeys / VT; ++u) {
-        const int32_t vj = blk + u * VT + vg;
-        vvalid[u] = vj < nkeys;
-        int64_t off = -1;
-        if (vvalid[u])
-          off = dev::token_offset(pages, it.kv_start + vj, a.page_size, a.page_shift, a.max_num_pages,
-                                  a.page_stride, a.token_stride);
-        vvalid[u] = off >= 0;
-#pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          if (vvalid[u])
-            vreg[u][c] = *reinterpret_cast<const uint4*>(vbase + off + (vi + VL * c) * E);
-          else
-            vreg[u][c] = make_uint4(0, 0, 0, 0);
-        }
-      }
+      __syncthreads();
+      const int32_t tlo = max(lo, sp * psz);
+      const int32_t thi = min(hi, (sp + np) * psz);
 
-      float scale[G];
+      // Element offset of key j's row; keys at or past thi re-read key thi-1.
+      auto row_off = [&](int32_t j) -> int64_t {
+        j = min(j, thi - 1);
+        return int64_t(s_pages[page_of(j) - sp]) * a.page_stride + int64_t(slot_of(j)) * a.token_stride;
+      };
+      auto load = [&](int32_t blk, uint4 (&kr)[KC], uint4 (&vr)[NU][VC]) {
+        int64_t koff;
+        int64_t voff[NU];
+        if constexpr (kAligned) {
+          // A 16-key block never crosses a page: one page id for the block.
+          const int64_t base = int64_t(s_pages[(blk >> pshift) - sp]) * a.page_stride;
+          const int32_t last = thi - 1 - blk;
+          const int32_t s0 = blk & (psz - 1);
+          koff = base + int64_t(s0 + min(key_in_block, last)) * a.token_stride;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float part = 0.f;
-        if (kvalid) {
+          for (int u = 0; u < NU; ++u) voff[u] = base + int64_t(s0 + min(u * VT + vg, last)) * a.token_stride;
+        } else {
+          koff = row_off(blk + key_in_block);
 #pragma unroll
-          for (int c = 0; c < KC; ++c) dot_chunk<T>(qreg[h][c], kreg[c], part);
+          for (int u = 0; u < NU; ++u) voff[u] = row_off(blk + u * VT + vg);
         }
-        float s = dev::quad_sum(part) * a.scale_log2;
-        s = kvalid ? s : -INFINITY;
-        const float m_new = fmaxf(m[h], dev::quads_max(s));
-        const bool live = m_new != -INFINITY;       // false only if every key so far was skipped
-        scale[h] = live ? dev::fast_exp2(m[h] - m_new) : 1.f;   // m[h] = -inf gives 0
-        const float p = live ? dev::fast_exp2(s - m_new) : 0.f;
-        l[h] = l[h] * scale[h] + p;
-        m[h] = m_new;
-        if (qi == 0) s_p[wave][qk][h] = p;
-      }
-      dev::wave_lds_sync();
+        const T* krow = kbase + koff;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const uint4*>(krow + (qi + 4 * c) * E);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int c = 0; c < VC; ++c)
+            vr[u][c] = *reinterpret_cast<const uint4*>(vbase + voff[u] + (vi + VL * c) * E);
+      };
 
-      // Value phase.
+      auto compute = [&](int32_t blk, uint4 (&kr)[KC], uint4 (&vr)[NU][VC]) {
+        const bool kok = blk + key_in_block < thi;
+        float scale[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+          float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < VC * E; ++e) acc[h][e] *= scale[h];
-#pragma unroll
-      for (int u = 0; u < kBlockKeys / VT; ++u) {
-        float pv[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pv[h] = s_p[wave][u * VT + vg][h];
-#pragma unroll
-        for (int c = 0; c < VC; ++c) {
-          float vf[E];
-          unpack_chunk<T>(vreg[u][c], vf);
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][c * E + e] = fmaf(pv[h], vf[e], acc[h][c * E + e]);
+          for (int c = 0; c < KC; ++c) dot_chunk<T>(qreg[h][c], kr[c], part);
+          float s = dev::quad_sum(part) * a.scale_log2;
+          s = kok ? s : -INFINITY;
+          const float m_new = fmaxf(m[h], group_max<QPG>(s));
+          const bool live = m_new != -INFINITY;       // false only while every key so far was skipped
+          scale[h] = live ? dev::fast_exp2(m[h] - m_new) : 1.f;
+          const float p = live ? dev::fast_exp2(s - m_new) : 0.f;
+          l[h] = l[h] * scale[h] + p;
+          m[h] = m_new;
+          if constexpr (kBF16) {
+            // lane qi of the quad stores heads qi, qi+4, ... as the bf16 half
+            // (u % 2) of the pair slot of pass pair u / 2.
+            if (h % 4 == qi)
+              reinterpret_cast<uint16_t*>(&s_p[wave][k_u / 2][k_g][h])[k_u % 2] = dev::f32_to_bf16(p);
+          } else {
+            if (h % 4 == qi) s_p[wave][k_u][k_g][h] = __float_as_uint(p);
+          }
         }
+        dev::wave_lds_sync();
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (__any(scale[h] != 1.f)) {
+#pragma unroll
+            for (int e = 0; e < VC * E; ++e) acc[h][e] *= scale[h];
+          }
+        }
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int w = 0; w < NU / 2; ++w) {
+            uint32_t pp[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) pp[h] = s_p[wave][w][vg][h];
+#pragma unroll
+            for (int c = 0; c < VC; ++c) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t x0 = word(vr[2 * w][c], i), x1 = word(vr[2 * w + 1][c], i);
+                const uint32_t even = __builtin_amdgcn_perm(x1, x0, 0x05040100u);  // dim 2i of both keys
+                const uint32_t odd = __builtin_amdgcn_perm(x1, x0, 0x07060302u);   // dim 2i+1
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                  acc[h][c * E + 2 * i] = dev::dot2_bf16(even, pp[h], acc[h][c * E + 2 * i]);
+                  acc[h][c * E + 2 * i + 1] = dev::dot2_bf16(odd, pp[h], acc[h][c * E + 2 * i + 1]);
+                }
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            float pv[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) pv[h] = __uint_as_float(s_p[wave][u][vg][h]);
+#pragma unroll
+            for (int c = 0; c < VC; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float x = __uint_as_float(word(vr[u][c], i));
+#pragma unroll
+                for (int h = 0; h < G; ++h) acc[h][c * E + i] = fmaf(pv[h], x, acc[h][c * E + i]);
+              }
+          }
+        }
+        dev::wave_lds_sync();
+      };
+
+      // Two register sets: the loads of block i+1 are in flight while block i computes.
+      constexpr int32_t kStride = kWaves * kBlockKeys;
+      uint4 ka[KC], kb[KC], va[NU][VC], vb[NU][VC];
+      int32_t blk = tlo + wave * kBlockKeys;
+      if (blk < thi) load(blk, ka, va);
+      while (blk < thi) {
+        if (blk + kStride < thi) load(blk + kStride, kb, vb);
+        compute(blk, ka, va);
+        blk += kStride;
+        if (blk >= thi) break;
+        if (blk + kStride < thi) load(blk + kStride, ka, va);
+        compute(blk, kb, vb);
+        blk += kStride;
       }
-      dev::wave_lds_sync();
     }
 
-    // Wave-level state: l summed over quads, acc summed over value rows.
+    // Wave state: rescale every group to the wave max, then sum l over quads
+    // and acc over value-phase groups.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      l[h] = dev::quads_sum(l[h]);
+      const float mw = dev::quads_max(m[h]);
+      const float f = m[h] == -INFINITY ? 0.f : dev::fast_exp2(m[h] - mw);
+      l[h] = dev::quads_sum(l[h] * f);
+      m[h] = mw;
 #pragma unroll
       for (int e = 0; e < VC * E; ++e) {
-        float x = acc[h][e];
+        float x = acc[h][e] * f;
 #pragma unroll
         for (int off = VL; off < 64; off <<= 1) x += __shfl_xor(x, off);
         acc[h][e] = x;
@@ -285,7 +370,11 @@ template <typename T, int D, int G>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_rows_kernel<T, D, G>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+  const bool aligned = a.page_shift >= 4;   // a power-of-two page of at least 16 keys
+  if (aligned)
+    hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

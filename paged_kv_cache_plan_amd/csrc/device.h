@@ -41,6 +41,7 @@ constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
+constexpr int kRowHalfMirror = 0x141;
 
 // Sum over the 4 lanes of a quad (every lane gets the total).
 __device__ __forceinline__ float quad_sum(float x) {
