@@ -181,7 +181,8 @@ pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new
  * Split policy ([DD] "Load balancing and split-KV decisions" gives the
  * trade-off, not an algorithm; this is our rule): chunk pages
  * C = fixed_split_pages if > 0, else max(ceil(256/page_size), ceil(W/T)) with
- * W = sum_b tiles_b * pages_b * heads_y and T = target_per_cu * num_cus.
+ * W = sum_b tiles_b * pages_b * heads_y and T = target_per_cu * num_cus; C is
+ * capped at 1024 pages (a kernel stages one chunk's page ids on chip).
  * Chunks are page-aligned and disjoint; causal tiles drop chunks they cannot
  * see.  Items run longest first.
  */

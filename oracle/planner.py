@@ -34,6 +34,7 @@ from __future__ import annotations
 DECODE, PREFILL, MLA = "decode", "prefill", "mla"
 
 MIN_SPLIT_TOKENS = 256          # a chunk holds at least this many tokens
+MAX_CHUNK_PAGES = 1024          # and at most this many pages (a kernel stages a chunk's page ids on chip)
 DEFAULT_TARGET_PER_CU = {DECODE: 4, PREFILL: 4, MLA: 1}
 MFMA_TILE_ROWS = 128            # prefill tile height counted in (row, head) pairs
 
@@ -62,7 +63,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     2. Page work W = sum_b tiles_b * n_b * heads_y; target T = target_per_cu *
        num_cus items.
     3. Chunk size C (pages) = fixed_split_pages if given, else
-       max(ceil(256 / P), ceil(W / T)).
+       max(ceil(256 / P), ceil(W / T)); either way at most 1024.
     4. Chunk c of request b covers keys [c*C*P, min((c+1)*C*P, K_b)).
     5. For tile t (local rows l0 .. l0+rows-1) the causal limit is
        diag = K_b - q_b + l0 (non-causal: diag = K_b); a chunk whose first key
@@ -92,6 +93,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
         chunk = fixed_split_pages
     else:
         chunk = max(_cdiv(MIN_SPLIT_TOKENS, page_size), _cdiv(work, target))
+    chunk = min(chunk, MAX_CHUNK_PAGES)
     chunk_tokens = chunk * page_size
 
     raw = []          # (cost, b, t, c_kept, fields) before slot assignment

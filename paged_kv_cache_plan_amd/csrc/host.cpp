@@ -136,6 +136,7 @@ pkv_status validate_impl(const int32_t* qo_indptr, const int32_t* kv_indptr,
 // ---------------------------------------------------------------- planner --
 
 constexpr int32_t kMinSplitTokens = 256;
+constexpr int64_t kMaxChunkPages = 1024;   // kernels stage one chunk's page ids on chip
 constexpr int32_t kMfmaTileRows = 128;   // prefill tile height in (row, head) pairs
 
 int32_t default_target(int32_t mode) { return mode == PKV_MODE_MLA_DECODE ? 1 : 4; }
@@ -245,6 +246,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   int64_t chunk = prm->fixed_split_pages > 0
                       ? prm->fixed_split_pages
                       : std::max<int64_t>(cdiv(kMinSplitTokens, prm->page_size), cdiv(work, target));
+  chunk = std::min(chunk, kMaxChunkPages);
   const int64_t chunk_tokens = chunk * prm->page_size;
 
   // Step 4-6: chunks per tile, causal pruning, partial-row assignment.

@@ -42,7 +42,13 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kD = 128;          // head dim
 constexpr int kKeys = 64;        // keys per LDS tile
-constexpr int kPitch = kD + 8;   // LDS row pitch in elements (272 bytes)
+// LDS row pitches (elements).  K rows are read 16 bytes per lane, 32 rows at
+// one column: a pitch of 68 dwords spreads consecutive rows over distinct
+// 4-bank groups.  V rows are read by the transposed load, 4 rows x 32 bytes
+// per 16-lane group: a pitch of 72 dwords puts those 4 rows on disjoint banks.
+constexpr int kPitchK = kD + 8;
+constexpr int kPitchV = kD + 16;
+constexpr int kMaxChunkPages = 1024;   // the planner never makes a chunk longer than this
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyMax = 8.f;  // rescale only when a row max grows by more than this (log2 units)
@@ -64,10 +70,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int G>
+template <int G, bool kPow2>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kKeys * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * kPitchK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kKeys * kPitchV];
+  __shared__ int32_t s_pages[kMaxChunkPages];
 
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
@@ -116,51 +123,63 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   const int32_t kv_lo = it.kv_start, kv_hi = it.kv_end;
   const int32_t ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kKeys - 1) / kKeys : 0;
 
+  // Page ids of the chunk (at most kMaxChunkPages, a planner guarantee) go to LDS once.
+  const int32_t pg_lo = kv_hi > kv_lo ? (kPow2 ? kv_lo >> pshift : kv_lo / psz) : 0;
+  const int32_t pg_n =
+      kv_hi > kv_lo ? min(kMaxChunkPages, (kPow2 ? (kv_hi - 1) >> pshift : (kv_hi - 1) / psz) - pg_lo + 1) : 0;
+  for (int i = tid; i < pg_n; i += kThreads) {
+    const int32_t pg = pages[pg_lo + i];
+    s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;
+  }
+  __syncthreads();
+
   // Tile loader: thread tid moves 16 bytes of 4 keys (key tid/16 + 16i, dims (tid%16)*8).
+  // Keys past the chunk end re-read the last key (their scores are masked).
   const int ld_key = tid >> 4, ld_chunk = tid & 15;
-  uint4 kst[4], vst[4];
-  auto page_slot = [&](int32_t j, int32_t& pg, int32_t& slot) {
-    int32_t pi;
-    if (pshift >= 0) {
-      pi = j >> pshift;
-      slot = j & (psz - 1);
-    } else {
-      pi = j / psz;
-      slot = j - pi * psz;
-    }
-    pg = pages[pi];
-    pg = uint32_t(pg) < max_pages ? pg : 0;
-  };
-  auto gload = [&](int32_t t0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t j = min(t0 + ld_key + 16 * i, kv_hi - 1);   // past the end: re-read the last key
-      int32_t pg, slot;
-      page_slot(j, pg, slot);
-      const int64_t off = int64_t(pg) * a.page_stride + int64_t(slot) * a.token_stride + ld_chunk * 8;
-      kst[i] = *reinterpret_cast<const uint4*>(kbase + off);
-      vst[i] = *reinterpret_cast<const uint4*>(vbase + off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = ld_key + 16 * i;
-      *reinterpret_cast<uint4*>(&s_k[buf][key * kPitch + ld_chunk * 8]) = kst[i];
-      *reinterpret_cast<uint4*>(&s_v[buf][key * kPitch + ld_chunk * 8]) = vst[i];
-    }
-  };
+  uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
+#define PKV_GLOAD(T0)                                                                            \
+  do {                                                                                           \
+    int64_t off_[4];                                                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                          \
+      const int32_t j_ = min((T0) + ld_key + 16 * i_, kv_hi - 1);                                \
+      const int32_t pi_ = kPow2 ? (j_ >> pshift) : (j_ / psz);                                   \
+      const int32_t sl_ = kPow2 ? (j_ & (psz - 1)) : (j_ - pi_ * psz);                           \
+      off_[i_] = int64_t(s_pages[min(pi_ - pg_lo, kMaxChunkPages - 1)]) * a.page_stride +      \
+                 int64_t(sl_) * a.token_stride + ld_chunk * 8;                                   \
+    }                                                                                            \
+    kst0 = *reinterpret_cast<const uint4*>(kbase + off_[0]);                                     \
+    kst1 = *reinterpret_cast<const uint4*>(kbase + off_[1]);                                     \
+    kst2 = *reinterpret_cast<const uint4*>(kbase + off_[2]);                                     \
+    kst3 = *reinterpret_cast<const uint4*>(kbase + off_[3]);                                     \
+    vst0 = *reinterpret_cast<const uint4*>(vbase + off_[0]);                                     \
+    vst1 = *reinterpret_cast<const uint4*>(vbase + off_[1]);                                     \
+    vst2 = *reinterpret_cast<const uint4*>(vbase + off_[2]);                                     \
+    vst3 = *reinterpret_cast<const uint4*>(vbase + off_[3]);                                     \
+  } while (0)
+#define PKV_LSTORE(BUF)                                                                          \
+  do {                                                                                           \
+    uint16_t* k_ = &s_k[(BUF)][ld_key * kPitchK + ld_chunk * 8];                                 \
+    uint16_t* v_ = &s_v[(BUF)][ld_key * kPitchV + ld_chunk * 8];                                 \
+    *reinterpret_cast<uint4*>(k_) = kst0;                                                        \
+    *reinterpret_cast<uint4*>(k_ + 16 * kPitchK) = kst1;                                         \
+    *reinterpret_cast<uint4*>(k_ + 32 * kPitchK) = kst2;                                         \
+    *reinterpret_cast<uint4*>(k_ + 48 * kPitchK) = kst3;                                         \
+    *reinterpret_cast<uint4*>(v_) = vst0;                                                        \
+    *reinterpret_cast<uint4*>(v_ + 16 * kPitchV) = vst1;                                         \
+    *reinterpret_cast<uint4*>(v_ + 32 * kPitchV) = vst2;                                         \
+    *reinterpret_cast<uint4*>(v_ + 48 * kPitchV) = vst3;                                         \
+  } while (0)
 
   if (ntiles > 0) {
-    gload(kv_lo);
-    lstore(0);
+    PKV_GLOAD(kv_lo);
+    PKV_LSTORE(0);
   }
   __syncthreads();
 
   for (int32_t t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int32_t t0 = kv_lo + t * kKeys;
-    if (t + 1 < ntiles) gload(t0 + kKeys);
+    if (t + 1 < ntiles) PKV_GLOAD(t0 + kKeys);
 
     // S^T = K Q^T for two 32-key blocks.
     f32x16_t sacc[2];
@@ -168,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-      const uint16_t* krow = &s_k[buf][(kb * 32 + col) * kPitch + 8 * h];
+      const uint16_t* krow = &s_k[buf][(kb * 32 + col) * kPitchK + 8 * h];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * s);
@@ -236,18 +255,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const uint16_t* base = &s_v[buf][(16 * ks + krow0) * kPitch + 32 * n + dsub];
+          const uint16_t* base = &s_v[buf][(16 * ks + krow0) * kPitchV + 32 * n + dsub];
           const bf16x4_t lo = tr_read(base);
-          const bf16x4_t hi = tr_read(base + 8 * kPitch);
+          const bf16x4_t hi = tr_read(base + 8 * kPitchV);
           const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[ks]), oacc[n], 0, 0, 0);
         }
       }
     }
 
-    if (t + 1 < ntiles) lstore(buf ^ 1);
+    if (t + 1 < ntiles) PKV_LSTORE(buf ^ 1);
     __syncthreads();
   }
+
+#undef PKV_GLOAD
+#undef PKV_LSTORE
 
   // Epilogue: row sum over both lane halves, normalise, write.
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -289,7 +311,10 @@ template <int G>
 hipError_t launch_g(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_mfma_kernel<G>, dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+  if (a.page_shift >= 0)
+    hipLaunchKernelGGL((prefill_mfma_kernel<G, true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<G, false>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
