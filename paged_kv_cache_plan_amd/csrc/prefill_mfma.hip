@@ -72,8 +72,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 template <int G, bool kPow2>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * kPitchK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kKeys * kPitchV];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * kPitchK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kKeys * kPitchV];
   __shared__ int32_t s_pages[kMaxChunkPages];
 
   const int32_t hkv = a.num_kv_heads;
@@ -133,86 +133,109 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   }
   __syncthreads();
 
-  // Tile loader: thread tid moves 16 bytes of 4 keys (key tid/16 + 16i, dims (tid%16)*8).
-  // Keys past the chunk end re-read the last key (their scores are masked).
+  // Tile loader: thread tid moves 16 bytes of 4 keys (key tid/16 + 16i,
+  // dims (tid%16)*8) of K or V.  Keys past the chunk end re-read the last key
+  // (their scores are masked to -inf, so their weights are exactly zero).
   const int ld_key = tid >> 4, ld_chunk = tid & 15;
+  // Full tiles on pages of at least 16 keys: a thread's four keys
+  // t0 + ld_key + 16i sit on page (t0 + 16i) >> shift, the same page for the
+  // whole workgroup, so only the slot depends on the thread.
+  const bool aligned = kPow2 && pshift >= 4;
+  const int64_t ld_lane_off = int64_t(ld_key) * a.token_stride + ld_chunk * 8;
+  auto tile_offsets = [&](int32_t t0, int64_t (&off)[4]) {
+    if (aligned && t0 + kKeys <= kv_hi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t j0 = t0 + 16 * i;
+        off[i] = int64_t(s_pages[(j0 >> pshift) - pg_lo]) * a.page_stride + int64_t(j0 & (psz - 1)) * a.token_stride +
+                 ld_lane_off;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t j = min(t0 + ld_key + 16 * i, kv_hi - 1);
+        const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
+        const int32_t sl = kPow2 ? (j & (psz - 1)) : (j - pi * psz);
+        off[i] = int64_t(s_pages[min(pi - pg_lo, kMaxChunkPages - 1)]) * a.page_stride + int64_t(sl) * a.token_stride +
+                 ld_chunk * 8;
+      }
+    }
+  };
   uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
-#define PKV_GLOAD(T0)                                                                            \
-  do {                                                                                           \
-    int64_t off_[4];                                                                             \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                          \
-      const int32_t j_ = min((T0) + ld_key + 16 * i_, kv_hi - 1);                                \
-      const int32_t pi_ = kPow2 ? (j_ >> pshift) : (j_ / psz);                                   \
-      const int32_t sl_ = kPow2 ? (j_ & (psz - 1)) : (j_ - pi_ * psz);                           \
-      off_[i_] = int64_t(s_pages[min(pi_ - pg_lo, kMaxChunkPages - 1)]) * a.page_stride +      \
-                 int64_t(sl_) * a.token_stride + ld_chunk * 8;                                   \
-    }                                                                                            \
-    kst0 = *reinterpret_cast<const uint4*>(kbase + off_[0]);                                     \
-    kst1 = *reinterpret_cast<const uint4*>(kbase + off_[1]);                                     \
-    kst2 = *reinterpret_cast<const uint4*>(kbase + off_[2]);                                     \
-    kst3 = *reinterpret_cast<const uint4*>(kbase + off_[3]);                                     \
-    vst0 = *reinterpret_cast<const uint4*>(vbase + off_[0]);                                     \
-    vst1 = *reinterpret_cast<const uint4*>(vbase + off_[1]);                                     \
-    vst2 = *reinterpret_cast<const uint4*>(vbase + off_[2]);                                     \
-    vst3 = *reinterpret_cast<const uint4*>(vbase + off_[3]);                                     \
-  } while (0)
-#define PKV_LSTORE(BUF)                                                                          \
-  do {                                                                                           \
-    uint16_t* k_ = &s_k[(BUF)][ld_key * kPitchK + ld_chunk * 8];                                 \
-    uint16_t* v_ = &s_v[(BUF)][ld_key * kPitchV + ld_chunk * 8];                                 \
-    *reinterpret_cast<uint4*>(k_) = kst0;                                                        \
-    *reinterpret_cast<uint4*>(k_ + 16 * kPitchK) = kst1;                                         \
-    *reinterpret_cast<uint4*>(k_ + 32 * kPitchK) = kst2;                                         \
-    *reinterpret_cast<uint4*>(k_ + 48 * kPitchK) = kst3;                                         \
-    *reinterpret_cast<uint4*>(v_) = vst0;                                                        \
-    *reinterpret_cast<uint4*>(v_ + 16 * kPitchV) = vst1;                                         \
-    *reinterpret_cast<uint4*>(v_ + 32 * kPitchV) = vst2;                                         \
-    *reinterpret_cast<uint4*>(v_ + 48 * kPitchV) = vst3;                                         \
-  } while (0)
+  auto gload_k = [&](int32_t t0) {
+    int64_t off[4];
+    tile_offsets(t0, off);
+    kst0 = *reinterpret_cast<const uint4*>(kbase + off[0]);
+    kst1 = *reinterpret_cast<const uint4*>(kbase + off[1]);
+    kst2 = *reinterpret_cast<const uint4*>(kbase + off[2]);
+    kst3 = *reinterpret_cast<const uint4*>(kbase + off[3]);
+  };
+  auto gload_v = [&](int32_t t0) {
+    int64_t off[4];
+    tile_offsets(t0, off);
+    vst0 = *reinterpret_cast<const uint4*>(vbase + off[0]);
+    vst1 = *reinterpret_cast<const uint4*>(vbase + off[1]);
+    vst2 = *reinterpret_cast<const uint4*>(vbase + off[2]);
+    vst3 = *reinterpret_cast<const uint4*>(vbase + off[3]);
+  };
+  uint16_t* const k_st = &s_k[ld_key * kPitchK + ld_chunk * 8];
+  uint16_t* const v_st = &s_v[ld_key * kPitchV + ld_chunk * 8];
+  auto lstore_k = [&]() {
+    *reinterpret_cast<uint4*>(k_st) = kst0;
+    *reinterpret_cast<uint4*>(k_st + 16 * kPitchK) = kst1;
+    *reinterpret_cast<uint4*>(k_st + 32 * kPitchK) = kst2;
+    *reinterpret_cast<uint4*>(k_st + 48 * kPitchK) = kst3;
+  };
+  auto lstore_v = [&]() {
+    *reinterpret_cast<uint4*>(v_st) = vst0;
+    *reinterpret_cast<uint4*>(v_st + 16 * kPitchV) = vst1;
+    *reinterpret_cast<uint4*>(v_st + 32 * kPitchV) = vst2;
+    *reinterpret_cast<uint4*>(v_st + 48 * kPitchV) = vst3;
+  };
 
-  if (ntiles > 0) {
-    PKV_GLOAD(kv_lo);
-    PKV_LSTORE(0);
-  }
-  __syncthreads();
-
-  for (int32_t t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int32_t t0 = kv_lo + t * kKeys;
-    if (t + 1 < ntiles) PKV_GLOAD(t0 + kKeys);
-
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16_t sacc[2];
+  // S^T of the K tile currently in LDS: two 32-key blocks.
+  const uint16_t* const k_rd = &s_k[col * kPitchK + 8 * h];
+  auto scores = [&](f32x16_t (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-      const uint16_t* krow = &s_k[buf][(kb * 32 + col) * kPitchK + 8 * h];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * s);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[s]), sacc[kb], 0, 0, 0);
+      for (int st = 0; st < 8; ++st) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(k_rd + kb * 32 * kPitchK + 16 * st);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[st]), sacc[kb], 0, 0, 0);
       }
     }
+  };
+
+  const int grp = lane >> 4, gi = lane & 15;
+  const uint16_t* const v_rd = &s_v[(4 * h + (gi >> 2)) * kPitchV + 16 * (grp & 1) + 4 * (gi & 3)];
+  const float c = a.scale_log2;
+
+  // One tile: softmax of S(t) (in scur) and O += V(t) P(t), while the scores
+  // S(t+1) of the K tile already in LDS are computed into snext.  On entry LDS
+  // holds K(t+1) and V(t); on exit it holds K(t+2) and V(t+1).
+  auto body = [&](int32_t t, f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
+    const int32_t t0 = kv_lo + t * kKeys;
+    if (t + 2 < ntiles) gload_k(t0 + 2 * kKeys);
+    if (t + 1 < ntiles) gload_v(t0 + kKeys);
 
     // Masking: key of value v in block kb is t0 + 32kb + 8(v/4) + 4h + v%4.
-    const bool need_mask = t0 + kKeys - 1 > wave_limit_min;
-    if (need_mask) {
+    if (t0 + kKeys - 1 > wave_limit_min) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int32_t j = t0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-          sacc[kb][v] = j <= limit ? sacc[kb][v] : -INFINITY;
+          scur[kb][v] = j <= limit ? scur[kb][v] : -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, scur[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float c = a.scale_log2;
     const float m_cand = mx * c;
     const bool grow = m_cand > m_used + kLazyMax || (m_used == -INFINITY && m_cand != -INFINITY);
     if (__any(grow)) {
@@ -225,51 +248,62 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[n][v] *= f;
     }
-    // Weights, packed as the B operand of the PV k-steps (8 keys per lane per step).
+
+    // S(t+1) on the matrix cores while the weights of tile t are formed.
+    scores(snext);
+    // exp2(-inf) = 0 covers masked keys; a row with no visible key yet has
+    // only -inf scores, so any finite shift works for it.
+    const float shift = m_used != -INFINITY ? m_used : 0.f;
     uint4 pb[4];
-    {
-      const bool live = m_used != -INFINITY;
-      float p[32];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < 4; ++ks) {
+      float p[8];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float sv = sacc[kb][v];
-          const float pv = (live && sv != -INFINITY) ? dev::fast_exp2(fmaf(sv, c, -m_used)) : 0.f;
-          p[kb * 16 + v] = pv;
-          lsum += pv;
-        }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        pb[ks] = make_uint4(pack2(p[8 * ks + 0], p[8 * ks + 1]), pack2(p[8 * ks + 2], p[8 * ks + 3]),
-                            pack2(p[8 * ks + 4], p[8 * ks + 5]), pack2(p[8 * ks + 6], p[8 * ks + 7]));
+      for (int e = 0; e < 8; ++e) {
+        p[e] = dev::fast_exp2(fmaf(scur[ks >> 1][8 * (ks & 1) + e], c, -shift));
+        lsum += p[e];
+      }
+      pb[ks] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
     }
 
     // O^T += V^T P^T: d-block n, k-step ks (16 keys).  The transposed read
     // gives lane i of each 16-lane group the value rows of 4 keys at one dim.
-    {
-      const int grp = lane >> 4, gi = lane & 15;
-      const int dsub = 16 * (grp & 1) + 4 * (gi & 3);
-      const int krow0 = 4 * h + (gi >> 2);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const uint16_t* base = &s_v[buf][(16 * ks + krow0) * kPitchV + 32 * n + dsub];
-          const bf16x4_t lo = tr_read(base);
-          const bf16x4_t hi = tr_read(base + 8 * kPitchV);
-          const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[ks]), oacc[n], 0, 0, 0);
-        }
+      for (int n = 0; n < 4; ++n) {
+        const uint16_t* base = v_rd + 16 * ks * kPitchV + 32 * n;
+        const bf16x4_t lo = tr_read(base);
+        const bf16x4_t hi = tr_read(base + 8 * kPitchV);
+        const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[ks]), oacc[n], 0, 0, 0);
       }
     }
 
-    if (t + 1 < ntiles) PKV_LSTORE(buf ^ 1);
+    __syncthreads();   // every wave is done with K(t+1) and V(t)
+    if (t + 2 < ntiles) lstore_k();
+    if (t + 1 < ntiles) lstore_v();
+    __syncthreads();
+  };
+
+  f32x16_t sa[2], sb[2];
+  if (ntiles > 0) {
+    gload_k(kv_lo);
+    gload_v(kv_lo);
+    lstore_k();
+    lstore_v();
+    __syncthreads();
+    scores(sa);
+    if (ntiles > 1) gload_k(kv_lo + kKeys);
+    __syncthreads();
+    if (ntiles > 1) lstore_k();
     __syncthreads();
   }
-
-#undef PKV_GLOAD
-#undef PKV_LSTORE
+  for (int32_t t = 0; t < ntiles; t += 2) {
+    body(t, sa, sb);
+    if (t + 1 >= ntiles) break;
+    body(t + 1, sb, sa);
+  }
 
   // Epilogue: row sum over both lane halves, normalise, write.
   const float ltot = lsum + __shfl_xor(lsum, 32);
