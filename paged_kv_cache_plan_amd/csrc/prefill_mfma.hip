@@ -195,13 +195,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
 
   // S^T of the K tile currently in LDS: two 32-key blocks.
   const uint16_t* const k_rd = &s_k[col * kPitchK + 8 * h];
+  // The two 32-key blocks alternate so consecutive MFMAs are independent.
   auto scores = [&](f32x16_t (&sacc)[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < 8; ++st) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const uint4 kv = *reinterpret_cast<const uint4*>(k_rd + kb * 32 * kPitchK + 16 * st);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[st]), sacc[kb], 0, 0, 0);
       }

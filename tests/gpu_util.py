@@ -78,7 +78,8 @@ def check_lse(got, ref, what: str, atol=LSE_ATOL, mask=None):
     if mask is not None:
         got, ref = got[mask], ref[mask]
     same_inf = np.isneginf(got) & np.isneginf(ref)
-    err = np.where(same_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):
+        err = np.where(same_inf, 0.0, np.abs(got - ref))
     assert np.all(np.isfinite(err)), f"{what}: non-finite LSE mismatch"
     assert err.max(initial=0.0) <= atol, f"{what}: LSE max err {err.max()}"
     return float(err.max(initial=0.0))
