@@ -88,10 +88,11 @@ def mla_bytes(b) -> dict:
 class Runner:
     """Device copies of one batch with ``layers`` independent KV pools."""
 
-    def __init__(self, b, layers: int):
+    def __init__(self, b, layers: int, time_merge: bool = False):
         import torch
         import paged_kv_cache_plan_amd as pkv
         self.b, self.torch, self.pkv = b, torch, pkv
+        self.time_merge = time_merge
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
@@ -132,7 +133,8 @@ class Runner:
         return self.plan
 
     def layer(self, i: int, ev=None):
-        """append + attention + merge for layer i; ev = (start, end) events around attention."""
+        """append + attention + merge for layer i; ev = (start, end) events around
+        attention (and the merge too when time_merge is set; run_mla always merges)."""
         b, plan = self.b, self.plan
         if b.mode == "mla":
             pool = self.pools[i % len(self.pools)]
@@ -150,9 +152,12 @@ class Runner:
         if ev:
             ev[0].record()
         plan.run_attention(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
+        if self.time_merge:
+            plan.run_merge(self.out, self.lse)
         if ev:
             ev[1].record()
-        plan.run_merge(self.out, self.lse)
+        if not self.time_merge:
+            plan.run_merge(self.out, self.lse)
 
 
 def measure(runner: Runner, layers: int, steps: int, warmup: int) -> dict:
@@ -217,6 +222,54 @@ def cpu_baseline(b, budget_s: float = 12.0) -> dict:
             "host_cpus": os.cpu_count()}
 
 
+COUNTER_KERNELS = {"decode": "attn_rows_kernel", "skewed": "attn_rows_kernel", "prefill": "prefill_mfma_kernel",
+                   "mla": "mla_decode_kernel"}
+
+
+def ingest_counters(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
+    """HBM bytes per launch of the workload's attention kernel from two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of
+    ``bench.py --only W --calibrate-copy-mib M``.  Each counter is scaled by
+    what it reads for the calibration pass: the fill of the M MiB source (its
+    WRITE_SIZE) and the plain device copy right after it (its FETCH_SIZE)."""
+    import csv
+
+    def rows(path):
+        with open(path) as f:
+            out = {}
+            for r in csv.DictReader(f):
+                out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+            return [out[k] for k in sorted(out)]
+
+    def calib(rs, counter):
+        for i, (name, val) in enumerate(rs):
+            if "FillFunctor" in name:
+                copy = next(v for n, v in rs[i + 1:] if "copyBuffer" in n)
+                return val if counter == "WRITE_SIZE" else copy
+        raise ValueError("no calibration fill/copy dispatch in the counter file")
+
+    f_rows, w_rows = rows(fetch_csv), rows(write_csv)
+    known_kib = None
+    for name, val in w_rows:
+        if "FillFunctor" in name:
+            known_kib = val        # fill of the calibration source: written once, exactly
+            break
+    if known_kib is None:
+        raise ValueError("no calibration fill dispatch")
+    f_scale = known_kib / calib(f_rows, "FETCH_SIZE")
+    w_scale = known_kib / calib(w_rows, "WRITE_SIZE")
+    sub = COUNTER_KERNELS[workload]
+    fetch = [v for n, v in f_rows if sub in n]
+    write = [v for n, v in w_rows if sub in n]
+    fb = float(np.mean(fetch)) * 1024 * f_scale
+    wb = float(np.mean(write)) * 1024 * w_scale
+    return {"source_hash": source_hash(), "kernel": sub, "dispatches": len(fetch),
+            "fetch_kib_raw": float(np.mean(fetch)), "write_kib_raw": float(np.mean(write)),
+            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+            "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+            "command": command}
+
+
 def read_traffic(kernel: str):
     """Counter-measured HBM traffic per launch from profiles/, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -243,7 +296,20 @@ def main():
                     help="time one workload (profiling runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files into profiles/traffic.json (no GPU)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        w, fcsv, wcsv = args.ingest_counters
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        data = json.load(open(path)) if os.path.exists(path) else {}
+        cmd = (f"rocprofv3 --pmc {{FETCH_SIZE|WRITE_SIZE}} -f csv -d <dir> -o p -- python3 bench.py --only {w} "
+               "--steps 2 --warmup 1 --layers 4 --secondary-layers 4 --no-cpu-baseline --calibrate-copy-mib 512")
+        data[w] = ingest_counters(w, fcsv, wcsv, cmd)
+        with open(path, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+        print(json.dumps(data[w]))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
@@ -295,11 +361,11 @@ def main():
     if "skewed" in which:
         b = wl.make("skewed")
         layers = args.secondary_layers
-        r = Runner(b, layers)
+        r = Runner(b, layers, time_merge=True)
         m = measure(r, layers, args.steps, args.warmup)
         nb = decode_bytes(b)
         result["skewed"] = dict(m, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9, bytes=nb)
-        log(f"skewed: attention {result['skewed']['gbs']:.1f} GB/s ({m['attn_ms_mean'] * 1e3:.1f} us)")
+        log(f"skewed: attention + merge {result['skewed']['gbs']:.1f} GB/s ({m['attn_ms_mean'] * 1e3:.1f} us)")
         del r
     if "mla" in which:
         b = wl.make("mla")
@@ -355,12 +421,13 @@ def main():
     if "skewed" in result:
         s = result["skewed"]
         line["skewed_decode"] = {"value": round(s["gbs"], 1), "unit": "GB/s", "frac": round(s["gbs"] / HBM_PEAK_GBS, 4),
-                                 "launch_us_mean": round(s["attn_ms_mean"] * 1e3, 2),
+                                 "run_us_mean": round(s["attn_ms_mean"] * 1e3, 2), "timed": "attention + merge",
                                  "merge_items": s["plan_info"]["num_merges"]}
     if "mla" in result:
         mm = result["mla"]
         line["mla_decode"] = {"value": round(mm["gbs"], 1), "unit": "GB/s", "frac": round(mm["gbs"] / HBM_PEAK_GBS, 4),
-                              "tflops": round(mm["tflops"], 2), "launch_us_mean": round(mm["attn_ms_mean"] * 1e3, 2)}
+                              "tflops": round(mm["tflops"], 2), "run_us_mean": round(mm["attn_ms_mean"] * 1e3, 2),
+                              "timed": "attention + merge"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl.make("decode"))
     print(json.dumps(line), flush=True)

@@ -100,8 +100,16 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Rows with many (head, dim) accumulators and wide register sets (float32, or
+// bf16 with 8 heads per group at head_dim 128) need more than 256 VGPRs; they
+// run one wave per SIMD instead of spilling.
+template <typename T, int D, int G>
+constexpr int rows_min_waves() {
+  return int(sizeof(T)) * D * G >= 2048 ? 1 : PKV_ROWS_MIN_WAVES;
+}
+
 template <typename T, int D, int G, bool kAligned>
-__global__ __launch_bounds__(kThreads, PKV_ROWS_MIN_WAVES) void attn_rows_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr int E = Elem<T>::kPer16;   // elements per 16-byte chunk
   constexpr int NCH = D / E;           // chunks per row
@@ -286,19 +294,27 @@ __global__ __launch_bounds__(kThreads, PKV_ROWS_MIN_WAVES) void attn_rows_kernel
         dev::wave_lds_sync();
       };
 
-      // Two register sets: the loads of block i+1 are in flight while block i computes.
+      // Two register sets: the loads of block i+1 are in flight while block i
+      // computes.  The prefetch is unconditional (past the end it re-reads the
+      // last block, which the caches serve) so that every path through the
+      // loop has the same loads outstanding and the wait before a block's
+      // compute covers only that block's own loads.
       constexpr int32_t kStride = kWaves * kBlockKeys;
+      const int32_t blk_max = kAligned ? ((thi - 1) & ~(kBlockKeys - 1)) : thi - 1;
       uint4 ka[KC], kb[KC], va[NU][VC], vb[NU][VC];
       int32_t blk = tlo + wave * kBlockKeys;
-      if (blk < thi) load(blk, ka, va);
-      while (blk < thi) {
-        if (blk + kStride < thi) load(blk + kStride, kb, vb);
-        compute(blk, ka, va);
-        blk += kStride;
-        if (blk >= thi) break;
-        if (blk + kStride < thi) load(blk + kStride, ka, va);
-        compute(blk, kb, vb);
-        blk += kStride;
+      if (blk < thi) {
+        load(blk, ka, va);
+        while (true) {
+          load(min(blk + kStride, blk_max), kb, vb);
+          compute(blk, ka, va);
+          blk += kStride;
+          if (blk >= thi) break;
+          load(min(blk + kStride, blk_max), ka, va);
+          compute(blk, kb, vb);
+          blk += kStride;
+          if (blk >= thi) break;
+        }
       }
     }
 

@@ -70,35 +70,110 @@ template <>
 __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float x) { p[i] = dev::f32_to_bf16(x); }
 
 // Split-KV merge: workgroup (merge item, head); the chunk states of row r are
-// partial rows slot0 + c*num_rows + r.
-template <typename T>
-__global__ __launch_bounds__(128) void merge_partials_kernel(const MergePartialArgs a) {
+// partial rows slot0 + c*num_rows + r.  A long row can have hundreds of
+// chunks, so the chunks are spread over the workgroup: the shift (largest
+// statistic) and the weight sum are block reductions, the normalised scales of
+// up to kMergeSeg chunks at a time are staged in LDS, and groups of threads
+// accumulate disjoint chunk subsets of the output row (4 dims per thread) whose
+// sums are added at the end.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeSeg = 512;
+
+__device__ __forceinline__ float block_reduce(float x, float* s_red, bool is_max) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  __syncthreads();   // s_red free (previous reduction fully read)
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = s_red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = is_max ? fmaxf(r, s_red[w]) : r + s_red[w];
+  return r;
+}
+
+template <typename T, bool kVec4>
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const MergePartialArgs a) {
+  __shared__ float s_w[kMergeSeg];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float4 s_acc[kMergeThreads];
   const MergeItem mi = a.merges[blockIdx.x];
   const int32_t h = blockIdx.y;
+  const int tid = threadIdx.x;
   const int32_t hq = a.num_heads, d_all = a.head_dim;
+  constexpr int kVec = kVec4 ? 4 : 1;
+  const int32_t nvec = d_all / kVec;
+  const int32_t tpr = min(nvec, kMergeThreads);   // threads per group (one vector each)
+  const int32_t groups = kMergeThreads / tpr;
+  const int32_t grp = tid / tpr, lv = tid - (tid / tpr) * tpr;
+  const int32_t n = mi.num_chunks;
   for (int32_t r = 0; r < mi.num_rows; ++r) {
+    const int64_t row_base = int64_t(mi.slot0) + r;   // partial row of chunk c: row_base + c * num_rows
     float mx = -INFINITY;
-    for (int32_t c = 0; c < mi.num_chunks; ++c)
-      mx = fmaxf(mx, a.part_lse[int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h]);
-    float z = 0.f;
+    for (int32_t c = tid; c < n; c += kMergeThreads)
+      mx = fmaxf(mx, a.part_lse[(row_base + int64_t(c) * mi.num_rows) * hq + h]);
+    mx = block_reduce(mx, s_red, true);
+    float zp = 0.f;
     if (mx != -INFINITY)
-      for (int32_t c = 0; c < mi.num_chunks; ++c) {
-        const float s = a.part_lse[int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h];
-        if (s != -INFINITY) z += dev::fast_exp2(s - mx);
+      for (int32_t c = tid; c < n; c += kMergeThreads) {
+        const float sc = a.part_lse[(row_base + int64_t(c) * mi.num_rows) * hq + h];
+        if (sc != -INFINITY) zp += dev::fast_exp2(sc - mx);
       }
+    const float z = block_reduce(zp, s_red, false);
+    const float inv_z = z > 0.f ? 1.f / z : 0.f;
     const int32_t row = mi.q_row0 + r;
     T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
-    for (int32_t d = threadIdx.x; d < d_all; d += blockDim.x) {
-      float acc = 0.f;
-      if (z > 0.f)
-        for (int32_t c = 0; c < mi.num_chunks; ++c) {
-          const int64_t prow = int64_t(mi.slot0 + c * mi.num_rows + r) * hq + h;
-          const float s = a.part_lse[prow];
-          if (s != -INFINITY) acc = fmaf(dev::fast_exp2(s - mx) / z, a.part_o[prow * d_all + d], acc);
+    for (int32_t v0 = 0; v0 < nvec; v0 += tpr) {
+      const int32_t v = v0 + lv;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int32_t seg = 0; seg < n && z > 0.f; seg += kMergeSeg) {
+        const int32_t m = min(kMergeSeg, n - seg);
+        __syncthreads();   // s_w free
+        for (int32_t i = tid; i < m; i += kMergeThreads) {
+          const float sc = a.part_lse[(row_base + int64_t(seg + i) * mi.num_rows) * hq + h];
+          s_w[i] = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx) * inv_z;
         }
-      store_f<T>(orow, d, acc);
+        __syncthreads();
+        if (grp < groups && v < nvec) {
+#pragma unroll 4
+          for (int32_t i = grp; i < m; i += groups) {
+            const float w = s_w[i];
+            if (w != 0.f) {
+              const float* src = a.part_o + ((row_base + int64_t(seg + i) * mi.num_rows) * hq + h) * d_all + v * kVec;
+              if constexpr (kVec4) {
+                const float4 x = *reinterpret_cast<const float4*>(src);
+                acc.x = fmaf(w, x.x, acc.x);
+                acc.y = fmaf(w, x.y, acc.y);
+                acc.z = fmaf(w, x.z, acc.z);
+                acc.w = fmaf(w, x.w, acc.w);
+              } else {
+                acc.x = fmaf(w, *src, acc.x);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();   // s_acc free
+      s_acc[tid] = acc;
+      __syncthreads();
+      if (grp == 0 && v < nvec) {
+        float4 t = acc;
+        for (int32_t g = 1; g < groups; ++g) {
+          const float4 u = s_acc[g * tpr + lv];
+          t.x += u.x;
+          t.y += u.y;
+          t.z += u.z;
+          t.w += u.w;
+        }
+        store_f<T>(orow, v * kVec, t.x);
+        if constexpr (kVec4) {
+          store_f<T>(orow, v * kVec + 1, t.y);
+          store_f<T>(orow, v * kVec + 2, t.z);
+          store_f<T>(orow, v * kVec + 3, t.w);
+        }
+      }
     }
-    if (threadIdx.x == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+    if (tid == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
   }
 }
 
@@ -178,10 +253,19 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
 
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t st) {
   const dim3 grid(uint32_t(a.num_merges), uint32_t(a.num_heads));
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, dim3(128), 0, st, a);
-  else
-    hipLaunchKernelGGL(merge_partials_kernel<float>, grid, dim3(128), 0, st, a);
+  const dim3 block(kMergeThreads);
+  const bool vec4 = a.head_dim % 4 == 0;
+  if (dtype == kBF16) {
+    if (vec4)
+      hipLaunchKernelGGL((merge_partials_kernel<uint16_t, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((merge_partials_kernel<uint16_t, false>), grid, block, 0, st, a);
+  } else {
+    if (vec4)
+      hipLaunchKernelGGL((merge_partials_kernel<float, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((merge_partials_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ constexpr int kStepsPerWave = kDim / 16 / kWaves;   // 9 score k-steps per wave
 constexpr int kLoads = kKeys * kChunks / kThreads;  // 16-byte loads per thread per tile
 constexpr int kMaxChunkPages = 1024;
 constexpr float kLazyMax = 8.f;
+constexpr int kXcds = 8;               // MI355X: 8 XCDs of 32 CUs
 static_assert(kKeys * kChunks % kThreads == 0, "tile loads split evenly");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -71,8 +72,14 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(const MlaArgs a
   __shared__ float s_part[kWaves][16][64];   // partial S^T per wave, [value][lane]
   __shared__ int32_t s_pages[kMaxChunkPages];
 
-  const int32_t item_idx = blockIdx.x / a.head_groups;
-  const int32_t grp = blockIdx.x - item_idx * a.head_groups;
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with
+  // its own L2.  The head groups of one item read the same latent rows, so
+  // they are given consecutive slots on one XCD: the k-th workgroup of XCD x
+  // takes item (k / head_groups) * 8 + x, head group k % head_groups.
+  const int32_t xcd = int32_t(blockIdx.x & (kXcds - 1)), k_on_xcd = int32_t(blockIdx.x / kXcds);
+  const int32_t item_idx = (k_on_xcd / a.head_groups) * kXcds + xcd;
+  const int32_t grp = k_on_xcd - (k_on_xcd / a.head_groups) * a.head_groups;
+  if (item_idx >= a.num_items) return;
   const Item it = a.items[item_idx];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(const MlaArgs a
 
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
   if (a.num_heads != a.head_groups * kHeadsPerGroup) return hipErrorInvalidValue;
-  const int64_t blocks = int64_t(a.num_items) * a.head_groups;
+  const int64_t blocks = (int64_t(a.num_items) + kXcds - 1) / kXcds * kXcds * a.head_groups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (a.page_shift >= 0)
     hipLaunchKernelGGL((mla_decode_kernel<true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);

@@ -14,7 +14,7 @@ no request owns (unused pages, page tails past last_page_len, and the slots
 an append is about to fill) holds NaN, so any read of them shows.
 
 Workloads (sizes follow the pages' worked example and the serving mixes
-described there; see the design doc for the recipe):
+described there):
   worked    3 requests, qo 3/1/4, kv 6/2/9, page 4, pool 16, heads 4/2, dim
             64, float32, NHD, causal, sm_scale 1/8.  ``literal_pages=True``
             uses the pages' own page ids 7,2 | 11 | 3,14,6.
