@@ -47,6 +47,16 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockKeys = 16;
 constexpr int kSegPages = 1024;   // page ids staged in LDS per segment
+// K and V rows are read once per launch: non-temporal loads (compile-time tunable).
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 1
+#endif
+constexpr bool kStreamKV = PKV_DECODE_NT != 0;
+// Key blocks in flight per wave (register sets): 2 or 3 (compile-time tunable;
+// 3 applies to bf16 only, where the extra set still fits in 256 VGPRs).
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 2
+#endif
 // Minimum waves per SIMD the register allocation must allow (compile-time tunable).
 #ifndef PKV_ROWS_MIN_WAVES
 #define PKV_ROWS_MIN_WAVES 2
@@ -76,6 +86,14 @@ __device__ __forceinline__ void dot_chunk<float>(const uint4& q, const uint4& k,
   acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
 }
 
+// Two floats as a bf16 pair (round to nearest even): lo in bits 0-15.
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+  dev::bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
@@ -87,16 +105,15 @@ __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) { *p =
 template <>
 __device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
 
-// Reductions over the QPG quads of one softmax group: 4 quads = a 16-lane
-// row, 2 quads = half a row.
-template <int QPG>
-__device__ __forceinline__ float group_max(float x) {
-  if constexpr (QPG == 4) {
-    x = fmaxf(x, dev::dpp<dev::kRowRor4>(x));
-    x = fmaxf(x, dev::dpp<dev::kRowRor8>(x));
-  } else {
-    x = fmaxf(x, dev::dpp<dev::kRowHalfMirror>(x));
-  }
+// Sum over the L lanes that share one key row (L = 16: a DPP row; L = 8: half
+// a row).  Every step pairs lanes symmetrically (x + partner), so all L lanes
+// end with bitwise the same sum.
+template <int L>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dev::dpp<dev::kQuadSwap1>(x);
+  x += dev::dpp<dev::kQuadSwap2>(x);
+  x += dev::dpp<dev::kRowHalfMirror>(x);
+  if constexpr (L == 16) x += dev::dpp<dev::kRowMirror>(x);
   return x;
 }
 
@@ -111,20 +128,17 @@ constexpr int rows_min_waves() {
 template <typename T, int D, int G, bool kAligned>
 __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
-  constexpr int E = Elem<T>::kPer16;   // elements per 16-byte chunk
-  constexpr int NCH = D / E;           // chunks per row
-  constexpr int KC = NCH / 4;          // score phase: chunks per lane (4 lanes per key)
-  constexpr int VL = NCH < 16 ? NCH : 16;  // value phase: lanes per row
-  constexpr int VC = NCH / VL;         // value phase: chunks per lane
-  constexpr int VT = 64 / VL;          // value phase: rows per load instruction = softmax groups
-  constexpr int NU = kBlockKeys / VT;  // value phase: passes per block = keys per group per block
-  constexpr int QPG = kBlockKeys / VT; // score phase: quads per softmax group
-  static_assert(NCH % 4 == 0 && NCH % VL == 0 && (QPG == 4 || QPG == 2), "unsupported head_dim");
-  static_assert(NU % 2 == 0, "value passes come in pairs");
+  constexpr int E = Elem<T>::kPer16;       // elements per 16-byte chunk
+  constexpr int NCH = D / E;               // chunks per key row
+  constexpr int VL = NCH < 16 ? NCH : 16;  // lanes per key row = one softmax group
+  constexpr int VC = NCH / VL;             // chunks per lane
+  constexpr int VT = 64 / VL;              // key rows per load instruction = groups per wave
+  constexpr int NU = kBlockKeys / VT;      // load instructions per block = keys per group per block
+  static_assert(NCH % VL == 0 && (VL == 16 || VL == 8), "unsupported head_dim");
+  static_assert(NU % 2 == 0, "keys of a group come in pairs");
+  constexpr int kDepth = (kBF16 && G <= 4) ? PKV_DECODE_DEPTH : 2;
 
   __shared__ int32_t s_pages[kSegPages];
-  // Block weights: bf16 pairs (keys 2w*VT+g, (2w+1)*VT+g) per head, or fp32.
-  __shared__ uint32_t s_p[kWaves][NU][VT][G];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_acc[kWaves][G][D];
@@ -135,12 +149,9 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   const Item it = a.items[item_idx];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // Score phase: quad qk scores key u*VT + g of the block, where g = qk / QPG
-  // is its softmax group and u = qk % QPG its pass in the value phase.
-  const int qk = lane >> 2, qi = lane & 3;
-  const int k_u = qk % QPG, k_g = qk / QPG;
-  const int key_in_block = k_u * VT + k_g;
-  const int vg = lane / VL, vi = lane % VL;    // value phase: group (= k_g of this lane), chunk column
+  // Group vg of the wave holds key u * VT + vg of each 16-key block (u < NU);
+  // lane vi of the group holds chunks vi + VL * c of those rows.
+  const int vg = lane / VL, vi = lane % VL;
 
   const T* kbase = static_cast<const T*>(a.k) + int64_t(kvh) * a.head_stride;
   const T* vbase = static_cast<const T*>(a.v) + int64_t(kvh) * a.head_stride;
@@ -158,14 +169,14 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
     const int32_t lo = it.kv_start;
     const int32_t hi = min(it.kv_end, it.diag + r + 1);
 
-    uint4 qreg[G][KC];
+    uint4 qreg[G][VC];
     const T* qrow = static_cast<const T*>(a.q) + int64_t(row) * a.q_stride_token +
                     int64_t(kvh * G) * a.q_stride_head;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + int64_t(h) * a.q_stride_head + (qi + 4 * c) * E);
+      for (int c = 0; c < VC; ++c)
+        qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + int64_t(h) * a.q_stride_head + (vi + VL * c) * E);
 
     float m[G], l[G], acc[G][VC * E];
 #pragma unroll
@@ -195,58 +206,65 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         j = min(j, thi - 1);
         return int64_t(s_pages[page_of(j) - sp]) * a.page_stride + int64_t(slot_of(j)) * a.token_stride;
       };
-      auto load = [&](int32_t blk, uint4 (&kr)[KC], uint4 (&vr)[NU][VC]) {
-        int64_t koff;
-        int64_t voff[NU];
+      // K and V rows of one block: instruction u moves key rows u*VT + g, each
+      // read by VL lanes as contiguous 16-byte chunks (whole rows per request).
+      auto load = [&](int32_t blk, uint4 (&kr)[NU][VC], uint4 (&vr)[NU][VC]) {
+        int64_t off[NU];
         if constexpr (kAligned) {
           // A 16-key block never crosses a page: one page id for the block.
           const int64_t base = int64_t(s_pages[(blk >> pshift) - sp]) * a.page_stride;
           const int32_t last = thi - 1 - blk;
           const int32_t s0 = blk & (psz - 1);
-          koff = base + int64_t(s0 + min(key_in_block, last)) * a.token_stride;
 #pragma unroll
-          for (int u = 0; u < NU; ++u) voff[u] = base + int64_t(s0 + min(u * VT + vg, last)) * a.token_stride;
+          for (int u = 0; u < NU; ++u) off[u] = base + int64_t(s0 + min(u * VT + vg, last)) * a.token_stride;
         } else {
-          koff = row_off(blk + key_in_block);
 #pragma unroll
-          for (int u = 0; u < NU; ++u) voff[u] = row_off(blk + u * VT + vg);
+          for (int u = 0; u < NU; ++u) off[u] = row_off(blk + u * VT + vg);
         }
-        const T* krow = kbase + koff;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) kr[c] = *reinterpret_cast<const uint4*>(krow + (qi + 4 * c) * E);
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-          for (int c = 0; c < VC; ++c)
-            vr[u][c] = *reinterpret_cast<const uint4*>(vbase + voff[u] + (vi + VL * c) * E);
+          for (int c = 0; c < VC; ++c) kr[u][c] = dev::load16<kStreamKV>(kbase + off[u] + (vi + VL * c) * E);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int c = 0; c < VC; ++c) vr[u][c] = dev::load16<kStreamKV>(vbase + off[u] + (vi + VL * c) * E);
       };
 
-      auto compute = [&](int32_t blk, uint4 (&kr)[KC], uint4 (&vr)[NU][VC]) {
-        const bool kok = blk + key_in_block < thi;
+      auto compute = [&](int32_t blk, uint4 (&kr)[NU][VC], uint4 (&vr)[NU][VC]) {
+        // Scores of the group's NU keys for the G heads; every lane of the
+        // group ends with all of them, so the softmax below is in-lane.
+        float p[NU][G];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const bool ok = blk + u * VT + vg < thi;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float part = 0.f;
+#pragma unroll
+            for (int c = 0; c < VC; ++c) dot_chunk<T>(qreg[h][c], kr[u][c], part);
+            const float sc = row_sum<VL>(part) * a.scale_log2;
+            p[u][h] = ok ? sc : -INFINITY;
+          }
+        }
         float scale[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float part = 0.f;
+          float mx = p[0][h];
 #pragma unroll
-          for (int c = 0; c < KC; ++c) dot_chunk<T>(qreg[h][c], kr[c], part);
-          float s = dev::quad_sum(part) * a.scale_log2;
-          s = kok ? s : -INFINITY;
-          const float m_new = fmaxf(m[h], group_max<QPG>(s));
-          const bool live = m_new != -INFINITY;       // false only while every key so far was skipped
+          for (int u = 1; u < NU; ++u) mx = fmaxf(mx, p[u][h]);
+          const float m_new = fmaxf(m[h], mx);
+          const bool live = m_new != -INFINITY;   // false only while every key so far was skipped
           scale[h] = live ? dev::fast_exp2(m[h] - m_new) : 1.f;
-          const float p = live ? dev::fast_exp2(s - m_new) : 0.f;
-          l[h] = l[h] * scale[h] + p;
-          m[h] = m_new;
-          if constexpr (kBF16) {
-            // lane qi of the quad stores heads qi, qi+4, ... as the bf16 half
-            // (u % 2) of the pair slot of pass pair u / 2.
-            if (h % 4 == qi)
-              reinterpret_cast<uint16_t*>(&s_p[wave][k_u / 2][k_g][h])[k_u % 2] = dev::f32_to_bf16(p);
-          } else {
-            if (h % 4 == qi) s_p[wave][k_u][k_g][h] = __float_as_uint(p);
+          float sum = 0.f;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            p[u][h] = live ? dev::fast_exp2(p[u][h] - m_new) : 0.f;
+            sum += p[u][h];
           }
+          l[h] = l[h] * scale[h] + sum;
+          m[h] = m_new;
         }
-        dev::wave_lds_sync();
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           if (__any(scale[h] != 1.f)) {
@@ -255,11 +273,13 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           }
         }
         if constexpr (kBF16) {
+          // Two keys per v_dot2c: the weights as a bf16 pair, the values of
+          // the same two keys paired per dim with v_perm.
 #pragma unroll
           for (int w = 0; w < NU / 2; ++w) {
             uint32_t pp[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) pp[h] = s_p[wave][w][vg][h];
+            for (int h = 0; h < G; ++h) pp[h] = pack_pair(p[2 * w][h], p[2 * w + 1][h]);
 #pragma unroll
             for (int c = 0; c < VC; ++c) {
 #pragma unroll
@@ -277,54 +297,76 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            float pv[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = __uint_as_float(s_p[wave][u][vg][h]);
+          for (int u = 0; u < NU; ++u)
 #pragma unroll
             for (int c = 0; c < VC; ++c)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float x = __uint_as_float(word(vr[u][c], i));
 #pragma unroll
-                for (int h = 0; h < G; ++h) acc[h][c * E + i] = fmaf(pv[h], x, acc[h][c * E + i]);
+                for (int h = 0; h < G; ++h) acc[h][c * E + i] = fmaf(p[u][h], x, acc[h][c * E + i]);
               }
-          }
         }
-        dev::wave_lds_sync();
       };
 
-      // Two register sets: the loads of block i+1 are in flight while block i
-      // computes.  The prefetch is unconditional (past the end it re-reads the
-      // last block, which the caches serve) so that every path through the
-      // loop has the same loads outstanding and the wait before a block's
-      // compute covers only that block's own loads.
+      // Register sets: the loads of the next block(s) are in flight while a
+      // block computes.  The prefetch is unconditional (past the end it
+      // re-reads the last block, which the caches serve) so that every path
+      // through the loop has the same loads outstanding and the wait before a
+      // block's compute covers only that block's own loads.
       constexpr int32_t kStride = kWaves * kBlockKeys;
       const int32_t blk_max = kAligned ? ((thi - 1) & ~(kBlockKeys - 1)) : thi - 1;
-      uint4 ka[KC], kb[KC], va[NU][VC], vb[NU][VC];
       int32_t blk = tlo + wave * kBlockKeys;
-      if (blk < thi) {
-        load(blk, ka, va);
-        while (true) {
+      if constexpr (kDepth == 3) {
+        uint4 ka[NU][VC], kb[NU][VC], kc[NU][VC], va[NU][VC], vb[NU][VC], vc[NU][VC];
+        if (blk < thi) {
+          load(blk, ka, va);
           load(min(blk + kStride, blk_max), kb, vb);
-          compute(blk, ka, va);
-          blk += kStride;
-          if (blk >= thi) break;
-          load(min(blk + kStride, blk_max), ka, va);
-          compute(blk, kb, vb);
-          blk += kStride;
-          if (blk >= thi) break;
+          while (true) {
+            load(min(blk + 2 * kStride, blk_max), kc, vc);
+            compute(blk, ka, va);
+            blk += kStride;
+            if (blk >= thi) break;
+            load(min(blk + 2 * kStride, blk_max), ka, va);
+            compute(blk, kb, vb);
+            blk += kStride;
+            if (blk >= thi) break;
+            load(min(blk + 2 * kStride, blk_max), kb, vb);
+            compute(blk, kc, vc);
+            blk += kStride;
+            if (blk >= thi) break;
+          }
+        }
+      } else {
+        uint4 ka[NU][VC], kb[NU][VC], va[NU][VC], vb[NU][VC];
+        if (blk < thi) {
+          load(blk, ka, va);
+          while (true) {
+            load(min(blk + kStride, blk_max), kb, vb);
+            compute(blk, ka, va);
+            blk += kStride;
+            if (blk >= thi) break;
+            load(min(blk + kStride, blk_max), ka, va);
+            compute(blk, kb, vb);
+            blk += kStride;
+            if (blk >= thi) break;
+          }
         }
       }
     }
 
-    // Wave state: rescale every group to the wave max, then sum l over quads
-    // and acc over value-phase groups.
+    // Wave state: rescale every group to the wave max, then sum l and acc
+    // over the groups (l and m are the same on all lanes of a group).
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mw = dev::quads_max(m[h]);
+      float mw = m[h];
+#pragma unroll
+      for (int off = VL; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
       const float f = m[h] == -INFINITY ? 0.f : dev::fast_exp2(m[h] - mw);
-      l[h] = dev::quads_sum(l[h] * f);
+      float lw = l[h] * f;
+#pragma unroll
+      for (int off = VL; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
+      l[h] = lw;
       m[h] = mw;
 #pragma unroll
       for (int e = 0; e < VC * E; ++e) {

@@ -41,7 +41,8 @@ constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
-constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;      // lane i <-> 15 - i within a row
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
 
 // Sum over the 4 lanes of a quad (every lane gets the total).
 __device__ __forceinline__ float quad_sum(float x) {
@@ -75,6 +76,20 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global load with the non-temporal hint: for data read once (the KV
+// stream of decode), so it does not displace reusable lines in the caches.
+// Streaming reads reach markedly higher HBM bandwidth this way on gfx950.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <bool kNT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+  if constexpr (kNT) {
+    const u32x4_t x = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  } else {
+    return *static_cast<const uint4*>(p);
+  }
+}
 
 // Element offset of token j's row (slot within its page) given the request's
 // page list: page kv_indices[page_base + j / P], slot j % P.  Returns -1 for a

@@ -48,6 +48,12 @@ constexpr int kLoads = kKeys * kChunks / kThreads;  // 16-byte loads per thread 
 constexpr int kMaxChunkPages = 1024;
 constexpr float kLazyMax = 8.f;
 constexpr int kXcds = 8;               // MI355X: 8 XCDs of 32 CUs
+// Latent rows are shared by the head groups of a chunk through L2; the
+// non-temporal hint is a compile-time choice.
+#ifndef PKV_MLA_NT
+#define PKV_MLA_NT 0
+#endif
+constexpr bool kStreamKV = PKV_MLA_NT != 0;
 static_assert(kKeys * kChunks % kThreads == 0, "tile loads split evenly");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(const MlaArgs a
   // i.e. key c / 72, 16-byte chunk c % 72 (ckv for chunks < 64, kpe after).
   // Keys past the chunk end re-read the last key (their scores are masked).
   // The nine staging registers are named individually so they stay in VGPRs.
-  auto src_of = [&](int32_t t0, int i) -> const uint4* {
+  auto src_of = [&](int32_t t0, int i) -> const void* {
     const int c = tid + kThreads * i;
     const int key = c / kChunks, part = c - (c / kChunks) * kChunks;
     const int32_t j = min(t0 + key, kv_hi - 1);
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(const MlaArgs a
     const int64_t off =
         int64_t(s_pages[min(pi - pg_lo, kMaxChunkPages - 1)]) * a.page_stride + int64_t(sl) * a.token_stride;
     const uint16_t* base = part < kDimCkv / 8 ? ckv + part * 8 : kpe + (part - kDimCkv / 8) * 8;
-    return reinterpret_cast<const uint4*>(base + off);
+    return base + off;
   };
   auto dst_of = [&](int i) -> uint4* {
     const int c = tid + kThreads * i;
@@ -144,15 +150,15 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(const MlaArgs a
   uint4 st0, st1, st2, st3, st4, st5, st6, st7, st8;
 #define PKV_MLA_GLOAD(T0)      \
   do {                         \
-    st0 = *src_of((T0), 0);    \
-    st1 = *src_of((T0), 1);    \
-    st2 = *src_of((T0), 2);    \
-    st3 = *src_of((T0), 3);    \
-    st4 = *src_of((T0), 4);    \
-    st5 = *src_of((T0), 5);    \
-    st6 = *src_of((T0), 6);    \
-    st7 = *src_of((T0), 7);    \
-    st8 = *src_of((T0), 8);    \
+    st0 = dev::load16<kStreamKV>(src_of((T0), 0));    \
+    st1 = dev::load16<kStreamKV>(src_of((T0), 1));    \
+    st2 = dev::load16<kStreamKV>(src_of((T0), 2));    \
+    st3 = dev::load16<kStreamKV>(src_of((T0), 3));    \
+    st4 = dev::load16<kStreamKV>(src_of((T0), 4));    \
+    st5 = dev::load16<kStreamKV>(src_of((T0), 5));    \
+    st6 = dev::load16<kStreamKV>(src_of((T0), 6));    \
+    st7 = dev::load16<kStreamKV>(src_of((T0), 7));    \
+    st8 = dev::load16<kStreamKV>(src_of((T0), 8));    \
   } while (0)
 #define PKV_MLA_LSTORE()  \
   do {                    \
