@@ -184,7 +184,9 @@ pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new
  * W = sum_b tiles_b * pages_b * heads_y and T = target_per_cu * num_cus; C is
  * capped at 1024 pages (a kernel stages one chunk's page ids on chip).
  * Chunks are page-aligned and disjoint; causal tiles drop chunks they cannot
- * see.  Items run longest first.
+ * see.  With tail_split S > 1, the final chunk of each tile, if longer than
+ * one page, is cut into S page-aligned pieces of ceil(pages/S) pages.  Items
+ * run longest first, so the schedule ends on small items.
  */
 typedef struct pkv_plan pkv_plan;
 
@@ -202,9 +204,10 @@ typedef struct pkv_plan_params {
   int32_t kv_dtype;
   int32_t num_cus;           /* 0: query the current device */
   int32_t fixed_split_pages; /* > 0 forces this chunk size in pages */
-  int32_t target_per_cu;     /* 0: default (decode 4, prefill 4, MLA 1) */
+  int32_t target_per_cu;     /* 0: default (decode 3, prefill 4, MLA 1) */
   int32_t mla_head_groups;   /* MLA only; 0: default */
   int32_t max_num_pages;     /* pool size, for the page-id range check */
+  int32_t tail_split;        /* 0: default (decode 2, prefill 1, MLA 1); 1: off */
 } pkv_plan_params;
 
 typedef struct pkv_plan_info {

@@ -35,7 +35,8 @@ DECODE, PREFILL, MLA = "decode", "prefill", "mla"
 
 MIN_SPLIT_TOKENS = 256          # a chunk holds at least this many tokens
 MAX_CHUNK_PAGES = 1024          # and at most this many pages (a kernel stages a chunk's page ids on chip)
-DEFAULT_TARGET_PER_CU = {DECODE: 4, PREFILL: 4, MLA: 1}
+DEFAULT_TARGET_PER_CU = {DECODE: 3, PREFILL: 4, MLA: 1}
+DEFAULT_TAIL_SPLIT = {DECODE: 2, PREFILL: 1, MLA: 1}
 MFMA_TILE_ROWS = 128            # prefill tile height counted in (row, head) pairs
 
 
@@ -53,7 +54,7 @@ def rows_per_tile(mode: str, group: int, kv_dtype: str) -> int:
 
 def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, heads_y: int,
          rows: int, causal: bool, num_cus: int, fixed_split_pages: int = 0,
-         target_per_cu: int = 0) -> dict:
+         target_per_cu: int = 0, tail_split: int = 0) -> dict:
     """Partition a batch into work items and merge items.
 
     Steps (all integer):
@@ -69,6 +70,11 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
        diag = K_b - q_b + l0 (non-causal: diag = K_b); a chunk whose first key
        exceeds diag + rows - 1 is dropped, and kv_end is clipped to
        diag + rows.
+    5b. Tail split S (default 2 for decode, else 1 = off): if S > 1, the
+       tile's last kept chunk, when it spans more than one page, is replaced
+       by pieces of ceil(pages / S) pages from its first key on (the last
+       piece ends where the chunk ended).  The longest-first order of step 7
+       then finishes on small items.
     6. A tile with one kept chunk writes directly; otherwise its chunks get
        consecutive partial rows and one merge item.  Partial rows are handed
        out tile by tile in (b, t) order.
@@ -82,6 +88,8 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
         causal = True        # a single decode row sees every key; diag = K - 1
     if target_per_cu <= 0:
         target_per_cu = DEFAULT_TARGET_PER_CU[mode]
+    if tail_split <= 0:
+        tail_split = DEFAULT_TAIL_SPLIT[mode]
     n_pages = [kv_indptr[b + 1] - kv_indptr[b] for b in range(batch)]
     k_lens = [page_size * (n_pages[b] - 1) + kv_last_page_len[b] for b in range(batch)]
     q_lens = [qo_indptr[b + 1] - qo_indptr[b] for b in range(batch)]
@@ -114,6 +122,12 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
                 if lo >= limit:
                     continue
                 kept.append((lo, min(hi, limit)))
+            if tail_split > 1 and kept:
+                lo, hi = kept[-1]
+                pages = _cdiv(hi - lo, page_size)
+                if pages > 1:
+                    step = _cdiv(pages, tail_split) * page_size
+                    kept[-1:] = [(s, min(hi, s + step)) for s in range(lo, hi, step)]
             q_row0 = qo_indptr[b] + l0
             if len(kept) == 1:
                 lo, hi = kept[0]

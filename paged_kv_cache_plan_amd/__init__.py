@@ -172,7 +172,7 @@ _DTYPES = {"f32": F32, "bf16": BF16}
 
 def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo=None, page_size,
                 causal=True, dtype="bf16", num_cus=0, fixed_split_pages=0, target_per_cu=0,
-                mla_head_groups=0, max_num_pages=0) -> PlanParams:
+                mla_head_groups=0, max_num_pages=0, tail_split=0) -> PlanParams:
     p = PlanParams()
     p.mode = _MODES[mode] if isinstance(mode, str) else mode
     p.batch_size = batch_size
@@ -184,6 +184,7 @@ def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, he
     p.q_dtype = p.kv_dtype = _DTYPES[dtype] if isinstance(dtype, str) else dtype
     p.num_cus, p.fixed_split_pages, p.target_per_cu = num_cus, fixed_split_pages, target_per_cu
     p.mla_head_groups, p.max_num_pages = mla_head_groups, max_num_pages
+    p.tail_split = tail_split
     return p
 
 

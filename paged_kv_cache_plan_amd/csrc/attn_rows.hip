@@ -52,6 +52,12 @@ constexpr int kSegPages = 1024;   // page ids staged in LDS per segment
 #define PKV_DECODE_NT 1
 #endif
 constexpr bool kStreamKV = PKV_DECODE_NT != 0;
+// Lanes that share one key row (16 or 8; compile-time tunable).  Each load
+// instruction then covers whole 128-byte lines of VT = 64 / lanes key rows.
+#ifndef PKV_DECODE_ROW_LANES
+#define PKV_DECODE_ROW_LANES 16
+#endif
+constexpr int kRowLanes = PKV_DECODE_ROW_LANES;
 // Key blocks in flight per wave (register sets): 2 or 3 (compile-time tunable;
 // 3 applies to bf16 only, where the extra set still fits in 256 VGPRs).
 #ifndef PKV_DECODE_DEPTH
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr int E = Elem<T>::kPer16;       // elements per 16-byte chunk
   constexpr int NCH = D / E;               // chunks per key row
-  constexpr int VL = NCH < 16 ? NCH : 16;  // lanes per key row = one softmax group
+  constexpr int VL = NCH < kRowLanes ? NCH : kRowLanes;  // lanes per key row = one softmax group
   constexpr int VC = NCH / VL;             // chunks per lane
   constexpr int VT = 64 / VL;              // key rows per load instruction = groups per wave
   constexpr int NU = kBlockKeys / VT;      // load instructions per block = keys per group per block

@@ -139,7 +139,10 @@ constexpr int32_t kMinSplitTokens = 256;
 constexpr int64_t kMaxChunkPages = 1024;   // kernels stage one chunk's page ids on chip
 constexpr int32_t kMfmaTileRows = 128;   // prefill tile height in (row, head) pairs
 
-int32_t default_target(int32_t mode) { return mode == PKV_MODE_MLA_DECODE ? 1 : 4; }
+int32_t default_target(int32_t mode) {
+  return mode == PKV_MODE_MLA_DECODE ? 1 : (mode == PKV_MODE_DECODE ? 3 : 4);
+}
+int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 1; }
 constexpr int32_t kMlaHeadsPerGroup = 32;   // the MLA kernel's head-group width
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype) {
@@ -192,7 +195,7 @@ pkv_status check_params(const pkv_plan_params* p) {
   } else if (p->head_dim_qk != p->head_dim_vo) {
     return fail(PKV_ERR_UNSUPPORTED, "head_dim_qk must equal head_dim_vo outside MLA");
   }
-  if (p->fixed_split_pages < 0 || p->target_per_cu < 0 || p->mla_head_groups < 0)
+  if (p->fixed_split_pages < 0 || p->target_per_cu < 0 || p->mla_head_groups < 0 || p->tail_split < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative planner knob");
   return PKV_OK;
 }
@@ -229,6 +232,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
       return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 32 heads");
   }
   const int32_t target_per_cu = prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode);
+  const int32_t tail_split = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);
   const bool causal = prefill ? prm->causal != 0 : true;
 
   // Step 1-3: tiles, page work, chunk size.
@@ -274,6 +278,19 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
         if (lo >= limit) break;
         const int64_t hi = std::min<int64_t>(std::min<int64_t>(lo + chunk_tokens, k), limit);
         kept.emplace_back(int32_t(lo), int32_t(hi));
+      }
+      // Tail split: the tile's final chunk, if longer than one page, becomes
+      // tail_split page-aligned pieces, so the end of the longest-first order
+      // is made of small items.
+      if (tail_split > 1 && !kept.empty()) {
+        const int64_t lo = kept.back().first, hi = kept.back().second;
+        const int64_t pages = cdiv(hi - lo, prm->page_size);
+        if (pages > 1) {
+          kept.pop_back();
+          const int64_t step = cdiv(pages, tail_split) * prm->page_size;
+          for (int64_t s0 = lo; s0 < hi; s0 += step)
+            kept.emplace_back(int32_t(s0), int32_t(std::min<int64_t>(hi, s0 + step)));
+        }
       }
       const int32_t q_row0 = int32_t((prefill ? qo_indptr[b] : b) + l0);
       if (kept.size() == 1) {

@@ -100,11 +100,12 @@ def test_append_validation():
 
 
 def _compare_plans(mode, qo_indptr, kv_indptr, kv_indices, last, page_size, hq, hkv, dtype, causal, num_cus,
-                   fixed=0, target=0, mla_groups=0):
+                   fixed=0, target=0, mla_groups=0, tail=0):
     params = pkv.plan_params(mode=mode, batch_size=len(last), num_qo_heads=hq, num_kv_heads=hkv,
                              head_dim_qk=576 if mode == "mla" else 128, head_dim_vo=512 if mode == "mla" else 128,
                              page_size=page_size, causal=causal, dtype=dtype, num_cus=num_cus,
-                             fixed_split_pages=fixed, target_per_cu=target, mla_head_groups=mla_groups)
+                             fixed_split_pages=fixed, target_per_cu=target, mla_head_groups=mla_groups,
+                             tail_split=tail)
     info, items, merges = pkv.plan_compute(params, qo_indptr=qo_indptr if mode == "prefill" else None,
                                            kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last)
     rows = pl.rows_per_tile(mode, hq // hkv, dtype)
@@ -112,7 +113,7 @@ def _compare_plans(mode, qo_indptr, kv_indptr, kv_indices, last, page_size, hq, 
     spec = pl.plan(mode=mode, qo_indptr=list(qo_indptr) if mode == "prefill" else None,
                    kv_indptr=list(kv_indptr), kv_last_page_len=list(last), page_size=page_size,
                    heads_y=info["heads_y"], rows=rows, causal=causal, num_cus=num_cus, fixed_split_pages=fixed,
-                   target_per_cu=target)
+                   target_per_cu=target, tail_split=tail)
     assert items.tolist() == spec["items"]
     assert merges.tolist() == spec["merges"]
     assert info["num_partial_rows"] == spec["num_partial_rows"]
@@ -160,7 +161,7 @@ def test_planner_matches_spec_randomised():
         dtype = "bf16" if (mode == "mla" or trial % 5) else "f32"
         _compare_plans(mode, qo, kv_indptr, None, last, page, hq, hkv, dtype, bool(trial % 2),
                        int(rng.integers(1, 400)), fixed=int(rng.choice([0, 0, 0, 1, 3, 50])),
-                       target=int(rng.choice([0, 1, 2, 8])))
+                       target=int(rng.choice([0, 1, 2, 8])), tail=int(rng.choice([0, 1, 2, 3])))
 
 
 def test_fingerprint_tracks_metadata():

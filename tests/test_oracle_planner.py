@@ -19,7 +19,7 @@ def test_hand_worked_decode_split():
     [256,512), [512,600) with partial rows 0, 1, 2; request 1 stays direct.
     Emission is by descending cost: 256, 256, 100, 88."""
     args = dict(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4],
-                page_size=16, heads_y=1, rows=1, causal=True, num_cus=1, target_per_cu=1)
+                page_size=16, heads_y=1, rows=1, causal=True, num_cus=1, target_per_cu=1, tail_split=1)
     p = pl.plan(**args)
     assert p["chunk_pages"] == 45 and not p["split"] and p["merges"] == []
     assert p["items"] == [[0, 1, 0, 600, 599, 0, -1, 0], [1, 1, 0, 100, 99, 38, -1, 1]]
@@ -28,6 +28,25 @@ def test_hand_worked_decode_split():
     assert p["merges"] == [[0, 1, 0, 3]]
     assert p["items"] == [[0, 1, 0, 256, 599, 0, 0, 0], [0, 1, 256, 512, 599, 0, 1, 0],
                           [1, 1, 0, 100, 99, 38, -1, 1], [0, 1, 512, 600, 599, 0, 2, 0]]
+
+
+def test_hand_worked_tail_split():
+    """The same two requests with 16-page chunks and tail split 2.  Request 0's
+    final chunk [512,600) spans 6 pages and becomes 3-page pieces [512,560)
+    and [560,600); request 1's only chunk [0,100) spans 7 pages and becomes
+    4-page pieces [0,64) and [64,100), so it now merges too.  Partial rows:
+    request 0 slots 0..3, request 1 slots 4, 5.  Emission by descending cost:
+    256, 256, 64, 48, 40, 36."""
+    p = pl.plan(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4], page_size=16,
+                heads_y=1, rows=1, causal=True, num_cus=1, fixed_split_pages=16, tail_split=2)
+    assert p["merges"] == [[0, 1, 0, 4], [1, 1, 4, 2]] and p["num_partial_rows"] == 6
+    assert p["items"] == [[0, 1, 0, 256, 599, 0, 0, 0], [0, 1, 256, 512, 599, 0, 1, 0],
+                          [1, 1, 0, 64, 99, 38, 4, 1], [0, 1, 512, 560, 599, 0, 2, 0],
+                          [0, 1, 560, 600, 599, 0, 3, 0], [1, 1, 64, 100, 99, 38, 5, 1]]
+    # a one-page final chunk is left whole
+    p = pl.plan(mode="decode", qo_indptr=None, kv_indptr=[0, 17], kv_last_page_len=[5], page_size=16,
+                heads_y=1, rows=1, causal=True, num_cus=1, fixed_split_pages=16, tail_split=2)
+    assert [(i[2], i[3]) for i in p["items"]] == [(0, 256), (256, 261)]
 
 
 def test_hand_worked_causal_pruning():
@@ -71,16 +90,18 @@ def test_partition_invariants(mode):
         rows = int(rng.choice([1, 2, 4, 32])) if mode == "prefill" else 1
         causal = bool(rng.integers(2)) if mode == "prefill" else True
         fixed = int(rng.choice([0, 0, 1, 2, 7]))
+        tail = int(rng.choice([0, 1, 2, 3]))
         p = pl.plan(mode=mode, qo_indptr=c["qo_indptr"], kv_indptr=c["kv_indptr"],
                     kv_last_page_len=c["kv_last_page_len"], page_size=c["page_size"],
                     heads_y=int(rng.integers(1, 9)), rows=rows, causal=causal,
-                    num_cus=int(rng.integers(1, 300)), fixed_split_pages=fixed)
+                    num_cus=int(rng.integers(1, 300)), fixed_split_pages=fixed, tail_split=tail)
         chunk_tok = p["chunk_pages"] * c["page_size"]
         qo = c["qo_indptr"] or list(range(len(c["k"]) + 1))
         by_tile = {}
         for it in p["items"]:
             q_row0, n_rows, lo, hi, diag, page_base, slot, b = it
-            assert lo % chunk_tok == 0 and 0 <= lo < hi and hi - lo <= chunk_tok
+            # page-aligned pieces, each inside one chunk
+            assert lo % c["page_size"] == 0 and 0 <= lo < hi and lo // chunk_tok == (hi - 1) // chunk_tok
             assert page_base == c["kv_indptr"][b] and qo[b] <= q_row0 < qo[b + 1]
             assert q_row0 + n_rows <= qo[b + 1] and n_rows >= 1
             by_tile.setdefault((b, q_row0), []).append(it)
