@@ -8,9 +8,20 @@
 //     (query row, head) pairs -- 128/G rows times the G query heads that share
 //     the kv head -- against one chunk of keys.  Wave w owns pairs
 //     [32w, 32w + 32).
-//   * Keys stream through LDS in tiles of 64, double-buffered: the page-table
-//     gather of tile t+1 (16-byte global loads, each row located through
-//     kv_indices) is in flight while tile t is consumed.
+//   * Keys stream through LDS in tiles of 64.  K and V tiles are both double
+//     buffered and filled by direct global->LDS loads (global_load_lds_dwordx4):
+//     no staging registers and no LDS store instructions.  The loads of K(t+2)
+//     and V(t+1) are issued right after the one barrier of tile t and have the
+//     whole tile to land.
+//   * Page gather: on pages of >= 16 keys (a power of two) the 16 keys that one
+//     load instruction covers share a page, so the page id is wave-uniform and
+//     its 64-bit offset is scalar arithmetic; each lane adds a fixed 32-bit
+//     offset.  Other page sizes and a chunk's partial last tile locate every
+//     key through the page table per lane.
+//   * Tiles are stored unpadded with an XOR swizzle of the 16-byte chunks of a
+//     row (K: chunk ^ (row & 15); V: chunk ^ 4*(row & 3)), chosen so that the
+//     K operand reads (16 rows, one chunk) and the transposed V reads (4 rows,
+//     32 bytes each) hit distinct LDS banks.
 //   * Scores are computed transposed, S^T = K Q^T (M = keys, N = pairs), so
 //     each lane holds the scores of ONE pair: the row max and row sum are
 //     in-lane over 32 keys plus one exchange with lane l^32.  Q stays in
@@ -24,7 +35,8 @@
 //     rescaled only when a row's max grows by more than 8 (so weights stay below
 //     2^8); masking (causal diagonal, chunk end) is applied only on tiles that
 //     need it ("Causality uses logical positions, not page numbers": row r of
-//     the tile sees key j iff j <= diag + r).
+//     the tile sees key j iff j <= diag + r).  The scores of tile t+1 are
+//     issued on the matrix cores interleaved with the exponentials of tile t.
 //
 // The epilogue writes the normalised rows (bf16) and base-2 LSE, or fp32
 // partial states for the split merge ("A worked split-KV example").
@@ -42,16 +54,16 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int kD = 128;          // head dim
 constexpr int kKeys = 64;        // keys per LDS tile
-// LDS row pitches (elements).  K rows are read 16 bytes per lane, 32 rows at
-// one column: a pitch of 68 dwords spreads consecutive rows over distinct
-// 4-bank groups.  V rows are read by the transposed load, 4 rows x 32 bytes
-// per 16-lane group: a pitch of 72 dwords puts those 4 rows on disjoint banks.
-constexpr int kPitchK = kD + 8;
-constexpr int kPitchV = kD + 16;
+constexpr int kTile = kKeys * kD;  // elements of one K or V tile (16 KiB)
 constexpr int kMaxChunkPages = 1024;   // the planner never makes a chunk longer than this
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyMax = 8.f;  // rescale only when a row max grows by more than this (log2 units)
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -70,10 +82,27 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// lds_wave_base + 16 l.  lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+// Barrier for tiles filled by direct loads: the loads count on vmcnt, and the
+// compiler does not always wait on them before a barrier at a loop header, so
+// each wave first waits for all of its own loads (vmcnt(0); expcnt and
+// lgkmcnt left at their maxima) and only then joins the barrier.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
 template <int G, bool kPow2>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * kPitchK];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kKeys * kPitchV];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTile];
   __shared__ int32_t s_pages[kMaxChunkPages];
 
   const int32_t hkv = a.num_kv_heads;
@@ -82,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   const Item it = a.items[item_idx];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;          // lane half: which 8-element k slice of an MFMA operand
   const int col = lane & 31;        // MFMA column: the pair this lane scores
 
@@ -96,11 +125,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   // Smallest row limit in the wave: tiles ending at or before it need no mask.
   const int32_t wave_limit_min = min(it.kv_end - 1, it.diag + (wave * 32) / G);
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(kvh) * a.head_stride;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(kvh) * a.head_stride;
+  const char* const kbase = static_cast<const char*>(a.k) + int64_t(kvh) * a.head_stride * 2;
+  const char* const vbase = static_cast<const char*>(a.v) + int64_t(kvh) * a.head_stride * 2;
   const int32_t* pages = a.kv_indices + it.page_base;
   const int32_t psz = a.page_size, pshift = a.page_shift;
   const uint32_t max_pages = uint32_t(a.max_num_pages);
+  const int64_t page_bytes = a.page_stride * 2;
+  const uint32_t tok_bytes = uint32_t(a.token_stride) * 2;   // the launcher bounds 16 rows of it below 2^31
 
   // Q^T as the B operand: k-step s covers dims [16s, 16s+16); this lane holds dims 16s + 8h + [0, 8).
   uint4 qreg[8];
@@ -123,7 +154,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   const int32_t kv_lo = it.kv_start, kv_hi = it.kv_end;
   const int32_t ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kKeys - 1) / kKeys : 0;
 
-  // Page ids of the chunk (at most kMaxChunkPages, a planner guarantee) go to LDS once.
+  // Page ids of the chunk (at most kMaxChunkPages, a planner guarantee) go to
+  // LDS once; ids outside the pool read page 0 instead.
   const int32_t pg_lo = kv_hi > kv_lo ? (kPow2 ? kv_lo >> pshift : kv_lo / psz) : 0;
   const int32_t pg_n =
       kv_hi > kv_lo ? min(kMaxChunkPages, (kPow2 ? (kv_hi - 1) >> pshift : (kv_hi - 1) / psz) - pg_lo + 1) : 0;
@@ -133,70 +165,52 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   }
   __syncthreads();
 
-  // Tile loader: thread tid moves 16 bytes of 4 keys (key tid/16 + 16i,
-  // dims (tid%16)*8) of K or V.  Keys past the chunk end re-read the last key
-  // (their scores are masked to -inf, so their weights are exactly zero).
-  const int ld_key = tid >> 4, ld_chunk = tid & 15;
-  // Full tiles on pages of at least 16 keys: a thread's four keys
-  // t0 + ld_key + 16i sit on page (t0 + 16i) >> shift, the same page for the
-  // whole workgroup, so only the slot depends on the thread.
+  // Tile loads.  Load instruction i of wave w fills tile rows 16i + 4w + [0, 4)
+  // (1 KiB); lane l writes row 16i + 4w + l/16, stored chunk l%16, which holds
+  // source chunk (l%16) ^ swizzle(row).  Keys past the chunk end re-read the
+  // last key (their scores are masked to -inf, so their weights are exactly zero).
+  const int dma_row = 4 * wave + (lane >> 4);                    // row within each 16-row group
+  const int ck = (lane & 15) ^ dma_row;                          // K: chunk ^ (row & 15)
+  const int cv = (lane & 15) ^ ((lane >> 4) << 2);               // V: chunk ^ 4 (row & 3)
+  const uint32_t lane_k = uint32_t(dma_row) * tok_bytes + uint32_t(ck) * 16;
+  const uint32_t lane_v = uint32_t(dma_row) * tok_bytes + uint32_t(cv) * 16;
   const bool aligned = kPow2 && pshift >= 4;
-  const int64_t ld_lane_off = int64_t(ld_key) * a.token_stride + ld_chunk * 8;
-  auto tile_offsets = [&](int32_t t0, int64_t (&off)[4]) {
-    if (aligned && t0 + kKeys <= kv_hi) {
+  // A full tile on pages of >= 16 keys: load instruction i covers keys
+  // t0 + 16i + [0, 16), all on one page, so its page offset is uniform.
+  auto tile_aligned = [&](int32_t t0) { return aligned && t0 + kKeys <= kv_hi; };
+  auto page_offsets = [&](int32_t t0, int64_t (&off)[4]) {
+    int32_t pg[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t j0 = t0 + 16 * i;
-        off[i] = int64_t(s_pages[(j0 >> pshift) - pg_lo]) * a.page_stride + int64_t(j0 & (psz - 1)) * a.token_stride +
-                 ld_lane_off;
-      }
-    } else {
+    for (int i = 0; i < 4; ++i) pg[i] = s_pages[((t0 + 16 * i) >> pshift) - pg_lo];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t j = min(t0 + ld_key + 16 * i, kv_hi - 1);
-        const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
-        const int32_t sl = kPow2 ? (j & (psz - 1)) : (j - pi * psz);
-        off[i] = int64_t(s_pages[min(pi - pg_lo, kMaxChunkPages - 1)]) * a.page_stride + int64_t(sl) * a.token_stride +
-                 ld_chunk * 8;
-      }
+    for (int i = 0; i < 4; ++i)
+      off[i] = int64_t(__builtin_amdgcn_readfirstlane(pg[i])) * page_bytes +
+               int64_t((t0 + 16 * i) & (psz - 1)) * tok_bytes;
+  };
+  auto dma_aligned = [&](const char* base, uint32_t lane_off, uint16_t* dst, const int64_t (&off)[4]) {
+    uint16_t* const wdst = dst + (4 * wave) * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(base + off[i] + lane_off, wdst + 16 * i * kD);
+  };
+  auto dma_general = [&](const char* base, int chunk, uint16_t* dst, int32_t t0) {
+    uint16_t* const wdst = dst + (4 * wave) * kD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t j = min(t0 + 16 * i + dma_row, kv_hi - 1);
+      const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
+      const int32_t sl = kPow2 ? (j & (psz - 1)) : (j - pi * psz);
+      const int32_t pg = s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
+      dma16(base + (int64_t(pg) * page_bytes + int64_t(sl) * tok_bytes + chunk * 16), wdst + 16 * i * kD);
     }
   };
-  uint4 kst0, kst1, kst2, kst3, vst0, vst1, vst2, vst3;
-  auto gload_k = [&](int32_t t0) {
-    int64_t off[4];
-    tile_offsets(t0, off);
-    kst0 = *reinterpret_cast<const uint4*>(kbase + off[0]);
-    kst1 = *reinterpret_cast<const uint4*>(kbase + off[1]);
-    kst2 = *reinterpret_cast<const uint4*>(kbase + off[2]);
-    kst3 = *reinterpret_cast<const uint4*>(kbase + off[3]);
-  };
-  auto gload_v = [&](int32_t t0) {
-    int64_t off[4];
-    tile_offsets(t0, off);
-    vst0 = *reinterpret_cast<const uint4*>(vbase + off[0]);
-    vst1 = *reinterpret_cast<const uint4*>(vbase + off[1]);
-    vst2 = *reinterpret_cast<const uint4*>(vbase + off[2]);
-    vst3 = *reinterpret_cast<const uint4*>(vbase + off[3]);
-  };
-  uint16_t* const k_st = &s_k[ld_key * kPitchK + ld_chunk * 8];
-  uint16_t* const v_st = &s_v[ld_key * kPitchV + ld_chunk * 8];
-  auto lstore_k = [&]() {
-    *reinterpret_cast<uint4*>(k_st) = kst0;
-    *reinterpret_cast<uint4*>(k_st + 16 * kPitchK) = kst1;
-    *reinterpret_cast<uint4*>(k_st + 32 * kPitchK) = kst2;
-    *reinterpret_cast<uint4*>(k_st + 48 * kPitchK) = kst3;
-  };
-  auto lstore_v = [&]() {
-    *reinterpret_cast<uint4*>(v_st) = vst0;
-    *reinterpret_cast<uint4*>(v_st + 16 * kPitchV) = vst1;
-    *reinterpret_cast<uint4*>(v_st + 32 * kPitchV) = vst2;
-    *reinterpret_cast<uint4*>(v_st + 48 * kPitchV) = vst3;
-  };
+  // Page offsets of the next tile, computed with its K load and reused for its
+  // V load one tile later.
+  int64_t off_next[4] = {0, 0, 0, 0};
 
-  // S^T of the K tile currently in LDS: two 32-key blocks.
-  const uint16_t* const k_rd = &s_k[col * kPitchK + 8 * h];
-  // The two 32-key blocks alternate so consecutive MFMAs are independent.
-  auto scores = [&](f32x16_t (&sacc)[2]) {
+  // S^T of the K tile in kbuf: two 32-key blocks.  Lane (col, h) reads row
+  // 32kb + col, source chunk 2st + h, stored at chunk (2st + h) ^ (col & 15).
+  const int kx = h ^ (col & 15);
+  auto scores = [&](const uint16_t* kbuf, f32x16_t (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -205,23 +219,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
     for (int st = 0; st < 8; ++st) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(k_rd + kb * 32 * kPitchK + 16 * st);
+        const uint4 kv = *reinterpret_cast<const uint4*>(kbuf + (kb * 32 + col) * kD + ((2 * st) ^ kx) * 8);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[st]), sacc[kb], 0, 0, 0);
       }
     }
   };
 
+  // V^T reads: 16-lane group grp, lane gi reads row 4h + gi/4 (+16ks, +8 for
+  // the upper half) at elements 32n + 16(grp&1) + 4(gi&3), i.e. source chunk
+  // 4n + 2(grp&1) + (gi&3)/2, stored at chunk 4(n ^ gi/4) + 2(grp&1) + (gi&3)/2.
   const int grp = lane >> 4, gi = lane & 15;
-  const uint16_t* const v_rd = &s_v[(4 * h + (gi >> 2)) * kPitchV + 16 * (grp & 1) + 4 * (gi & 3)];
+  const int v_lane = (4 * h + (gi >> 2)) * kD + (2 * (grp & 1) + ((gi & 3) >> 1)) * 8 + 4 * (gi & 1);
+  const int v_sw = gi >> 2;
   const float c = a.scale_log2;
 
-  // One tile: softmax of S(t) (in scur) and O += V(t) P(t), while the scores
-  // S(t+1) of the K tile already in LDS are computed into snext.  On entry LDS
-  // holds K(t+1) and V(t); on exit it holds K(t+2) and V(t+1).
-  auto body = [&](int32_t t, f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
+  // One tile.  On entry S(t) is in scur, K(t+1) and V(t) are (being) loaded
+  // into kread / vread.  Issues K(t+2) -> kdma and V(t+1) -> vdma.
+  auto body = [&](int32_t t, const uint16_t* kread, const uint16_t* vread, uint16_t* kdma, uint16_t* vdma,
+                  f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
     const int32_t t0 = kv_lo + t * kKeys;
-    if (t + 2 < ntiles) gload_k(t0 + 2 * kKeys);
-    if (t + 1 < ntiles) gload_v(t0 + kKeys);
+    // K(t+1) and V(t) have landed for every wave, and every wave is done
+    // reading kdma (K(t)) and vdma (V(t-1)).
+    dma_barrier();
+    if (t + 1 < ntiles) {
+      if (tile_aligned(t0 + kKeys)) dma_aligned(vbase, lane_v, vdma, off_next);
+      else dma_general(vbase, cv, vdma, t0 + kKeys);
+    }
+    if (t + 2 < ntiles) {
+      if (tile_aligned(t0 + 2 * kKeys)) {
+        page_offsets(t0 + 2 * kKeys, off_next);
+        dma_aligned(kbase, lane_k, kdma, off_next);
+      } else {
+        dma_general(kbase, ck, kdma, t0 + 2 * kKeys);
+      }
+    }
 
     // Masking: key of value v in block kb is t0 + 32kb + 8(v/4) + 4h + v%4.
     if (t0 + kKeys - 1 > wave_limit_min) {
@@ -252,21 +283,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
         for (int v = 0; v < 16; ++v) oacc[n][v] *= f;
     }
 
-    // S(t+1) on the matrix cores while the weights of tile t are formed.
-    scores(snext);
+    // S(t+1) on the matrix cores while the weights of tile t are formed (on
+    // the last tile the scores of a stale buffer are computed and dropped).
+    scores(kread, snext);
     // exp2(-inf) = 0 covers masked keys; a row with no visible key yet has
-    // only -inf scores, so any finite shift works for it.
+    // only -inf scores, so any finite shift works for it.  The row sum adds
+    // the fp32 weights (two chains).
     const float shift = m_used != -INFINITY ? m_used : 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
     uint4 pb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = dev::fast_exp2(fmaf(scur[ks >> 1][8 * (ks & 1) + e], c, -shift));
-        lsum += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = dev::fast_exp2(fmaf(scur[ks >> 1][8 * (ks & 1) + e], c, -shift));
       pb[ks] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        ls0 += p[e];
+        ls1 += p[e + 1];
+      }
+    }
+    lsum += ls0 + ls1;
+    // Interleave: K reads run ahead, each score MFMA is followed by a share of
+    // the exponential work.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
+      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
 
     // O^T += V^T P^T: d-block n, k-step ks (16 keys).  The transposed read
@@ -275,37 +321,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const uint16_t* base = v_rd + 16 * ks * kPitchV + 32 * n;
+        const uint16_t* base = vread + 16 * ks * kD + v_lane + 32 * (n ^ v_sw);
         const bf16x4_t lo = tr_read(base);
-        const bf16x4_t hi = tr_read(base + 8 * kPitchV);
+        const bf16x4_t hi = tr_read(base + 8 * kD);
         const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[ks]), oacc[n], 0, 0, 0);
       }
     }
-
-    __syncthreads();   // every wave is done with K(t+1) and V(t)
-    if (t + 2 < ntiles) lstore_k();
-    if (t + 1 < ntiles) lstore_v();
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i < 13) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
   };
 
   f32x16_t sa[2], sb[2];
   if (ntiles > 0) {
-    gload_k(kv_lo);
-    gload_v(kv_lo);
-    lstore_k();
-    lstore_v();
-    __syncthreads();
-    scores(sa);
-    if (ntiles > 1) gload_k(kv_lo + kKeys);
-    __syncthreads();
-    if (ntiles > 1) lstore_k();
-    __syncthreads();
+    if (tile_aligned(kv_lo)) {
+      page_offsets(kv_lo, off_next);
+      dma_aligned(kbase, lane_k, s_k0, off_next);
+      dma_aligned(vbase, lane_v, s_v0, off_next);
+    } else {
+      dma_general(kbase, ck, s_k0, kv_lo);
+      dma_general(vbase, cv, s_v0, kv_lo);
+    }
+    if (ntiles > 1) {
+      if (tile_aligned(kv_lo + kKeys)) {
+        page_offsets(kv_lo + kKeys, off_next);
+        dma_aligned(kbase, lane_k, s_k1, off_next);
+      } else {
+        dma_general(kbase, ck, s_k1, kv_lo + kKeys);
+      }
+    }
+    dma_barrier();
+    scores(s_k0, sa);
   }
   for (int32_t t = 0; t < ntiles; t += 2) {
-    body(t, sa, sb);
+    body(t, s_k1, s_v0, s_k0, s_v1, sa, sb);
     if (t + 1 >= ntiles) break;
-    body(t + 1, sb, sa);
+    body(t + 1, s_k0, s_v1, s_k1, s_v0, sb, sa);
   }
 
   // Epilogue: row sum over both lane halves, normalise, write.
@@ -359,7 +414,9 @@ hipError_t launch_g(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& a, hipStream_t st,
                                bool* supported) {
-  if (head_dim == kD) {
+  // The tile loader forms 16 rows of token stride as a 32-bit byte offset.
+  const bool strides_ok = a.token_stride >= 0 && a.token_stride * 2 * 16 < (int64_t(1) << 31);
+  if (head_dim == kD && strides_ok) {
     *supported = true;
     switch (group) {
       case 1: return launch_g<1>(a, st);

@@ -158,6 +158,26 @@ def test_prefill_full_size_append_then_run(torch, pkv):
     print("prefill parity", rep)
 
 
+@pytest.mark.parametrize("fixed", [4, 12, 64])
+def test_prefill_forced_chunk_lengths(torch, pkv, fixed):
+    """The full-size prefill batch split into chunks of 4, 12 and 64 pages
+    (1, 3 and 16 key tiles): every tile pipeline depth, each chunk's partial
+    last tile, and the merge of up to ~40 partial states per row.  Checked on
+    the first head of two kv heads; the LSE bar catches a stale key tile that
+    the output tolerance alone can miss."""
+    b = wl.make("prefill", poison=True)
+    k_dev, v_dev = gu.to_dev(b.k_cache, "bf16"), gu.to_dev(b.v_cache, "bf16")
+    _append_on_gpu(pkv, b, k_dev, v_dev)
+    torch.cuda.synchronize()
+    k_exp, v_exp = _expected_after_append(b, b.k_cache, b.v_cache)
+    heads = [0, 9]
+    plan, o, lse = _run_gqa(pkv, torch, b, k_cache=k_dev, v_cache=v_dev, fixed_split_pages=fixed)
+    ro, rl = _oracle(b, k_exp, v_exp, heads=heads)
+    gu.check_close(gu.as_f64(o[:, heads], "bf16"), ro[:, heads], "bf16", f"prefill o fixed={fixed}")
+    gu.check_lse(lse[:, heads], rl[:, heads], f"prefill lse fixed={fixed}")
+    assert plan.info["num_merges"] > 0
+
+
 def test_mla_decode_full_size(torch, pkv):
     """32 requests, kv U[1024, 8192], page 64, latent cache [pages, 64, 576],
     128 heads, sm_scale 1/sqrt(576)."""
