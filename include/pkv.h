@@ -186,7 +186,8 @@ pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new
  * Chunks are page-aligned and disjoint; causal tiles drop chunks they cannot
  * see.  With tail_split S > 1, the final chunk of each tile, if longer than
  * one page, is cut into S page-aligned pieces of ceil(pages/S) pages.  Items
- * run longest first, so the schedule ends on small items.
+ * run most keys first (ties: request, tile, chunk), so the schedule ends on
+ * small items.
  */
 typedef struct pkv_plan pkv_plan;
 

@@ -37,7 +37,7 @@ MIN_SPLIT_TOKENS = 256          # a chunk holds at least this many tokens
 MAX_CHUNK_PAGES = 1024          # and at most this many pages (a kernel stages a chunk's page ids on chip)
 DEFAULT_TARGET_PER_CU = {DECODE: 3, PREFILL: 4, MLA: 1}
 DEFAULT_TAIL_SPLIT = {DECODE: 2, PREFILL: 1, MLA: 1}
-MFMA_TILE_ROWS = 128            # prefill tile height counted in (row, head) pairs
+MFMA_TILE_ROWS = 256            # prefill tile height counted in (row, head) pairs
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -46,7 +46,7 @@ def _cdiv(a: int, b: int) -> int:
 
 def rows_per_tile(mode: str, group: int, kv_dtype: str) -> int:
     """Query rows per work item: 1 for decode, MLA and float32 prefill; for
-    bfloat16 prefill as many rows as fit a 128-high tile of (row, head) pairs."""
+    bfloat16 prefill as many rows as fit a 256-high tile of (row, head) pairs."""
     if mode != PREFILL or kv_dtype == "f32":
         return 1
     return max(1, MFMA_TILE_ROWS // group)
@@ -78,8 +78,9 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     6. A tile with one kept chunk writes directly; otherwise its chunks get
        consecutive partial rows and one merge item.  Partial rows are handed
        out tile by tile in (b, t) order.
-    7. Items are emitted by descending cost (kv_end - kv_start) * rows, ties
-       broken by ascending (b, t, c).
+    7. Items are emitted by descending key count kv_end - kv_start (a tile's
+       kernel time follows its keys, not its rows), ties broken by ascending
+       (b, t, c).
     """
     batch = len(kv_last_page_len)
     if qo_indptr is None:
@@ -104,7 +105,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     chunk = min(chunk, MAX_CHUNK_PAGES)
     chunk_tokens = chunk * page_size
 
-    raw = []          # (cost, b, t, c_kept, fields) before slot assignment
+    raw = []          # (key count, b, t, c_kept, fields) before slot assignment
     merges = []
     slot = 0
     split_any = False
@@ -131,13 +132,13 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
             q_row0 = qo_indptr[b] + l0
             if len(kept) == 1:
                 lo, hi = kept[0]
-                raw.append(((hi - lo) * n_rows, b, t, 0,
+                raw.append((hi - lo, b, t, 0,
                             [q_row0, n_rows, lo, hi, diag, kv_indptr[b], -1, b]))
                 continue
             split_any = True
             merges.append([q_row0, n_rows, slot, len(kept)])
             for ci, (lo, hi) in enumerate(kept):
-                raw.append(((hi - lo) * n_rows, b, t, ci,
+                raw.append((hi - lo, b, t, ci,
                             [q_row0, n_rows, lo, hi, diag, kv_indptr[b], slot + ci * n_rows, b]))
             slot += len(kept) * n_rows
     raw.sort(key=lambda e: (-e[0], e[1], e[2], e[3]))

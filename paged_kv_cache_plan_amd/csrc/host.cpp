@@ -137,7 +137,7 @@ pkv_status validate_impl(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
 constexpr int32_t kMinSplitTokens = 256;
 constexpr int64_t kMaxChunkPages = 1024;   // kernels stage one chunk's page ids on chip
-constexpr int32_t kMfmaTileRows = 128;   // prefill tile height in (row, head) pairs
+constexpr int32_t kMfmaTileRows = 256;   // prefill tile height in (row, head) pairs
 
 int32_t default_target(int32_t mode) {
   return mode == PKV_MODE_MLA_DECODE ? 1 : (mode == PKV_MODE_DECODE ? 3 : 4);
@@ -295,7 +295,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
       const int32_t q_row0 = int32_t((prefill ? qo_indptr[b] : b) + l0);
       if (kept.size() == 1) {
         Item it{q_row0, int32_t(n_rows), kept[0].first, kept[0].second, int32_t(diag), kv_indptr[b], -1, b};
-        raw.push_back({int64_t(kept[0].second - kept[0].first) * n_rows, b, int32_t(t), 0, it});
+        raw.push_back({int64_t(kept[0].second - kept[0].first), b, int32_t(t), 0, it});
         continue;
       }
       split_any = true;
@@ -305,12 +305,13 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
       for (size_t ci = 0; ci < kept.size(); ++ci) {
         Item it{q_row0, int32_t(n_rows), kept[ci].first, kept[ci].second, int32_t(diag), kv_indptr[b],
                 int32_t(slot + int64_t(ci) * n_rows), b};
-        raw.push_back({int64_t(kept[ci].second - kept[ci].first) * n_rows, b, int32_t(t), int32_t(ci), it});
+        raw.push_back({int64_t(kept[ci].second - kept[ci].first), b, int32_t(t), int32_t(ci), it});
       }
       slot += int64_t(kept.size()) * n_rows;
     }
   }
-  // Step 7: longest first; (b, t, c) breaks ties, so the order is unique.
+  // Step 7: most keys first (a tile's kernel time follows its key count, not
+  // its row count); (b, t, c) breaks ties, so the order is unique.
   std::sort(raw.begin(), raw.end(), [](const Raw& x, const Raw& y) {
     if (x.cost != y.cost) return x.cost > y.cost;
     if (x.b != y.b) return x.b < y.b;

@@ -4,15 +4,17 @@
 // is gathered ("Deep Dive - FlashInfer", "Ragged prefill and paged decode"),
 // so both products run on v_mfma_f32_32x32x16_bf16:
 //
-//   * A workgroup (4 waves) owns one work item for one kv head: up to 128
-//     (query row, head) pairs -- 128/G rows times the G query heads that share
-//     the kv head -- against one chunk of keys.  Wave w owns pairs
-//     [32w, 32w + 32).
-//   * Keys stream through LDS in tiles of 64.  K and V tiles are both double
-//     buffered and filled by direct global->LDS loads (global_load_lds_dwordx4):
-//     no staging registers and no LDS store instructions.  The loads of K(t+2)
-//     and V(t+1) are issued right after the one barrier of tile t and have the
-//     whole tile to land.
+//   * A workgroup (8 waves, two per SIMD) owns one work item for one kv head:
+//     up to 256 (query row, head) pairs -- 256/G rows times the G query heads
+//     that share the kv head -- against one chunk of keys.  Wave w owns pairs
+//     [32w, 32w + 32).  All eight waves consume the same K/V tiles, so each
+//     tile brought on chip feeds 256 pairs.
+//   * Keys stream through LDS in tiles of 64, in a ring of four K and four V
+//     tiles filled by direct global->LDS loads (global_load_lds_dwordx4): no
+//     staging registers and no LDS store instructions.  The loads of K(t+4) and
+//     V(t+3) are issued right after the one barrier of tile t and have three
+//     whole tiles to land; the barrier waits only for the loads issued three
+//     tiles earlier.
 //   * Page gather: on pages of >= 16 keys (a power of two) the 16 keys that one
 //     load instruction covers share a page, so the page id is wave-uniform and
 //     its 64-bit offset is scalar arithmetic; each lane adds a fixed 32-bit
@@ -56,7 +58,7 @@ constexpr int kD = 128;          // head dim
 constexpr int kKeys = 64;        // keys per LDS tile
 constexpr int kTile = kKeys * kD;  // elements of one K or V tile (16 KiB)
 constexpr int kMaxChunkPages = 1024;   // the planner never makes a chunk longer than this
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyMax = 8.f;  // rescale only when a row max grows by more than this (log2 units)
 
@@ -83,26 +85,48 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // 16 bytes from global memory straight into LDS: lane l of the wave writes
-// lds_wave_base + 16 l.  lds_wave_base must be wave-uniform.
+// lds_wave_base + 16 l (the LDS address goes in M0, so it must be
+// wave-uniform).  Issued as inline assembly so that the compiler neither
+// reorders it nor inserts waits for it: the kernel's own protocol orders these
+// loads (each tile barrier waits until only the latest tile step's loads are
+// outstanding, and the kernel drains them all before its epilogue).
 __device__ __forceinline__ void dma16(const void* src, uint16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
 }
 
-// Barrier for tiles filled by direct loads: the loads count on vmcnt, and the
-// compiler does not always wait on them before a barrier at a loop header, so
-// each wave first waits for all of its own loads (vmcnt(0); expcnt and
-// lgkmcnt left at their maxima) and only then joins the barrier.
+// Waits for every outstanding tile load of this wave.
+__device__ __forceinline__ void dma_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Pins a value in registers at this point of the instruction stream, so the
+// compiler cannot sink its computation into a later block.
+__device__ __forceinline__ void keep(const uint4& x) {
+  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+
+// Barrier for tiles filled by direct loads.  The loads count on vmcnt; a
+// plain __syncthreads() carries a release fence that the compiler lowers to
+// vmcnt(0) (the loads write LDS), which would drain every prefetch.  Instead
+// each wave waits until at most 2 * kLoadsPerTile of its own loads -- those of
+// the two most recent tile steps -- are outstanding and all its LDS reads have
+// returned, then joins the barrier.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+constexpr int kLoadsPerTile = 4;   // per thread and tile step: 2 for a K tile + 2 for a V tile
 __device__ __forceinline__ void dma_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  static_assert(kLoadsPerTile == 4, "the wait count below is written out");
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int G, bool kPow2>
-__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTile];
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArgs a) {
+  // Ring slot i holds K(t+1) (first half) and V(t) (second half) for the
+  // tile steps t with t % 4 == i: exactly what step t reads, and what step
+  // t-3 loads.  Four separate arrays, so the compiler can tell the slot being
+  // read from the slots being loaded.
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b2[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b3[2 * kTile];
   __shared__ int32_t s_pages[kMaxChunkPages];
 
   const int32_t hkv = a.num_kv_heads;
@@ -165,47 +189,64 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   }
   __syncthreads();
 
-  // Tile loads.  Load instruction i of wave w fills tile rows 16i + 4w + [0, 4)
-  // (1 KiB); lane l writes row 16i + 4w + l/16, stored chunk l%16, which holds
-  // source chunk (l%16) ^ swizzle(row).  Keys past the chunk end re-read the
-  // last key (their scores are masked to -inf, so their weights are exactly zero).
-  const int dma_row = 4 * wave + (lane >> 4);                    // row within each 16-row group
+  // Tile loads.  A tile is four groups of 16 rows.  Load instruction i (0, 1)
+  // of wave w fills rows 16g + 4(w%4) + [0, 4) of group g = 2i + w/4 (1 KiB);
+  // lane l writes row 16g + 4(w%4) + l/16, stored chunk l%16, which holds
+  // source chunk (l%16) ^ swizzle(row).  Keys past the chunk end (and whole
+  // tiles past it) re-read the last key: their scores are masked to -inf or
+  // never used, so their weights are exactly zero.
+  const int w4 = wave & 3, gh = wave >> 2;
+  const int dma_row = 4 * w4 + (lane >> 4);                      // row within each 16-row group
   const int ck = (lane & 15) ^ dma_row;                          // K: chunk ^ (row & 15)
   const int cv = (lane & 15) ^ ((lane >> 4) << 2);               // V: chunk ^ 4 (row & 3)
   const uint32_t lane_k = uint32_t(dma_row) * tok_bytes + uint32_t(ck) * 16;
   const uint32_t lane_v = uint32_t(dma_row) * tok_bytes + uint32_t(cv) * 16;
   const bool aligned = kPow2 && pshift >= 4;
-  // A full tile on pages of >= 16 keys: load instruction i covers keys
-  // t0 + 16i + [0, 16), all on one page, so its page offset is uniform.
+  // A full tile on pages of >= 16 keys: each 16-row group covers keys
+  // t0 + 16g + [0, 16), all on one page, so its page offset is uniform.
   auto tile_aligned = [&](int32_t t0) { return aligned && t0 + kKeys <= kv_hi; };
-  auto page_offsets = [&](int32_t t0, int64_t (&off)[4]) {
-    int32_t pg[4];
+  // Byte offsets of this wave's two groups (g = gh, 2 + gh) of an aligned tile.
+  auto page_offsets = [&](int32_t t0, int64_t (&off)[2]) {
+    int32_t pg[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pg[i] = s_pages[((t0 + 16 * i) >> pshift) - pg_lo];
+    for (int i = 0; i < 2; ++i) pg[i] = s_pages[((t0 + 16 * (2 * i + gh)) >> pshift) - pg_lo];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       off[i] = int64_t(__builtin_amdgcn_readfirstlane(pg[i])) * page_bytes +
-               int64_t((t0 + 16 * i) & (psz - 1)) * tok_bytes;
+               int64_t((t0 + 16 * (2 * i + gh)) & (psz - 1)) * tok_bytes;
   };
-  auto dma_aligned = [&](const char* base, uint32_t lane_off, uint16_t* dst, const int64_t (&off)[4]) {
-    uint16_t* const wdst = dst + (4 * wave) * kD;
+  auto dma_aligned = [&](const char* base, uint32_t lane_off, uint16_t* dst, const int64_t (&off)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(base + off[i] + lane_off, wdst + 16 * i * kD);
+    for (int i = 0; i < 2; ++i) dma16(base + off[i] + lane_off, dst + (16 * (2 * i + gh) + 4 * w4) * kD);
   };
   auto dma_general = [&](const char* base, int chunk, uint16_t* dst, int32_t t0) {
-    uint16_t* const wdst = dst + (4 * wave) * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t j = min(t0 + 16 * i + dma_row, kv_hi - 1);
+    for (int i = 0; i < 2; ++i) {
+      const int g = 2 * i + gh;
+      const int32_t j = min(t0 + 16 * g + dma_row, kv_hi - 1);
       const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
       const int32_t sl = kPow2 ? (j & (psz - 1)) : (j - pi * psz);
       const int32_t pg = s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
-      dma16(base + (int64_t(pg) * page_bytes + int64_t(sl) * tok_bytes + chunk * 16), wdst + 16 * i * kD);
+      dma16(base + (int64_t(pg) * page_bytes + int64_t(sl) * tok_bytes + chunk * 16), dst + (16 * g + 4 * w4) * kD);
     }
   };
-  // Page offsets of the next tile, computed with its K load and reused for its
-  // V load one tile later.
-  int64_t off_next[4] = {0, 0, 0, 0};
+  // Every tile step issues exactly kLoadsPerTile loads per thread (tiles past
+  // the chunk end load the last key), so the barrier's wait count is exact.
+  // The K load of a tile computes its page offsets; its V load one step later
+  // reuses them.
+  int64_t off_next[2] = {0, 0};
+  auto load_k = [&](uint16_t* dst, int32_t t0) {
+    if (tile_aligned(t0)) {
+      page_offsets(t0, off_next);
+      dma_aligned(kbase, lane_k, dst, off_next);
+    } else {
+      dma_general(kbase, ck, dst, t0);
+    }
+  };
+  auto load_v = [&](uint16_t* dst, int32_t t0) {   // after load_k of the same tile
+    if (tile_aligned(t0)) dma_aligned(vbase, lane_v, dst, off_next);
+    else dma_general(vbase, cv, dst, t0);
+  };
 
   // S^T of the K tile in kbuf: two 32-key blocks.  Lane (col, h) reads row
   // 32kb + col, source chunk 2st + h, stored at chunk (2st + h) ^ (col & 15).
@@ -233,43 +274,31 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
   const int v_sw = gi >> 2;
   const float c = a.scale_log2;
 
-  // One tile.  On entry S(t) is in scur, K(t+1) and V(t) are (being) loaded
-  // into kread / vread.  Issues K(t+2) -> kdma and V(t+1) -> vdma.
-  auto body = [&](int32_t t, const uint16_t* kread, const uint16_t* vread, uint16_t* kdma, uint16_t* vdma,
-                  f32x16_t (&scur)[2], f32x16_t (&snext)[2]) {
-    const int32_t t0 = kv_lo + t * kKeys;
-    // K(t+1) and V(t) have landed for every wave, and every wave is done
-    // reading kdma (K(t)) and vdma (V(t-1)).
-    dma_barrier();
-    if (t + 1 < ntiles) {
-      if (tile_aligned(t0 + kKeys)) dma_aligned(vbase, lane_v, vdma, off_next);
-      else dma_general(vbase, cv, vdma, t0 + kKeys);
-    }
-    if (t + 2 < ntiles) {
-      if (tile_aligned(t0 + 2 * kKeys)) {
-        page_offsets(t0 + 2 * kKeys, off_next);
-        dma_aligned(kbase, lane_k, kdma, off_next);
-      } else {
-        dma_general(kbase, ck, kdma, t0 + 2 * kKeys);
-      }
-    }
-
-    // Masking: key of value v in block kb is t0 + 32kb + 8(v/4) + 4h + v%4.
+  // Causal / chunk-end mask of a score tile whose first key is t0: the key of
+  // value v in block kb is t0 + 32kb + 8(v/4) + 4h + v%4.  Tiles that end at
+  // or before every row limit of the wave need none.
+  auto mask_tile = [&](f32x16_t (&sc)[2], int32_t t0) {
     if (t0 + kKeys - 1 > wave_limit_min) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int32_t j = t0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-          scur[kb][v] = j <= limit ? scur[kb][v] : -INFINITY;
+          sc[kb][v] = j <= limit ? sc[kb][v] : -INFINITY;
         }
     }
+  };
+  auto tile_max = [&](const f32x16_t (&sc)[2]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, scur[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][v]);
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  // Lazy running max: move to the tile max only when it exceeds the current
+  // shift by more than kLazyMax (the accumulator and sum are rescaled then).
+  auto update_max = [&](float mx) {
     const float m_cand = mx * c;
     const bool grow = m_cand > m_used + kLazyMax || (m_used == -INFINITY && m_cand != -INFINITY);
     if (__any(grow)) {
@@ -282,85 +311,94 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const AttnArg
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[n][v] *= f;
     }
+  };
+  // Weights of k-step ks (16 keys) of a tile as the bf16 B operand of the PV
+  // product.  exp2(-inf) = 0 covers masked keys; a row with no visible key yet
+  // has only -inf scores, so any finite shift works for it.  The row sum adds
+  // the fp32 weights.
+  auto weights = [&](const f32x16_t (&sc)[2], int ks, float shift, float& ls0, float& ls1) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = dev::fast_exp2(fmaf(sc[ks >> 1][8 * (ks & 1) + e], c, -shift));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      ls0 += p[e];
+      ls1 += p[e + 1];
+    }
+    return make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+  };
+  // O^T += V^T P^T for k-step ks (16 keys), all four 32-dim blocks.  The
+  // transposed read gives lane i of each 16-lane group the value rows of 4
+  // keys at one dim.
+  auto pv_step = [&](const uint16_t* vbuf, int ks, const uint4& pbk) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const uint16_t* base = vbuf + 16 * ks * kD + v_lane + 32 * (n ^ v_sw);
+      const bf16x4_t lo = tr_read(base);
+      const bf16x4_t hi = tr_read(base + 8 * kD);
+      const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pbk), oacc[n], 0, 0, 0);
+    }
+  };
 
-    // S(t+1) on the matrix cores while the weights of tile t are formed (on
-    // the last tile the scores of a stale buffer are computed and dropped).
-    scores(kread, snext);
-    // exp2(-inf) = 0 covers masked keys; a row with no visible key yet has
-    // only -inf scores, so any finite shift works for it.  The row sum adds
-    // the fp32 weights (two chains).
+  // One tile step t, in phases: the weights of tile t (vector work), O +=
+  // V(t) P(t) (16 MFMAs), then S(t+1) = K(t+1) Q^T (16 MFMAs) into the same
+  // registers, then its mask and max.  One score tile is live at a time, which
+  // leaves the registers to keep several LDS reads in flight ahead of the
+  // MFMAs; the two waves that share a SIMD overlap one's vector phase with
+  // the other's matrix phase.  On entry S(t) is in sc (masked, its max folded
+  // into m_used) and K(t+1), V(t) are (being) loaded into kread / vread;
+  // V(t+3) -> vdma and K(t+4) -> kdma are issued here.
+  auto body = [&](int32_t t, const uint16_t* kread, const uint16_t* vread, uint16_t* kdma, uint16_t* vdma,
+                  f32x16_t (&sc)[2]) {
+    const int32_t t0 = kv_lo + t * kKeys;
+    // K(t+1) and V(t) have landed for every wave, and every wave is done
+    // reading the slot of step t-1, which now takes V(t+3) and K(t+4).
+    dma_barrier();
+    load_v(vdma, t0 + 3 * kKeys);
+    load_k(kdma, t0 + 4 * kKeys);
     const float shift = m_used != -INFINITY ? m_used : 0.f;
     float ls0 = 0.f, ls1 = 0.f;
     uint4 pb[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = dev::fast_exp2(fmaf(scur[ks >> 1][8 * (ks & 1) + e], c, -shift));
-      pb[ks] = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        ls0 += p[e];
-        ls1 += p[e + 1];
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks) pb[ks] = weights(sc, ks, shift, ls0, ls1);
     lsum += ls0 + ls1;
-    // Interleave: K reads run ahead, each score MFMA is followed by a share of
-    // the exponential work.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
-      if (i < 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-
-    // O^T += V^T P^T: d-block n, k-step ks (16 keys).  The transposed read
-    // gives lane i of each 16-lane group the value rows of 4 keys at one dim.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint16_t* base = vread + 16 * ks * kD + v_lane + 32 * (n ^ v_sw);
-        const bf16x4_t lo = tr_read(base);
-        const bf16x4_t hi = tr_read(base + 8 * kD);
-        const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16x8(pb[ks]), oacc[n], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (i < 13) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    for (int ks = 0; ks < 4; ++ks) pv_step(vread, ks, pb[ks]);
+    if (t + 1 < ntiles) {
+      scores(kread, sc);
+      mask_tile(sc, t0 + kKeys);
+      update_max(tile_max(sc));
     }
   };
 
-  f32x16_t sa[2], sb[2];
+  // The prologue loads K(0) (slot 3), then V(s) and K(s+1) into slot s for
+  // s = 0, 1, 2, and waits for all but the last two steps.
+  f32x16_t sc[2];
   if (ntiles > 0) {
-    if (tile_aligned(kv_lo)) {
-      page_offsets(kv_lo, off_next);
-      dma_aligned(kbase, lane_k, s_k0, off_next);
-      dma_aligned(vbase, lane_v, s_v0, off_next);
-    } else {
-      dma_general(kbase, ck, s_k0, kv_lo);
-      dma_general(vbase, cv, s_v0, kv_lo);
-    }
-    if (ntiles > 1) {
-      if (tile_aligned(kv_lo + kKeys)) {
-        page_offsets(kv_lo + kKeys, off_next);
-        dma_aligned(kbase, lane_k, s_k1, off_next);
-      } else {
-        dma_general(kbase, ck, s_k1, kv_lo + kKeys);
-      }
-    }
+    load_k(s_b3, kv_lo);
+    load_v(s_b0 + kTile, kv_lo);
+    load_k(s_b0, kv_lo + kKeys);
+    load_v(s_b1 + kTile, kv_lo + kKeys);
+    load_k(s_b1, kv_lo + 2 * kKeys);
+    load_v(s_b2 + kTile, kv_lo + 2 * kKeys);
+    load_k(s_b2, kv_lo + 3 * kKeys);
     dma_barrier();
-    scores(s_k0, sa);
-  }
-  for (int32_t t = 0; t < ntiles; t += 2) {
-    body(t, s_k1, s_v0, s_k0, s_v1, sa, sb);
-    if (t + 1 >= ntiles) break;
-    body(t + 1, s_k0, s_v1, s_k1, s_v0, sb, sa);
+    scores(s_b3, sc);
+    mask_tile(sc, kv_lo);
+    update_max(tile_max(sc));
+    for (int32_t t = 0; t < ntiles; t += 4) {
+      body(t, s_b0, s_b0 + kTile, s_b3, s_b3 + kTile, sc);
+      if (t + 1 >= ntiles) break;
+      body(t + 1, s_b1, s_b1 + kTile, s_b0, s_b0 + kTile, sc);
+      if (t + 2 >= ntiles) break;
+      body(t + 2, s_b2, s_b2 + kTile, s_b1, s_b1 + kTile, sc);
+      if (t + 3 >= ntiles) break;
+      body(t + 3, s_b3, s_b3 + kTile, s_b2, s_b2 + kTile, sc);
+    }
+    // The last steps loaded tiles past the chunk end; they must land before
+    // the workgroup can exit and its LDS be reused.
+    dma_drain();
   }
 
   // Epilogue: row sum over both lane halves, normalise, write.

@@ -17,7 +17,7 @@ def test_hand_worked_decode_split():
     Unforced with one CU and target 1: chunk = max(16, 45) = 45 pages, nothing
     splits.  Forced to 16-page chunks: request 0 splits into keys [0,256),
     [256,512), [512,600) with partial rows 0, 1, 2; request 1 stays direct.
-    Emission is by descending cost: 256, 256, 100, 88."""
+    Emission is by descending key count: 256, 256, 100, 88."""
     args = dict(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4],
                 page_size=16, heads_y=1, rows=1, causal=True, num_cus=1, target_per_cu=1, tail_split=1)
     p = pl.plan(**args)
@@ -35,7 +35,7 @@ def test_hand_worked_tail_split():
     final chunk [512,600) spans 6 pages and becomes 3-page pieces [512,560)
     and [560,600); request 1's only chunk [0,100) spans 7 pages and becomes
     4-page pieces [0,64) and [64,100), so it now merges too.  Partial rows:
-    request 0 slots 0..3, request 1 slots 4, 5.  Emission by descending cost:
+    request 0 slots 0..3, request 1 slots 4, 5.  Emission by descending key count:
     256, 256, 64, 48, 40, 36."""
     p = pl.plan(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4], page_size=16,
                 heads_y=1, rows=1, causal=True, num_cus=1, fixed_split_pages=16, tail_split=2)
@@ -47,6 +47,17 @@ def test_hand_worked_tail_split():
     p = pl.plan(mode="decode", qo_indptr=None, kv_indptr=[0, 17], kv_last_page_len=[5], page_size=16,
                 heads_y=1, rows=1, causal=True, num_cus=1, fixed_split_pages=16, tail_split=2)
     assert [(i[2], i[3]) for i in p["items"]] == [(0, 256), (256, 261)]
+
+
+def test_order_follows_key_count_not_rows():
+    """One prefill request, 6 new rows after a 26-token prefix (K = 32), page
+    4, tiles of 4 rows, one chunk.  Tile 0 (4 rows) sees keys < 30, tile 1
+    (2 rows) sees keys < 32: tile 1 has more keys, so it is emitted first even
+    though it has fewer rows (a tile's kernel time follows its keys)."""
+    p = pl.plan(mode="prefill", qo_indptr=[0, 6], kv_indptr=[0, 8], kv_last_page_len=[4],
+                page_size=4, heads_y=1, rows=4, causal=True, num_cus=1, fixed_split_pages=8)
+    # tile 1: diag = K - q + 4 = 30, kv_end = K; tile 0: diag 26, kv_end = 26 + 4
+    assert p["items"] == [[4, 2, 0, 32, 30, 0, -1, 0], [0, 4, 0, 30, 26, 0, -1, 0]]
 
 
 def test_hand_worked_causal_pruning():
@@ -127,7 +138,7 @@ def test_partition_invariants(mode):
                 assert slots == [m[0][2] + c_ * its[0][1] for c_ in range(len(its))]
         total = sum(m[1] * m[3] for m in p["merges"])
         assert total == p["num_partial_rows"]
-        costs = [(i[3] - i[2]) * i[1] for i in p["items"]]
+        costs = [i[3] - i[2] for i in p["items"]]
         assert costs == sorted(costs, reverse=True)
         if fixed == 1:
             assert all(i[3] - i[2] <= c["page_size"] for i in p["items"])
@@ -136,9 +147,10 @@ def test_partition_invariants(mode):
 def test_rows_per_tile_rule():
     assert pl.rows_per_tile("decode", 4, "bf16") == 1
     assert pl.rows_per_tile("prefill", 4, "f32") == 1
-    assert pl.rows_per_tile("prefill", 4, "bf16") == 32
-    assert pl.rows_per_tile("prefill", 1, "bf16") == 128
+    assert pl.rows_per_tile("prefill", 4, "bf16") == 64
+    assert pl.rows_per_tile("prefill", 1, "bf16") == 256
     assert pl.rows_per_tile("prefill", 256, "bf16") == 1
+    assert pl.rows_per_tile("prefill", 512, "bf16") == 1
 
 
 def test_empty_batch_and_empty_requests():
