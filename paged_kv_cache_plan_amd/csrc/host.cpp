@@ -630,6 +630,7 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, 
   pkv::MergePartialArgs m;
   m.merges = plan->d_merges;
   m.num_merges = plan->info.num_merges;
+  m.max_rows = plan->info.rows_per_tile;
   m.num_heads = p.num_qo_heads;
   m.head_dim = p.head_dim_vo;
   m.part_o = plan->d_part_o;
@@ -699,6 +700,7 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
     pkv::MergePartialArgs m;
     m.merges = plan->d_merges;
     m.num_merges = plan->info.num_merges;
+    m.max_rows = plan->info.rows_per_tile;
     m.num_heads = p.num_qo_heads;
     m.head_dim = 512;
     m.part_o = plan->d_part_o;

@@ -59,6 +59,7 @@ struct AttnArgs {
 struct MergePartialArgs {
   const MergeItem* merges;
   int32_t num_merges;
+  int32_t max_rows;    // largest num_rows over the merge items
   int32_t num_heads;
   int32_t head_dim;
   const float* part_o;

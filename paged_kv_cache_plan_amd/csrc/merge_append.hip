@@ -11,6 +11,8 @@
 // combine, and keep shift + log2(sum); an empty state (-inf) contributes
 // nothing and two empty states stay empty.
 
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -69,15 +71,31 @@ __device__ __forceinline__ void store_f<float>(float* p, int64_t i, float x) { p
 template <>
 __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float x) { p[i] = dev::f32_to_bf16(x); }
 
-// Split-KV merge: workgroup (merge item, head); the chunk states of row r are
-// partial rows slot0 + c*num_rows + r.  A long row can have hundreds of
-// chunks, so the chunks are spread over the workgroup: the shift (largest
-// statistic) and the weight sum are block reductions, the normalised scales of
-// up to kMergeSeg chunks at a time are staged in LDS, and groups of threads
-// accumulate disjoint chunk subsets of the output row (4 dims per thread) whose
-// sums are added at the end.
+// Split-KV merge: workgroup (merge item, head, block of kMergeRows rows); the
+// chunk states of row r are partial rows slot0 + c*num_rows + r.
+//   * Up to 64 chunks (the usual case): wave w merges row 4z + w on its own.
+//     Lane c holds chunk c's statistic, so the shift (largest statistic) and
+//     the weight sum are wave reductions; then every lane accumulates its dims
+//     over the chunks, reading each chunk's scale from the lane that owns it.
+//   * More chunks (one long row split hundreds of ways): the workgroup merges
+//     its rows one at a time with the chunks spread over all threads: the shift
+//     and the weight sum are block reductions, the normalised scales of up to
+//     kMergeSeg chunks at a time are staged in LDS, and groups of threads
+//     accumulate disjoint chunk subsets of the output row (4 dims per thread)
+//     whose sums are added at the end.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeRows = kMergeThreads / 64;   // rows per workgroup
+constexpr int kMergeWaveChunks = 64;            // chunk count up to which one wave merges a row
 constexpr int kMergeSeg = 512;
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
 
 __device__ __forceinline__ float block_reduce(float x, float* s_red, bool is_max) {
   for (int o = 32; o >= 1; o >>= 1) {
@@ -101,13 +119,41 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   const int32_t h = blockIdx.y;
   const int tid = threadIdx.x;
   const int32_t hq = a.num_heads, d_all = a.head_dim;
+  const int32_t r_lo = int32_t(blockIdx.z) * kMergeRows;
+  const int32_t r_hi = min(mi.num_rows, r_lo + kMergeRows);
+  if (r_lo >= r_hi) return;   // uniform over the workgroup
+  const int32_t n = mi.num_chunks;
+
+  if (n <= kMergeWaveChunks) {
+    const int32_t r = r_lo + (tid >> 6);
+    const int lane = tid & 63;
+    if (r >= r_hi) return;
+    const int64_t row_base = int64_t(mi.slot0) + r;
+    const float sc = lane < n ? a.part_lse[(row_base + int64_t(lane) * mi.num_rows) * hq + h] : -INFINITY;
+    const float mx = wave_max(sc);
+    const float wl = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);   // mx finite whenever sc is
+    const float z = wave_sum(wl);
+    const float scale = z > 0.f ? wl / z : 0.f;
+    const int32_t row = mi.q_row0 + r;
+    T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
+    for (int32_t d = lane; d < d_all; d += 64) {
+      float acc = 0.f;
+      for (int32_t c = 0; c < n; ++c) {
+        const float w = __shfl(scale, c);
+        if (w != 0.f) acc = fmaf(w, a.part_o[((row_base + int64_t(c) * mi.num_rows) * hq + h) * d_all + d], acc);
+      }
+      store_f<T>(orow, d, acc);
+    }
+    if (lane == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+    return;
+  }
+
   constexpr int kVec = kVec4 ? 4 : 1;
   const int32_t nvec = d_all / kVec;
   const int32_t tpr = min(nvec, kMergeThreads);   // threads per group (one vector each)
   const int32_t groups = kMergeThreads / tpr;
   const int32_t grp = tid / tpr, lv = tid - (tid / tpr) * tpr;
-  const int32_t n = mi.num_chunks;
-  for (int32_t r = 0; r < mi.num_rows; ++r) {
+  for (int32_t r = r_lo; r < r_hi; ++r) {
     const int64_t row_base = int64_t(mi.slot0) + r;   // partial row of chunk c: row_base + c * num_rows
     float mx = -INFINITY;
     for (int32_t c = tid; c < n; c += kMergeThreads)
@@ -252,7 +298,9 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
 }
 
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t st) {
-  const dim3 grid(uint32_t(a.num_merges), uint32_t(a.num_heads));
+  const int32_t row_blocks = (std::max(a.max_rows, 1) + kMergeRows - 1) / kMergeRows;
+  if (row_blocks > 65535 || a.num_heads > 65535) return hipErrorInvalidValue;
+  const dim3 grid(uint32_t(a.num_merges), uint32_t(a.num_heads), uint32_t(row_blocks));
   const dim3 block(kMergeThreads);
   const bool vec4 = a.head_dim % 4 == 0;
   if (dtype == kBF16) {
