@@ -143,7 +143,7 @@ int32_t default_target(int32_t mode) {
   return mode == PKV_MODE_MLA_DECODE ? 1 : (mode == PKV_MODE_DECODE ? 3 : 4);
 }
 int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 1; }
-constexpr int32_t kMlaHeadsPerGroup = 32;   // the MLA kernel's head-group width
+constexpr int32_t kMlaHeadsPerGroup = 64;   // the MLA kernel's head-group width
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype) {
   if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32) return 1;
@@ -229,7 +229,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   if (mla) {
     heads_y = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
     if (heads_y < 1 || prm->num_qo_heads != heads_y * kMlaHeadsPerGroup)
-      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 32 heads");
+      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 heads");
   }
   const int32_t target_per_cu = prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode);
   const int32_t tail_split = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);

@@ -73,7 +73,8 @@ __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float 
 
 // Split-KV merge: workgroup (merge item, head, block of kMergeRows rows); the
 // chunk states of row r are partial rows slot0 + c*num_rows + r.
-//   * Up to 64 chunks (the usual case): wave w merges row 4z + w on its own.
+//   * Up to 64 chunks (the usual case): each row of the block is merged by
+//     one, two or four waves (a block with fewer rows splits each row's dims).
 //     Lane c holds chunk c's statistic, so the shift (largest statistic) and
 //     the weight sum are wave reductions; then every lane accumulates its dims
 //     over the chunks, reading each chunk's scale from the lane that owns it.
@@ -125,9 +126,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   const int32_t n = mi.num_chunks;
 
   if (n <= kMergeWaveChunks) {
-    const int32_t r = r_lo + (tid >> 6);
+    // Waves per row: all four share one row (each a quarter of its dims) when
+    // the block has one row, two share a row when it has two.
+    const int32_t rows_here = r_hi - r_lo;
+    const int32_t wpr = rows_here == 1 ? 4 : (rows_here == 2 ? 2 : 1);
+    const int32_t w = tid >> 6;
+    const int32_t r = r_lo + w / wpr;
+    const int32_t slice = w - (w / wpr) * wpr;
     const int lane = tid & 63;
     if (r >= r_hi) return;
+    const int32_t d_lo = slice * d_all / wpr, d_hi = (slice + 1) * d_all / wpr;
     const int64_t row_base = int64_t(mi.slot0) + r;
     const float sc = lane < n ? a.part_lse[(row_base + int64_t(lane) * mi.num_rows) * hq + h] : -INFINITY;
     const float mx = wave_max(sc);
@@ -136,15 +144,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     const float scale = z > 0.f ? wl / z : 0.f;
     const int32_t row = mi.q_row0 + r;
     T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
-    for (int32_t d = lane; d < d_all; d += 64) {
+    // Every lane stays active through the chunk loop: the scale of chunk c
+    // lives in lane c, so lanes past the slice end only skip the load/store.
+    for (int32_t d0 = d_lo; d0 < d_hi; d0 += 64) {
+      const int32_t d = d0 + lane;
+      const bool own = d < d_hi;
       float acc = 0.f;
       for (int32_t c = 0; c < n; ++c) {
         const float w = __shfl(scale, c);
-        if (w != 0.f) acc = fmaf(w, a.part_o[((row_base + int64_t(c) * mi.num_rows) * hq + h) * d_all + d], acc);
+        if (own && w != 0.f)
+          acc = fmaf(w, a.part_o[((row_base + int64_t(c) * mi.num_rows) * hq + h) * d_all + d], acc);
       }
-      store_f<T>(orow, d, acc);
+      if (own) store_f<T>(orow, d, acc);
     }
-    if (lane == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+    if (slice == 0 && lane == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
     return;
   }
 
