@@ -27,6 +27,8 @@ planner    the work-partition specification (our reading; the pages give the
            trade-offs but no algorithm).
 attention  numpy float64 paged attention (GQA, NHD/HND, causal) and MLA.
 merge      base-2 log-sum-exp state merge, pairwise and multi-way.
+cascade    multi-level cascade attention: per-level states over one paged
+           cache, merged per query row.
 brute      pure-Python ``math`` attention for tiny inputs; pins ``attention``.
 
 Pin status (see the tests under ``tests/test_oracle_*.py``): every function

@@ -40,6 +40,8 @@ REASONS = (
     "head_group",        # completion: num_qo_heads % num_kv_heads == 0, both >= 1
     "decode_qo_len",     # completion: decode mode has exactly one query row per request
     "append_collision",  # completion: two appended tokens may not share a slot
+    "cascade_rows",      # completion: every cascade level covers the same query rows
+    "cascade_nesting",   # completion: cascade levels nest (each node is a union of next-level nodes)
 )
 
 

@@ -54,7 +54,7 @@ def rows_per_tile(mode: str, group: int, kv_dtype: str) -> int:
 
 def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, heads_y: int,
          rows: int, causal: bool, num_cus: int, fixed_split_pages: int = 0,
-         target_per_cu: int = 0, tail_split: int = 0) -> dict:
+         target_per_cu: int = 0, tail_split: int = 0, all_partial: bool = False) -> dict:
     """Partition a batch into work items and merge items.
 
     Steps (all integer):
@@ -75,9 +75,10 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
        by pieces of ceil(pages / S) pages from its first key on (the last
        piece ends where the chunk ended).  The longest-first order of step 7
        then finishes on small items.
-    6. A tile with one kept chunk writes directly; otherwise its chunks get
-       consecutive partial rows and one merge item.  Partial rows are handed
-       out tile by tile in (b, t) order.
+    6. A tile with one kept chunk writes directly (unless ``all_partial``,
+       used by cascades, where every tile's rows must be merged later);
+       otherwise its chunks get consecutive partial rows and one merge item.
+       Partial rows are handed out tile by tile in (b, t) order.
     7. Items are emitted by descending key count kv_end - kv_start (a tile's
        kernel time follows its keys, not its rows), ties broken by ascending
        (b, t, c).
@@ -130,7 +131,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
                     step = _cdiv(pages, tail_split) * page_size
                     kept[-1:] = [(s, min(hi, s + step)) for s in range(lo, hi, step)]
             q_row0 = qo_indptr[b] + l0
-            if len(kept) == 1:
+            if len(kept) == 1 and not all_partial:
                 lo, hi = kept[0]
                 raw.append((hi - lo, b, t, 0,
                             [q_row0, n_rows, lo, hi, diag, kv_indptr[b], -1, b]))
@@ -151,3 +152,62 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
         "rows_per_tile": rows,
         "target": target,
     }
+
+
+def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: int, causal: bool,
+                 num_cus: int, fixed_split_pages: int = 0, target_per_cu: int = 0,
+                 tail_split: int = 0) -> dict:
+    """Work list of a multi-level cascade ("FlashInfer 中的 KV-Cache 布局",
+    multi-level cascade layout: each level has its own qo_indptr and page
+    table over the shared queries and cache).
+
+    ``levels``: list of dicts with qo_indptr, kv_indptr, kv_last_page_len.
+    Steps (our reading; the pages give the layout, not a schedule):
+    1. Level l is planned as "decode" when every node has exactly one query
+       row, else as "prefill"; rows per tile follow ``rows_per_tile``; only
+       the last level is causal.
+    2. Each level is planned by ``plan`` with ``all_partial``: every tile's
+       states go to partial rows, numbered on from the previous level's.
+    3. A level's page_base is offset by the page ids of all earlier levels
+       (kv_indptr[-1] of each): the device array holds the levels' page
+       lists back to back, level 0 first.
+    4. Merge list, one entry per query row in row order: the partial rows of
+       that row's states, level by level, chunk by chunk (row_ptr has
+       rows + 1 entries, slots lists the partial rows).
+    Items of a level keep ``plan``'s order; levels run in level order.
+    """
+    out_levels = []
+    items = []
+    slot_base = 0
+    page_base = 0
+    total_rows = int(levels[0]["qo_indptr"][-1])
+    per_row = [[] for _ in range(total_rows)]
+    for li, lv in enumerate(levels):
+        qo = [int(x) for x in lv["qo_indptr"]]
+        nodes = len(qo) - 1
+        mode = DECODE if nodes > 0 and all(qo[n + 1] - qo[n] == 1 for n in range(nodes)) else PREFILL
+        rows = rows_per_tile(mode, group, kv_dtype)
+        p = plan(mode=mode, qo_indptr=None if mode == DECODE else qo, kv_indptr=[int(x) for x in lv["kv_indptr"]],
+                 kv_last_page_len=[int(x) for x in lv["kv_last_page_len"]], page_size=page_size, heads_y=heads_y,
+                 rows=rows, causal=causal and li == len(levels) - 1, num_cus=num_cus,
+                 fixed_split_pages=fixed_split_pages, target_per_cu=target_per_cu, tail_split=tail_split,
+                 all_partial=True)
+        for it in p["items"]:
+            it = list(it)
+            it[5] += page_base
+            it[6] += slot_base
+            items.append(it)
+        for q_row0, n_rows, slot0, n_chunks in p["merges"]:
+            for r in range(n_rows):
+                per_row[q_row0 + r].extend(slot_base + slot0 + c * n_rows + r for c in range(n_chunks))
+        out_levels.append({"mode": mode, "rows_per_tile": rows, "num_items": len(p["items"]),
+                           "chunk_pages": p["chunk_pages"], "num_partial_rows": p["num_partial_rows"]})
+        slot_base += p["num_partial_rows"]
+        page_base += int(lv["kv_indptr"][-1])
+    row_ptr = [0]
+    slots = []
+    for lst in per_row:
+        slots.extend(lst)
+        row_ptr.append(len(slots))
+    return {"levels": out_levels, "items": items, "row_ptr": row_ptr, "slots": slots,
+            "num_partial_rows": slot_base, "total_rows": total_rows}

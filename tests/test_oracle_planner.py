@@ -160,3 +160,89 @@ def test_empty_batch_and_empty_requests():
     p = pl.plan(mode="prefill", qo_indptr=[0, 0, 2], kv_indptr=[0, 1, 2], kv_last_page_len=[3, 4],
                 page_size=4, heads_y=1, rows=4, causal=True, num_cus=8)
     assert [i[7] for i in p["items"]] == [1]
+
+
+def test_hand_worked_cascade():
+    """Two levels over 3 query rows, page 4, group 1, float32 (one row per tile).
+    Level 0: one node (rows 0..2) with 10 keys (3 pages); prefill mode (3 rows),
+    not causal, 8-key chunks: [0,8) and [8,10) for each of the 3 row tiles.
+    Level 1: nodes of 1 row each (decode mode) with 5, 2 and 4 keys (2, 1, 1
+    pages), one chunk each.  Level 0's partial rows come first (tile r gets
+    slots 2r, 2r+1), then level 1's (6, 7, 8).  Level 1's page_base is shifted
+    by level 0's 3 page ids."""
+    levels = [{"qo_indptr": [0, 3], "kv_indptr": [0, 3], "kv_last_page_len": [2]},
+              {"qo_indptr": [0, 1, 2, 3], "kv_indptr": [0, 2, 3, 4], "kv_last_page_len": [1, 2, 4]}]
+    p = pl.plan_cascade(levels=levels, page_size=4, group=1, kv_dtype="f32", heads_y=1, causal=True,
+                        num_cus=1, fixed_split_pages=2, tail_split=1)
+    assert [lv["mode"] for lv in p["levels"]] == ["prefill", "decode"]
+    assert [lv["num_items"] for lv in p["levels"]] == [6, 3]
+    assert p["items"][:6] == [[0, 1, 0, 8, 10, 0, 0, 0], [1, 1, 0, 8, 10, 0, 2, 0], [2, 1, 0, 8, 10, 0, 4, 0],
+                              [0, 1, 8, 10, 10, 0, 1, 0], [1, 1, 8, 10, 10, 0, 3, 0], [2, 1, 8, 10, 10, 0, 5, 0]]
+    assert p["items"][6:] == [[0, 1, 0, 5, 4, 3, 6, 0], [2, 1, 0, 4, 3, 6, 8, 2], [1, 1, 0, 2, 1, 5, 7, 1]]
+    assert p["row_ptr"] == [0, 3, 6, 9]
+    assert p["slots"] == [0, 1, 6, 2, 3, 7, 4, 5, 8]
+    assert p["num_partial_rows"] == 9
+
+
+def test_cascade_plan_invariants():
+    """Random trees: every partial row belongs to exactly one query row; each
+    row lists one state per chunk of the tile holding it at every level; the
+    level's items cover its nodes' keys as in a plain plan."""
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n_req = int(rng.integers(1, 10))
+        qo_lens = [int(x) for x in rng.integers(0 if trial % 3 else 1, 5, size=n_req)]
+        if trial % 3 == 0:
+            qo_lens = [1] * n_req
+        rows = list(np.cumsum([0] + qo_lens))
+        # level 0: one root; level 1: random groups; level 2: leaves
+        cuts = sorted(set([0, n_req] + [int(x) for x in rng.integers(0, n_req + 1, size=2)]))
+        page = int(rng.choice([1, 4, 16]))
+        levels = []
+        for bounds in ([0, n_req], cuts, list(range(n_req + 1))):
+            nodes = len(bounds) - 1
+            k = [int(rng.integers(1, 90)) for _ in range(nodes)]
+            if bounds == list(range(n_req + 1)):
+                k = [max(x, q) for x, q in zip(k, qo_lens)]
+            n = [math.ceil(x / page) for x in k]
+            levels.append({"qo_indptr": [rows[b] for b in bounds], "kv_indptr": list(np.cumsum([0] + n)),
+                           "kv_last_page_len": [x - (m - 1) * page for x, m in zip(k, n)], "k": k})
+        group = int(rng.choice([1, 4, 8]))
+        dtype = str(rng.choice(["f32", "bf16"]))
+        causal = bool(rng.integers(2))
+        p = pl.plan_cascade(levels=levels, page_size=page, group=group, kv_dtype=dtype, heads_y=2,
+                            causal=causal, num_cus=int(rng.integers(1, 300)),
+                            fixed_split_pages=int(rng.choice([0, 1, 3])), tail_split=int(rng.choice([0, 1, 2])))
+        total = rows[-1]
+        assert p["total_rows"] == total and len(p["row_ptr"]) == total + 1
+        assert sorted(p["slots"]) == list(range(p["num_partial_rows"]))
+        off = 0
+        page_base = 0
+        slot_base = 0
+        for li, (lv, info) in enumerate(zip(levels, p["levels"])):
+            its = p["items"][off:off + info["num_items"]]
+            off += info["num_items"]
+            qo = lv["qo_indptr"]
+            one_row = all(qo[n + 1] - qo[n] == 1 for n in range(len(qo) - 1))
+            assert info["mode"] == ("decode" if one_row else "prefill")
+            # the same items as a plain plan of the level, shifted
+            ref = pl.plan(mode=info["mode"], qo_indptr=None if one_row else qo, kv_indptr=lv["kv_indptr"],
+                          kv_last_page_len=lv["kv_last_page_len"], page_size=page, heads_y=2,
+                          rows=info["rows_per_tile"], causal=causal and li == 2,
+                          num_cus=1, fixed_split_pages=info["chunk_pages"], all_partial=True,
+                          tail_split=1 if info["mode"] == "prefill" else 0)
+            if p["levels"][li]["chunk_pages"] == ref["chunk_pages"]:
+                for it in its:
+                    assert it[5] - page_base == lv["kv_indptr"][it[7]] and it[6] >= slot_base
+            page_base += lv["kv_indptr"][-1]
+            slot_base += info["num_partial_rows"]
+            # every row gets exactly the chunks of its level-l tile
+            for r in range(total):
+                mine = [it for it in its if it[0] <= r < it[0] + it[1]]
+                assert mine, (li, r)
+                lst = p["slots"][p["row_ptr"][r]:p["row_ptr"][r + 1]]
+                got = sorted(it[6] + (r - it[0]) for it in mine)
+                assert all(s in lst for s in got)
+        assert off == len(p["items"])
+        for r in range(total):
+            assert p["row_ptr"][r + 1] - p["row_ptr"][r] >= 3

@@ -27,6 +27,15 @@ described there):
             appended before attention.
   mla       32 requests, qo 1, kv U[1024, 8192], page 64, latent cache
             [pages, 64, 512 + 64] bfloat16, 128 heads, sm_scale 1/sqrt(576).
+  cascade   shared-prefix decode over a 3-level tree: 64 requests; level 0
+            one node (all requests) with a 16384-token prefix; level 1 eight
+            nodes of 8 requests, U[1024, 4096] tokens each; level 2 one leaf
+            per request, U[128, 1024] tokens ending with its query row; page
+            16, heads 32/8, dim 128, bfloat16, NHD.  Each level has its own
+            page table over one shared pool ("FlashInfer 中的 KV-Cache 布局",
+            multi-level cascade layout).  ``cascade_small`` is the same tree
+            shape at 8 requests (nodes 3/2/3), page 4, heads 4/2, dim 64,
+            float32, qo U[1, 4] per leaf, causal.
 """
 
 from __future__ import annotations
@@ -38,8 +47,9 @@ import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
 
-WORKLOADS = ("worked", "decode", "skewed", "prefill", "mla")
-SEEDS = {"worked": 1000, "decode": 1001, "skewed": 1002, "prefill": 1003, "mla": 1004}
+WORKLOADS = ("worked", "decode", "skewed", "prefill", "mla", "cascade", "cascade_small")
+SEEDS = {"worked": 1000, "decode": 1001, "skewed": 1002, "prefill": 1003, "mla": 1004, "cascade": 1005,
+         "cascade_small": 1006}
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -267,4 +277,91 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                      qo_lens=[1] * batch, kv_lens=kv_lens, qo_indptr=qo_indptr,
                      kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
                      max_num_pages=pool, q=q_ckv, q_kpe=q_kpe, k_cache=cache, v_cache=None)
+    if name in ("cascade", "cascade_small"):
+        return _cascade(name, rng, o, scale, poison)
     raise KeyError(name)
+
+
+def _cascade(name, rng, o, scale, poison):
+    """A request tree as levels of nodes over one page pool.
+
+    ``tree`` lists, per level, how many consecutive requests each node holds
+    (the last level must be all ones: one leaf per request).  ``level_kv``
+    gives each level's (lo, hi) token range per node; a leaf's range is
+    raised to at least its qo_len, since the leaf holds the request's new
+    tokens.  Every node owns its own pages (shared nodes once, not once per
+    request).  Q rows are ragged over requests, like a prefill batch.
+    """
+    small = name == "cascade_small"
+    if small:
+        tree = o.get("tree", [[8], [3, 2, 3], [1] * 8])
+        level_kv = o.get("level_kv", [(37, 37), (5, 20), (1, 12)])
+        qo_range = o.get("qo_range", (1, 4))
+        defaults = dict(page_size=4, hq=4, hkv=2, dim=64, dtype="f32", layout="NHD")
+    else:
+        tree = o.get("tree", [[1 * 64], [8] * 8, [1] * 64])
+        level_kv = o.get("level_kv", [(int(16384 * scale),) * 2, (int(1024 * scale), int(4096 * scale)),
+                                      (int(128 * scale), int(1024 * scale))])
+        qo_range = o.get("qo_range", (1, 1))
+        defaults = dict(page_size=16, hq=32, hkv=8, dim=128, dtype="bf16", layout="NHD")
+    cfg = {k: o.get(k, v) for k, v in defaults.items()}
+    page_size, hq, hkv, dim, dtype, layout = (cfg[k] for k in ("page_size", "hq", "hkv", "dim", "dtype", "layout"))
+    batch = sum(tree[0])
+    for lv in tree:
+        if sum(lv) != batch:
+            raise ValueError("every level must cover every request")
+    if any(n != 1 for n in tree[-1]):
+        raise ValueError("the last level holds one leaf per request")
+    # Lengths: qo per request, then kv per node, level by level.
+    qo_lens = [int(x) for x in rng.integers(qo_range[0], qo_range[1], size=batch, endpoint=True)]
+    node_kv = []
+    for li, lv in enumerate(tree):
+        lo, hi = level_kv[li]
+        lens = [int(x) for x in rng.integers(max(1, lo), max(1, hi), size=len(lv), endpoint=True)]
+        if li == len(tree) - 1:
+            lens = [max(k, q) for k, q in zip(lens, qo_lens)]
+        node_kv.append(lens)
+    n_pages = [[math.ceil(k / page_size) for k in lens] for lens in node_kv]
+    need = sum(sum(x) for x in n_pages)
+    pool = o.get("pool", need + need // 8 + 1)
+    perm = rng.permutation(pool)
+    levels = []
+    start = 0
+    for li, lv in enumerate(tree):
+        rows = np.zeros(len(lv) + 1, dtype=np.int32)
+        req = np.cumsum([0] + list(lv))
+        rows[1:] = [sum(qo_lens[req[i]:req[i + 1]]) for i in range(len(lv))]
+        rows = np.cumsum(rows).astype(np.int32)
+        starts = start + np.cumsum([0] + n_pages[li])
+        _, kv_indptr, kv_indices, last = _csr(node_kv[li], page_size,
+                                              lambda b, n, s=starts: perm[s[b]:s[b] + n])
+        start = int(starts[-1])
+        levels.append({"qo_indptr": rows, "kv_indptr": kv_indptr, "kv_indices": kv_indices,
+                       "kv_last_page_len": last, "kv_lens": node_kv[li], "num_requests": list(lv)})
+    qo_indptr = np.zeros(batch + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    nnz = int(qo_indptr[-1])
+    q = _payload(rng, (nnz, hq, dim), dtype)
+    shape = _cache_shape(layout, pool, page_size, hkv, dim)
+    all_pages = np.concatenate([lv["kv_indices"] for lv in levels])
+    k_cache = _pool(rng, shape, dtype, all_pages)
+    v_cache = _pool(rng, shape, dtype, all_pages)
+    leaf = levels[-1]
+    k_new = _payload(rng, (nnz, hkv, dim), dtype)
+    v_new = _payload(rng, (nnz, hkv, dim), dtype)
+    if poison:
+        used = []
+        for li, lv in enumerate(levels):
+            for b in range(len(lv["kv_lens"])):
+                hi = lv["kv_lens"][b] - (qo_lens[b] if li == len(levels) - 1 else 0)
+                used.append(_slots(lv["kv_indptr"], lv["kv_indices"], page_size, b, 0, hi))
+        used = np.concatenate(used)
+        _poison(k_cache, layout, used, dtype)
+        _poison(v_cache, layout, used, dtype)
+    return Batch(name=name, mode="cascade", dtype=dtype, layout=layout, page_size=page_size,
+                 num_qo_heads=hq, num_kv_heads=hkv, head_dim=dim, causal=o.get("causal", True),
+                 sm_scale=o.get("sm_scale", 1.0 / math.sqrt(dim)), qo_lens=qo_lens,
+                 kv_lens=list(leaf["kv_lens"]), qo_indptr=qo_indptr, kv_indptr=leaf["kv_indptr"],
+                 kv_indices=leaf["kv_indices"], kv_last_page_len=leaf["kv_last_page_len"],
+                 max_num_pages=pool, q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
+                 append_indptr=qo_indptr.copy(), extra={"levels": levels})
