@@ -83,6 +83,27 @@ def mla_bytes(b) -> dict:
     return {"kv": kv, "attn": kv + q + o + lse + idx, "flops": flops}
 
 
+def cascade_bytes(b) -> dict:
+    """Algorithmic bytes of one cascade run: every node's K and V rows once per
+    kv head (shared nodes once, not once per request), Q read, O and LSE
+    written, page ids read.  ``flat_kv`` is what the same batch reads through
+    a flat page table (every request reading its whole path)."""
+    es = 2 if b.dtype == "bf16" else 4
+    row = b.num_kv_heads * b.head_dim * 2 * es
+    levels = b.extra["levels"]
+    kv = sum(sum(lv["kv_lens"]) for lv in levels) * row
+    q = b.nnz * b.num_qo_heads * b.head_dim * es
+    lse = b.nnz * b.num_qo_heads * 4
+    idx = sum(int(lv["kv_indptr"][-1]) for lv in levels) * 4
+    flat_tokens = 0
+    for r in range(b.batch_size):
+        row0 = int(b.qo_indptr[r])
+        for lv in levels:
+            n = int(np.searchsorted(lv["qo_indptr"], row0, side="right")) - 1
+            flat_tokens += lv["kv_lens"][n]
+    return {"kv": kv, "attn": kv + 2 * q + lse + idx, "flat_kv": flat_tokens * row}
+
+
 # ---------------------------------------------------------------- runners --
 
 class Runner:
@@ -160,6 +181,54 @@ class Runner:
             plan.run_merge(self.out, self.lse)
 
 
+class CascadeRunner(Runner):
+    """A cascade batch: per layer, append the new rows into the leaves, then
+    pkv_cascade_run (one attention launch per level + the row merge)."""
+
+    def __init__(self, b, layers: int):
+        import torch
+        import paged_kv_cache_plan_amd as pkv
+        self.b, self.torch, self.pkv = b, torch, pkv
+        self.time_merge = True
+        dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+                             if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
+        bf = b.dtype == "bf16"
+        self.levels = b.extra["levels"]
+        self.q = dev(b.q, bf)
+        self.all_indices = dev(np.concatenate([lv["kv_indices"][:lv["kv_indptr"][-1]] for lv in self.levels]), False)
+        self.kv_indices = dev(b.kv_indices, False)
+        k0, v0 = dev(b.k_cache, bf), dev(b.v_cache, bf)
+        self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(layers - 1)]
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((b.nnz, b.num_qo_heads), dtype=torch.float32, device="cuda")
+        self.k_new, self.v_new = dev(b.k_new, bf), dev(b.v_new, bf)
+        self.append_indptr = dev(b.append_indptr, False)
+        self.kv_indptr_d = dev(b.kv_indptr, False)
+        self.last_d = dev(b.kv_last_page_len, False)
+        self.params = pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=b.num_qo_heads,
+                                      num_kv_heads=b.num_kv_heads, head_dim_qk=b.head_dim, page_size=b.page_size,
+                                      causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages)
+        info = pkv.cascade_plan_compute(self.params, self.levels)[0]
+        self.workspace = torch.empty(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+        self.staging = torch.empty(max(info["staging_bytes"], 256), dtype=torch.uint8, pin_memory=True)
+        self.plan = None
+
+    def make_plan(self):
+        self.plan = self.pkv.CascadePlan(self.params, self.levels, workspace=self.workspace, staging=self.staging)
+        return self.plan
+
+    def layer(self, i: int, ev=None):
+        b = self.b
+        k, v = self.pools[i % len(self.pools)]
+        self.pkv.append_paged_kv(self.k_new, self.v_new, self.append_indptr, self.kv_indptr_d, self.kv_indices,
+                                 self.last_d, k, v, layout=b.layout, page_size=b.page_size)
+        if ev:
+            ev[0].record()
+        self.plan.run(self.q, k, v, self.all_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
+        if ev:
+            ev[1].record()
+
+
 def measure(runner: Runner, layers: int, steps: int, warmup: int) -> dict:
     """Time `steps` steps (plan + `layers` layers each); attention timed per launch."""
     torch = runner.torch
@@ -223,7 +292,7 @@ def cpu_baseline(b, budget_s: float = 12.0) -> dict:
 
 
 COUNTER_KERNELS = {"decode": "attn_rows_kernel", "skewed": "attn_rows_kernel", "prefill": "prefill_mfma_kernel",
-                   "mla": "mla_decode_kernel"}
+                   "mla": "mla_decode_kernel", "cascade": "prefill_mfma_kernel"}
 
 
 def ingest_counters(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
@@ -292,7 +361,7 @@ def main():
     ap.add_argument("--secondary-layers", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla", "cascade"], default=None,
                     help="time one workload (profiling runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -333,7 +402,8 @@ def main():
         log(f"calibration copy: {n} bytes read, {n} bytes written")
 
     result = {}
-    which = [args.only] if args.only else ["decode"] + ([] if args.no_secondary else ["prefill", "skewed", "mla"])
+    which = [args.only] if args.only else ["decode"] + ([] if args.no_secondary else
+                                                        ["prefill", "skewed", "mla", "cascade"])
 
     if "decode" in which:
         b = wl.make("decode", with_append=True)
@@ -378,6 +448,25 @@ def main():
         log(f"mla: run {result['mla']['gbs']:.1f} GB/s, {result['mla']['tflops']:.1f} TFLOP/s "
             f"({m['attn_ms_mean'] * 1e3:.1f} us)")
         del r
+
+    if "cascade" in which:
+        b = wl.make("cascade")
+        layers = args.secondary_layers
+        r = CascadeRunner(b, layers)
+        m = measure(r, layers, args.steps, args.warmup)
+        nb = cascade_bytes(b)
+        del r
+        # The same batch through a flat page table (each request reads its whole path).
+        fl = wl.flat_levels(b)
+        bf = wl.Batch(**{**b.__dict__, "mode": "decode", "kv_indptr": fl["kv_indptr"], "kv_indices": fl["kv_indices"],
+                         "kv_last_page_len": fl["kv_last_page_len"], "kv_lens": fl["kv_lens"], "extra": {}})
+        rf = Runner(bf, layers, time_merge=True)
+        mf = measure(rf, layers, max(2, args.steps // 4), 1)
+        del rf
+        result["cascade"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
+                                 flat_us=mf["attn_ms_mean"] * 1e3)
+        log(f"cascade: run {m['attn_ms_mean'] * 1e3:.1f} us ({result['cascade']['gbs']:.1f} GB/s unique), "
+            f"flat decode {mf['attn_ms_mean'] * 1e3:.1f} us")
 
     if args.only and args.only != "decode":
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk != "plan_info"} for k, v in result.items()}))
@@ -428,6 +517,18 @@ def main():
         line["mla_decode"] = {"value": round(mm["gbs"], 1), "unit": "GB/s", "frac": round(mm["gbs"] / HBM_PEAK_GBS, 4),
                               "tflops": round(mm["tflops"], 2), "run_us_mean": round(mm["attn_ms_mean"] * 1e3, 2),
                               "timed": "attention + merge"}
+    if "cascade" in result:
+        c = result["cascade"]
+        run_s = c["attn_ms_mean"] * 1e-3
+        line["cascade"] = {"value": round(c["gbs"], 1), "unit": "GB/s", "frac": round(c["gbs"] / HBM_PEAK_GBS, 4),
+                           "run_us_mean": round(c["attn_ms_mean"] * 1e3, 2),
+                           "timed": "all level launches + row merge",
+                           "flat_equivalent_gbs": round(c["bytes"]["flat_kv"] / run_s / 1e9, 1),
+                           "flat_decode_us_mean": round(c["flat_us"], 2),
+                           "speedup_vs_flat_decode": round(c["flat_us"] / (c["attn_ms_mean"] * 1e3), 2),
+                           "workload": "shared-prefix decode: 64 requests, 3-level tree (16384-token root, "
+                                       "8 branches U[1024,4096], leaves U[128,1024]), page 16, 32/8 heads, "
+                                       "d128, bf16"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl.make("decode"))
     print(json.dumps(line), flush=True)

@@ -65,7 +65,9 @@ typedef enum {
   PKV_META_QO_EXCEEDS_KV = 9,    /* completion: qo_len > kv_len (kv_len counts the new tokens) */
   PKV_META_HEAD_GROUP = 10,      /* completion: num_qo_heads not a multiple of num_kv_heads */
   PKV_META_DECODE_QO_LEN = 11,   /* completion: decode mode needs qo_len == 1 */
-  PKV_META_APPEND_COLLISION = 12 /* completion: two appended tokens target one slot */
+  PKV_META_APPEND_COLLISION = 12, /* completion: two appended tokens target one slot */
+  PKV_META_CASCADE_ROWS = 13,    /* completion: no cascade level, or levels cover different row counts */
+  PKV_META_CASCADE_NESTING = 14  /* completion: a cascade level's node boundary is not one of the next level's */
 } pkv_meta_reason;
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -331,6 +333,105 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
                        const void* ckv, const void* kpe, int64_t page_stride,
                        int64_t token_stride, const int32_t* d_kv_indices, void* o, float* lse,
                        float sm_scale, void* stream);
+
+/* --------------------------------------------------------------- cascade -- */
+
+/*
+ * Multi-level cascade attention ([KVL] "多级级联推理数据布局"): the queries
+ * and outputs stay one ragged tensor and every level's keys live in the one
+ * paged cache; level l views them through its own qo_indptr (query rows of
+ * each node, i.e. of each subtree of the request tree) and its own page table
+ * (kv_indptr, kv_indices, kv_last_page_len as in pkv_run).  Row i's output is
+ * attention over the keys of all nodes on its path, level 0 first: the merge
+ * of its per-level states ([DD] "Core mechanism: schedule work around state":
+ * output plus base-2 LSE composes across shared prefixes).
+ *
+ * Readings (the layout page leaves them open): every level covers all rows
+ * and the levels nest (each node's rows are whole nodes of the next level);
+ * the keys of a shared level precede every query token below it, so only the
+ * last level, whose nodes are requests, applies the bottom-right causal mask
+ * (params->causal); the per-request metadata rules of pkv_validate hold per
+ * level, except that a shared node may hold fewer keys than rows.
+ *
+ * Schedule (ours): each level is planned like pkv_plan_create -- as decode
+ * when every node has one row, else as prefill, so a node shared by many
+ * rows runs the MFMA tile kernel and its keys are read once for all of them
+ * -- except that every tile writes fp32 partial states.  A row-indexed merge
+ * then folds, per query row, the partial states of all its levels and
+ * chunks.  pkv_cascade_run enqueues one attention launch per level and one
+ * merge.
+ */
+typedef struct pkv_cascade_level {
+  int32_t num_nodes;
+  const int32_t* qo_indptr;        /* host, num_nodes+1: query rows of each node */
+  const int32_t* kv_indptr;        /* host, num_nodes+1: pages of each node */
+  const int32_t* kv_indices;       /* host page ids of the level, or NULL (range check skipped) */
+  int64_t num_indices;
+  const int32_t* kv_last_page_len; /* host, num_nodes */
+} pkv_cascade_level;
+
+typedef struct pkv_cascade_info {
+  int32_t num_levels;
+  int32_t total_rows;        /* query rows (every level's qo_indptr[num_nodes]) */
+  int32_t num_items;         /* work items over all levels */
+  int32_t num_partial_rows;  /* partial states per head (every item writes some) */
+  int32_t num_merge_slots;   /* entries of the row-indexed merge list (= num_partial_rows) */
+  int32_t reserved;
+  int64_t workspace_bytes;
+  int64_t staging_bytes;
+  uint64_t fingerprint;
+} pkv_cascade_info;
+
+typedef struct pkv_cascade_plan pkv_cascade_plan;
+
+/*
+ * Host-only cascade planning.  params: heads, dims, page size, dtypes, causal,
+ * num_cus, max_num_pages and the split knobs apply to every level; mode and
+ * batch_size are ignored (each level's mode follows from its node row counts,
+ * its batch is its node count).  levels[0 .. num_levels) are host structs.
+ * Metadata is checked level by level (pkv_meta_reason; PKV_META_CASCADE_* for
+ * the cross-level rules).  Fills info and, when given, level_info
+ * (num_levels entries: each level's plan as pkv_plan_get_info reports it),
+ * the work list (info.num_items * PKV_ITEM_WORDS int32, levels back to back;
+ * page_base counts into the concatenated page ids of all levels, out_slot
+ * into the shared partial rows), the merge row pointers (total_rows + 1
+ * int32) and the merge slot list (num_merge_slots int32).  Pass NULL buffers
+ * to query sizes; PKV_ERR_WORKSPACE if a non-NULL buffer is too small.
+ */
+pkv_status pkv_cascade_plan_compute(const pkv_plan_params* params, int32_t num_levels,
+                                    const pkv_cascade_level* levels, pkv_cascade_info* info,
+                                    pkv_plan_info* level_info, int32_t* items_out, int64_t items_capacity,
+                                    int32_t* row_ptr_out, int64_t row_ptr_capacity, int32_t* slots_out,
+                                    int64_t slots_capacity);
+
+/*
+ * Build a cascade plan and upload it (workspace and staging rules as for
+ * pkv_plan_create; ws_bytes >= info.workspace_bytes, staging_bytes >=
+ * info.staging_bytes).  The plan (library-owned host memory) is valid for
+ * this exact batch until pkv_cascade_plan_destroy.
+ */
+pkv_status pkv_cascade_plan_create(const pkv_plan_params* params, int32_t num_levels,
+                                   const pkv_cascade_level* levels, void* d_workspace, size_t ws_bytes,
+                                   void* h_staging, size_t staging_bytes, void* stream,
+                                   pkv_cascade_plan** plan_out);
+
+pkv_status pkv_cascade_plan_get_info(const pkv_cascade_plan* plan, pkv_cascade_info* info);
+
+/*
+ * Run a cascade: one attention launch per level (levels in order), then the
+ * row-indexed merge into o / lse, all on `stream`; no allocation, no host
+ * synchronisation.
+ *   q, cache, o, lse, sm_scale   as for pkv_run (q/o hold every query row)
+ *   d_kv_indices  device int32: the page ids of level 0 (kv_indptr[num_nodes]
+ *                 of them), then those of level 1, and so on -- the same
+ *                 values the plan was built on
+ */
+pkv_status pkv_cascade_run(const pkv_cascade_plan* plan, const void* q, int64_t q_stride_token,
+                           int64_t q_stride_head, const pkv_cache_desc* cache, const int32_t* d_kv_indices,
+                           void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse,
+                           float sm_scale, void* stream);
+
+pkv_status pkv_cascade_plan_destroy(pkv_cascade_plan* plan);
 
 /* ----------------------------------------------------------------- merge -- */
 

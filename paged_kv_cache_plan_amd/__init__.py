@@ -17,8 +17,8 @@ import os
 
 import numpy as np
 
-from ._abi import (BF16, DECODE, F32, HND, MLA_DECODE, NHD, PREFILL, STATUS_NAMES, CacheDesc, PlanInfo,
-                   PlanParams, load_library)
+from ._abi import (BF16, DECODE, F32, HND, MLA_DECODE, NHD, PREFILL, STATUS_NAMES, CacheDesc, CascadeInfo,
+                   CascadeLevel, PlanInfo, PlanParams, load_library)
 
 _lib = None
 
@@ -300,6 +300,97 @@ class Plan:
         h = getattr(self, "_handle", None)
         if h and _lib is not None:
             _lib.pkv_plan_destroy(h)
+            self._handle = None
+
+
+# ---------------------------------------------------------------- cascade --
+
+def _cascade_levels(levels):
+    """Host level structs (and the int32 arrays they point at, kept alive)."""
+    keep = []
+    arr = (CascadeLevel * max(1, len(levels)))()
+    for i, lv in enumerate(levels):
+        qo, qo_p = _host_i32(lv["qo_indptr"], "qo_indptr")
+        kvp, kvp_p = _host_i32(lv["kv_indptr"], "kv_indptr")
+        idx, idx_p = _host_i32(lv.get("kv_indices"), "kv_indices")
+        last, last_p = _host_i32(lv["kv_last_page_len"], "kv_last_page_len")
+        keep += [qo, kvp, idx, last]
+        arr[i].num_nodes = len(last)
+        arr[i].qo_indptr, arr[i].kv_indptr, arr[i].kv_indices, arr[i].kv_last_page_len = qo_p, kvp_p, idx_p, last_p
+        arr[i].num_indices = 0 if idx is None else len(idx)
+    return arr, keep
+
+
+def cascade_plan_compute(params: PlanParams, levels):
+    """pkv_cascade_plan_compute (host only): (info dict, per-level info dicts, items [n, 8],
+    row_ptr [rows + 1], slots [n_slots]), all int32 arrays."""
+    arr, keep = _cascade_levels(levels)
+    info = CascadeInfo()
+    L = lib()
+    _check(L.pkv_cascade_plan_compute(ctypes.byref(params), len(levels), arr, ctypes.byref(info), None, None, 0,
+                                      None, 0, None, 0))
+    lvl = (PlanInfo * max(1, len(levels)))()
+    items = np.zeros((info.num_items, 8), dtype=np.int32)
+    row_ptr = np.zeros(info.total_rows + 1, dtype=np.int32)
+    slots = np.zeros(info.num_merge_slots, dtype=np.int32)
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(L.pkv_cascade_plan_compute(ctypes.byref(params), len(levels), arr, ctypes.byref(info), lvl,
+                                      p32(items), items.size, p32(row_ptr), row_ptr.size, p32(slots), slots.size))
+    return info.as_dict(), [lvl[i].as_dict() for i in range(len(levels))], items, row_ptr, slots
+
+
+class CascadePlan:
+    """pkv_cascade_plan_create / pkv_cascade_run / pkv_cascade_plan_destroy.
+
+    ``levels``: list of dicts with host int32 qo_indptr, kv_indptr, kv_indices
+    (optional) and kv_last_page_len, level 0 (the root) first.  Workspace and
+    staging are allocated here with torch unless passed in."""
+
+    def __init__(self, params: PlanParams, levels, *, workspace=None, staging=None, stream=None):
+        import torch
+        self.params = params
+        self._levels, self._keep = _cascade_levels(levels)
+        info = CascadeInfo()
+        _check(lib().pkv_cascade_plan_compute(ctypes.byref(params), len(levels), self._levels, ctypes.byref(info),
+                                              None, None, 0, None, 0, None, 0))
+        ws_bytes = max(int(info.workspace_bytes), 256)
+        st_bytes = max(int(info.staging_bytes), 256)
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        if staging is None or staging.numel() < st_bytes:
+            staging = torch.empty(st_bytes, dtype=torch.uint8, pin_memory=True)
+        self.workspace, self.staging = workspace, staging
+        handle = ctypes.c_void_p()
+        _check(lib().pkv_cascade_plan_create(ctypes.byref(params), len(levels), self._levels,
+                                             ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                             ctypes.c_void_p(staging.data_ptr()), staging.numel(), _stream(stream),
+                                             ctypes.byref(handle)))
+        self._handle = handle
+
+    @property
+    def info(self) -> dict:
+        out = CascadeInfo()
+        _check(lib().pkv_cascade_plan_get_info(self._handle, ctypes.byref(out)))
+        return out.as_dict()
+
+    def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None):
+        """pkv_cascade_run.  kv_indices: device int32, the levels' page ids back to back (level 0 first)."""
+        import torch
+        p = self.params
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk)
+        if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
+            raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        _check(lib().pkv_cascade_run(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
+                                     _dev(kv_indices, "kv_indices", torch.int32), _dev(out, "out", q.dtype),
+                                     out.stride(0), out.stride(1), None if lse is None else _dev(lse, "lse"),
+                                     ctypes.c_float(sm_scale), _stream(stream)))
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h and _lib is not None:
+            _lib.pkv_cascade_plan_destroy(h)
             self._handle = None
 
 

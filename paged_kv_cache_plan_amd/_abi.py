@@ -15,7 +15,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "METADATA", 3: "UNSUPPORTED", 4: "
 META_REASONS = {
     "batch_size": 1, "page_size": 2, "indptr_start": 3, "indptr_order": 4, "empty_page_list": 5,
     "last_page_len": 6, "page_index": 7, "indices_length": 8, "qo_exceeds_kv": 9, "head_group": 10,
-    "decode_qo_len": 11, "append_collision": 12,
+    "decode_qo_len": 11, "append_collision": 12, "cascade_rows": 13, "cascade_nesting": 14,
 }
 F32, BF16 = 0, 1
 NHD, HND = 0, 1
@@ -47,6 +47,21 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class CascadeLevel(ctypes.Structure):
+    _fields_ = [("num_nodes", ctypes.c_int32), ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
+                ("kv_indptr", ctypes.POINTER(ctypes.c_int32)), ("kv_indices", ctypes.POINTER(ctypes.c_int32)),
+                ("num_indices", ctypes.c_int64), ("kv_last_page_len", ctypes.POINTER(ctypes.c_int32))]
+
+
+class CascadeInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_levels", "total_rows", "num_items", "num_partial_rows", "num_merge_slots", "reserved")] + [
+        ("workspace_bytes", ctypes.c_int64), ("staging_bytes", ctypes.c_int64), ("fingerprint", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -75,6 +90,15 @@ SIGNATURES = {
                                  ctypes.c_float, _vp]),
     "pkv_run_merge": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "pkv_run_mla": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.c_float, _vp]),
+    "pkv_cascade_plan_compute": (_i32, [ctypes.POINTER(PlanParams), _i32, ctypes.POINTER(CascadeLevel),
+                                        ctypes.POINTER(CascadeInfo), ctypes.POINTER(PlanInfo), _i32p, _i64, _i32p,
+                                        _i64, _i32p, _i64]),
+    "pkv_cascade_plan_create": (_i32, [ctypes.POINTER(PlanParams), _i32, ctypes.POINTER(CascadeLevel), _vp,
+                                       ctypes.c_size_t, _vp, ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]),
+    "pkv_cascade_plan_get_info": (_i32, [_vp, ctypes.POINTER(CascadeInfo)]),
+    "pkv_cascade_run": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64,
+                               _vp, ctypes.c_float, _vp]),
+    "pkv_cascade_plan_destroy": (_i32, [_vp]),
     "pkv_merge_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "pkv_merge_states": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
 }

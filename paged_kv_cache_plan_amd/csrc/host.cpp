@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -88,7 +89,7 @@ pkv_status validate_impl(const int32_t* qo_indptr, const int32_t* kv_indptr,
                          const int32_t* kv_indices, int64_t num_indices,
                          const int32_t* last, int32_t batch, int32_t page_size,
                          int32_t max_num_pages, int32_t hq, int32_t hkv, bool decode,
-                         std::vector<int32_t>* kv_len_out) {
+                         std::vector<int32_t>* kv_len_out, bool check_qo_kv = true) {
   if (batch < 0) return meta_fail(PKV_META_BATCH_SIZE, "negative batch size");
   if (page_size < 1) return meta_fail(PKV_META_PAGE_SIZE, fmt("page_size %lld < 1", page_size));
   if (hq < 1 || hkv < 1 || hq % hkv != 0)
@@ -127,7 +128,7 @@ pkv_status validate_impl(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const int64_t len = int64_t(page_size) * (kv_indptr[b + 1] - kv_indptr[b] - 1) + last[b];
     if (decode && q != 1)
       return meta_fail(PKV_META_DECODE_QO_LEN, fmt("request %lld: decode needs qo_len 1, got %lld", b, q));
-    if (q > len)
+    if (check_qo_kv && q > len)
       return meta_fail(PKV_META_QO_EXCEEDS_KV, fmt("request %lld: qo_len %lld > kv_len %lld", b, q, len));
   }
   return PKV_OK;
@@ -200,9 +201,12 @@ pkv_status check_params(const pkv_plan_params* p) {
   return PKV_OK;
 }
 
+// all_partial: every tile writes partial rows (a cascade merges them later);
+// check_qo_kv = false drops the qo_len <= kv_len rule (a cascade's shared
+// levels may hold fewer keys than their subtree has query rows).
 pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const int32_t* kv_indptr,
                      const int32_t* kv_indices, int64_t num_indices, const int32_t* last,
-                     PlanResult* out) {
+                     PlanResult* out, bool all_partial = false, bool check_qo_kv = true) {
   pkv_status s = check_params(prm);
   if (s) return s;
   const bool prefill = prm->mode == PKV_MODE_PREFILL;
@@ -213,7 +217,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   const int32_t max_pages = prm->max_num_pages > 0 ? prm->max_num_pages : INT32_MAX;
   std::vector<int32_t> kv_len;
   s = validate_impl(qo_indptr, kv_indptr, kv_indices, num_indices, last, batch, prm->page_size,
-                    max_pages, prm->num_qo_heads, prm->num_kv_heads, !prefill, &kv_len);
+                    max_pages, prm->num_qo_heads, prm->num_kv_heads, !prefill, &kv_len, check_qo_kv);
   if (s) return s;
 
   int32_t num_cus = prm->num_cus;
@@ -293,7 +297,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
         }
       }
       const int32_t q_row0 = int32_t((prefill ? qo_indptr[b] : b) + l0);
-      if (kept.size() == 1) {
+      if (kept.size() == 1 && !all_partial) {
         Item it{q_row0, int32_t(n_rows), kept[0].first, kept[0].second, int32_t(diag), kv_indptr[b], -1, b};
         raw.push_back({int64_t(kept[0].second - kept[0].first), b, int32_t(t), 0, it});
         continue;
@@ -345,10 +349,161 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   return PKV_OK;
 }
 
+// ---------------------------------------------------------------- cascade --
+
+struct CascadeResult {
+  std::vector<Item> items;
+  std::vector<int32_t> row_ptr, slots;
+  std::vector<pkv_plan_info> level_info;
+  std::vector<int32_t> level_mode, level_item_off;
+  pkv_cascade_info info;
+};
+
+// Level checks in the oracle's order: every level's page-table rules (a
+// shared level without qo_len <= kv_len, its qo_indptr checked after its
+// pages), then equal row counts, then nesting.
+pkv_status cascade_validate(const pkv_plan_params* prm, int32_t num_levels, const pkv_cascade_level* lv) {
+  if (num_levels < 1 || !lv) return meta_fail(PKV_META_CASCADE_ROWS, "a cascade needs at least one level");
+  const int32_t max_pages = prm->max_num_pages > 0 ? prm->max_num_pages : INT32_MAX;
+  for (int32_t l = 0; l < num_levels; ++l) {
+    const pkv_cascade_level& L = lv[l];
+    if (L.num_nodes < 0) return meta_fail(PKV_META_BATCH_SIZE, fmt("level %lld: negative node count", l));
+    if (!L.qo_indptr) return fail(PKV_ERR_INVALID_ARG, fmt("level %lld: null qo_indptr", l));
+    pkv_status s;
+    if (l == num_levels - 1) {
+      s = validate_impl(L.qo_indptr, L.kv_indptr, L.kv_indices, L.num_indices, L.kv_last_page_len, L.num_nodes,
+                        prm->page_size, max_pages, prm->num_qo_heads, prm->num_kv_heads, false, nullptr);
+    } else {
+      s = validate_impl(nullptr, L.kv_indptr, L.kv_indices, L.num_indices, L.kv_last_page_len, L.num_nodes,
+                        prm->page_size, max_pages, prm->num_qo_heads, prm->num_kv_heads, false, nullptr);
+      if (!s) s = check_indptr("qo_indptr", L.qo_indptr, L.num_nodes);
+    }
+    if (s) return s;
+  }
+  const int32_t rows = lv[0].qo_indptr[lv[0].num_nodes];
+  for (int32_t l = 1; l < num_levels; ++l)
+    if (lv[l].qo_indptr[lv[l].num_nodes] != rows)
+      return meta_fail(PKV_META_CASCADE_ROWS, fmt("level %lld covers %lld query rows, level 0 %lld", l,
+                                                  lv[l].qo_indptr[lv[l].num_nodes], rows));
+  for (int32_t l = 0; l + 1 < num_levels; ++l) {
+    const pkv_cascade_level& up = lv[l];
+    const pkv_cascade_level& dn = lv[l + 1];
+    // Both indptrs are non-decreasing: walk them together.
+    int32_t j = 0;
+    for (int32_t i = 0; i <= up.num_nodes; ++i) {
+      const int32_t b = up.qo_indptr[i];
+      while (j <= dn.num_nodes && dn.qo_indptr[j] < b) ++j;
+      if (j > dn.num_nodes || dn.qo_indptr[j] != b)
+        return meta_fail(PKV_META_CASCADE_NESTING,
+                         fmt("level %lld has node boundary %lld that level %lld does not", l, b, l + 1));
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status cascade_impl(const pkv_plan_params* prm, int32_t num_levels, const pkv_cascade_level* lv,
+                        CascadeResult* out) {
+  pkv_status s = cascade_validate(prm, num_levels, lv);
+  if (s) return s;
+  const int32_t rows = lv[0].qo_indptr[lv[0].num_nodes];
+  std::vector<std::vector<int32_t>> per_row(static_cast<size_t>(rows));
+  out->items.clear();
+  out->level_info.clear();
+  out->level_mode.clear();
+  out->level_item_off.clear();
+  int64_t slot_base = 0, page_base = 0;
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t l = 0; l < num_levels; ++l) {
+    const pkv_cascade_level& L = lv[l];
+    bool one_row = L.num_nodes > 0;
+    for (int32_t n = 0; n < L.num_nodes && one_row; ++n) one_row = L.qo_indptr[n + 1] - L.qo_indptr[n] == 1;
+    pkv_plan_params p = *prm;
+    p.mode = one_row ? PKV_MODE_DECODE : PKV_MODE_PREFILL;
+    p.batch_size = L.num_nodes;
+    p.causal = (prm->causal && l == num_levels - 1) ? 1 : 0;
+    PlanResult r;
+    s = plan_impl(&p, one_row ? nullptr : L.qo_indptr, L.kv_indptr, L.kv_indices, L.num_indices,
+                  L.kv_last_page_len, &r, true, l == num_levels - 1);
+    if (s) return s;
+    if (slot_base + r.info.num_partial_rows > INT32_MAX || page_base + L.kv_indptr[L.num_nodes] > INT32_MAX)
+      return fail(PKV_ERR_INVALID_ARG, "cascade too large for int32 slots or page offsets");
+    out->level_item_off.push_back(int32_t(out->items.size()));
+    for (Item it : r.items) {
+      it.page_base += int32_t(page_base);
+      it.out_slot += int32_t(slot_base);
+      out->items.push_back(it);
+    }
+    for (const MergeItem& m : r.merges)
+      for (int32_t rr = 0; rr < m.num_rows; ++rr)
+        for (int32_t c = 0; c < m.num_chunks; ++c)
+          per_row[size_t(m.q_row0 + rr)].push_back(int32_t(slot_base + m.slot0 + int64_t(c) * m.num_rows + rr));
+    out->level_info.push_back(r.info);
+    out->level_mode.push_back(p.mode);
+    h = fnv1a(h, &r.info.fingerprint, sizeof(uint64_t));
+    h = fnv1a(h, L.qo_indptr, sizeof(int32_t) * (L.num_nodes + 1));   // decode levels do not hash it
+    slot_base += r.info.num_partial_rows;
+    page_base += L.kv_indptr[L.num_nodes];
+  }
+  out->row_ptr.assign(size_t(rows) + 1, 0);
+  out->slots.clear();
+  out->slots.reserve(size_t(slot_base));
+  for (int32_t r = 0; r < rows; ++r) {
+    out->slots.insert(out->slots.end(), per_row[size_t(r)].begin(), per_row[size_t(r)].end());
+    out->row_ptr[size_t(r) + 1] = int32_t(out->slots.size());
+  }
+  pkv_cascade_info& in = out->info;
+  std::memset(&in, 0, sizeof in);
+  in.num_levels = num_levels;
+  in.total_rows = rows;
+  in.num_items = int32_t(out->items.size());
+  in.num_partial_rows = int32_t(slot_base);
+  in.num_merge_slots = int32_t(out->slots.size());
+  const int64_t hq = prm->num_qo_heads;
+  in.staging_bytes = align256(int64_t(out->items.size()) * sizeof(Item)) + align256(int64_t(rows + 1) * 4) +
+                     align256(int64_t(out->slots.size()) * 4);
+  in.workspace_bytes = in.staging_bytes + align256(slot_base * hq * 4) + align256(slot_base * hq * prm->head_dim_vo * 4);
+  in.fingerprint = h;
+  return PKV_OK;
+}
+
 // Pinned staging buffers remember the event of the last upload made from
 // them, so a later plan does not overwrite bytes still being copied.
 std::mutex g_staging_mu;
 std::unordered_map<void*, hipEvent_t> g_staging_events;
+
+// Copies a plan's host-built tables to the start of the device workspace.
+// With a pinned staging buffer the copy is asynchronous; the buffer's event
+// records it, and a later upload from the same buffer first waits for that
+// event.  Without one, the bytes go through a temporary host vector and the
+// stream is synchronised before it is freed.
+hipError_t upload_staging(void* h_staging, void* ws, int64_t bytes, hipStream_t st,
+                          const std::function<void(char*)>& fill) {
+  hipError_t e;
+  if (h_staging) {
+    std::lock_guard<std::mutex> lock(g_staging_mu);
+    auto it = g_staging_events.find(h_staging);
+    if (it == g_staging_events.end()) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+      it = g_staging_events.emplace(h_staging, ev).first;
+    } else {
+      e = hipEventSynchronize(it->second);   // the previous upload from this buffer
+      if (e != hipSuccess) return e;
+    }
+    char* hs = static_cast<char*>(h_staging);
+    std::memset(hs, 0, size_t(bytes));
+    fill(hs);
+    e = hipMemcpyAsync(ws, hs, size_t(bytes), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(it->second, st);
+    return e;
+  }
+  std::vector<char> tmp(size_t(bytes), 0);
+  fill(tmp.data());
+  e = hipMemcpyAsync(ws, tmp.data(), tmp.size(), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e;
+}
 
 }  // namespace
 
@@ -472,36 +627,10 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
     return hip_fail(e, "hipGetDevice");
   }
   if (in.staging_bytes > 0) {
-    if (h_staging) {
-      std::lock_guard<std::mutex> lock(g_staging_mu);
-      auto it = g_staging_events.find(h_staging);
-      if (it == g_staging_events.end()) {
-        hipEvent_t ev;
-        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-        if (e != hipSuccess) {
-          delete plan;
-          return hip_fail(e, "hipEventCreate");
-        }
-        it = g_staging_events.emplace(h_staging, ev).first;
-      } else {
-        e = hipEventSynchronize(it->second);   // the previous upload from this buffer
-        if (e != hipSuccess) {
-          delete plan;
-          return hip_fail(e, "waiting for the previous plan upload");
-        }
-      }
-      char* hs = static_cast<char*>(h_staging);
+    e = upload_staging(h_staging, ws, in.staging_bytes, st, [&](char* hs) {
       std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
       std::memcpy(hs + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
-      e = hipMemcpyAsync(ws, hs, size_t(in.staging_bytes), hipMemcpyHostToDevice, st);
-      if (e == hipSuccess) e = hipEventRecord(it->second, st);
-    } else {
-      std::vector<char> tmp(size_t(in.staging_bytes), 0);
-      std::memcpy(tmp.data(), r.items.data(), r.items.size() * sizeof(Item));
-      std::memcpy(tmp.data() + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
-      e = hipMemcpyAsync(ws, tmp.data(), tmp.size(), hipMemcpyHostToDevice, st);
-      if (e == hipSuccess) e = hipStreamSynchronize(st);
-    }
+    });
     if (e != hipSuccess) {
       delete plan;
       return hip_fail(e, "uploading the plan");
@@ -550,13 +679,17 @@ static pkv_status check_ptr16(const void* p, const char* what) {
 
 static bool stride_ok(int64_t stride, size_t esize) { return stride >= 0 && (stride * int64_t(esize)) % 16 == 0; }
 
-pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stride_token,
-                             int64_t q_stride_head, const pkv_cache_desc* cache, const int32_t* d_kv_indices,
-                             void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
-                             void* stream) {
-  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
-  const pkv_plan_params& p = plan->params;
-  if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by pkv_run_attention and pkv_cascade_run; fills
+// every AttnArgs field except the work list and the partial buffers.
+pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_items, const void* q,
+                        int64_t q_stride_token, int64_t q_stride_head, const pkv_cache_desc* cache,
+                        const int32_t* d_kv_indices, void* o, int64_t o_stride_token, int64_t o_stride_head,
+                        float* lse, float sm_scale, pkv::AttnArgs* a) {
+  if (!cache) return fail(PKV_ERR_INVALID_ARG, "null cache");
   if (cache->page_size != p.page_size || cache->num_kv_heads != p.num_kv_heads ||
       cache->head_dim != p.head_dim_qk || cache->dtype != p.kv_dtype)
     return fail(PKV_ERR_INVALID_ARG, "cache descriptor does not match the plan");
@@ -567,46 +700,48 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
   if ((s = check_ptr16(q, "q")) || (s = check_ptr16(o, "o")) || (s = check_ptr16(cache->k, "cache k")) ||
       (s = check_ptr16(cache->v, "cache v")))
     return s;
-  if (!d_kv_indices && plan->info.num_items > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
+  if (!d_kv_indices && has_items) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
   if (!stride_ok(q_stride_token, es) || !stride_ok(q_stride_head, es) || !stride_ok(o_stride_token, es) ||
       !stride_ok(o_stride_head, es) || !stride_ok(cache->page_stride, es) ||
       !stride_ok(cache->token_stride, es) || !stride_ok(cache->head_stride, es))
     return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+  if (hipGetDevice(&dev) != hipSuccess || dev != plan_device)
     return fail(PKV_ERR_INVALID_ARG, "plan was built on another device");
-  if (plan->info.num_items == 0) return ok();
-
-  pkv::AttnArgs a;
-  a.items = plan->d_items;
-  a.num_items = plan->info.num_items;
-  a.num_kv_heads = p.num_kv_heads;
-  a.num_qo_heads = p.num_qo_heads;
-  a.q = q;
-  a.q_stride_token = q_stride_token;
-  a.q_stride_head = q_stride_head;
-  a.k = cache->k;
-  a.v = cache->v;
-  a.page_stride = cache->page_stride;
-  a.token_stride = cache->token_stride;
-  a.head_stride = cache->head_stride;
-  a.page_size = cache->page_size;
-  a.page_shift = page_shift_of(cache->page_size);
-  a.max_num_pages = cache->max_num_pages;
-  a.kv_indices = d_kv_indices;
-  a.o = o;
-  a.o_stride_token = o_stride_token;
-  a.o_stride_head = o_stride_head;
-  a.lse = lse;
-  a.part_o = plan->d_part_o;
-  a.part_lse = plan->d_part_lse;
+  a->items = nullptr;
+  a->num_items = 0;
+  a->num_kv_heads = p.num_kv_heads;
+  a->num_qo_heads = p.num_qo_heads;
+  a->q = q;
+  a->q_stride_token = q_stride_token;
+  a->q_stride_head = q_stride_head;
+  a->k = cache->k;
+  a->v = cache->v;
+  a->page_stride = cache->page_stride;
+  a->token_stride = cache->token_stride;
+  a->head_stride = cache->head_stride;
+  a->page_size = cache->page_size;
+  a->page_shift = page_shift_of(cache->page_size);
+  a->max_num_pages = cache->max_num_pages;
+  a->kv_indices = d_kv_indices;
+  a->o = o;
+  a->o_stride_token = o_stride_token;
+  a->o_stride_head = o_stride_head;
+  a->lse = lse;
+  a->part_o = nullptr;
+  a->part_lse = nullptr;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(p.head_dim_qk));
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  return PKV_OK;
+}
+
+// The attention kernel for a plan's mode: the MFMA tile kernel for bf16
+// prefill, the row kernel otherwise.
+pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::AttnArgs& a, hipStream_t st) {
   const int32_t group = p.num_qo_heads / p.num_kv_heads;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   bool supported = false;
   hipError_t e;
-  if (p.mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
+  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
     e = pkv::launch_prefill_mfma(p.head_dim_qk, group, a, st, &supported);
   else
     e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
@@ -614,6 +749,31 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
     return fail(PKV_ERR_UNSUPPORTED, fmt("no kernel for head_dim %lld, group %lld, dtype %lld",
                                          p.head_dim_qk, group, p.kv_dtype));
   if (e != hipSuccess) return hip_fail(e, "launching attention");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stride_token,
+                             int64_t q_stride_head, const pkv_cache_desc* cache, const int32_t* d_kv_indices,
+                             void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                             void* stream) {
+  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
+  const pkv_plan_params& p = plan->params;
+  if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
+  pkv::AttnArgs a;
+  pkv_status s = prepare_attn(p, plan->device, plan->info.num_items > 0, q, q_stride_token, q_stride_head, cache,
+                              d_kv_indices, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (s) return s;
+  if (plan->info.num_items == 0) return ok();
+  a.items = plan->d_items;
+  a.num_items = plan->info.num_items;
+  a.part_o = plan->d_part_o;
+  a.part_lse = plan->d_part_lse;
+  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream));
+  if (s) return s;
   return ok();
 }
 
@@ -774,6 +934,152 @@ pkv_status pkv_merge_states(const void* v, const float* s, void* v_out, float* s
   hipError_t e = pkv::launch_merge_many(dtype, v, s, v_out, s_out, num_rows, num_states, num_heads, head_dim,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching merge_states");
+  return ok();
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------- cascade --
+
+struct pkv_cascade_plan {
+  pkv_plan_params params;
+  pkv_cascade_info info;
+  std::vector<pkv_plan_info> level_info;
+  std::vector<int32_t> level_mode, level_item_off;
+  Item* d_items;
+  int32_t* d_row_ptr;
+  int32_t* d_slots;
+  float* d_part_lse;
+  float* d_part_o;
+  int device;
+};
+
+extern "C" {
+
+pkv_status pkv_cascade_plan_compute(const pkv_plan_params* params, int32_t num_levels,
+                                    const pkv_cascade_level* levels, pkv_cascade_info* info,
+                                    pkv_plan_info* level_info, int32_t* items_out, int64_t items_capacity,
+                                    int32_t* row_ptr_out, int64_t row_ptr_capacity, int32_t* slots_out,
+                                    int64_t slots_capacity) {
+  pkv_status s = check_params(params);
+  if (s) return s;
+  CascadeResult r;
+  s = cascade_impl(params, num_levels, levels, &r);
+  if (s) return s;
+  if (info) *info = r.info;
+  if (level_info) std::copy(r.level_info.begin(), r.level_info.end(), level_info);
+  if (items_out) {
+    if (items_capacity < int64_t(r.items.size()) * PKV_ITEM_WORDS)
+      return fail(PKV_ERR_WORKSPACE, "work-item buffer too small");
+    std::memcpy(items_out, r.items.data(), r.items.size() * sizeof(Item));
+  }
+  if (row_ptr_out) {
+    if (row_ptr_capacity < int64_t(r.row_ptr.size())) return fail(PKV_ERR_WORKSPACE, "row pointer buffer too small");
+    std::memcpy(row_ptr_out, r.row_ptr.data(), r.row_ptr.size() * 4);
+  }
+  if (slots_out) {
+    if (slots_capacity < int64_t(r.slots.size())) return fail(PKV_ERR_WORKSPACE, "slot buffer too small");
+    std::memcpy(slots_out, r.slots.data(), r.slots.size() * 4);
+  }
+  return ok();
+}
+
+pkv_status pkv_cascade_plan_create(const pkv_plan_params* params, int32_t num_levels,
+                                   const pkv_cascade_level* levels, void* d_workspace, size_t ws_bytes,
+                                   void* h_staging, size_t staging_bytes, void* stream,
+                                   pkv_cascade_plan** plan_out) {
+  if (!plan_out) return fail(PKV_ERR_INVALID_ARG, "null plan_out");
+  *plan_out = nullptr;
+  pkv_status s = check_params(params);
+  if (s) return s;
+  CascadeResult r;
+  s = cascade_impl(params, num_levels, levels, &r);
+  if (s) return s;
+  const pkv_cascade_info& in = r.info;
+  if (in.workspace_bytes > 0 && (!d_workspace || int64_t(ws_bytes) < in.workspace_bytes))
+    return fail(PKV_ERR_WORKSPACE, fmt("workspace %lld bytes < %lld needed", int64_t(ws_bytes), in.workspace_bytes));
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (h_staging && int64_t(staging_bytes) < in.staging_bytes)
+    return fail(PKV_ERR_WORKSPACE, fmt("staging %lld bytes < %lld needed", int64_t(staging_bytes), in.staging_bytes));
+  char* ws = static_cast<char*>(d_workspace);
+  const int64_t items_bytes = align256(int64_t(r.items.size()) * sizeof(Item));
+  const int64_t rp_bytes = align256(int64_t(r.row_ptr.size()) * 4);
+  const int64_t lse_bytes = align256(int64_t(in.num_partial_rows) * params->num_qo_heads * 4);
+  pkv_cascade_plan* plan = new pkv_cascade_plan;
+  plan->params = *params;
+  plan->info = in;
+  plan->level_info = r.level_info;
+  plan->level_mode = r.level_mode;
+  plan->level_item_off = r.level_item_off;
+  plan->d_items = reinterpret_cast<Item*>(ws);
+  plan->d_row_ptr = reinterpret_cast<int32_t*>(ws + items_bytes);
+  plan->d_slots = reinterpret_cast<int32_t*>(ws + items_bytes + rp_bytes);
+  plan->d_part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
+  plan->d_part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
+  hipError_t e = hipGetDevice(&plan->device);
+  if (e == hipSuccess && in.staging_bytes > 0)
+    e = upload_staging(h_staging, ws, in.staging_bytes, static_cast<hipStream_t>(stream), [&](char* hs) {
+      std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
+      std::memcpy(hs + items_bytes, r.row_ptr.data(), r.row_ptr.size() * 4);
+      std::memcpy(hs + items_bytes + rp_bytes, r.slots.data(), r.slots.size() * 4);
+    });
+  if (e != hipSuccess) {
+    delete plan;
+    return hip_fail(e, "uploading the cascade plan");
+  }
+  *plan_out = plan;
+  return ok();
+}
+
+pkv_status pkv_cascade_plan_get_info(const pkv_cascade_plan* plan, pkv_cascade_info* info) {
+  if (!plan || !info) return fail(PKV_ERR_INVALID_ARG, "null argument");
+  *info = plan->info;
+  return ok();
+}
+
+pkv_status pkv_cascade_run(const pkv_cascade_plan* plan, const void* q, int64_t q_stride_token,
+                           int64_t q_stride_head, const pkv_cache_desc* cache, const int32_t* d_kv_indices,
+                           void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse,
+                           float sm_scale, void* stream) {
+  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
+  const pkv_plan_params& p = plan->params;
+  pkv::AttnArgs a;
+  pkv_status s = prepare_attn(p, plan->device, plan->info.num_items > 0, q, q_stride_token, q_stride_head, cache,
+                              d_kv_indices, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (s) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  a.part_o = plan->d_part_o;
+  a.part_lse = plan->d_part_lse;
+  for (size_t l = 0; l < plan->level_info.size(); ++l) {
+    const int32_t n = plan->level_info[l].num_items;
+    if (n == 0) continue;
+    a.items = plan->d_items + plan->level_item_off[l];
+    a.num_items = n;
+    s = launch_attn_mode(plan->level_mode[l], p, a, st);
+    if (s) return s;
+  }
+  if (plan->info.total_rows > 0) {
+    pkv::MergeRowsArgs m;
+    m.row_ptr = plan->d_row_ptr;
+    m.slots = plan->d_slots;
+    m.num_rows = plan->info.total_rows;
+    m.num_heads = p.num_qo_heads;
+    m.head_dim = p.head_dim_vo;
+    m.part_o = plan->d_part_o;
+    m.part_lse = plan->d_part_lse;
+    m.o = o;
+    m.o_stride_token = o_stride_token;
+    m.o_stride_head = o_stride_head;
+    m.lse = lse;
+    hipError_t e = pkv::launch_merge_rows(p.kv_dtype, m, st);
+    if (e != hipSuccess) return hip_fail(e, "launching the cascade merge");
+  }
+  return ok();
+}
+
+pkv_status pkv_cascade_plan_destroy(pkv_cascade_plan* plan) {
+  delete plan;
   return ok();
 }
 

@@ -69,6 +69,21 @@ struct MergePartialArgs {
   float* lse;
 };
 
+// Row-indexed merge (cascades): query row r folds the partial rows
+// slots[row_ptr[r] .. row_ptr[r+1]) into o / lse.
+struct MergeRowsArgs {
+  const int32_t* row_ptr;   // [num_rows + 1]
+  const int32_t* slots;
+  int32_t num_rows;
+  int32_t num_heads;
+  int32_t head_dim;
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  int64_t o_stride_token, o_stride_head;
+  float* lse;
+};
+
 struct MlaArgs {
   const Item* items;
   int32_t num_items;
@@ -97,6 +112,7 @@ hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& 
                                bool* supported);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t stream);
+hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t stream);
 hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st,
                          int64_t new_sh, const int32_t* append_indptr, const int32_t* kv_indptr,
                          const int32_t* kv_indices, const int32_t* last_page_len, int32_t batch,

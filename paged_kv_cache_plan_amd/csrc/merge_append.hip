@@ -236,6 +236,64 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   }
 }
 
+// Row-indexed merge (cascades): one wave per (query row, head, 64-dim slice).
+// The row's states are the partial rows listed in slots[row_ptr[r] ..
+// row_ptr[r+1]); they come from different levels and tiles, so no stride
+// relates them.  Lanes take the states 64 at a time: the shift and the
+// weight sum are wave reductions over all of them, then each lane
+// accumulates one dim of the slice, reading each state's partial row and
+// scale from the lane that loaded it.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_rows_kernel(const MergeRowsArgs a, int32_t slices) {
+  const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int32_t hq = a.num_heads, d_all = a.head_dim;
+  if (unit >= int64_t(a.num_rows) * hq * slices) return;   // whole wave
+  const int32_t slice = int32_t(unit % slices);
+  const int64_t rh = unit / slices;
+  const int32_t h = int32_t(rh % hq);
+  const int32_t r = int32_t(rh / hq);
+  const int32_t p0 = a.row_ptr[r];
+  const int32_t n = a.row_ptr[r + 1] - p0;
+  float mx = -INFINITY;
+  for (int32_t c = lane; c < n; c += 64) mx = fmaxf(mx, a.part_lse[int64_t(a.slots[p0 + c]) * hq + h]);
+  mx = wave_max(mx);
+  float zl = 0.f;
+  if (mx != -INFINITY)
+    for (int32_t c = lane; c < n; c += 64) {
+      const float sc = a.part_lse[int64_t(a.slots[p0 + c]) * hq + h];
+      if (sc != -INFINITY) zl += dev::fast_exp2(sc - mx);
+    }
+  const float z = wave_sum(zl);
+  const float inv_z = z > 0.f ? 1.f / z : 0.f;
+  const int32_t d = slice * 64 + lane;
+  const bool own = d < d_all;
+  float acc = 0.f;
+  // All lanes stay active through the shuffles; lanes past the row's last
+  // dim only skip their loads.
+  for (int32_t cb = 0; cb < n && z > 0.f; cb += 64) {
+    const int32_t c = cb + lane;
+    int32_t slot_l = 0;
+    float w_l = 0.f;
+    if (c < n) {
+      slot_l = a.slots[p0 + c];
+      const float sc = a.part_lse[int64_t(slot_l) * hq + h];
+      w_l = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx) * inv_z;
+    }
+    const int32_t m = min(64, n - cb);
+    for (int32_t i = 0; i < m; ++i) {
+      const float w = __shfl(w_l, i);
+      const int32_t sl = __shfl(slot_l, i);
+      if (own && w != 0.f) acc = fmaf(w, a.part_o[(int64_t(sl) * hq + h) * d_all + d], acc);
+    }
+  }
+  if (own) {
+    T* orow = static_cast<T*>(a.o) + int64_t(r) * a.o_stride_token + int64_t(h) * a.o_stride_head;
+    store_f<T>(orow, d, acc);
+  }
+  if (slice == 0 && lane == 0 && a.lse) a.lse[int64_t(r) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+}
+
 // Pairwise merge: one wave per (row, head).  Each wave reads both statistics
 // before any lane writes, so v_out / s_out may alias the inputs.
 template <typename T>
@@ -327,6 +385,18 @@ hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipSt
     else
       hipLaunchKernelGGL((merge_partials_kernel<float, false>), grid, block, 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t st) {
+  if (a.num_rows <= 0 || a.num_heads <= 0 || a.head_dim <= 0) return hipSuccess;
+  const int32_t slices = (a.head_dim + 63) / 64;
+  const int64_t blocks = (int64_t(a.num_rows) * a.num_heads * slices + 3) / 4;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((merge_rows_kernel<uint16_t>), dim3(uint32_t(blocks)), dim3(256), 0, st, a, slices);
+  else
+    hipLaunchKernelGGL((merge_rows_kernel<float>), dim3(uint32_t(blocks)), dim3(256), 0, st, a, slices);
   return hipGetLastError();
 }
 

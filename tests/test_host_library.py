@@ -191,3 +191,110 @@ def test_plan_rejects_bad_inputs():
     with pytest.raises(pkv.PkvError) as e:
         pkv.plan_compute(mla, qo_indptr=None, kv_indptr=[0, 1], kv_indices=None, kv_last_page_len=[5])
     assert e.value.status == _abi.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- cascade --
+
+from oracle import cascade as oc  # noqa: E402
+
+
+def _cascade_params(hq, hkv, page, dtype, causal, num_cus, fixed=0, target=0, tail=0, max_pages=0):
+    return pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=hq, num_kv_heads=hkv, head_dim_qk=128,
+                           page_size=page, causal=causal, dtype=dtype, num_cus=num_cus, fixed_split_pages=fixed,
+                           target_per_cu=target, tail_split=tail, max_num_pages=max_pages)
+
+
+def _compare_cascade(levels, page, hq, hkv, dtype, causal, num_cus, fixed=0, target=0, tail=0):
+    params = _cascade_params(hq, hkv, page, dtype, causal, num_cus, fixed, target, tail)
+    info, lvl, items, row_ptr, slots = pkv.cascade_plan_compute(params, levels)
+    spec = pl.plan_cascade(levels=levels, page_size=page, group=hq // hkv, kv_dtype=dtype, heads_y=hkv,
+                           causal=causal, num_cus=num_cus, fixed_split_pages=fixed, target_per_cu=target,
+                           tail_split=tail)
+    assert items.tolist() == spec["items"]
+    assert row_ptr.tolist() == spec["row_ptr"]
+    assert slots.tolist() == spec["slots"]
+    assert info["num_partial_rows"] == spec["num_partial_rows"] == info["num_merge_slots"]
+    assert info["total_rows"] == spec["total_rows"]
+    assert [x["num_items"] for x in lvl] == [x["num_items"] for x in spec["levels"]]
+    assert [x["mode"] for x in lvl] == [{"decode": 0, "prefill": 1}[x["mode"]] for x in spec["levels"]]
+    assert [x["chunk_pages"] for x in lvl] == [x["chunk_pages"] for x in spec["levels"]]
+    return info
+
+
+@pytest.mark.parametrize("name", ["cascade", "cascade_small"])
+def test_cascade_planner_matches_spec_on_workloads(name):
+    b = wl.make(name)
+    for num_cus in (256, 80):
+        info = _compare_cascade(b.extra["levels"], b.page_size, b.num_qo_heads, b.num_kv_heads, b.dtype,
+                                b.causal, num_cus)
+        assert info["num_items"] > 0
+
+
+def test_cascade_planner_matches_spec_randomised():
+    rng = np.random.default_rng(44)
+    for trial in range(60):
+        n_req = int(rng.integers(1, 12))
+        qo_lens = [1] * n_req if trial % 2 else [int(x) for x in rng.integers(0, 40, size=n_req)]
+        rows = list(np.cumsum([0] + qo_lens))
+        page = int(rng.choice([1, 4, 16]))
+        depth = int(rng.integers(1, 4))
+        bounds = [[0, n_req]]
+        for _ in range(depth - 2):
+            bounds.append(sorted(set(bounds[-1] + [int(x) for x in rng.integers(0, n_req + 1, size=2)])))
+        if depth > 1:
+            bounds.append(list(range(n_req + 1)))
+        else:
+            bounds = [list(range(n_req + 1))]
+        levels = []
+        for li, bd in enumerate(bounds):
+            k = [int(rng.integers(1, 3000)) for _ in range(len(bd) - 1)]
+            if li == len(bounds) - 1:
+                k = [max(x, q) for x, q in zip(k, qo_lens)]
+            n = [math.ceil(x / page) for x in k]
+            levels.append({"qo_indptr": np.array([rows[i] for i in bd], np.int32),
+                           "kv_indptr": np.array([0] + list(np.cumsum(n)), np.int32),
+                           "kv_last_page_len": np.array([x - (m - 1) * page for x, m in zip(k, n)], np.int32)})
+        hq, hkv = [(32, 8), (8, 8), (16, 2)][trial % 3]
+        _compare_cascade(levels, page, hq, hkv, "bf16" if trial % 4 else "f32", bool(trial % 3),
+                         int(rng.integers(1, 400)), fixed=int(rng.choice([0, 0, 1, 3])),
+                         target=int(rng.choice([0, 1, 4])), tail=int(rng.choice([0, 1, 2])))
+
+
+def _lv(qo, kv_pages, last, indices=None):
+    indptr = [0]
+    for n in kv_pages:
+        indptr.append(indptr[-1] + n)
+    return {"qo_indptr": qo, "kv_indptr": indptr,
+            "kv_indices": list(range(indptr[-1])) if indices is None else indices, "kv_last_page_len": last}
+
+
+CASCADE_CASES = [
+    [],
+    [_lv([0, 5], [3], [2]), _lv([0, 2, 5], [1, 2], [4, 1]), _lv([0, 1, 2, 4, 5], [1, 1, 1, 1], [1, 2, 2, 3])],
+    [_lv([0, 4], [3], [2]), _lv([0, 1, 2, 4, 5], [1, 1, 1, 1], [1, 2, 2, 3])],
+    [_lv([0, 3, 5], [1, 1], [4, 4]), _lv([0, 2, 5], [1, 2], [4, 4])],
+    [_lv([0, 5], [3], [2]), _lv([0, 2, 5], [1, 1], [1, 2])],
+    [_lv([0, 5], [1], [1]), _lv([0, 2, 5], [1, 1], [2, 3])],
+    [_lv([0, 5], [3], [5]), _lv([0, 5], [2], [4])],
+    [_lv([0, 5], [3], [2], indices=[0, 1, 99]), _lv([0, 5], [2], [4])],
+    [_lv([1, 5], [3], [2]), _lv([0, 5], [2], [4])],
+    [_lv([0, 5], [0], [2]), _lv([0, 5], [2], [4])],
+]
+
+
+@pytest.mark.parametrize("levels", CASCADE_CASES)
+def test_cascade_validation_matches_oracle(levels):
+    try:
+        want = oc.validate_levels(levels, page_size=4, max_num_pages=64)
+        want_reason = None
+    except md.MetadataError as e:
+        want_reason = e.reason
+    params = _cascade_params(1, 1, 4, "f32", True, 8, max_pages=64)
+    if want_reason is None:
+        info = pkv.cascade_plan_compute(params, levels)[0]
+        assert info["num_levels"] == len(levels) and want
+    else:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.cascade_plan_compute(params, levels)
+        assert e.value.status == _abi.ERR_METADATA
+        assert e.value.reason == _abi.META_REASONS[want_reason]

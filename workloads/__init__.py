@@ -31,7 +31,9 @@ described there):
             one node (all requests) with a 16384-token prefix; level 1 eight
             nodes of 8 requests, U[1024, 4096] tokens each; level 2 one leaf
             per request, U[128, 1024] tokens ending with its query row; page
-            16, heads 32/8, dim 128, bfloat16, NHD.  Each level has its own
+            16, heads 32/8, dim 128, bfloat16, NHD.  Shared nodes hold whole
+            pages (lengths rounded up to the page size), so the batch also has
+            a flat one-level page table (``flat_levels``).  Each level has its own
             page table over one shared pool ("FlashInfer 中的 KV-Cache 布局",
             multi-level cascade layout).  ``cascade_small`` is the same tree
             shape at 8 requests (nodes 3/2/3), page 4, heads 4/2, dim 64,
@@ -320,6 +322,8 @@ def _cascade(name, rng, o, scale, poison):
         lens = [int(x) for x in rng.integers(max(1, lo), max(1, hi), size=len(lv), endpoint=True)]
         if li == len(tree) - 1:
             lens = [max(k, q) for k, q in zip(lens, qo_lens)]
+        elif o.get("shared_full_pages", not small):
+            lens = [-(-k // page_size) * page_size for k in lens]
         node_kv.append(lens)
     n_pages = [[math.ceil(k / page_size) for k in lens] for lens in node_kv]
     need = sum(sum(x) for x in n_pages)
@@ -365,3 +369,28 @@ def _cascade(name, rng, o, scale, poison):
                  kv_indices=leaf["kv_indices"], kv_last_page_len=leaf["kv_last_page_len"],
                  max_num_pages=pool, q=q, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new,
                  append_indptr=qo_indptr.copy(), extra={"levels": levels})
+
+
+def flat_levels(b: Batch) -> dict:
+    """One-level page table of a cascade batch whose shared nodes hold whole
+    pages: request r's pages are those of its nodes, level by level."""
+    levels = b.extra["levels"]
+    P = b.page_size
+    for lv in levels[:-1]:
+        if any(k % P for k in lv["kv_lens"]):
+            raise ValueError("a shared node ends inside a page")
+    indptr, indices, lens = [0], [], []
+    for r in range(b.batch_size):
+        row = int(b.qo_indptr[r])
+        total = 0
+        for lv in levels:
+            qo = lv["qo_indptr"]
+            n = int(np.searchsorted(qo, row, side="right")) - 1
+            while qo[n + 1] == qo[n]:      # skip empty nodes that share the boundary
+                n += 1
+            indices.extend(int(x) for x in lv["kv_indices"][lv["kv_indptr"][n]:lv["kv_indptr"][n + 1]])
+            total += lv["kv_lens"][n]
+        indptr.append(len(indices))
+        lens.append(total)
+    return {"kv_indptr": np.asarray(indptr, np.int32), "kv_indices": np.asarray(indices, np.int32),
+            "kv_last_page_len": levels[-1]["kv_last_page_len"].copy(), "kv_lens": lens}
