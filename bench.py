@@ -185,7 +185,7 @@ class CascadeRunner(Runner):
     """A cascade batch: per layer, append the new rows into the leaves, then
     pkv_cascade_run (one attention launch per level + the row merge)."""
 
-    def __init__(self, b, layers: int):
+    def __init__(self, b, layers: int, target_per_cu: int = 0):
         import torch
         import paged_kv_cache_plan_amd as pkv
         self.b, self.torch, self.pkv = b, torch, pkv
@@ -207,7 +207,8 @@ class CascadeRunner(Runner):
         self.last_d = dev(b.kv_last_page_len, False)
         self.params = pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=b.num_qo_heads,
                                       num_kv_heads=b.num_kv_heads, head_dim_qk=b.head_dim, page_size=b.page_size,
-                                      causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages)
+                                      causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages,
+                                      target_per_cu=target_per_cu)
         info = pkv.cascade_plan_compute(self.params, self.levels)[0]
         self.workspace = torch.empty(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
         self.staging = torch.empty(max(info["staging_bytes"], 256), dtype=torch.uint8, pin_memory=True)
@@ -363,6 +364,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla", "cascade"], default=None,
                     help="time one workload (profiling runs)")
+    ap.add_argument("--cascade-target", type=int, default=0,
+                    help="planner target items per CU for every cascade level (0: the per-mode default)")
+    ap.add_argument("--no-flat", action="store_true", help="skip the flat-page-table comparison run")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
@@ -452,21 +456,23 @@ def main():
     if "cascade" in which:
         b = wl.make("cascade")
         layers = args.secondary_layers
-        r = CascadeRunner(b, layers)
+        r = CascadeRunner(b, layers, args.cascade_target)
         m = measure(r, layers, args.steps, args.warmup)
         nb = cascade_bytes(b)
         del r
-        # The same batch through a flat page table (each request reads its whole path).
-        fl = wl.flat_levels(b)
-        bf = wl.Batch(**{**b.__dict__, "mode": "decode", "kv_indptr": fl["kv_indptr"], "kv_indices": fl["kv_indices"],
-                         "kv_last_page_len": fl["kv_last_page_len"], "kv_lens": fl["kv_lens"], "extra": {}})
-        rf = Runner(bf, layers, time_merge=True)
-        mf = measure(rf, layers, max(2, args.steps // 4), 1)
-        del rf
-        result["cascade"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
-                                 flat_us=mf["attn_ms_mean"] * 1e3)
+        flat_us = float("nan")
+        if not args.no_flat:
+            # The same batch through a flat page table (each request reads its whole path).
+            fl = wl.flat_levels(b)
+            bf = wl.Batch(**{**b.__dict__, "mode": "decode", "kv_indptr": fl["kv_indptr"],
+                             "kv_indices": fl["kv_indices"], "kv_last_page_len": fl["kv_last_page_len"],
+                             "kv_lens": fl["kv_lens"], "extra": {}})
+            rf = Runner(bf, layers, time_merge=True)
+            flat_us = measure(rf, layers, max(2, args.steps // 4), 1)["attn_ms_mean"] * 1e3
+            del rf
+        result["cascade"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9, flat_us=flat_us)
         log(f"cascade: run {m['attn_ms_mean'] * 1e3:.1f} us ({result['cascade']['gbs']:.1f} GB/s unique), "
-            f"flat decode {mf['attn_ms_mean'] * 1e3:.1f} us")
+            f"flat decode {flat_us:.1f} us")
 
     if args.only and args.only != "decode":
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk != "plan_info"} for k, v in result.items()}))

@@ -356,7 +356,9 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
  * Schedule (ours): each level is planned like pkv_plan_create -- as decode
  * when every node has one row, else as prefill, so a node shared by many
  * rows runs the MFMA tile kernel and its keys are read once for all of them
- * -- except that every tile writes fp32 partial states.  A row-indexed merge
+ * -- except that every tile writes fp32 partial states and that, unless
+ * params->target_per_cu is set, every level targets one item per CU (each
+ * level is a launch of its own).  A row-indexed merge
  * then folds, per query row, the partial states of all its levels and
  * chunks.  pkv_cascade_run enqueues one attention launch per level and one
  * merge.

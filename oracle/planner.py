@@ -37,6 +37,7 @@ MIN_SPLIT_TOKENS = 256          # a chunk holds at least this many tokens
 MAX_CHUNK_PAGES = 1024          # and at most this many pages (a kernel stages a chunk's page ids on chip)
 DEFAULT_TARGET_PER_CU = {DECODE: 3, PREFILL: 4, MLA: 1}
 DEFAULT_TAIL_SPLIT = {DECODE: 2, PREFILL: 1, MLA: 1}
+CASCADE_TARGET_PER_CU = 1       # cascade levels run one launch each: one item per CU by default
 MFMA_TILE_ROWS = 256            # prefill tile height counted in (row, head) pairs
 
 
@@ -168,6 +169,9 @@ def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: 
        the last level is causal.
     2. Each level is planned by ``plan`` with ``all_partial``: every tile's
        states go to partial rows, numbered on from the previous level's.
+       Unless ``target_per_cu`` is given, every level targets one item per
+       CU (a level is one launch of its own; larger chunks also mean fewer
+       partial states to merge).
     3. A level's page_base is offset by the page ids of all earlier levels
        (kv_indptr[-1] of each): the device array holds the levels' page
        lists back to back, level 0 first.
@@ -190,7 +194,8 @@ def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: 
         p = plan(mode=mode, qo_indptr=None if mode == DECODE else qo, kv_indptr=[int(x) for x in lv["kv_indptr"]],
                  kv_last_page_len=[int(x) for x in lv["kv_last_page_len"]], page_size=page_size, heads_y=heads_y,
                  rows=rows, causal=causal and li == len(levels) - 1, num_cus=num_cus,
-                 fixed_split_pages=fixed_split_pages, target_per_cu=target_per_cu, tail_split=tail_split,
+                 fixed_split_pages=fixed_split_pages,
+                 target_per_cu=target_per_cu if target_per_cu > 0 else CASCADE_TARGET_PER_CU, tail_split=tail_split,
                  all_partial=True)
         for it in p["items"]:
             it = list(it)

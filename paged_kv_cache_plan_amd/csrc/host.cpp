@@ -145,6 +145,7 @@ int32_t default_target(int32_t mode) {
 }
 int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 1; }
 constexpr int32_t kMlaHeadsPerGroup = 64;   // the MLA kernel's head-group width
+constexpr int32_t kCascadeTargetPerCu = 1;
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype) {
   if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32) return 1;
@@ -421,6 +422,9 @@ pkv_status cascade_impl(const pkv_plan_params* prm, int32_t num_levels, const pk
     p.mode = one_row ? PKV_MODE_DECODE : PKV_MODE_PREFILL;
     p.batch_size = L.num_nodes;
     p.causal = (prm->causal && l == num_levels - 1) ? 1 : 0;
+    // A level is one launch of its own: by default one item per CU (larger
+    // chunks also leave fewer partial states to merge).
+    if (p.target_per_cu <= 0) p.target_per_cu = kCascadeTargetPerCu;
     PlanResult r;
     s = plan_impl(&p, one_row ? nullptr : L.qo_indptr, L.kv_indptr, L.kv_indices, L.num_indices,
                   L.kv_last_page_len, &r, true, l == num_levels - 1);

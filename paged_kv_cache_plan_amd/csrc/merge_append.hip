@@ -13,6 +13,8 @@
 
 #include <algorithm>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -236,15 +238,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   }
 }
 
-// Row-indexed merge (cascades): one wave per (query row, head, 64-dim slice).
-// The row's states are the partial rows listed in slots[row_ptr[r] ..
-// row_ptr[r+1]); they come from different levels and tiles, so no stride
-// relates them.  Lanes take the states 64 at a time: the shift and the
-// weight sum are wave reductions over all of them, then each lane
-// accumulates one dim of the slice, reading each state's partial row and
-// scale from the lane that loaded it.
-template <typename T>
+// Row-indexed merge (cascades): one wave per (query row, head, slice of
+// 64 * VW dims; lane l owns VW consecutive dims).  The row's states are the
+// partial rows listed in slots[row_ptr[r] .. row_ptr[r+1]); they come from
+// different levels and tiles, so no stride relates them.  Lanes take the
+// states 64 at a time: the shift and the weight sum are wave reductions over
+// all of them; then every lane accumulates its dims over the states, reading
+// each state's partial row and normalised scale from the lane that loaded it,
+// four states per step so that four loads are in flight.  Every listed
+// partial row was written by the attention launches (empty ones as (0, -inf)),
+// so a zero-weight state is read and multiplied by 0 rather than skipped.
+template <typename T, int VW>
 __global__ __launch_bounds__(256) void merge_rows_kernel(const MergeRowsArgs a, int32_t slices) {
+  using V = typename std::conditional<VW == 2, float2, float>::type;
   const int64_t unit = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int32_t hq = a.num_heads, d_all = a.head_dim;
@@ -266,30 +272,48 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const MergeRowsArgs a, 
     }
   const float z = wave_sum(zl);
   const float inv_z = z > 0.f ? 1.f / z : 0.f;
-  const int32_t d = slice * 64 + lane;
+  const int32_t d = (slice * 64 + lane) * VW;
   const bool own = d < d_all;
-  float acc = 0.f;
-  // All lanes stay active through the shuffles; lanes past the row's last
-  // dim only skip their loads.
+  const int32_t dd = own ? d : 0;   // lanes past the row's dims read dim 0 and store nothing
+  float acc[VW];
+#pragma unroll
+  for (int v = 0; v < VW; ++v) acc[v] = 0.f;
+  const float* po = a.part_o + int64_t(h) * d_all + dd;
+  const int64_t row_stride = int64_t(hq) * d_all;
   for (int32_t cb = 0; cb < n && z > 0.f; cb += 64) {
     const int32_t c = cb + lane;
-    int32_t slot_l = 0;
+    int32_t slot_l = a.slots[p0 + min(c, n - 1)];
     float w_l = 0.f;
     if (c < n) {
-      slot_l = a.slots[p0 + c];
       const float sc = a.part_lse[int64_t(slot_l) * hq + h];
       w_l = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx) * inv_z;
     }
     const int32_t m = min(64, n - cb);
-    for (int32_t i = 0; i < m; ++i) {
-      const float w = __shfl(w_l, i);
-      const int32_t sl = __shfl(slot_l, i);
-      if (own && w != 0.f) acc = fmaf(w, a.part_o[(int64_t(sl) * hq + h) * d_all + d], acc);
+    for (int32_t i = 0; i < m; i += 4) {
+      V x[4];
+      float w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int src = min(i + j, m - 1);   // past the batch: the last state again, weight 0
+        w[j] = i + j < m ? __shfl(w_l, src) : 0.f;
+        const int32_t sl = __shfl(slot_l, src);
+        x[j] = *reinterpret_cast<const V*>(po + int64_t(sl) * row_stride);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (VW == 2) {
+          acc[0] = fmaf(w[j], x[j].x, acc[0]);
+          acc[1] = fmaf(w[j], x[j].y, acc[1]);
+        } else {
+          acc[0] = fmaf(w[j], x[j], acc[0]);
+        }
+      }
     }
   }
   if (own) {
     T* orow = static_cast<T*>(a.o) + int64_t(r) * a.o_stride_token + int64_t(h) * a.o_stride_head;
-    store_f<T>(orow, d, acc);
+#pragma unroll
+    for (int v = 0; v < VW; ++v) store_f<T>(orow, d + v, acc[v]);
   }
   if (slice == 0 && lane == 0 && a.lse) a.lse[int64_t(r) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
 }
@@ -390,13 +414,22 @@ hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipSt
 
 hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t st) {
   if (a.num_rows <= 0 || a.num_heads <= 0 || a.head_dim <= 0) return hipSuccess;
-  const int32_t slices = (a.head_dim + 63) / 64;
+  const bool pair = a.head_dim % 128 == 0;   // two dims per lane (8-byte loads)
+  const int32_t slices = pair ? a.head_dim / 128 : (a.head_dim + 63) / 64;
   const int64_t blocks = (int64_t(a.num_rows) * a.num_heads * slices + 3) / 4;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL((merge_rows_kernel<uint16_t>), dim3(uint32_t(blocks)), dim3(256), 0, st, a, slices);
-  else
-    hipLaunchKernelGGL((merge_rows_kernel<float>), dim3(uint32_t(blocks)), dim3(256), 0, st, a, slices);
+  const dim3 grid{static_cast<uint32_t>(blocks)}, block{256};
+  if (dtype == kBF16) {
+    if (pair)
+      hipLaunchKernelGGL((merge_rows_kernel<uint16_t, 2>), grid, block, 0, st, a, slices);
+    else
+      hipLaunchKernelGGL((merge_rows_kernel<uint16_t, 1>), grid, block, 0, st, a, slices);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((merge_rows_kernel<float, 2>), grid, block, 0, st, a, slices);
+    else
+      hipLaunchKernelGGL((merge_rows_kernel<float, 1>), grid, block, 0, st, a, slices);
+  }
   return hipGetLastError();
 }
 
