@@ -278,6 +278,70 @@ pkv_status pkv_plan_check(const pkv_plan* plan, const int32_t* qo_indptr,
 
 pkv_status pkv_plan_destroy(pkv_plan* plan);
 
+/* ------------------------------------------------ fixed-capacity plans -- */
+
+/*
+ * Plans for captured runs ([DD] "Plan then run": plan does host work and
+ * device copies, so it cannot be captured; compatible run calls can, and
+ * graph-mode plans reserve their metadata buffers, fix the batch size and
+ * bound the total query rows and page-index capacity -- stable addresses do
+ * not make stale contents correct).
+ *
+ * pkv_graph_plan_create reserves, inside the caller's workspace, a work list,
+ * a merge list and partial-state buffers of fixed capacity, plus two device
+ * counters (zero until the first update).  pkv_plan_update -- host work plus
+ * one asynchronous copy on `stream`, not capturable -- plans a batch of
+ * exactly params->batch_size requests with the ordinary planner and writes
+ * its lists and counts to those fixed addresses.  Runs on such a plan
+ * (pkv_run, pkv_run_attention, pkv_run_merge, pkv_run_mla) launch grids sized
+ * by the capacities; workgroups past the live counts exit at once.  Launch
+ * shapes and pointers are therefore the same after every update, so a run
+ * captured once replays correctly for every later batch within the
+ * capacities, as long as the caller keeps q, the caches, kv_indices, o and
+ * lse at fixed addresses and refreshes their contents.  The update's copy is
+ * ordered on `stream`: runs of the previous batch must be ordered before it.
+ *
+ * Derived capacities (used for a field left 0).  With R the plan's rows per
+ * tile, tiles = B (decode, MLA) or ceil(max_total_rows / R) + B (prefill),
+ * S the tail split, T = target_per_cu * num_cus, hy the kv heads or MLA head
+ * groups and N = max_total_pages:
+ *   max_items        = tiles*S + (fixed_split_pages > 0 ? ceil(tiles*N / fixed_split_pages)
+ *                                                       : ceil(T / hy) + ceil(tiles*N / 1024))
+ *   max_merges       = tiles
+ *   max_partial_rows = max_items * R
+ * These bound every plan the planner can make within max_total_rows and N.
+ */
+typedef struct pkv_graph_caps {
+  int32_t max_total_rows;    /* prefill: bound on qo_indptr[B]; decode and MLA: ignored (B rows) */
+  int32_t max_total_pages;   /* bound on kv_indptr[B] */
+  int32_t max_items;         /* 0: derived */
+  int32_t max_merges;        /* 0: derived */
+  int32_t max_partial_rows;  /* 0: derived */
+  int32_t reserved;
+} pkv_graph_caps;
+
+/* Resolve the capacities (caps_out, derived fields filled in) and the
+ * workspace / pinned staging sizes of a fixed-capacity plan.  Host only
+ * (queries the device only if params->num_cus == 0). */
+pkv_status pkv_graph_plan_size(const pkv_plan_params* params, const pkv_graph_caps* caps,
+                               pkv_graph_caps* caps_out, int64_t* workspace_bytes, int64_t* staging_bytes);
+
+/* Create a fixed-capacity plan.  d_workspace (256-byte aligned) and the
+ * pinned h_staging (required) must hold the sizes pkv_graph_plan_size
+ * reports and stay owned by this plan until pkv_plan_destroy.  Zeroes the
+ * counters with one asynchronous copy on `stream`. */
+pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_caps* caps, void* d_workspace,
+                                 size_t ws_bytes, void* h_staging, size_t staging_bytes, void* stream,
+                                 pkv_plan** plan_out);
+
+/* Plan a new batch into a fixed-capacity plan (host arrays as for
+ * pkv_plan_create).  PKV_ERR_INVALID_ARG for an ordinary plan; the metadata
+ * errors of pkv_plan_create; PKV_ERR_WORKSPACE if the batch exceeds a
+ * capacity (the plan then keeps its previous batch). */
+pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, int64_t num_indices, const int32_t* kv_last_page_len,
+                           void* stream);
+
 /* ------------------------------------------------------------------- run -- */
 
 /*

@@ -18,7 +18,7 @@ import os
 import numpy as np
 
 from ._abi import (BF16, DECODE, F32, HND, MLA_DECODE, NHD, PREFILL, STATUS_NAMES, CacheDesc, CascadeInfo,
-                   CascadeLevel, PlanInfo, PlanParams, load_library)
+                   CascadeLevel, GraphCaps, PlanInfo, PlanParams, load_library)
 
 _lib = None
 
@@ -73,6 +73,13 @@ def _host_i32(x, name):
         raise TypeError(f"{name} must be int32, got {getattr(x, 'dtype', type(x))}")
     x = np.ascontiguousarray(x)
     return x, x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _check_batch(params, qo, kvp, last):
+    """The C ABI reads B+1 / B entries (B = params.batch_size) from these host arrays."""
+    b = params.batch_size
+    if last is None or kvp is None or len(last) != b or len(kvp) != b + 1 or (qo is not None and len(qo) != b + 1):
+        raise ValueError(f"metadata lengths do not match batch_size {b}")
 
 
 def _dev(t, name, dtype=None):
@@ -224,6 +231,7 @@ class Plan:
                                                     (kv_indices, "kv_indices"),
                                                     (kv_last_page_len, "kv_last_page_len"))]
         (qo, qo_p), (kvp, kvp_p), (idx, idx_p), (last, last_p) = self._meta
+        _check_batch(params, qo, kvp, last)
         n_idx = 0 if idx is None else len(idx)
         info = PlanInfo()
         _check(lib().pkv_plan_compute(ctypes.byref(params), qo_p, kvp_p, idx_p, n_idx, last_p, None, 0, None, 0,
@@ -301,6 +309,54 @@ class Plan:
         if h and _lib is not None:
             _lib.pkv_plan_destroy(h)
             self._handle = None
+
+
+# --------------------------------------------------- fixed-capacity plans --
+
+def graph_caps(*, max_total_rows=0, max_total_pages, max_items=0, max_merges=0, max_partial_rows=0) -> GraphCaps:
+    c = GraphCaps()
+    c.max_total_rows, c.max_total_pages = max_total_rows, max_total_pages
+    c.max_items, c.max_merges, c.max_partial_rows = max_items, max_merges, max_partial_rows
+    return c
+
+
+def graph_plan_size(params: PlanParams, caps: GraphCaps):
+    """pkv_graph_plan_size: (resolved capacities dict, workspace bytes, staging bytes)."""
+    out = GraphCaps()
+    ws, st = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().pkv_graph_plan_size(ctypes.byref(params), ctypes.byref(caps), ctypes.byref(out), ctypes.byref(ws),
+                                     ctypes.byref(st)))
+    return out.as_dict(), ws.value, st.value
+
+
+class GraphPlan(Plan):
+    """pkv_graph_plan_create / pkv_plan_update: a fixed-capacity plan whose
+    runs launch the same grids with the same pointers after every update, so
+    they can be captured once (torch.cuda.graph) and replayed per batch."""
+
+    def __init__(self, params: PlanParams, caps: GraphCaps, *, stream=None):
+        import torch
+        self.params = params
+        self.caps, ws_bytes, st_bytes = graph_plan_size(params, caps)
+        self.workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        self.staging = torch.empty(max(st_bytes, 256), dtype=torch.uint8, pin_memory=True)
+        self._meta = []
+        handle = ctypes.c_void_p()
+        _check(lib().pkv_graph_plan_create(ctypes.byref(params), ctypes.byref(caps),
+                                           ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                           ctypes.c_void_p(self.staging.data_ptr()), self.staging.numel(),
+                                           _stream(stream), ctypes.byref(handle)))
+        self._handle = handle
+
+    def update(self, *, kv_indptr, kv_last_page_len, kv_indices=None, qo_indptr=None, stream=None):
+        """pkv_plan_update (host work + one asynchronous copy; not capturable)."""
+        self._meta = [_host_i32(x, n) for x, n in ((qo_indptr, "qo_indptr"), (kv_indptr, "kv_indptr"),
+                                                    (kv_indices, "kv_indices"),
+                                                    (kv_last_page_len, "kv_last_page_len"))]
+        (qo, qo_p), (kvp, kvp_p), (idx, idx_p), (last, last_p) = self._meta
+        _check_batch(self.params, qo, kvp, last)
+        _check(lib().pkv_plan_update(self._handle, qo_p, kvp_p, idx_p, 0 if idx is None else len(idx), last_p,
+                                     _stream(stream)))
 
 
 # ---------------------------------------------------------------- cascade --

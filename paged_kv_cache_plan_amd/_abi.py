@@ -47,6 +47,14 @@ class PlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class GraphCaps(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_total_rows", "max_total_pages", "max_items", "max_merges", "max_partial_rows", "reserved")]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
 class CascadeLevel(ctypes.Structure):
     _fields_ = [("num_nodes", ctypes.c_int32), ("qo_indptr", ctypes.POINTER(ctypes.c_int32)),
                 ("kv_indptr", ctypes.POINTER(ctypes.c_int32)), ("kv_indices", ctypes.POINTER(ctypes.c_int32)),
@@ -84,6 +92,11 @@ SIGNATURES = {
     "pkv_plan_get_info": (_i32, [_vp, ctypes.POINTER(PlanInfo)]),
     "pkv_plan_check": (_i32, [_vp, _i32p, _i32p, _i32p, _i64, _i32p]),
     "pkv_plan_destroy": (_i32, [_vp]),
+    "pkv_graph_plan_size": (_i32, [ctypes.POINTER(PlanParams), ctypes.POINTER(GraphCaps), ctypes.POINTER(GraphCaps),
+                                   ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "pkv_graph_plan_create": (_i32, [ctypes.POINTER(PlanParams), ctypes.POINTER(GraphCaps), _vp, ctypes.c_size_t, _vp,
+                                     ctypes.c_size_t, _vp, ctypes.POINTER(_vp)]),
+    "pkv_plan_update": (_i32, [_vp, _i32p, _i32p, _i32p, _i64, _i32p, _vp]),
     "pkv_run": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp, ctypes.c_float,
                        _vp]),
     "pkv_run_attention": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp,

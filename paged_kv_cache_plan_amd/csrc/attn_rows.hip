@@ -152,6 +152,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
   const int32_t kvh = blockIdx.x - item_idx * hkv;
+  if (a.live_items && item_idx >= *a.live_items) return;   // fixed-capacity grid: whole workgroup
   const Item it = a.items[item_idx];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

@@ -519,6 +519,20 @@ struct pkv_plan {
   float* d_part_lse;
   float* d_part_o;
   int device;
+  // Fixed-capacity plans (pkv_graph_plan_create): every run launches grids
+  // sized by the capacities and the kernels read the live counts from
+  // d_counts, so one captured graph serves every later update.
+  bool graph = false;
+  pkv_graph_caps caps{};
+  int32_t* d_counts = nullptr;   // [0] live items, [1] live merge items
+  char* d_ws = nullptr;
+  void* h_staging = nullptr;
+  int64_t staging_bytes = 0;
+
+  int32_t grid_items() const { return graph ? caps.max_items : info.num_items; }
+  int32_t grid_merges() const { return graph ? caps.max_merges : info.num_merges; }
+  const int32_t* live_items() const { return graph ? d_counts : nullptr; }
+  const int32_t* live_merges() const { return graph ? d_counts + 1 : nullptr; }
 };
 
 extern "C" {
@@ -714,6 +728,7 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
     return fail(PKV_ERR_INVALID_ARG, "plan was built on another device");
   a->items = nullptr;
   a->num_items = 0;
+  a->live_items = nullptr;
   a->num_kv_heads = p.num_kv_heads;
   a->num_qo_heads = p.num_qo_heads;
   a->q = q;
@@ -768,12 +783,14 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
   const pkv_plan_params& p = plan->params;
   if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
   pkv::AttnArgs a;
-  pkv_status s = prepare_attn(p, plan->device, plan->info.num_items > 0, q, q_stride_token, q_stride_head, cache,
+  const int32_t grid_items = plan->grid_items();
+  pkv_status s = prepare_attn(p, plan->device, grid_items > 0, q, q_stride_token, q_stride_head, cache,
                               d_kv_indices, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
   if (s) return s;
-  if (plan->info.num_items == 0) return ok();
+  if (grid_items == 0) return ok();
   a.items = plan->d_items;
-  a.num_items = plan->info.num_items;
+  a.num_items = grid_items;
+  a.live_items = plan->live_items();
   a.part_o = plan->d_part_o;
   a.part_lse = plan->d_part_lse;
   s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream));
@@ -784,7 +801,7 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
 pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, int64_t o_stride_head,
                          float* lse, void* stream) {
   if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
-  if (plan->info.num_merges == 0) return ok();
+  if (plan->grid_merges() == 0) return ok();
   const pkv_plan_params& p = plan->params;
   const size_t es = dtype_size(p.kv_dtype);
   pkv_status s = check_ptr16(o, "o");
@@ -793,7 +810,8 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, 
     return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
   pkv::MergePartialArgs m;
   m.merges = plan->d_merges;
-  m.num_merges = plan->info.num_merges;
+  m.num_merges = plan->grid_merges();
+  m.live_merges = plan->live_merges();
   m.max_rows = plan->info.rows_per_tile;
   m.num_heads = p.num_qo_heads;
   m.head_dim = p.head_dim_vo;
@@ -831,14 +849,15 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
     return s;
   if (!stride_ok(page_stride, 2) || !stride_ok(token_stride, 2))
     return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
-  if (!d_kv_indices && plan->info.num_items > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
+  if (!d_kv_indices && plan->grid_items() > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
     return fail(PKV_ERR_INVALID_ARG, "plan was built on another device");
-  if (plan->info.num_items == 0) return ok();
+  if (plan->grid_items() == 0) return ok();
   pkv::MlaArgs a;
   a.items = plan->d_items;
-  a.num_items = plan->info.num_items;
+  a.num_items = plan->grid_items();
+  a.live_items = plan->live_items();
   a.num_heads = p.num_qo_heads;
   a.head_groups = plan->info.heads_y;
   a.q_ckv = q_ckv;
@@ -860,10 +879,11 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = pkv::launch_mla_decode(a, st);
   if (e != hipSuccess) return hip_fail(e, "launching MLA decode");
-  if (plan->info.num_merges > 0) {
+  if (plan->grid_merges() > 0) {
     pkv::MergePartialArgs m;
     m.merges = plan->d_merges;
-    m.num_merges = plan->info.num_merges;
+    m.num_merges = plan->grid_merges();
+    m.live_merges = plan->live_merges();
     m.max_rows = plan->info.rows_per_tile;
     m.num_heads = p.num_qo_heads;
     m.head_dim = 512;
@@ -938,6 +958,168 @@ pkv_status pkv_merge_states(const void* v, const float* s, void* v_out, float* s
   hipError_t e = pkv::launch_merge_many(dtype, v, s, v_out, s_out, num_rows, num_states, num_heads, head_dim,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching merge_states");
+  return ok();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- fixed-capacity plans --
+
+namespace {
+
+struct GraphLayout {
+  pkv_graph_caps caps;
+  int32_t rows_per_tile;
+  int64_t items_off, merges_off, staging_bytes, lse_off, o_off, workspace_bytes;
+};
+
+pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, GraphLayout* g) {
+  pkv_status s = check_params(prm);
+  if (s) return s;
+  if (!in) return fail(PKV_ERR_INVALID_ARG, "null capacities");
+  if (prm->batch_size < 0) return meta_fail(PKV_META_BATCH_SIZE, "negative batch size");
+  if (prm->page_size < 1) return meta_fail(PKV_META_PAGE_SIZE, "page_size < 1");
+  if (prm->num_qo_heads < 1 || prm->num_kv_heads < 1 || prm->num_qo_heads % prm->num_kv_heads != 0)
+    return meta_fail(PKV_META_HEAD_GROUP, "qo heads do not group over kv heads");
+  if (in->max_total_pages < 0 || in->max_total_rows < 0 || in->max_items < 0 || in->max_merges < 0 ||
+      in->max_partial_rows < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative capacity");
+  const bool prefill = prm->mode == PKV_MODE_PREFILL;
+  const bool mla = prm->mode == PKV_MODE_MLA_DECODE;
+  const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
+  const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype);
+  int64_t hy = prm->num_kv_heads;
+  if (mla) {
+    hy = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
+    if (hy < 1 || prm->num_qo_heads != hy * kMlaHeadsPerGroup)
+      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 heads");
+  }
+  int32_t num_cus = prm->num_cus;
+  if (num_cus <= 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
+  }
+  const int64_t B = prm->batch_size;
+  const int64_t tiles = prefill ? cdiv(in->max_total_rows, R) + B : B;
+  const int64_t S = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);
+  const int64_t T = int64_t(prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode)) * num_cus;
+  const int64_t N = in->max_total_pages;
+  const int64_t items = tiles * S + (prm->fixed_split_pages > 0 ? cdiv(tiles * N, prm->fixed_split_pages)
+                                                               : cdiv(T, hy) + cdiv(tiles * N, kMaxChunkPages));
+  pkv_graph_caps c = *in;
+  if (c.max_items == 0) c.max_items = int32_t(std::min<int64_t>(items, INT32_MAX));
+  if (c.max_merges == 0) c.max_merges = int32_t(std::min<int64_t>(tiles, INT32_MAX));
+  if (c.max_partial_rows == 0) c.max_partial_rows = int32_t(std::min<int64_t>(int64_t(c.max_items) * R, INT32_MAX));
+  c.reserved = 0;
+  g->caps = c;
+  g->rows_per_tile = int32_t(R);
+  g->items_off = 256;   // the two counters
+  g->merges_off = g->items_off + align256(int64_t(c.max_items) * sizeof(Item));
+  g->staging_bytes = g->merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
+  g->lse_off = g->staging_bytes;
+  g->o_off = g->lse_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * 4);
+  g->workspace_bytes = g->o_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * prm->head_dim_vo * 4);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_graph_plan_size(const pkv_plan_params* params, const pkv_graph_caps* caps,
+                               pkv_graph_caps* caps_out, int64_t* workspace_bytes, int64_t* staging_bytes) {
+  GraphLayout g;
+  pkv_status s = graph_layout(params, caps, &g);
+  if (s) return s;
+  if (caps_out) *caps_out = g.caps;
+  if (workspace_bytes) *workspace_bytes = g.workspace_bytes;
+  if (staging_bytes) *staging_bytes = g.staging_bytes;
+  return ok();
+}
+
+pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_caps* caps, void* d_workspace,
+                                 size_t ws_bytes, void* h_staging, size_t staging_bytes, void* stream,
+                                 pkv_plan** plan_out) {
+  if (!plan_out) return fail(PKV_ERR_INVALID_ARG, "null plan_out");
+  *plan_out = nullptr;
+  GraphLayout g;
+  pkv_status s = graph_layout(params, caps, &g);
+  if (s) return s;
+  if (!d_workspace || int64_t(ws_bytes) < g.workspace_bytes)
+    return fail(PKV_ERR_WORKSPACE, fmt("workspace %lld bytes < %lld needed", int64_t(ws_bytes), g.workspace_bytes));
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (!h_staging) return fail(PKV_ERR_INVALID_ARG, "a fixed-capacity plan needs a pinned staging buffer");
+  if (int64_t(staging_bytes) < g.staging_bytes)
+    return fail(PKV_ERR_WORKSPACE, fmt("staging %lld bytes < %lld needed", int64_t(staging_bytes), g.staging_bytes));
+  char* ws = static_cast<char*>(d_workspace);
+  pkv_plan* plan = new pkv_plan;
+  plan->params = *params;
+  std::memset(&plan->info, 0, sizeof plan->info);
+  plan->info.mode = params->mode;
+  plan->info.batch_size = params->batch_size;
+  plan->info.rows_per_tile = g.rows_per_tile;
+  plan->info.workspace_bytes = g.workspace_bytes;
+  plan->info.staging_bytes = g.staging_bytes;
+  plan->graph = true;
+  plan->caps = g.caps;
+  plan->d_ws = ws;
+  plan->d_counts = reinterpret_cast<int32_t*>(ws);
+  plan->d_items = reinterpret_cast<Item*>(ws + g.items_off);
+  plan->d_merges = reinterpret_cast<MergeItem*>(ws + g.merges_off);
+  plan->d_part_lse = reinterpret_cast<float*>(ws + g.lse_off);
+  plan->d_part_o = reinterpret_cast<float*>(ws + g.o_off);
+  plan->h_staging = h_staging;
+  plan->staging_bytes = g.staging_bytes;
+  hipError_t e = hipGetDevice(&plan->device);
+  if (e == hipSuccess)   // counters (and lists) start at zero: a run before the first update does nothing
+    e = upload_staging(h_staging, ws, 256, static_cast<hipStream_t>(stream), [](char*) {});
+  if (e != hipSuccess) {
+    delete plan;
+    return hip_fail(e, "initialising the fixed-capacity plan");
+  }
+  *plan_out = plan;
+  return ok();
+}
+
+pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, int64_t num_indices, const int32_t* kv_last_page_len,
+                           void* stream) {
+  if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
+  if (!plan->graph) return fail(PKV_ERR_INVALID_ARG, "pkv_plan_update needs a fixed-capacity plan");
+  PlanResult r;
+  pkv_status s = plan_impl(&plan->params, qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len, &r);
+  if (s) return s;
+  const pkv_graph_caps& c = plan->caps;
+  const int32_t B = plan->params.batch_size;
+  if (plan->params.mode == PKV_MODE_PREFILL && r.info.total_rows > c.max_total_rows)
+    return fail(PKV_ERR_WORKSPACE, fmt("%lld query rows > capacity %lld", r.info.total_rows, c.max_total_rows));
+  if (kv_indptr[B] > c.max_total_pages)
+    return fail(PKV_ERR_WORKSPACE, fmt("%lld pages > capacity %lld", kv_indptr[B], c.max_total_pages));
+  if (r.info.num_items > c.max_items || r.info.num_merges > c.max_merges ||
+      r.info.num_partial_rows > c.max_partial_rows)
+    return fail(PKV_ERR_WORKSPACE, fmt("plan needs %lld items / %lld merges / %lld partial rows", r.info.num_items,
+                                       r.info.num_merges, r.info.num_partial_rows) +
+                                       fmt(" (capacity %lld / %lld / %lld)", c.max_items, c.max_merges,
+                                           c.max_partial_rows));
+  const int64_t items_off = 256;
+  const int64_t merges_off = items_off + align256(int64_t(c.max_items) * sizeof(Item));
+  const int64_t upload = merges_off + int64_t(r.merges.size()) * sizeof(MergeItem);
+  hipError_t e = upload_staging(plan->h_staging, plan->d_ws, upload, static_cast<hipStream_t>(stream),
+                                [&](char* hs) {
+                                  int32_t* counts = reinterpret_cast<int32_t*>(hs);
+                                  counts[0] = r.info.num_items;
+                                  counts[1] = r.info.num_merges;
+                                  std::memcpy(hs + items_off, r.items.data(), r.items.size() * sizeof(Item));
+                                  std::memcpy(hs + merges_off, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+                                });
+  if (e != hipSuccess) return hip_fail(e, "uploading the plan");
+  const int64_t ws_bytes = plan->info.workspace_bytes, st_bytes = plan->info.staging_bytes;
+  plan->info = r.info;
+  plan->info.workspace_bytes = ws_bytes;
+  plan->info.staging_bytes = st_bytes;
   return ok();
 }
 

@@ -36,7 +36,8 @@ enum DType : int32_t { kF32 = 0, kBF16 = 1 };
 
 struct AttnArgs {
   const Item* items;
-  int32_t num_items;
+  int32_t num_items;       // items the grid covers
+  const int32_t* live_items;  // null, or a device count: items at or past it exit at once
   int32_t num_kv_heads;
   int32_t num_qo_heads;
   const void* q;
@@ -58,7 +59,8 @@ struct AttnArgs {
 
 struct MergePartialArgs {
   const MergeItem* merges;
-  int32_t num_merges;
+  int32_t num_merges;      // merge items the grid covers
+  const int32_t* live_merges;  // null, or a device count: merge items at or past it exit at once
   int32_t max_rows;    // largest num_rows over the merge items
   int32_t num_heads;
   int32_t head_dim;
@@ -86,7 +88,8 @@ struct MergeRowsArgs {
 
 struct MlaArgs {
   const Item* items;
-  int32_t num_items;
+  int32_t num_items;       // items the grid covers
+  const int32_t* live_items;  // null, or a device count: items at or past it exit at once
   int32_t num_heads;
   int32_t head_groups;
   const void* q_ckv;   // [B, H, 512]

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   __shared__ float s_w[kMergeSeg];
   __shared__ float s_red[kMergeThreads / 64];
   __shared__ float4 s_acc[kMergeThreads];
+  if (a.live_merges && int32_t(blockIdx.x) >= *a.live_merges) return;   // fixed-capacity grid
   const MergeItem mi = a.merges[blockIdx.x];
   const int32_t h = blockIdx.y;
   const int tid = threadIdx.x;

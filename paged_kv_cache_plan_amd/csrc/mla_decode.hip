@@ -113,6 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
   const int32_t item_idx = (k_on_xcd / a.head_groups) * kXcds + xcd;
   const int32_t hgrp = k_on_xcd - (k_on_xcd / a.head_groups) * a.head_groups;
   if (item_idx >= a.num_items) return;
+  if (a.live_items && item_idx >= *a.live_items) return;   // fixed-capacity grid: whole workgroup
   const Item it = a.items[item_idx];
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
   const int32_t kvh = blockIdx.x - item_idx * hkv;
+  if (a.live_items && item_idx >= *a.live_items) return;   // fixed-capacity grid: whole workgroup
   const Item it = a.items[item_idx];
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -298,3 +298,52 @@ def test_cascade_validation_matches_oracle(levels):
             pkv.cascade_plan_compute(params, levels)
         assert e.value.status == _abi.ERR_METADATA
         assert e.value.reason == _abi.META_REASONS[want_reason]
+
+
+# --------------------------------------------------- fixed-capacity plans --
+
+@pytest.mark.parametrize("mode", ["decode", "prefill", "mla"])
+def test_graph_capacities_bound_every_plan(mode):
+    """The derived capacities of a fixed-capacity plan hold every plan the
+    planner spec makes for batches within them (random lengths, fixed split
+    sizes, targets and tail splits)."""
+    rng = np.random.default_rng({"decode": 1, "prefill": 2, "mla": 3}[mode])
+    for trial in range(40):
+        B = int(rng.integers(1, 24))
+        page = int(rng.choice([1, 4, 16, 64]))
+        max_pages = int(rng.integers(B, 40 * B + 1))
+        max_rows = int(rng.integers(B, 300 * B)) if mode == "prefill" else B
+        hq, hkv = (128, 1) if mode == "mla" else [(32, 8), (8, 2), (16, 16)][trial % 3]
+        dtype = "bf16" if (mode == "mla" or trial % 4) else "f32"
+        fixed = int(rng.choice([0, 0, 1, 5]))
+        target, tail = int(rng.choice([0, 1, 3])), int(rng.choice([0, 1, 2, 3]))
+        num_cus = int(rng.integers(1, 300))
+        params = pkv.plan_params(mode=mode, batch_size=B, num_qo_heads=hq, num_kv_heads=hkv,
+                                 head_dim_qk=576 if mode == "mla" else 128, head_dim_vo=512 if mode == "mla" else 128,
+                                 page_size=page, dtype=dtype, num_cus=num_cus, fixed_split_pages=fixed,
+                                 target_per_cu=target, tail_split=tail)
+        caps, ws, st = pkv.graph_plan_size(params, pkv.graph_caps(max_total_rows=max_rows, max_total_pages=max_pages))
+        assert ws >= st > 0
+        for _ in range(5):
+            # a batch at (or near) the capacities
+            n = np.maximum(1, rng.multinomial(max_pages - B, np.ones(B) / B) + 1) if rng.random() < 0.7 else \
+                rng.integers(1, max(2, max_pages // B) + 1, size=B)
+            n = [int(x) for x in n]
+            if sum(n) > max_pages:
+                continue
+            last = [int(rng.integers(1, page + 1)) for _ in range(B)]
+            k = [page * (m - 1) + t for m, t in zip(n, last)]
+            if mode == "prefill":
+                q = [int(x) for x in rng.multinomial(max_rows, np.ones(B) / B)]
+                q = [min(a, b) for a, b in zip(q, k)]
+                qo = list(np.cumsum([0] + q))
+            else:
+                qo = None
+            spec = pl.plan(mode=mode, qo_indptr=qo, kv_indptr=list(np.cumsum([0] + n)), kv_last_page_len=last,
+                           page_size=page, heads_y=hkv if mode != "mla" else 2, rows=pl.rows_per_tile(mode, hq // hkv,
+                                                                                                      dtype),
+                           causal=bool(trial % 2), num_cus=num_cus, fixed_split_pages=fixed, target_per_cu=target,
+                           tail_split=tail)
+            assert len(spec["items"]) <= caps["max_items"], (trial, len(spec["items"]), caps)
+            assert len(spec["merges"]) <= caps["max_merges"]
+            assert spec["num_partial_rows"] <= caps["max_partial_rows"]
