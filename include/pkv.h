@@ -76,6 +76,18 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
  * (page_size, heads, head_dim) for NHD and (heads, page_size, head_dim) for HND. */
 typedef enum { PKV_NHD = 0, PKV_HND = 1 } pkv_layout;
 
+/* Key/value storage ([KVL] "页表布局" and "Ragged Tensor"). */
+typedef enum {
+  PKV_KV_PAGED = 0,   /* CSR page table over a page pool (pkv_run, pkv_run_masked) */
+  PKV_KV_RAGGED = 1   /* request b's keys are data[kv_indptr[b] .. kv_indptr[b+1]) (pkv_run_ragged) */
+} pkv_kv_format;
+
+/* Visibility ([KVL] "掩码布局（2D Ragged Tensor）"). */
+typedef enum {
+  PKV_MASK_NONE = 0,   /* all keys, or the bottom-right causal rule when params.causal */
+  PKV_MASK_CUSTOM = 1  /* a bit-packed per-request mask decides; params.causal must be 0 */
+} pkv_mask_mode;
+
 typedef enum {
   PKV_MODE_DECODE = 0,     /* one query row per request; no qo_indptr ([DD] "Plan then run") */
   PKV_MODE_PREFILL = 1,    /* ragged query rows (chunked prefill / append), optional causal mask */
@@ -211,6 +223,8 @@ typedef struct pkv_plan_params {
   int32_t mla_head_groups;   /* MLA only; 0: default */
   int32_t max_num_pages;     /* pool size, for the page-id range check */
   int32_t tail_split;        /* 0: default (decode 2, prefill 1, MLA 1); 1: off */
+  int32_t kv_format;         /* pkv_kv_format; ragged needs PKV_MODE_PREFILL */
+  int32_t mask_mode;         /* pkv_mask_mode; custom needs PKV_MODE_PREFILL and causal == 0 */
 } pkv_plan_params;
 
 typedef struct pkv_plan_info {
@@ -229,6 +243,7 @@ typedef struct pkv_plan_info {
   int64_t workspace_bytes;   /* device workspace this plan needs */
   int64_t staging_bytes;     /* pinned staging this plan needs */
   uint64_t fingerprint;      /* hash of params + metadata (staleness check) */
+  int64_t mask_bits;         /* custom mask: sum over requests of qo_len * kv_len */
 } pkv_plan_info;
 
 /* Work item / merge item sizes in int32 words (layout documented in the
@@ -498,6 +513,50 @@ pkv_status pkv_cascade_run(const pkv_cascade_plan* plan, const void* q, int64_t 
                            float sm_scale, void* stream);
 
 pkv_status pkv_cascade_plan_destroy(pkv_cascade_plan* plan);
+
+/* ----------------------------------------------- ragged KV, custom masks -- */
+
+/*
+ * Custom-mask run ([KVL] "掩码布局（2D Ragged Tensor）"): as pkv_run, for a
+ * plan made with mask_mode = PKV_MASK_CUSTOM.  Request b's mask is a qo_len x
+ * kv_len boolean matrix, query-major; the matrices of all requests are
+ * concatenated (request b starts at element sum_{c<b} qo_len_c * kv_len_c)
+ * and bit-packed little-endian: element e is bit e % 8 of byte e / 8 (numpy
+ * packbits order, which is what pkv_packbits writes).  Row i of request b
+ * sees key j iff its element is 1; a row that sees no key gets (0, -inf).
+ *   d_mask  device, at least ceil(info.mask_bits / 32) * 4 bytes (read in
+ *           aligned 32-bit words)
+ * Custom-masked plans run one query row per work item on the row kernel.
+ */
+pkv_status pkv_run_masked(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                          const pkv_cache_desc* cache, const int32_t* d_kv_indices, const uint8_t* d_mask,
+                          void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                          void* stream);
+
+/*
+ * Ragged-KV run ([KVL] "Ragged Tensor"): for a plan made with kv_format =
+ * PKV_KV_RAGGED (kv_indptr counts tokens; kv_indices and kv_last_page_len are
+ * not used by the planner and may be NULL).  Key j of request b is row
+ * kv_indptr[b] + j of the data tensors.
+ *   k, v         device, element (token t, kv head h, dim d) at
+ *                k + t*kv_stride_token + h*kv_stride_head + d (NHD: strides
+ *                Hkv*D and D), dtype of the plan
+ *   d_kv_indptr  device int32, B+1 entries, the same values the plan was built on
+ *   d_mask       device bit-packed custom mask (as for pkv_run_masked) for a
+ *                custom-masked plan, else NULL
+ * Other arguments as for pkv_run.
+ */
+pkv_status pkv_run_ragged(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                          const void* k, const void* v, int64_t kv_stride_token, int64_t kv_stride_head,
+                          const int32_t* d_kv_indptr, const uint8_t* d_mask, void* o, int64_t o_stride_token,
+                          int64_t o_stride_head, float* lse, float sm_scale, void* stream);
+
+/*
+ * Pack n device bytes (0 = false, anything else = true) into the
+ * little-endian bit layout above: d_packed receives ceil(n / 32) 32-bit words
+ * (ceil(n/32)*4 bytes; bits past n are 0).  Asynchronous on `stream`.
+ */
+pkv_status pkv_packbits(const uint8_t* d_bool, int64_t n, uint8_t* d_packed, void* stream);
 
 /* ----------------------------------------------------------------- merge -- */
 

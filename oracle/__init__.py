@@ -29,6 +29,8 @@ attention  numpy float64 paged attention (GQA, NHD/HND, causal) and MLA.
 merge      base-2 log-sum-exp state merge, pairwise and multi-way.
 cascade    multi-level cascade attention: per-level states over one paged
            cache, merged per query row.
+mask       ragged KV and the 2-D ragged custom mask (offsets, little-endian
+           bit packing, attention over ragged keys).
 brute      pure-Python ``math`` attention for tiny inputs; pins ``attention``.
 
 Pin status (see the tests under ``tests/test_oracle_*.py``): every function

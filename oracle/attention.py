@@ -84,7 +84,7 @@ def gather_request(cache, layout: str, kv_indptr, kv_indices, page_size: int, b:
 def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
                     page_size: int, layout: str, num_kv_heads: int, causal: bool = True,
                     sm_scale: float | None = None, q_dtype: str = "f32", kv_dtype: str = "f32",
-                    requests=None, heads=None, key_range=None):
+                    requests=None, heads=None, key_range=None, custom_mask=None):
     """Batched attention of ragged queries against a paged KV cache.
 
     q [nnz, Hq, Dqk]; k_cache/v_cache in the tuple form (see
@@ -97,6 +97,11 @@ def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv
     alignment, "Causality uses logical positions, not page numbers");
     otherwise it sees every key.  sm_scale defaults to 1/sqrt(Dqk), the scale
     of the ordinary logits in "Core mechanism: schedule work around state".
+
+    ``custom_mask``: a flattened boolean 2-D ragged mask ("FlashInfer 中的
+    KV-Cache 布局", "掩码布局"): request b's q_b x K_b block, query-major,
+    starts at the sum of q x K over the earlier requests; True keeps a key.
+    It takes the place of the causal rule.
 
     ``requests`` / ``heads`` restrict the work to a sample (other outputs stay
     NaN).  ``key_range`` = (lo, hi) restricts every request to keys
@@ -118,6 +123,11 @@ def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv
     lse = np.full((nnz, hq), np.nan)
     reqs = range(batch) if requests is None else requests
     head_list = range(hq) if heads is None else heads
+    mask_off = [0]
+    for b in range(batch):
+        mask_off.append(mask_off[-1] + (qo_indptr[b + 1] - qo_indptr[b]) * lens[b])
+    if custom_mask is not None and len(custom_mask) != mask_off[-1]:
+        raise md.MetadataError("mask_length", f"mask has {len(custom_mask)} entries, the batch needs {mask_off[-1]}")
     for b in reqs:
         r0, r1 = qo_indptr[b], qo_indptr[b + 1]
         n_q = r1 - r0
@@ -128,7 +138,10 @@ def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv
         vb = upcast(gather_request(v_cache, layout, kv_indptr, kv_indices, page_size, b, k_len), kv_dtype)
         i = np.arange(n_q)[:, None]
         j = np.arange(k_len)[None, :]
-        mask = (j <= k_len - n_q + i) if causal else np.ones((n_q, k_len), dtype=bool)
+        if custom_mask is not None:
+            mask = np.asarray(custom_mask[mask_off[b]:mask_off[b + 1]], dtype=bool).reshape(n_q, k_len)
+        else:
+            mask = (j <= k_len - n_q + i) if causal else np.ones((n_q, k_len), dtype=bool)
         if key_range is not None:
             mask = mask & (j >= key_range[0]) & (j < key_range[1])
         qb = upcast(q[r0:r1], q_dtype)

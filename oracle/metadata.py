@@ -42,6 +42,7 @@ REASONS = (
     "append_collision",  # completion: two appended tokens may not share a slot
     "cascade_rows",      # completion: every cascade level covers the same query rows
     "cascade_nesting",   # completion: cascade levels nest (each node is a union of next-level nodes)
+    "mask_length",       # the flattened custom mask holds sum(qo_len * kv_len) entries (KV-Cache layouts, mask layout)
 )
 
 

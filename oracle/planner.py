@@ -45,10 +45,14 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def rows_per_tile(mode: str, group: int, kv_dtype: str) -> int:
-    """Query rows per work item: 1 for decode, MLA and float32 prefill; for
-    bfloat16 prefill as many rows as fit a 256-high tile of (row, head) pairs."""
-    if mode != PREFILL or kv_dtype == "f32":
+RAGGED_PAGE = 16                # ragged keys are chunked as if in pages of this many tokens
+
+
+def rows_per_tile(mode: str, group: int, kv_dtype: str, masked: bool = False) -> int:
+    """Query rows per work item: 1 for decode, MLA, float32 prefill and
+    custom-masked prefill; for bfloat16 prefill as many rows as fit a
+    256-high tile of (row, head) pairs."""
+    if mode != PREFILL or kv_dtype == "f32" or masked:
         return 1
     return max(1, MFMA_TILE_ROWS // group)
 
@@ -216,3 +220,31 @@ def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: 
         row_ptr.append(len(slots))
     return {"levels": out_levels, "items": items, "row_ptr": row_ptr, "slots": slots,
             "num_partial_rows": slot_base, "total_rows": total_rows}
+
+
+def plan_ragged(*, qo_indptr, kv_indptr, heads_y: int, rows: int, causal: bool, num_cus: int,
+                fixed_split_pages: int = 0, target_per_cu: int = 0, tail_split: int = 0) -> dict:
+    """Work list over ragged keys ("FlashInfer 中的 KV-Cache 布局", "Ragged
+    Tensor": request b's keys are data[kv_indptr[b]:kv_indptr[b+1]]).
+
+    The keys are chunked as if they sat in pages of RAGGED_PAGE tokens (a
+    request of K keys has ceil(K / RAGGED_PAGE) such pages, the last holding
+    the rest), planned by ``plan`` in prefill mode, and every item's
+    page_base is then the request index b: the device reads request b's first
+    key position from entry b of kv_indptr and addresses keys as one
+    contiguous run from there.  A request with no keys has no rows (qo_len <=
+    kv_len), hence no tiles.
+    """
+    batch = len(kv_indptr) - 1
+    lens = [kv_indptr[b + 1] - kv_indptr[b] for b in range(batch)]
+    pages = [_cdiv(k, RAGGED_PAGE) for k in lens]
+    v_indptr = [0]
+    for n in pages:
+        v_indptr.append(v_indptr[-1] + n)
+    last = [k - RAGGED_PAGE * (n - 1) if n else 0 for k, n in zip(lens, pages)]
+    p = plan(mode=PREFILL, qo_indptr=qo_indptr, kv_indptr=v_indptr, kv_last_page_len=last,
+             page_size=RAGGED_PAGE, heads_y=heads_y, rows=rows, causal=causal, num_cus=num_cus,
+             fixed_split_pages=fixed_split_pages, target_per_cu=target_per_cu, tail_split=tail_split)
+    for it in p["items"]:
+        it[5] = it[7]
+    return p

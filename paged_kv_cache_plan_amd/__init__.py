@@ -17,8 +17,9 @@ import os
 
 import numpy as np
 
-from ._abi import (BF16, DECODE, F32, HND, MLA_DECODE, NHD, PREFILL, STATUS_NAMES, CacheDesc, CascadeInfo,
-                   CascadeLevel, GraphCaps, PlanInfo, PlanParams, load_library)
+from ._abi import (BF16, DECODE, F32, HND, KV_PAGED, KV_RAGGED, MASK_CUSTOM, MASK_NONE, MLA_DECODE, NHD, PREFILL,
+                   STATUS_NAMES, CacheDesc, CascadeInfo, CascadeLevel, GraphCaps, PlanInfo, PlanParams,
+                   load_library)
 
 _lib = None
 
@@ -78,7 +79,9 @@ def _host_i32(x, name):
 def _check_batch(params, qo, kvp, last):
     """The C ABI reads B+1 / B entries (B = params.batch_size) from these host arrays."""
     b = params.batch_size
-    if last is None or kvp is None or len(last) != b or len(kvp) != b + 1 or (qo is not None and len(qo) != b + 1):
+    ragged = params.kv_format == KV_RAGGED
+    if (kvp is None or len(kvp) != b + 1 or (qo is not None and len(qo) != b + 1)
+            or (not ragged and (last is None or len(last) != b))):
         raise ValueError(f"metadata lengths do not match batch_size {b}")
 
 
@@ -179,7 +182,7 @@ _DTYPES = {"f32": F32, "bf16": BF16}
 
 def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo=None, page_size,
                 causal=True, dtype="bf16", num_cus=0, fixed_split_pages=0, target_per_cu=0,
-                mla_head_groups=0, max_num_pages=0, tail_split=0) -> PlanParams:
+                mla_head_groups=0, max_num_pages=0, tail_split=0, ragged=False, custom_mask=False) -> PlanParams:
     p = PlanParams()
     p.mode = _MODES[mode] if isinstance(mode, str) else mode
     p.batch_size = batch_size
@@ -192,6 +195,8 @@ def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, he
     p.num_cus, p.fixed_split_pages, p.target_per_cu = num_cus, fixed_split_pages, target_per_cu
     p.mla_head_groups, p.max_num_pages = mla_head_groups, max_num_pages
     p.tail_split = tail_split
+    p.kv_format = KV_RAGGED if ragged else KV_PAGED
+    p.mask_mode = MASK_CUSTOM if custom_mask else MASK_NONE
     return p
 
 
@@ -289,6 +294,39 @@ class Plan:
         """pkv_run_merge: merge the split tiles' partial states into out / lse."""
         _check(lib().pkv_run_merge(self._handle, _dev(out, "out"), out.stride(0), out.stride(1),
                                    None if lse is None else _dev(lse, "lse"), _stream(stream)))
+
+    def run_masked(self, q, k_cache, v_cache, kv_indices, mask_packed, out, lse=None, *, layout, sm_scale=0.0,
+                   stream=None):
+        """pkv_run_masked: mask_packed is the device bit-packed custom mask (see ``packbits``)."""
+        import torch
+        p = self.params
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk)
+        if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
+            raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        _check(lib().pkv_run_masked(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
+                                    _dev(kv_indices, "kv_indices", torch.int32), _dev(mask_packed, "mask", torch.uint8),
+                                    _dev(out, "out", q.dtype), out.stride(0), out.stride(1),
+                                    None if lse is None else _dev(lse, "lse"), ctypes.c_float(sm_scale),
+                                    _stream(stream)))
+
+    def run_ragged(self, q, k, v, kv_indptr, out, lse=None, *, mask_packed=None, sm_scale=0.0, stream=None):
+        """pkv_run_ragged: k, v [tokens, Hkv, D] device tensors; kv_indptr device int32 [B+1]."""
+        import torch
+        if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
+            raise ValueError("k and v must be [tokens, heads, dim] with equal strides and contiguous dim")
+        if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
+            raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        _check(lib().pkv_run_ragged(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), _dev(k, "k", q.dtype),
+                                    _dev(v, "v", q.dtype), k.stride(0), k.stride(1),
+                                    _dev(kv_indptr, "kv_indptr", torch.int32),
+                                    None if mask_packed is None else _dev(mask_packed, "mask", torch.uint8),
+                                    _dev(out, "out", q.dtype), out.stride(0), out.stride(1),
+                                    None if lse is None else _dev(lse, "lse"), ctypes.c_float(sm_scale),
+                                    _stream(stream)))
 
     def run_mla(self, q_ckv, q_kpe, ckv, kpe, kv_indices, out, lse=None, *, sm_scale=0.0, stream=None):
         """pkv_run_mla.  ckv/kpe are [pages, P, 512] / [pages, P, 64] views (same page/token strides)."""
@@ -466,6 +504,21 @@ def append_paged_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, kv_last_
                                      _dev(kv_indptr, "kv_indptr", i32), _dev(kv_indices, "kv_indices", i32),
                                      _dev(kv_last_page_len, "kv_last_page_len", i32), kv_last_page_len.numel(),
                                      k_new.shape[0], ctypes.byref(desc), _stream(stream)))
+
+
+def packbits(mask_bool, stream=None):
+    """pkv_packbits: a device bool/uint8 tensor -> device uint8 tensor of
+    ceil(n / 32) * 4 bytes, element e at bit e % 8 of byte e // 8."""
+    import torch
+    m = mask_bool.contiguous()
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise TypeError("mask must be bool or uint8")
+    n = m.numel()
+    out = torch.zeros(max(4, (n + 31) // 32 * 4), dtype=torch.uint8, device=m.device)
+    _check(lib().pkv_packbits(_dev(m, "mask"), n, _dev(out, "packed"), _stream(stream)))
+    return out
 
 
 def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):

@@ -20,6 +20,8 @@ META_REASONS = {
 F32, BF16 = 0, 1
 NHD, HND = 0, 1
 DECODE, PREFILL, MLA_DECODE = 0, 1, 2
+KV_PAGED, KV_RAGGED = 0, 1
+MASK_NONE, MASK_CUSTOM = 0, 1
 
 
 class CacheDesc(ctypes.Structure):
@@ -34,14 +36,15 @@ class PlanParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "batch_size", "num_qo_heads", "num_kv_heads", "head_dim_qk", "head_dim_vo", "page_size", "causal",
         "q_dtype", "kv_dtype", "num_cus", "fixed_split_pages", "target_per_cu", "mla_head_groups",
-        "max_num_pages", "tail_split")]
+        "max_num_pages", "tail_split", "kv_format", "mask_mode")]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "batch_size", "num_items", "num_merges", "num_partial_rows", "chunk_pages", "split",
         "rows_per_tile", "heads_y", "num_cus", "target", "total_rows")] + [
-        ("workspace_bytes", ctypes.c_int64), ("staging_bytes", ctypes.c_int64), ("fingerprint", ctypes.c_uint64)]
+        ("workspace_bytes", ctypes.c_int64), ("staging_bytes", ctypes.c_int64), ("fingerprint", ctypes.c_uint64),
+        ("mask_bits", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -112,6 +115,11 @@ SIGNATURES = {
     "pkv_cascade_run": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64,
                                _vp, ctypes.c_float, _vp]),
     "pkv_cascade_plan_destroy": (_i32, [_vp]),
+    "pkv_run_masked": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i64, _i64, _vp,
+                              ctypes.c_float, _vp]),
+    "pkv_run_ragged": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp,
+                              ctypes.c_float, _vp]),
+    "pkv_packbits": (_i32, [_vp, _i64, _vp, _vp]),
     "pkv_merge_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "pkv_merge_states": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp]),
 }

@@ -131,7 +131,7 @@ constexpr int rows_min_waves() {
   return int(sizeof(T)) * D * G >= 2048 ? 1 : PKV_ROWS_MIN_WAVES;
 }
 
-template <typename T, int D, int G, bool kAligned>
+template <typename T, int D, int G, bool kAligned, bool kMask>
 __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr int E = Elem<T>::kPer16;       // elements per 16-byte chunk
@@ -175,6 +175,11 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
     const int32_t row = it.q_row0 + r;
     const int32_t lo = it.kv_start;
     const int32_t hi = min(it.kv_end, it.diag + r + 1);
+    int64_t mask_bit0 = 0;   // bit of (row, key 0) in the packed custom mask
+    if constexpr (kMask) {
+      const MaskRow mr = a.mask_rows[it.batch];
+      mask_bit0 = mr.bit0 + int64_t(row - mr.q_start) * mr.kv_len;
+    }
 
     uint4 qreg[G][VC];
     const T* qrow = static_cast<const T*>(a.q) + int64_t(row) * a.q_stride_token +
@@ -244,7 +249,12 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         float p[NU][G];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-          const bool ok = blk + u * VT + vg < thi;
+          const int32_t key = blk + u * VT + vg;
+          bool ok = key < thi;
+          if constexpr (kMask) {   // custom mask: the key's bit in this row
+            const int64_t bit = mask_bit0 + (ok ? key : 0);
+            ok = ok && ((a.mask[bit >> 5] >> (bit & 31)) & 1u);
+          }
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float part = 0.f;
@@ -436,10 +446,18 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const bool aligned = a.page_shift >= 4;   // a power-of-two page of at least 16 keys
-  if (aligned)
-    hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+  const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
+  if (a.mask) {
+    if (aligned)
+      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false, true>), grid, block, 0, st, a);
+  } else {
+    if (aligned)
+      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true, false>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

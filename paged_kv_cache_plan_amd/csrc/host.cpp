@@ -147,16 +147,37 @@ int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 
 constexpr int32_t kMlaHeadsPerGroup = 64;   // the MLA kernel's head-group width
 constexpr int32_t kCascadeTargetPerCu = 1;
 
-int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype) {
-  if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32) return 1;
+constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
+
+int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
+  if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32 || mask_mode == PKV_MASK_CUSTOM) return 1;
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
 
 struct PlanResult {
   std::vector<Item> items;
   std::vector<MergeItem> merges;
+  std::vector<pkv::MaskRow> mask_rows;   // custom-masked plans: one per request
   pkv_plan_info info;
 };
+
+// Ragged metadata, in the oracle's order: heads, qo_indptr, kv_indptr, then
+// qo_len <= kv_len per request.
+pkv_status validate_ragged(const int32_t* qo_indptr, const int32_t* kv_indptr, int32_t batch, int32_t hq,
+                           int32_t hkv) {
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return meta_fail(PKV_META_HEAD_GROUP, fmt("%lld qo heads do not group over %lld kv heads", hq, hkv));
+  if (batch < 0) return meta_fail(PKV_META_BATCH_SIZE, "negative batch size");
+  if (!qo_indptr || !kv_indptr) return fail(PKV_ERR_INVALID_ARG, "null metadata pointer");
+  pkv_status s = check_indptr("qo_indptr", qo_indptr, batch);
+  if (!s) s = check_indptr("kv_indptr", kv_indptr, batch);
+  if (s) return s;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t q = int64_t(qo_indptr[b + 1]) - qo_indptr[b], k = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
+    if (q > k) return meta_fail(PKV_META_QO_EXCEEDS_KV, fmt("request %lld: qo_len %lld > kv_len %lld", b, q, k));
+  }
+  return PKV_OK;
+}
 
 uint64_t fnv1a(uint64_t h, const void* data, size_t bytes) {
   const unsigned char* p = static_cast<const unsigned char*>(data);
@@ -174,7 +195,7 @@ uint64_t fingerprint(const pkv_plan_params& prm, const int32_t* qo, const int32_
   const int32_t b = prm.batch_size;
   if (qo) h = fnv1a(h, qo, sizeof(int32_t) * (b + 1));
   h = fnv1a(h, kv_indptr, sizeof(int32_t) * (b + 1));
-  if (b > 0) h = fnv1a(h, last, sizeof(int32_t) * b);
+  if (b > 0 && last) h = fnv1a(h, last, sizeof(int32_t) * b);
   if (kv_indices) {
     const int64_t n = std::min<int64_t>(num_indices, kv_indptr[b]);
     h = fnv1a(h, kv_indices, sizeof(int32_t) * n);
@@ -199,6 +220,14 @@ pkv_status check_params(const pkv_plan_params* p) {
   }
   if (p->fixed_split_pages < 0 || p->target_per_cu < 0 || p->mla_head_groups < 0 || p->tail_split < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative planner knob");
+  if (p->kv_format != PKV_KV_PAGED && p->kv_format != PKV_KV_RAGGED)
+    return fail(PKV_ERR_INVALID_ARG, fmt("unknown kv_format %lld", p->kv_format));
+  if (p->mask_mode != PKV_MASK_NONE && p->mask_mode != PKV_MASK_CUSTOM)
+    return fail(PKV_ERR_INVALID_ARG, fmt("unknown mask_mode %lld", p->mask_mode));
+  if ((p->kv_format == PKV_KV_RAGGED || p->mask_mode == PKV_MASK_CUSTOM) && p->mode != PKV_MODE_PREFILL)
+    return fail(PKV_ERR_UNSUPPORTED, "ragged KV and custom masks need prefill mode");
+  if (p->mask_mode == PKV_MASK_CUSTOM && p->causal)
+    return fail(PKV_ERR_INVALID_ARG, "a custom mask replaces the causal rule: set causal to 0");
   return PKV_OK;
 }
 
@@ -216,10 +245,35 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   if (prefill && !qo_indptr) return fail(PKV_ERR_INVALID_ARG, "prefill needs qo_indptr");
   const int32_t batch = prm->batch_size;
   const int32_t max_pages = prm->max_num_pages > 0 ? prm->max_num_pages : INT32_MAX;
+  const bool ragged = prm->kv_format == PKV_KV_RAGGED;
   std::vector<int32_t> kv_len;
-  s = validate_impl(qo_indptr, kv_indptr, kv_indices, num_indices, last, batch, prm->page_size,
-                    max_pages, prm->num_qo_heads, prm->num_kv_heads, !prefill, &kv_len, check_qo_kv);
-  if (s) return s;
+  // Ragged keys are planned over a virtual page table of kRaggedPage-token
+  // pages; items then address request b's keys from entry b of kv_indptr.
+  std::vector<int32_t> v_indptr, v_last;
+  int32_t page_size = prm->page_size;
+  const int32_t* const user_kv_indptr = kv_indptr;
+  const int32_t* const user_last = last;
+  if (ragged) {
+    s = validate_ragged(qo_indptr, kv_indptr, batch, prm->num_qo_heads, prm->num_kv_heads);
+    if (s) return s;
+    page_size = kRaggedPage;
+    v_indptr.assign(size_t(batch) + 1, 0);
+    v_last.assign(size_t(batch), 0);
+    kv_len.assign(size_t(batch), 0);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t k = kv_indptr[b + 1] - kv_indptr[b];
+      const int32_t n = int32_t(cdiv(k, kRaggedPage));
+      kv_len[b] = k;
+      v_indptr[b + 1] = v_indptr[b] + n;
+      v_last[b] = n ? k - kRaggedPage * (n - 1) : 0;
+    }
+    kv_indptr = v_indptr.data();
+    last = v_last.data();
+  } else {
+    s = validate_impl(qo_indptr, kv_indptr, kv_indices, num_indices, last, batch, prm->page_size,
+                      max_pages, prm->num_qo_heads, prm->num_kv_heads, !prefill, &kv_len, check_qo_kv);
+    if (s) return s;
+  }
 
   int32_t num_cus = prm->num_cus;
   if (num_cus <= 0) {
@@ -229,7 +283,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
     if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
   }
   const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
-  const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype);
+  const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode);
   int32_t heads_y = prm->num_kv_heads;
   if (mla) {
     heads_y = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
@@ -254,9 +308,9 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   const int64_t target = int64_t(target_per_cu) * num_cus;
   int64_t chunk = prm->fixed_split_pages > 0
                       ? prm->fixed_split_pages
-                      : std::max<int64_t>(cdiv(kMinSplitTokens, prm->page_size), cdiv(work, target));
+                      : std::max<int64_t>(cdiv(kMinSplitTokens, page_size), cdiv(work, target));
   chunk = std::min(chunk, kMaxChunkPages);
-  const int64_t chunk_tokens = chunk * prm->page_size;
+  const int64_t chunk_tokens = chunk * page_size;
 
   // Step 4-6: chunks per tile, causal pruning, partial-row assignment.
   struct Raw {
@@ -289,10 +343,10 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
       // is made of small items.
       if (tail_split > 1 && !kept.empty()) {
         const int64_t lo = kept.back().first, hi = kept.back().second;
-        const int64_t pages = cdiv(hi - lo, prm->page_size);
+        const int64_t pages = cdiv(hi - lo, page_size);
         if (pages > 1) {
           kept.pop_back();
-          const int64_t step = cdiv(pages, tail_split) * prm->page_size;
+          const int64_t step = cdiv(pages, tail_split) * page_size;
           for (int64_t s0 = lo; s0 < hi; s0 += step)
             kept.emplace_back(int32_t(s0), int32_t(std::min<int64_t>(hi, s0 + step)));
         }
@@ -326,6 +380,18 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   if (raw.size() > size_t(INT32_MAX)) return fail(PKV_ERR_INVALID_ARG, "too many work items");
   out->items.resize(raw.size());
   for (size_t i = 0; i < raw.size(); ++i) out->items[i] = raw[i].it;
+  if (ragged)
+    for (Item& it : out->items) it.page_base = it.batch;   // entry b of kv_indptr: request b's first key
+  // Custom mask: where each request's rows start in the packed mask.
+  out->mask_rows.clear();
+  int64_t mask_bits = 0;
+  if (prm->mask_mode == PKV_MASK_CUSTOM) {
+    out->mask_rows.resize(size_t(batch));
+    for (int32_t b = 0; b < batch; ++b) {
+      out->mask_rows[b] = {mask_bits, qo_indptr[b], kv_len[b]};
+      mask_bits += q_len[b] * int64_t(kv_len[b]);
+    }
+  }
 
   pkv_plan_info& in = out->info;
   std::memset(&in, 0, sizeof in);
@@ -342,11 +408,13 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   in.target = int32_t(std::min<int64_t>(target, INT32_MAX));
   in.total_rows = int32_t(total_rows);
   const int64_t hq = prm->num_qo_heads;
+  in.mask_bits = mask_bits;
   const int64_t staging = align256(int64_t(out->items.size()) * sizeof(Item)) +
-                          align256(int64_t(out->merges.size()) * sizeof(MergeItem));
+                          align256(int64_t(out->merges.size()) * sizeof(MergeItem)) +
+                          align256(int64_t(out->mask_rows.size()) * sizeof(pkv::MaskRow));
   in.staging_bytes = staging;
   in.workspace_bytes = staging + align256(slot * hq * 4) + align256(slot * hq * prm->head_dim_vo * 4);
-  in.fingerprint = fingerprint(*prm, qo_indptr, kv_indptr, kv_indices, num_indices, last);
+  in.fingerprint = fingerprint(*prm, qo_indptr, user_kv_indptr, kv_indices, num_indices, user_last);
   return PKV_OK;
 }
 
@@ -404,6 +472,8 @@ pkv_status cascade_validate(const pkv_plan_params* prm, int32_t num_levels, cons
 
 pkv_status cascade_impl(const pkv_plan_params* prm, int32_t num_levels, const pkv_cascade_level* lv,
                         CascadeResult* out) {
+  if (prm->kv_format != PKV_KV_PAGED || prm->mask_mode != PKV_MASK_NONE)
+    return fail(PKV_ERR_UNSUPPORTED, "cascades run on paged caches without custom masks");
   pkv_status s = cascade_validate(prm, num_levels, lv);
   if (s) return s;
   const int32_t rows = lv[0].qo_indptr[lv[0].num_nodes];
@@ -516,6 +586,7 @@ struct pkv_plan {
   pkv_plan_info info;
   Item* d_items;
   MergeItem* d_merges;
+  pkv::MaskRow* d_mask_rows = nullptr;   // custom-masked plans
   float* d_part_lse;
   float* d_part_o;
   int device;
@@ -637,8 +708,9 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
   plan->info = in;
   plan->d_items = reinterpret_cast<Item*>(ws);
   plan->d_merges = reinterpret_cast<MergeItem*>(ws + items_bytes);
-  plan->d_part_lse = reinterpret_cast<float*>(ws + items_bytes + merges_bytes);
-  plan->d_part_o = reinterpret_cast<float*>(ws + items_bytes + merges_bytes + lse_bytes);
+  plan->d_mask_rows = reinterpret_cast<pkv::MaskRow*>(ws + items_bytes + merges_bytes);
+  plan->d_part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
+  plan->d_part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
   hipError_t e = hipGetDevice(&plan->device);
   if (e != hipSuccess) {
     delete plan;
@@ -648,6 +720,7 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
     e = upload_staging(h_staging, ws, in.staging_bytes, st, [&](char* hs) {
       std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
       std::memcpy(hs + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+      std::memcpy(hs + items_bytes + merges_bytes, r.mask_rows.data(), r.mask_rows.size() * sizeof(pkv::MaskRow));
     });
     if (e != hipSuccess) {
       delete plan;
@@ -749,6 +822,8 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
   a->lse = lse;
   a->part_o = nullptr;
   a->part_lse = nullptr;
+  a->mask = nullptr;
+  a->mask_rows = nullptr;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(p.head_dim_qk));
   a->scale_log2 = scale * 1.4426950408889634f;
   return PKV_OK;
@@ -760,7 +835,7 @@ pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::A
   const int32_t group = p.num_qo_heads / p.num_kv_heads;
   bool supported = false;
   hipError_t e;
-  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
+  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16 && !a.mask)
     e = pkv::launch_prefill_mfma(p.head_dim_qk, group, a, st, &supported);
   else
     e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
@@ -782,6 +857,8 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
   if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
   const pkv_plan_params& p = plan->params;
   if (p.mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_INVALID_ARG, "MLA plans run through pkv_run_mla");
+  if (p.kv_format == PKV_KV_RAGGED) return fail(PKV_ERR_INVALID_ARG, "ragged plans run through pkv_run_ragged");
+  if (p.mask_mode == PKV_MASK_CUSTOM) return fail(PKV_ERR_INVALID_ARG, "custom-masked plans run through pkv_run_masked");
   pkv::AttnArgs a;
   const int32_t grid_items = plan->grid_items();
   pkv_status s = prepare_attn(p, plan->device, grid_items > 0, q, q_stride_token, q_stride_head, cache,
@@ -835,6 +912,103 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, 
   if (s) return s;
   if (plan->params.mode == PKV_MODE_MLA_DECODE) return ok();
   return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Attention then split merge for an AttnArgs whose data fields are filled.
+pkv_status run_with_args(const pkv_plan* plan, pkv::AttnArgs& a, void* o, int64_t o_stride_token,
+                         int64_t o_stride_head, float* lse, void* stream) {
+  const int32_t grid_items = plan->grid_items();
+  if (grid_items > 0) {
+    a.items = plan->d_items;
+    a.num_items = grid_items;
+    a.live_items = plan->live_items();
+    a.part_o = plan->d_part_o;
+    a.part_lse = plan->d_part_lse;
+    pkv_status s = launch_attn_mode(plan->params.mode, plan->params, a, static_cast<hipStream_t>(stream));
+    if (s) return s;
+  }
+  return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
+}
+
+pkv_status check_mask_arg(const pkv_plan* plan, const uint8_t* d_mask, pkv::AttnArgs* a) {
+  if (plan->params.mask_mode != PKV_MASK_CUSTOM) {
+    if (d_mask) return fail(PKV_ERR_INVALID_ARG, "the plan was made without a custom mask");
+    return PKV_OK;
+  }
+  if (!d_mask && plan->grid_items() > 0) return fail(PKV_ERR_INVALID_ARG, "null custom mask");
+  if (reinterpret_cast<uintptr_t>(d_mask) % 4 != 0) return fail(PKV_ERR_INVALID_ARG, "mask must be 4-byte aligned");
+  a->mask = reinterpret_cast<const uint32_t*>(d_mask);
+  a->mask_rows = plan->d_mask_rows;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_run_masked(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                          const pkv_cache_desc* cache, const int32_t* d_kv_indices, const uint8_t* d_mask,
+                          void* o, int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                          void* stream) {
+  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
+  const pkv_plan_params& p = plan->params;
+  if (p.mask_mode != PKV_MASK_CUSTOM) return fail(PKV_ERR_INVALID_ARG, "the plan was made without a custom mask");
+  if (p.kv_format == PKV_KV_RAGGED) return fail(PKV_ERR_INVALID_ARG, "ragged plans run through pkv_run_ragged");
+  pkv::AttnArgs a;
+  pkv_status s = prepare_attn(p, plan->device, plan->grid_items() > 0, q, q_stride_token, q_stride_head, cache,
+                              d_kv_indices, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (!s) s = check_mask_arg(plan, d_mask, &a);
+  if (s) return s;
+  s = run_with_args(plan, a, o, o_stride_token, o_stride_head, lse, stream);
+  return s ? s : ok();
+}
+
+pkv_status pkv_run_ragged(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                          const void* k, const void* v, int64_t kv_stride_token, int64_t kv_stride_head,
+                          const int32_t* d_kv_indptr, const uint8_t* d_mask, void* o, int64_t o_stride_token,
+                          int64_t o_stride_head, float* lse, float sm_scale, void* stream) {
+  if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
+  const pkv_plan_params& p = plan->params;
+  if (p.kv_format != PKV_KV_RAGGED) return fail(PKV_ERR_INVALID_ARG, "not a ragged plan");
+  // The ragged tensors as a cache of one unbounded page per request: page b
+  // starts at token kv_indptr[b] (page stride = token stride), so key j is
+  // slot j of that page.
+  pkv_cache_desc desc;
+  desc.k = const_cast<void*>(k);
+  desc.v = const_cast<void*>(v);
+  desc.page_stride = kv_stride_token;
+  desc.token_stride = kv_stride_token;
+  desc.head_stride = kv_stride_head;
+  desc.max_num_pages = p.max_num_pages;
+  desc.page_size = p.page_size;
+  desc.num_kv_heads = p.num_kv_heads;
+  desc.head_dim = p.head_dim_qk;
+  desc.dtype = p.kv_dtype;
+  desc.layout = PKV_NHD;
+  pkv::AttnArgs a;
+  pkv_status s = prepare_attn(p, plan->device, plan->grid_items() > 0, q, q_stride_token, q_stride_head, &desc,
+                              d_kv_indptr, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (!s) s = check_mask_arg(plan, d_mask, &a);
+  if (s) return s;
+  a.page_size = 1 << 30;
+  a.page_shift = 30;
+  a.max_num_pages = INT32_MAX;
+  s = run_with_args(plan, a, o, o_stride_token, o_stride_head, lse, stream);
+  return s ? s : ok();
+}
+
+pkv_status pkv_packbits(const uint8_t* d_bool, int64_t n, uint8_t* d_packed, void* stream) {
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n == 0) return ok();
+  if (!d_bool || !d_packed) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(d_packed) % 4 != 0) return fail(PKV_ERR_INVALID_ARG, "output must be 4-byte aligned");
+  hipError_t e = pkv::launch_packbits(d_bool, n, reinterpret_cast<uint32_t*>(d_packed), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching packbits");
+  return ok();
 }
 
 pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kpe, const void* ckv,
@@ -970,7 +1144,7 @@ namespace {
 struct GraphLayout {
   pkv_graph_caps caps;
   int32_t rows_per_tile;
-  int64_t items_off, merges_off, staging_bytes, lse_off, o_off, workspace_bytes;
+  int64_t items_off, merges_off, mask_off, staging_bytes, lse_off, o_off, workspace_bytes;
 };
 
 pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, GraphLayout* g) {
@@ -987,7 +1161,9 @@ pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, Gr
   const bool prefill = prm->mode == PKV_MODE_PREFILL;
   const bool mla = prm->mode == PKV_MODE_MLA_DECODE;
   const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
-  const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype);
+  if (prm->kv_format == PKV_KV_RAGGED)
+    return fail(PKV_ERR_UNSUPPORTED, "fixed-capacity plans are built for paged caches");
+  const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode);
   int64_t hy = prm->num_kv_heads;
   if (mla) {
     hy = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
@@ -1017,7 +1193,8 @@ pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, Gr
   g->rows_per_tile = int32_t(R);
   g->items_off = 256;   // the two counters
   g->merges_off = g->items_off + align256(int64_t(c.max_items) * sizeof(Item));
-  g->staging_bytes = g->merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
+  g->mask_off = g->merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
+  g->staging_bytes = g->mask_off + (prm->mask_mode == PKV_MASK_CUSTOM ? align256(B * sizeof(pkv::MaskRow)) : 0);
   g->lse_off = g->staging_bytes;
   g->o_off = g->lse_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * 4);
   g->workspace_bytes = g->o_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * prm->head_dim_vo * 4);
@@ -1069,6 +1246,7 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
   plan->d_counts = reinterpret_cast<int32_t*>(ws);
   plan->d_items = reinterpret_cast<Item*>(ws + g.items_off);
   plan->d_merges = reinterpret_cast<MergeItem*>(ws + g.merges_off);
+  plan->d_mask_rows = reinterpret_cast<pkv::MaskRow*>(ws + g.mask_off);
   plan->d_part_lse = reinterpret_cast<float*>(ws + g.lse_off);
   plan->d_part_o = reinterpret_cast<float*>(ws + g.o_off);
   plan->h_staging = h_staging;
@@ -1106,7 +1284,9 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
                                            c.max_partial_rows));
   const int64_t items_off = 256;
   const int64_t merges_off = items_off + align256(int64_t(c.max_items) * sizeof(Item));
-  const int64_t upload = merges_off + int64_t(r.merges.size()) * sizeof(MergeItem);
+  const int64_t mask_off = merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
+  const int64_t upload = r.mask_rows.empty() ? merges_off + int64_t(r.merges.size()) * sizeof(MergeItem)
+                                             : mask_off + int64_t(r.mask_rows.size()) * sizeof(pkv::MaskRow);
   hipError_t e = upload_staging(plan->h_staging, plan->d_ws, upload, static_cast<hipStream_t>(stream),
                                 [&](char* hs) {
                                   int32_t* counts = reinterpret_cast<int32_t*>(hs);
@@ -1114,6 +1294,8 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
                                   counts[1] = r.info.num_merges;
                                   std::memcpy(hs + items_off, r.items.data(), r.items.size() * sizeof(Item));
                                   std::memcpy(hs + merges_off, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+                                  std::memcpy(hs + mask_off, r.mask_rows.data(),
+                                              r.mask_rows.size() * sizeof(pkv::MaskRow));
                                 });
   if (e != hipSuccess) return hip_fail(e, "uploading the plan");
   const int64_t ws_bytes = plan->info.workspace_bytes, st_bytes = plan->info.staging_bytes;

@@ -34,6 +34,15 @@ static_assert(sizeof(MergeItem) == 16, "merge item is four int32");
 
 enum DType : int32_t { kF32 = 0, kBF16 = 1 };
 
+// Custom mask of one request: bit (q_start + i, j) of the packed mask is
+// bit0 + i * kv_len + j.
+struct MaskRow {
+  int64_t bit0;
+  int32_t q_start;
+  int32_t kv_len;
+};
+static_assert(sizeof(MaskRow) == 16, "mask row is 16 bytes");
+
 struct AttnArgs {
   const Item* items;
   int32_t num_items;       // items the grid covers
@@ -55,6 +64,8 @@ struct AttnArgs {
   float* part_o;       // [partial rows, Hq, Dvo]
   float* part_lse;     // [partial rows, Hq]
   float scale_log2;    // sm_scale * log2(e)
+  const uint32_t* mask;        // packed custom mask (little-endian bits), or null
+  const MaskRow* mask_rows;    // per request, when mask is set
 };
 
 struct MergePartialArgs {
@@ -125,6 +136,7 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
 hipError_t launch_merge_pair(int32_t dtype, const void* va, const float* sa, const void* vb,
                              const float* sb, void* vo, float* so, int64_t rows, int32_t heads,
                              int32_t dim, hipStream_t stream);
+hipError_t launch_packbits(const uint8_t* in, int64_t n, uint32_t* out, hipStream_t stream);
 hipError_t launch_merge_many(int32_t dtype, const void* v, const float* s, void* vo, float* so,
                              int64_t rows, int32_t states, int32_t heads, int32_t dim,
                              hipStream_t stream);

@@ -319,6 +319,19 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(const MergeRowsArgs a, 
   if (slice == 0 && lane == 0 && a.lse) a.lse[int64_t(r) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
 }
 
+// Bit packing of a boolean array: thread w packs elements [32w, 32w + 32)
+// into word w, element 32w + i at bit i (little-endian bytes: element e at
+// bit e % 8 of byte e / 8).
+__global__ __launch_bounds__(256) void packbits_kernel(const uint8_t* in, int64_t n, uint32_t* out) {
+  const int64_t w = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t e0 = w * 32;
+  if (e0 >= n) return;
+  uint32_t word = 0;
+  for (int i = 0; i < 32; ++i)
+    if (e0 + i < n && in[e0 + i] != 0) word |= 1u << i;
+  out[w] = word;
+}
+
 // Pairwise merge: one wave per (row, head).  Each wave reads both statistics
 // before any lane writes, so v_out / s_out may alias the inputs.
 template <typename T>
@@ -431,6 +444,15 @@ hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t 
     else
       hipLaunchKernelGGL((merge_rows_kernel<float, 1>), grid, block, 0, st, a, slices);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_packbits(const uint8_t* in, int64_t n, uint32_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t words = (n + 31) / 32;
+  const int64_t blocks = (words + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(packbits_kernel, dim3(uint32_t(blocks)), dim3(256), 0, st, in, n, out);
   return hipGetLastError();
 }
 

@@ -347,3 +347,77 @@ def test_graph_capacities_bound_every_plan(mode):
             assert len(spec["items"]) <= caps["max_items"], (trial, len(spec["items"]), caps)
             assert len(spec["merges"]) <= caps["max_merges"]
             assert spec["num_partial_rows"] <= caps["max_partial_rows"]
+
+
+# --------------------------------------------------- ragged KV, custom masks --
+
+from oracle import mask as omask  # noqa: E402
+
+
+def test_ragged_planner_matches_spec_randomised():
+    rng = np.random.default_rng(55)
+    for trial in range(80):
+        B = int(rng.integers(1, 10))
+        kv = [int(x) for x in rng.integers(0, 3000, size=B)]
+        q = [int(rng.integers(0, k + 1)) if k else 0 for k in kv]
+        hq, hkv = [(32, 8), (8, 8), (16, 2)][trial % 3]
+        dtype = "bf16" if trial % 4 else "f32"
+        masked = trial % 5 == 0
+        causal = bool(trial % 2) and not masked
+        fixed, tail = int(rng.choice([0, 0, 1, 3])), int(rng.choice([0, 1, 2]))
+        num_cus = int(rng.integers(1, 300))
+        params = pkv.plan_params(mode="prefill", batch_size=B, num_qo_heads=hq, num_kv_heads=hkv, head_dim_qk=128,
+                                 page_size=16, causal=causal, dtype=dtype, num_cus=num_cus, fixed_split_pages=fixed,
+                                 tail_split=tail, ragged=True, custom_mask=masked)
+        qo = np.array([0] + list(np.cumsum(q)), np.int32)
+        kvp = np.array([0] + list(np.cumsum(kv)), np.int32)
+        info, items, merges = pkv.plan_compute(params, qo_indptr=qo, kv_indptr=kvp, kv_indices=None,
+                                               kv_last_page_len=None)
+        rows = pl.rows_per_tile("prefill", hq // hkv, dtype, masked=masked)
+        spec = pl.plan_ragged(qo_indptr=list(qo), kv_indptr=list(kvp), heads_y=hkv, rows=rows, causal=causal,
+                              num_cus=num_cus, fixed_split_pages=fixed, tail_split=tail)
+        assert items.tolist() == spec["items"] and merges.tolist() == spec["merges"]
+        assert info["rows_per_tile"] == rows
+        assert info["mask_bits"] == (omask.mask_indptr(q, kv)[-1] if masked else 0)
+
+
+@pytest.mark.parametrize("qo,kv", [
+    ([0, 3, 5], [0, 40, 57]),
+    ([1, 3, 5], [0, 40, 57]),
+    ([0, 3, 2], [0, 40, 57]),
+    ([0, 3, 5], [0, 40, 39]),
+    ([0, 3, 50], [0, 40, 57]),
+    ([0, 0, 0], [0, 0, 9]),
+])
+def test_ragged_validation_matches_oracle(qo, kv):
+    try:
+        omask.validate_ragged(qo_indptr=qo, kv_indptr=kv, num_qo_heads=4, num_kv_heads=2)
+        want = None
+    except md.MetadataError as e:
+        want = e.reason
+    params = pkv.plan_params(mode="prefill", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                             page_size=16, causal=False, dtype="f32", num_cus=4, ragged=True)
+    kw = dict(qo_indptr=np.array(qo, np.int32), kv_indptr=np.array(kv, np.int32), kv_indices=None,
+              kv_last_page_len=None)
+    if want is None:
+        pkv.plan_compute(params, **kw)
+    else:
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.plan_compute(params, **kw)
+        assert e.value.reason == _abi.META_REASONS[want]
+
+
+def test_mask_and_ragged_parameter_rules():
+    base = dict(batch_size=1, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64, page_size=4, dtype="f32", num_cus=4)
+    meta = dict(qo_indptr=np.array([0, 2], np.int32), kv_indptr=np.array([0, 1], np.int32),
+                kv_indices=np.array([0], np.int32), kv_last_page_len=np.array([3], np.int32))
+    with pytest.raises(pkv.PkvError) as e:       # a custom mask replaces the causal rule
+        pkv.plan_compute(pkv.plan_params(mode="prefill", causal=True, custom_mask=True, **base), **meta)
+    assert e.value.status == _abi.ERR_INVALID_ARG
+    for mode in ("decode", "mla"):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.plan_compute(pkv.plan_params(mode=mode, causal=False, ragged=True, **base),
+                             **dict(meta, qo_indptr=None))
+        assert e.value.status == _abi.ERR_UNSUPPORTED
+    info = pkv.plan_compute(pkv.plan_params(mode="prefill", causal=False, custom_mask=True, **base), **meta)[0]
+    assert info["mask_bits"] == 2 * 3 and info["rows_per_tile"] == 1

@@ -246,3 +246,26 @@ def test_cascade_plan_invariants():
         assert off == len(p["items"])
         for r in range(total):
             assert p["row_ptr"][r + 1] - p["row_ptr"][r] >= 3
+
+
+def test_masked_prefill_runs_one_row_per_tile():
+    assert pl.rows_per_tile("prefill", 4, "bf16", masked=True) == 1
+    assert pl.rows_per_tile("prefill", 4, "bf16", masked=False) == 64
+
+
+def test_hand_worked_ragged_plan():
+    """Two requests: 3 rows over 40 keys, 2 rows over 17 keys; virtual pages
+    of 16 keys (3 and 2 pages); one-row tiles, not causal, 2-page chunks:
+    request 0 chunks [0,32) [32,40), request 1 [0,17).  page_base is the
+    request index."""
+    p = pl.plan_ragged(qo_indptr=[0, 3, 5], kv_indptr=[0, 40, 57], heads_y=1, rows=1, causal=False, num_cus=1,
+                       fixed_split_pages=2, tail_split=1)
+    assert p["chunk_pages"] == 2
+    req0 = sorted((i[0], i[2], i[3]) for i in p["items"] if i[7] == 0)
+    assert req0 == [(r, lo, hi) for r in range(3) for lo, hi in ((0, 32), (32, 40))]
+    req1 = sorted((i[0], i[2], i[3], i[6]) for i in p["items"] if i[7] == 1)
+    assert req1 == [(3, 0, 17, -1), (4, 0, 17, -1)]
+    assert all(i[5] == i[7] for i in p["items"])
+    # a request without keys (and rows) makes no items
+    p = pl.plan_ragged(qo_indptr=[0, 0, 2], kv_indptr=[0, 0, 5], heads_y=1, rows=1, causal=True, num_cus=1)
+    assert [i[7] for i in p["items"]] == [1, 1]
