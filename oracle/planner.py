@@ -69,7 +69,10 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     2. Page work W = sum_b tiles_b * n_b * heads_y; target T = target_per_cu *
        num_cus items.
     3. Chunk size C (pages) = fixed_split_pages if given, else
-       max(ceil(256 / P), ceil(W / T)); either way at most 1024.
+       max(ceil(256 / P), ceil(W / T)); either way at most 1024.  MLA (whose
+       kernel holds one workgroup per CU) then grows C to the smallest size
+       whose item count times heads_y is at most T (or 1024), so that the
+       per-request rounding does not spill a second, nearly empty round.
     4. Chunk c of request b covers keys [c*C*P, min((c+1)*C*P, K_b)).
     5. For tile t (local rows l0 .. l0+rows-1) the causal limit is
        diag = K_b - q_b + l0 (non-causal: diag = K_b); a chunk whose first key
@@ -109,6 +112,20 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
     else:
         chunk = max(_cdiv(MIN_SPLIT_TOKENS, page_size), _cdiv(work, target))
     chunk = min(chunk, MAX_CHUNK_PAGES)
+    if mode == MLA and fixed_split_pages <= 0:
+        def units(c):
+            return sum(tiles[b] * _cdiv(n_pages[b], c) for b in range(batch)) * heads_y
+        lo, hi = chunk, MAX_CHUNK_PAGES
+        if units(hi) <= target:
+            while lo < hi:                      # smallest c in [lo, hi] with units(c) <= target
+                mid = (lo + hi) // 2
+                if units(mid) <= target:
+                    hi = mid
+                else:
+                    lo = mid + 1
+            chunk = lo
+        else:
+            chunk = MAX_CHUNK_PAGES
     chunk_tokens = chunk * page_size
 
     raw = []          # (key count, b, t, c_kept, fields) before slot assignment

@@ -310,6 +310,27 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
                       ? prm->fixed_split_pages
                       : std::max<int64_t>(cdiv(kMinSplitTokens, page_size), cdiv(work, target));
   chunk = std::min(chunk, kMaxChunkPages);
+  if (mla && prm->fixed_split_pages <= 0) {
+    // The MLA kernel holds one workgroup per CU: grow the chunk to the
+    // smallest size whose workgroup count fits the target, so the rounding of
+    // every request to whole chunks does not spill into a second round.
+    auto units = [&](int64_t c) {
+      int64_t u = 0;
+      for (int32_t b = 0; b < batch; ++b) u += tiles[b] * cdiv(n_pages[b], c);
+      return u * heads_y;
+    };
+    if (units(kMaxChunkPages) <= target) {
+      int64_t lo = chunk, hi = kMaxChunkPages;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (units(mid) <= target) hi = mid;
+        else lo = mid + 1;
+      }
+      chunk = lo;
+    } else {
+      chunk = kMaxChunkPages;
+    }
+  }
   const int64_t chunk_tokens = chunk * page_size;
 
   // Step 4-6: chunks per tile, causal pruning, partial-row assignment.

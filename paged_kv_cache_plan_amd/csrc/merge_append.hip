@@ -148,17 +148,49 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     const int32_t row = mi.q_row0 + r;
     T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
     // Every lane stays active through the chunk loop: the scale of chunk c
-    // lives in lane c, so lanes past the slice end only skip the load/store.
-    for (int32_t d0 = d_lo; d0 < d_hi; d0 += 64) {
-      const int32_t d = d0 + lane;
-      const bool own = d < d_hi;
-      float acc = 0.f;
-      for (int32_t c = 0; c < n; ++c) {
-        const float w = __shfl(scale, c);
-        if (own && w != 0.f)
-          acc = fmaf(w, a.part_o[((row_base + int64_t(c) * mi.num_rows) * hq + h) * d_all + d], acc);
+    // lives in lane c.  With an even slice width each lane owns two
+    // consecutive dims (8-byte loads); chunks go four at a time so four loads
+    // are in flight, the steps past the last chunk re-reading it with weight 0.
+    // Lanes past the slice end read dim d_lo and store nothing.
+    const float* pbase = a.part_o + (row_base * hq + h) * d_all;
+    const int64_t chunk_stride = int64_t(mi.num_rows) * hq * d_all;
+    if (kVec4 && ((d_hi - d_lo) & 1) == 0) {
+      for (int32_t d0 = d_lo; d0 < d_hi; d0 += 128) {
+        const int32_t d = d0 + 2 * lane;
+        const bool own = d < d_hi;
+        const float* src = pbase + (own ? d : d_lo);
+        float acc0 = 0.f, acc1 = 0.f;
+        for (int32_t c = 0; c < n; c += 4) {
+          float2 x[4];
+          float w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int32_t cc = min(c + j, n - 1);
+            w[j] = c + j < n ? __shfl(scale, cc) : 0.f;
+            x[j] = *reinterpret_cast<const float2*>(src + int64_t(cc) * chunk_stride);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc0 = fmaf(w[j], x[j].x, acc0);
+            acc1 = fmaf(w[j], x[j].y, acc1);
+          }
+        }
+        if (own) {
+          store_f<T>(orow, d, acc0);
+          store_f<T>(orow, d + 1, acc1);
+        }
       }
-      if (own) store_f<T>(orow, d, acc);
+    } else {
+      for (int32_t d0 = d_lo; d0 < d_hi; d0 += 64) {
+        const int32_t d = d0 + lane;
+        const bool own = d < d_hi;
+        float acc = 0.f;
+        for (int32_t c = 0; c < n; ++c) {
+          const float w = __shfl(scale, c);
+          if (own && w != 0.f) acc = fmaf(w, pbase[int64_t(c) * chunk_stride + d], acc);
+        }
+        if (own) store_f<T>(orow, d, acc);
+      }
     }
     if (slice == 0 && lane == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
     return;
