@@ -70,7 +70,12 @@ typedef enum {
   PKV_META_CASCADE_NESTING = 14  /* completion: a cascade level's node boundary is not one of the next level's */
 } pkv_meta_reason;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* PKV_FP8_E4M3: 8-bit E4M3 codes (the OCP fp8 format: bias 7, no infinity,
+ * largest finite 448), for the K/V cache only, with bf16 queries and outputs
+ * ([KVL] "布局：NHD/HND" notes low-precision fp8 caches and that HND suits
+ * them).  Stored value x stands for x * k_scale (keys) or x * v_scale
+ * (values), one scale per tensor (pkv_cache_desc). */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* [KVL] "布局：NHD/HND": the last three dims of a page are
  * (page_size, heads, head_dim) for NHD and (heads, page_size, head_dim) for HND. */
@@ -125,6 +130,8 @@ typedef struct pkv_cache_desc {
   int32_t head_dim;
   int32_t dtype;   /* pkv_dtype */
   int32_t layout;  /* pkv_layout */
+  float k_scale;   /* fp8 caches: dequantisation factor of every key (<= 0: 1) */
+  float v_scale;   /* fp8 caches: dequantisation factor of every value (<= 0: 1) */
 } pkv_cache_desc;
 
 /*
@@ -215,8 +222,8 @@ typedef struct pkv_plan_params {
   int32_t page_size;
   int32_t causal;            /* prefill: bottom-right causal mask ([DD] "Causality uses
                                 logical positions, not page numbers"); ignored by decode */
-  int32_t q_dtype;           /* pkv_dtype; must equal kv_dtype */
-  int32_t kv_dtype;
+  int32_t q_dtype;           /* pkv_dtype of q and o; equals kv_dtype, or bf16 over an fp8 cache */
+  int32_t kv_dtype;          /* an fp8 cache runs decode / prefill (head_dim 128) on the row kernel */
   int32_t num_cus;           /* 0: query the current device */
   int32_t fixed_split_pages; /* > 0 forces this chunk size in pages */
   int32_t target_per_cu;     /* 0: default (decode 3, prefill 4, MLA 1) */

@@ -21,18 +21,39 @@ from . import metadata as md
 LN2 = math.log(2.0)
 
 
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one 8-bit E4M3 code (the OCP 8-bit floating-point format:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+    holds the subnormals m/8 * 2^-6; the one all-ones pattern per sign is NaN
+    and there is no infinity, so the largest finite value is 448)."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_FP8_TABLE = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
 def upcast(x, dtype: str) -> np.ndarray:
     """Exact float64 view of stored values.
 
-    ``dtype`` is "f32" (a float32 array) or "bf16" (the raw 16-bit patterns of
+    ``dtype`` is "f32" (a float32 array), "bf16" (the raw 16-bit patterns of
     bfloat16 numbers in a uint16 array; a bfloat16 is the upper half of a
-    float32, so shifting the pattern up by 16 bits is exact).
+    float32, so shifting the pattern up by 16 bits is exact) or "fp8" (uint8
+    E4M3 codes, see ``fp8_e4m3_value``; every code is exact in float64).
     """
     x = np.asarray(x)
     if dtype == "f32":
         return x.astype(np.float64)
     if dtype == "bf16":
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return _FP8_TABLE[x.astype(np.uint8)]
     raise ValueError(dtype)
 
 
@@ -84,7 +105,8 @@ def gather_request(cache, layout: str, kv_indptr, kv_indices, page_size: int, b:
 def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
                     page_size: int, layout: str, num_kv_heads: int, causal: bool = True,
                     sm_scale: float | None = None, q_dtype: str = "f32", kv_dtype: str = "f32",
-                    requests=None, heads=None, key_range=None, custom_mask=None):
+                    requests=None, heads=None, key_range=None, custom_mask=None, k_scale: float = 1.0,
+                    v_scale: float = 1.0):
     """Batched attention of ragged queries against a paged KV cache.
 
     q [nnz, Hq, Dqk]; k_cache/v_cache in the tuple form (see
@@ -102,6 +124,9 @@ def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv
     KV-Cache 布局", "掩码布局"): request b's q_b x K_b block, query-major,
     starts at the sum of q x K over the earlier requests; True keeps a key.
     It takes the place of the causal rule.
+
+    ``k_scale`` / ``v_scale`` multiply every stored key / value (the
+    dequantisation of a low-precision cache, one factor per tensor).
 
     ``requests`` / ``heads`` restrict the work to a sample (other outputs stay
     NaN).  ``key_range`` = (lo, hi) restricts every request to keys
@@ -134,8 +159,8 @@ def paged_attention(q, k_cache, v_cache, *, qo_indptr, kv_indptr, kv_indices, kv
         if n_q == 0:
             continue
         k_len = lens[b]
-        kb = upcast(gather_request(k_cache, layout, kv_indptr, kv_indices, page_size, b, k_len), kv_dtype)
-        vb = upcast(gather_request(v_cache, layout, kv_indptr, kv_indices, page_size, b, k_len), kv_dtype)
+        kb = upcast(gather_request(k_cache, layout, kv_indptr, kv_indices, page_size, b, k_len), kv_dtype) * k_scale
+        vb = upcast(gather_request(v_cache, layout, kv_indptr, kv_indices, page_size, b, k_len), kv_dtype) * v_scale
         i = np.arange(n_q)[:, None]
         j = np.arange(k_len)[None, :]
         if custom_mask is not None:

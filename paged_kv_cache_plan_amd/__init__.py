@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-from ._abi import (BF16, DECODE, F32, HND, KV_PAGED, KV_RAGGED, MASK_CUSTOM, MASK_NONE, MLA_DECODE, NHD, PREFILL,
+from ._abi import (BF16, DECODE, F32, FP8_E4M3, HND, KV_PAGED, KV_RAGGED, MASK_CUSTOM, MASK_NONE, MLA_DECODE, NHD, PREFILL,
                    STATUS_NAMES, CacheDesc, CascadeInfo, CascadeLevel, GraphCaps, PlanInfo, PlanParams,
                    load_library)
 
@@ -101,6 +101,8 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):   # E4M3 codes
+        return FP8_E4M3
     raise TypeError(f"unsupported payload dtype {t.dtype}")
 
 
@@ -120,7 +122,8 @@ def device_num_cus() -> int:
     return out.value
 
 
-def cache_desc(k, v, layout: str, page_size: int, num_kv_heads: int, head_dim: int) -> CacheDesc:
+def cache_desc(k, v, layout: str, page_size: int, num_kv_heads: int, head_dim: int, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> CacheDesc:
     """Descriptor of a paged cache given as two 4-D views (either the tuple
     form or the K/V halves of a 5-D [pages, 2, ...] tensor).  Strides are taken
     from the tensors; the innermost (dim) stride must be 1."""
@@ -146,6 +149,7 @@ def cache_desc(k, v, layout: str, page_size: int, num_kv_heads: int, head_dim: i
     d.page_size, d.num_kv_heads, d.head_dim = page_size, num_kv_heads, head_dim
     d.dtype = _dtype_code(k)
     d.layout = NHD if layout == "NHD" else HND
+    d.k_scale, d.v_scale = k_scale, v_scale
     return d
 
 
@@ -177,12 +181,13 @@ def validate_append(*, append_indptr, kv_indptr, kv_indices, kv_last_page_len, p
 # ------------------------------------------------------------------- plan --
 
 _MODES = {"decode": DECODE, "prefill": PREFILL, "mla": MLA_DECODE}
-_DTYPES = {"f32": F32, "bf16": BF16}
+_DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 
 
 def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo=None, page_size,
                 causal=True, dtype="bf16", num_cus=0, fixed_split_pages=0, target_per_cu=0,
-                mla_head_groups=0, max_num_pages=0, tail_split=0, ragged=False, custom_mask=False) -> PlanParams:
+                mla_head_groups=0, max_num_pages=0, tail_split=0, ragged=False, custom_mask=False,
+                kv_dtype=None) -> PlanParams:
     p = PlanParams()
     p.mode = _MODES[mode] if isinstance(mode, str) else mode
     p.batch_size = batch_size
@@ -192,6 +197,8 @@ def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, he
     p.page_size = page_size
     p.causal = int(causal)
     p.q_dtype = p.kv_dtype = _DTYPES[dtype] if isinstance(dtype, str) else dtype
+    if kv_dtype is not None:
+        p.kv_dtype = _DTYPES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
     p.num_cus, p.fixed_split_pages, p.target_per_cu = num_cus, fixed_split_pages, target_per_cu
     p.mla_head_groups, p.max_num_pages = mla_head_groups, max_num_pages
     p.tail_split = tail_split
@@ -270,12 +277,12 @@ class Plan:
         _check(lib().pkv_plan_check(self._handle, qo_p, kvp_p, idx_p, 0 if idx is None else len(idx), last_p))
 
     def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None,
-            _entry="pkv_run"):
+            _entry="pkv_run", k_scale=1.0, v_scale=1.0):
         """pkv_run.  q [nnz, Hq, D] and out [nnz, Hq, D] device tensors of the plan's dtype;
         k_cache/v_cache 4-D views (see ``cache_desc``); kv_indices device int32; lse float32 [nnz, Hq]."""
         import torch
         p = self.params
-        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk)
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk, k_scale, v_scale)
         if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
             raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
@@ -285,10 +292,11 @@ class Plan:
                                       out.stride(0), out.stride(1), None if lse is None else _dev(lse, "lse"),
                                       ctypes.c_float(sm_scale), _stream(stream)))
 
-    def run_attention(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None):
+    def run_attention(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None,
+                      k_scale=1.0, v_scale=1.0):
         """pkv_run_attention: the attention kernel only (split tiles stay as partial states)."""
         self.run(q, k_cache, v_cache, kv_indices, out, lse, layout=layout, sm_scale=sm_scale, stream=stream,
-                 _entry="pkv_run_attention")
+                 _entry="pkv_run_attention", k_scale=k_scale, v_scale=v_scale)
 
     def run_merge(self, out, lse=None, *, stream=None):
         """pkv_run_merge: merge the split tiles' partial states into out / lse."""
@@ -296,11 +304,11 @@ class Plan:
                                    None if lse is None else _dev(lse, "lse"), _stream(stream)))
 
     def run_masked(self, q, k_cache, v_cache, kv_indices, mask_packed, out, lse=None, *, layout, sm_scale=0.0,
-                   stream=None):
+                   stream=None, k_scale=1.0, v_scale=1.0):
         """pkv_run_masked: mask_packed is the device bit-packed custom mask (see ``packbits``)."""
         import torch
         p = self.params
-        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk)
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk, k_scale, v_scale)
         if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
             raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
@@ -467,11 +475,12 @@ class CascadePlan:
         _check(lib().pkv_cascade_plan_get_info(self._handle, ctypes.byref(out)))
         return out.as_dict()
 
-    def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None):
+    def run(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, layout, sm_scale=0.0, stream=None,
+            k_scale=1.0, v_scale=1.0):
         """pkv_cascade_run.  kv_indices: device int32, the levels' page ids back to back (level 0 first)."""
         import torch
         p = self.params
-        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk)
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk, k_scale, v_scale)
         if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
             raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):

@@ -17,7 +17,7 @@ META_REASONS = {
     "last_page_len": 6, "page_index": 7, "indices_length": 8, "qo_exceeds_kv": 9, "head_group": 10,
     "decode_qo_len": 11, "append_collision": 12, "cascade_rows": 13, "cascade_nesting": 14,
 }
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 NHD, HND = 0, 1
 DECODE, PREFILL, MLA_DECODE = 0, 1, 2
 KV_PAGED, KV_RAGGED = 0, 1
@@ -29,7 +29,7 @@ class CacheDesc(ctypes.Structure):
                 ("token_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
                 ("max_num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("layout", ctypes.c_int32)]
+                ("layout", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PlanParams(ctypes.Structure):

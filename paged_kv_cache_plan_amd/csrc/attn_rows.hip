@@ -36,6 +36,12 @@
 //
 // Multi-row tiles (float32 prefill) loop over their rows; row r sees key j iff
 // j <= diag + r ("Causality uses logical positions, not page numbers").
+//
+// An fp8 cache (E4M3 codes, "FlashInfer 中的 KV-Cache 布局" names fp8 caches)
+// is read at one byte per element: a 16-byte load holds 16 codes, which
+// v_cvt_scalef32_pk_bf16_fp8 expands (exactly) into two bf16 chunks, so the
+// arithmetic is the bf16 path's.  The per-tensor K scale is folded into the
+// logit scale and the V scale is applied to the normalised output.
 
 #include "device.h"
 #include "internal.h"
@@ -131,13 +137,32 @@ constexpr int rows_min_waves() {
   return int(sizeof(T)) * D * G >= 2048 ? 1 : PKV_ROWS_MIN_WAVES;
 }
 
-template <typename T, int D, int G, bool kAligned, bool kMask>
+// 16 fp8 codes -> two chunks of 8 bf16 values (exact conversion).
+__device__ __forceinline__ void expand_fp8(const uint4& raw, uint4& lo, uint4& hi) {
+  auto cv0 = [](uint32_t w) {   // codes in bytes 0, 1
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  };
+  auto cv1 = [](uint32_t w) {   // codes in bytes 2, 3
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  };
+  lo = make_uint4(cv0(raw.x), cv1(raw.x), cv0(raw.y), cv1(raw.y));
+  hi = make_uint4(cv0(raw.z), cv1(raw.z), cv0(raw.w), cv1(raw.w));
+}
+
+// T: query / output elements (bf16 bits or float).  TK: stored K/V elements
+// (T itself, or uint8_t E4M3 codes with T = bf16).
+template <typename T, typename TK, int D, int G, bool kAligned, bool kMask>
 __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
-  constexpr int E = Elem<T>::kPer16;       // elements per 16-byte chunk
-  constexpr int NCH = D / E;               // chunks per key row
+  constexpr bool kFp8 = sizeof(TK) == 1;
+  static_assert(!kFp8 || kBF16, "fp8 caches compute on the bf16 path");
+  constexpr int E = Elem<T>::kPer16;       // elements per (expanded) 16-byte chunk
+  constexpr int RE = 16 / int(sizeof(TK)); // elements per 16-byte load of K or V
+  constexpr int X = RE / E;                // expanded chunks per load (2 for fp8)
+  constexpr int NCH = D / RE;              // loads per key row
   constexpr int VL = NCH < kRowLanes ? NCH : kRowLanes;  // lanes per key row = one softmax group
-  constexpr int VC = NCH / VL;             // chunks per lane
+  constexpr int VCR = NCH / VL;            // loads per lane and key row
+  constexpr int VC = VCR * X;              // expanded chunks per lane
   constexpr int VT = 64 / VL;              // key rows per load instruction = groups per wave
   constexpr int NU = kBlockKeys / VT;      // load instructions per block = keys per group per block
   static_assert(NCH % VL == 0 && (VL == 16 || VL == 8), "unsupported head_dim");
@@ -160,8 +185,10 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   // lane vi of the group holds chunks vi + VL * c of those rows.
   const int vg = lane / VL, vi = lane % VL;
 
-  const T* kbase = static_cast<const T*>(a.k) + int64_t(kvh) * a.head_stride;
-  const T* vbase = static_cast<const T*>(a.v) + int64_t(kvh) * a.head_stride;
+  const TK* kbase = static_cast<const TK*>(a.k) + int64_t(kvh) * a.head_stride;
+  const TK* vbase = static_cast<const TK*>(a.v) + int64_t(kvh) * a.head_stride;
+  // Expanded chunk c = X * cr + x of lane vi covers dims dim_of(c) + [0, E).
+  auto dim_of = [&](int c) { return (vi + VL * (c / X)) * RE + (c % X) * E; };
   const int32_t* pages = a.kv_indices + it.page_base;
   const int32_t hq = a.num_qo_heads;
   const int32_t psz = a.page_size, pshift = a.page_shift;
@@ -188,7 +215,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int c = 0; c < VC; ++c)
-        qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + int64_t(h) * a.q_stride_head + (vi + VL * c) * E);
+        qreg[h][c] = *reinterpret_cast<const uint4*>(qrow + int64_t(h) * a.q_stride_head + dim_of(c));
 
     float m[G], l[G], acc[G][VC * E];
 #pragma unroll
@@ -220,7 +247,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       };
       // K and V rows of one block: instruction u moves key rows u*VT + g, each
       // read by VL lanes as contiguous 16-byte chunks (whole rows per request).
-      auto load = [&](int32_t blk, uint4 (&kr)[NU][VC], uint4 (&vr)[NU][VC]) {
+      auto load = [&](int32_t blk, uint4 (&kr)[NU][VCR], uint4 (&vr)[NU][VCR]) {
         int64_t off[NU];
         if constexpr (kAligned) {
           // A 16-key block never crosses a page: one page id for the block.
@@ -236,14 +263,28 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-          for (int c = 0; c < VC; ++c) kr[u][c] = dev::load16<kStreamKV>(kbase + off[u] + (vi + VL * c) * E);
+          for (int c = 0; c < VCR; ++c) kr[u][c] = dev::load16<kStreamKV>(kbase + off[u] + (vi + VL * c) * RE);
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-          for (int c = 0; c < VC; ++c) vr[u][c] = dev::load16<kStreamKV>(vbase + off[u] + (vi + VL * c) * E);
+          for (int c = 0; c < VCR; ++c) vr[u][c] = dev::load16<kStreamKV>(vbase + off[u] + (vi + VL * c) * RE);
       };
 
-      auto compute = [&](int32_t blk, uint4 (&kr)[NU][VC], uint4 (&vr)[NU][VC]) {
+      auto compute = [&](int32_t blk, uint4 (&kraw)[NU][VCR], uint4 (&vraw)[NU][VCR]) {
+        // K and V rows as bf16 / f32 chunks (fp8 codes expanded in registers).
+        uint4 kr[NU][VC], vr[NU][VC];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int c = 0; c < VCR; ++c) {
+            if constexpr (kFp8) {
+              expand_fp8(kraw[u][c], kr[u][2 * c], kr[u][2 * c + 1]);
+              expand_fp8(vraw[u][c], vr[u][2 * c], vr[u][2 * c + 1]);
+            } else {
+              kr[u][c] = kraw[u][c];
+              vr[u][c] = vraw[u][c];
+            }
+          }
         // Scores of the group's NU keys for the G heads; every lane of the
         // group ends with all of them, so the softmax below is in-lane.
         float p[NU][G];
@@ -335,7 +376,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       const int32_t blk_max = kAligned ? ((thi - 1) & ~(kBlockKeys - 1)) : thi - 1;
       int32_t blk = tlo + wave * kBlockKeys;
       if constexpr (kDepth == 3) {
-        uint4 ka[NU][VC], kb[NU][VC], kc[NU][VC], va[NU][VC], vb[NU][VC], vc[NU][VC];
+        uint4 ka[NU][VCR], kb[NU][VCR], kc[NU][VCR], va[NU][VCR], vb[NU][VCR], vc[NU][VCR];
         if (blk < thi) {
           load(blk, ka, va);
           load(min(blk + kStride, blk_max), kb, vb);
@@ -355,7 +396,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           }
         }
       } else {
-        uint4 ka[NU][VC], kb[NU][VC], va[NU][VC], vb[NU][VC];
+        uint4 ka[NU][VCR], kb[NU][VCR], va[NU][VCR], vb[NU][VCR];
         if (blk < thi) {
           load(blk, ka, va);
           while (true) {
@@ -399,7 +440,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
 #pragma unroll
         for (int c = 0; c < VC; ++c)
 #pragma unroll
-          for (int e = 0; e < E; ++e) s_acc[wave][h][(vi + VL * c) * E + e] = acc[h][c * E + e];
+          for (int e = 0; e < E; ++e) s_acc[wave][h][dim_of(c) + e] = acc[h][c * E + e];
     }
     if (lane == 0) {
 #pragma unroll
@@ -424,7 +465,8 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         oo += f * s_acc[w][h][d];
       }
       const bool empty = !(ll > 0.f);
-      const float out = empty ? 0.f : oo / ll;
+      float out = empty ? 0.f : oo / ll;
+      if constexpr (kFp8) out *= a.v_scale;
       const float lse2 = empty ? -INFINITY : mm + __log2f(ll);
       const int32_t head = kvh * G + h;
       if (it.out_slot < 0) {
@@ -441,7 +483,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, typename TK, int D, int G>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -449,27 +491,27 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
   if (a.mask) {
     if (aligned)
-      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, true, true>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false, true>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, false, true>), grid, block, 0, st, a);
   } else {
     if (aligned)
-      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, true, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, true, false>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((attn_rows_kernel<T, D, G, false, false>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, false, false>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename TK, int D>
 hipError_t launch_g(int32_t group, const AttnArgs& a, hipStream_t st, bool* ok) {
   *ok = true;
   switch (group) {
-    case 1: return launch_t<T, D, 1>(a, st);
-    case 2: return launch_t<T, D, 2>(a, st);
-    case 4: return launch_t<T, D, 4>(a, st);
+    case 1: return launch_t<T, TK, D, 1>(a, st);
+    case 2: return launch_t<T, TK, D, 2>(a, st);
+    case 4: return launch_t<T, TK, D, 4>(a, st);
     case 8:
-      if (sizeof(T) == 2) return launch_t<T, D, 8>(a, st);
+      if (sizeof(T) == 2) return launch_t<T, TK, D, 8>(a, st);
       break;
     default: break;
   }
@@ -483,11 +525,13 @@ hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, cons
                             hipStream_t st, bool* supported) {
   *supported = false;
   if (dtype == kBF16) {
-    if (head_dim == 128) return launch_g<uint16_t, 128>(group, a, st, supported);
-    if (head_dim == 64) return launch_g<uint16_t, 64>(group, a, st, supported);
+    if (head_dim == 128) return launch_g<uint16_t, uint16_t, 128>(group, a, st, supported);
+    if (head_dim == 64) return launch_g<uint16_t, uint16_t, 64>(group, a, st, supported);
   } else if (dtype == kF32) {
-    if (head_dim == 128) return launch_g<float, 128>(group, a, st, supported);
-    if (head_dim == 64) return launch_g<float, 64>(group, a, st, supported);
+    if (head_dim == 128) return launch_g<float, float, 128>(group, a, st, supported);
+    if (head_dim == 64) return launch_g<float, float, 64>(group, a, st, supported);
+  } else if (dtype == kFP8) {   // bf16 queries over an E4M3 cache
+    if (head_dim == 128) return launch_g<uint16_t, uint8_t, 128>(group, a, st, supported);
   }
   return hipSuccess;
 }

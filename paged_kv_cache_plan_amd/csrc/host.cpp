@@ -68,7 +68,7 @@ int page_shift_of(int32_t p) {
   return s;
 }
 
-size_t dtype_size(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
+size_t dtype_size(int32_t dt) { return dt == PKV_F32 ? 4 : (dt == PKV_FP8_E4M3 ? 1 : 2); }
 
 // ------------------------------------------------------------- validation --
 
@@ -150,7 +150,7 @@ constexpr int32_t kCascadeTargetPerCu = 1;
 constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
-  if (mode != PKV_MODE_PREFILL || kv_dtype == PKV_F32 || mask_mode == PKV_MASK_CUSTOM) return 1;
+  if (mode != PKV_MODE_PREFILL || kv_dtype != PKV_BF16 || mask_mode == PKV_MASK_CUSTOM) return 1;
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
 
@@ -207,10 +207,12 @@ pkv_status check_params(const pkv_plan_params* p) {
   if (!p) return fail(PKV_ERR_INVALID_ARG, "null params");
   if (p->mode < PKV_MODE_DECODE || p->mode > PKV_MODE_MLA_DECODE)
     return fail(PKV_ERR_INVALID_ARG, fmt("unknown mode %lld", p->mode));
-  if (p->q_dtype != p->kv_dtype)
-    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must equal kv_dtype");
-  if (p->kv_dtype != PKV_F32 && p->kv_dtype != PKV_BF16)
+  const bool fp8 = p->kv_dtype == PKV_FP8_E4M3;
+  if (fp8 ? p->q_dtype != PKV_BF16 : p->q_dtype != p->kv_dtype)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must equal kv_dtype (bf16 queries over an fp8 cache)");
+  if (p->kv_dtype != PKV_F32 && p->kv_dtype != PKV_BF16 && !fp8)
     return fail(PKV_ERR_UNSUPPORTED, fmt("dtype %lld", p->kv_dtype));
+  if (fp8 && p->mode == PKV_MODE_MLA_DECODE) return fail(PKV_ERR_UNSUPPORTED, "MLA runs on bf16 caches");
   if (p->head_dim_qk < 1 || p->head_dim_vo < 1) return fail(PKV_ERR_INVALID_ARG, "head dims must be >= 1");
   if (p->mode == PKV_MODE_MLA_DECODE) {
     if (p->num_kv_heads != 1 || p->head_dim_qk != 576 || p->head_dim_vo != 512 || p->kv_dtype != PKV_BF16)
@@ -807,15 +809,15 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
     return fail(PKV_ERR_INVALID_ARG, "cache descriptor does not match the plan");
   if (p.max_num_pages > 0 && cache->max_num_pages != p.max_num_pages)
     return fail(PKV_ERR_INVALID_ARG, "cache page count does not match the plan");
-  const size_t es = dtype_size(p.kv_dtype);
+  const size_t es = dtype_size(p.q_dtype), es_kv = dtype_size(p.kv_dtype);
   pkv_status s;
   if ((s = check_ptr16(q, "q")) || (s = check_ptr16(o, "o")) || (s = check_ptr16(cache->k, "cache k")) ||
       (s = check_ptr16(cache->v, "cache v")))
     return s;
   if (!d_kv_indices && has_items) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
   if (!stride_ok(q_stride_token, es) || !stride_ok(q_stride_head, es) || !stride_ok(o_stride_token, es) ||
-      !stride_ok(o_stride_head, es) || !stride_ok(cache->page_stride, es) ||
-      !stride_ok(cache->token_stride, es) || !stride_ok(cache->head_stride, es))
+      !stride_ok(o_stride_head, es) || !stride_ok(cache->page_stride, es_kv) ||
+      !stride_ok(cache->token_stride, es_kv) || !stride_ok(cache->head_stride, es_kv))
     return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev != plan_device)
@@ -847,6 +849,11 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
   a->mask_rows = nullptr;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(p.head_dim_qk));
   a->scale_log2 = scale * 1.4426950408889634f;
+  a->v_scale = 1.f;
+  if (p.kv_dtype == PKV_FP8_E4M3) {   // the key scale multiplies every logit
+    if (cache->k_scale > 0.f) a->scale_log2 *= cache->k_scale;
+    if (cache->v_scale > 0.f) a->v_scale = cache->v_scale;
+  }
   return PKV_OK;
 }
 
@@ -901,7 +908,7 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, 
   if (!plan) return fail(PKV_ERR_INVALID_ARG, "null plan");
   if (plan->grid_merges() == 0) return ok();
   const pkv_plan_params& p = plan->params;
-  const size_t es = dtype_size(p.kv_dtype);
+  const size_t es = dtype_size(p.q_dtype);
   pkv_status s = check_ptr16(o, "o");
   if (s) return s;
   if (!stride_ok(o_stride_token, es) || !stride_ok(o_stride_head, es))
@@ -919,7 +926,7 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, 
   m.o_stride_token = o_stride_token;
   m.o_stride_head = o_stride_head;
   m.lse = lse;
-  hipError_t e = pkv::launch_merge_partials(p.kv_dtype, m, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_merge_partials(p.q_dtype, m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching the split merge");
   return ok();
 }
@@ -1104,7 +1111,7 @@ pkv_status pkv_append_paged_kv(const void* k_new, const void* v_new, int64_t new
   if (!cache) return fail(PKV_ERR_INVALID_ARG, "null cache");
   if (batch_size < 0 || nnz < 0) return fail(PKV_ERR_INVALID_ARG, "negative batch or nnz");
   if (nnz == 0) return ok();
-  if (cache->dtype != PKV_F32 && cache->dtype != PKV_BF16)
+  if (cache->dtype != PKV_F32 && cache->dtype != PKV_BF16 && cache->dtype != PKV_FP8_E4M3)
     return fail(PKV_ERR_UNSUPPORTED, "cache dtype");
   if (cache->page_size < 1 || cache->num_kv_heads < 1 || cache->head_dim < 1)
     return fail(PKV_ERR_INVALID_ARG, "cache shape");
@@ -1461,7 +1468,7 @@ pkv_status pkv_cascade_run(const pkv_cascade_plan* plan, const void* q, int64_t 
     m.o_stride_token = o_stride_token;
     m.o_stride_head = o_stride_head;
     m.lse = lse;
-    hipError_t e = pkv::launch_merge_rows(p.kv_dtype, m, st);
+    hipError_t e = pkv::launch_merge_rows(p.q_dtype, m, st);
     if (e != hipSuccess) return hip_fail(e, "launching the cascade merge");
   }
   return ok();

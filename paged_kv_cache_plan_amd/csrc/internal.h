@@ -32,7 +32,7 @@ struct MergeItem {
 };
 static_assert(sizeof(MergeItem) == 16, "merge item is four int32");
 
-enum DType : int32_t { kF32 = 0, kBF16 = 1 };
+enum DType : int32_t { kF32 = 0, kBF16 = 1, kFP8 = 2 };   // kFP8: E4M3 codes (K/V storage only)
 
 // Custom mask of one request: bit (q_start + i, j) of the packed mask is
 // bit0 + i * kv_len + j.
@@ -66,6 +66,7 @@ struct AttnArgs {
   float scale_log2;    // sm_scale * log2(e)
   const uint32_t* mask;        // packed custom mask (little-endian bits), or null
   const MaskRow* mask_rows;    // per request, when mask is set
+  float v_scale;               // fp8 caches: factor applied to the normalised output
 };
 
 struct MergePartialArgs {

@@ -429,7 +429,7 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
                          const int32_t* last_page_len, int32_t batch, int32_t nnz, void* k, void* v,
                          int64_t page_stride, int64_t token_stride, int64_t head_stride, int32_t page_size,
                          int32_t num_heads, int32_t head_dim, int32_t max_num_pages, hipStream_t st) {
-  const int64_t es = dtype == kF32 ? 4 : 2;
+  const int64_t es = dtype == kF32 ? 4 : (dtype == kFP8 ? 1 : 2);
   const int32_t row_chunks = int32_t(head_dim * es / 16);
   hipLaunchKernelGGL(append_kernel, dim3(uint32_t(nnz)), dim3(256), 0, st, static_cast<const char*>(k_new),
                      static_cast<const char*>(v_new), new_st * es, new_sh * es, append_indptr, kv_indptr, kv_indices,

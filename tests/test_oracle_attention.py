@@ -226,3 +226,33 @@ def test_mla_decode_is_sdpa_with_concatenated_keys():
         assert np.allclose(o[b], ref[0, :, 0].numpy(), atol=1e-12)
         s = (q[0, :, 0] @ k[0, 0].T) * scale
         assert np.allclose(lse[b], (torch.logsumexp(s, dim=-1) / math.log(2)).numpy(), atol=1e-12)
+
+
+# ------------------------------------------------------------ fp8 storage --
+
+def test_fp8_e4m3_decoding_matches_torch_for_every_code():
+    """All 256 E4M3 codes against torch's float8_e4m3fn (an independent
+    implementation of the same OCP format), NaN codes included."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = at.upcast(codes, "fp8")
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    # a few hand values: 1.0, -2.0, the largest finite, the smallest subnormal
+    assert at.fp8_e4m3_value(0x38) == 1.0 and at.fp8_e4m3_value(0xC0) == -2.0
+    assert at.fp8_e4m3_value(0x7E) == 448.0 and at.fp8_e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_fp8_scales_fold_into_scores_and_outputs():
+    """k_scale multiplies every score (same as scaling sm_scale) and v_scale
+    every output; the LSE shifts only through the scores."""
+    rng = np.random.default_rng(9)
+    c = _random_paged(rng, [2, 3], [9, 14], 4, 4, 2, 16)
+    codes_k = rng.integers(0, 0x77, size=c["k"].shape).astype(np.uint8)
+    codes_v = rng.integers(0, 0x77, size=c["v"].shape).astype(np.uint8)
+    codes_k[rng.random(codes_k.shape) < 0.5] |= 0x80
+    kw = dict(qo_indptr=c["qo_indptr"], kv_indptr=c["kv_indptr"], kv_indices=c["kv_indices"],
+              kv_last_page_len=c["last"], page_size=4, layout="NHD", num_kv_heads=2, kv_dtype="fp8")
+    o1, l1 = at.paged_attention(c["q"], codes_k, codes_v, sm_scale=0.1, k_scale=0.5, v_scale=3.0, **kw)
+    o2, l2 = at.paged_attention(c["q"], codes_k, codes_v, sm_scale=0.05, **kw)
+    assert np.max(np.abs(o1 - 3.0 * o2)) < 1e-12 and np.max(np.abs(l1 - l2)) < 1e-12

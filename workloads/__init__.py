@@ -48,6 +48,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)        # E4M3: exponent and mantissa all ones
 
 WORKLOADS = ("worked", "decode", "skewed", "prefill", "mla", "cascade", "cascade_small")
 SEEDS = {"worked": 1000, "decode": 1001, "skewed": 1002, "prefill": 1003, "mla": 1004, "cascade": 1005,
@@ -61,15 +62,29 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
+def to_fp8_codes(x: np.ndarray) -> np.ndarray:
+    """Round float32 to E4M3 (nearest, ties to even, saturating at 448, as
+    torch's float8_e4m3fn conversion does); return the 8-bit codes."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def _payload(rng, shape, dtype: str):
     x = rng.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "fp8":
+        return to_fp8_codes(x)
     return to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _storage(dtype: str):
+    return {"bf16": np.uint16, "fp8": np.uint8}.get(dtype, np.float32)
 
 
 def _pool(rng, shape, dtype: str, owned_pages):
     """A page pool whose owned pages (in ascending page id) get fresh N(0, 1)
     draws; pages nobody owns stay zero (or NaN once poisoned)."""
-    pool = np.zeros(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    pool = np.zeros(shape, dtype=_storage(dtype))
     pages = np.unique(np.asarray(owned_pages, dtype=np.int64))
     step = 2048
     for i in range(0, len(pages), step):
@@ -83,7 +98,7 @@ class Batch:
     """One synthetic batch.  Arrays are numpy; metadata is int32."""
     name: str
     mode: str                      # "decode" | "prefill" | "mla"
-    dtype: str                     # "f32" | "bf16" (payload storage)
+    dtype: str                     # "f32" | "bf16": queries and outputs (and K/V unless kv_dtype says)
     layout: str                    # "NHD" | "HND" (ignored for mla)
     page_size: int
     num_qo_heads: int
@@ -106,6 +121,11 @@ class Batch:
     v_new: np.ndarray = None
     append_indptr: np.ndarray = None
     extra: dict = field(default_factory=dict)
+    kv_dtype: str = None           # K/V storage when it differs from dtype ("fp8": E4M3 codes)
+
+    def __post_init__(self):
+        if self.kv_dtype is None:
+            self.kv_dtype = self.dtype
 
     @property
     def batch_size(self) -> int:
@@ -136,7 +156,7 @@ def _poison(cache, layout, used_slots, dtype):
     keep = np.zeros((pages, page_size), dtype=bool)
     if len(used_slots):
         keep[used_slots[:, 0], used_slots[:, 1]] = True
-    nan = BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    nan = {"bf16": BF16_NAN, "fp8": FP8_NAN}.get(dtype, np.float32(np.nan))
     if layout == "NHD":
         cache[~keep] = nan
     else:
@@ -150,19 +170,20 @@ def _slots(kv_indptr, kv_indices, page_size, b, lo, hi):
 
 
 def _gqa_batch(name, rng, *, mode, qo_lens, kv_lens, page_size, pool, pages_for_request, hq, hkv,
-               dim, dtype, layout, causal, sm_scale, with_append, poison):
+               dim, dtype, layout, causal, sm_scale, with_append, poison, kv_dtype=None):
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     n_pages, kv_indptr, kv_indices, last = _csr(kv_lens, page_size, pages_for_request)
     qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int32)
     qo_indptr[1:] = np.cumsum(qo_lens)
     nnz = int(qo_indptr[-1])
     q = _payload(rng, (nnz, hq, dim), dtype)
     shape = _cache_shape(layout, pool, page_size, hkv, dim)
-    k_cache = _pool(rng, shape, dtype, kv_indices)
-    v_cache = _pool(rng, shape, dtype, kv_indices)
+    k_cache = _pool(rng, shape, kv_dtype, kv_indices)
+    v_cache = _pool(rng, shape, kv_dtype, kv_indices)
     k_new = v_new = append_indptr = None
     if with_append:
-        k_new = _payload(rng, (nnz, hkv, dim), dtype)
-        v_new = _payload(rng, (nnz, hkv, dim), dtype)
+        k_new = _payload(rng, (nnz, hkv, dim), kv_dtype)
+        v_new = _payload(rng, (nnz, hkv, dim), kv_dtype)
         append_indptr = qo_indptr.copy()
     if poison:
         # Slots holding cached history keep their values; everything else
@@ -170,9 +191,9 @@ def _gqa_batch(name, rng, *, mode, qo_lens, kv_lens, page_size, pool, pages_for_
         hist = [_slots(kv_indptr, kv_indices, page_size, b, 0,
                        kv_lens[b] - (qo_lens[b] if with_append else 0)) for b in range(len(kv_lens))]
         used = np.concatenate(hist) if hist else np.zeros((0, 2), np.int64)
-        _poison(k_cache, layout, used, dtype)
-        _poison(v_cache, layout, used, dtype)
-    return Batch(name=name, mode=mode, dtype=dtype, layout=layout, page_size=page_size,
+        _poison(k_cache, layout, used, kv_dtype)
+        _poison(v_cache, layout, used, kv_dtype)
+    return Batch(name=name, mode=mode, dtype=dtype, kv_dtype=kv_dtype, layout=layout, page_size=page_size,
                  num_qo_heads=hq, num_kv_heads=hkv, head_dim=dim, causal=causal, sm_scale=sm_scale,
                  qo_lens=list(qo_lens), kv_lens=list(kv_lens), qo_indptr=qo_indptr,
                  kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
@@ -229,7 +250,7 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                           hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=o.get("dim", 128),
                           dtype=o.get("dtype", "bf16"), layout=layout, causal=True,
                           sm_scale=o.get("sm_scale", 1.0 / math.sqrt(o.get("dim", 128))),
-                          with_append=o.get("with_append", False), poison=poison)
+                          with_append=o.get("with_append", False), poison=poison, kv_dtype=o.get("kv_dtype"))
     if name == "prefill":
         batch = o.get("batch", 8)
         qlo, qhi = o.get("qo_range", (max(1, int(512 * scale)), max(1, int(2048 * scale))))
@@ -249,7 +270,7 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                           hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=dim,
                           dtype=o.get("dtype", "bf16"), layout=o.get("layout", "HND"),
                           causal=o.get("causal", True), sm_scale=o.get("sm_scale", 1.0 / math.sqrt(dim)),
-                          with_append=True, poison=poison)
+                          with_append=True, poison=poison, kv_dtype=o.get("kv_dtype"))
     if name == "mla":
         batch = o.get("batch", max(1, int(round(32 * scale))))
         lo, hi = o.get("kv_range", (max(1, int(1024 * scale)), max(1, int(8192 * scale))))
