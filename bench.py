@@ -58,12 +58,13 @@ def decode_bytes(b) -> dict:
     per kv head, Q read, O and LSE written, page ids read; append reads and
     writes the new rows."""
     es = 2 if b.dtype == "bf16" else 4
-    kv = sum(b.kv_lens) * b.num_kv_heads * b.head_dim * 2 * es
+    es_kv = {"bf16": 2, "fp8": 1}.get(b.kv_dtype, 4)
+    kv = sum(b.kv_lens) * b.num_kv_heads * b.head_dim * 2 * es_kv
     q = b.nnz * b.num_qo_heads * b.head_dim * es
     o = q
     lse = b.nnz * b.num_qo_heads * 4
     idx = int(b.kv_indptr[-1]) * 4
-    append = 0 if b.k_new is None else 2 * 2 * b.k_new.size * es
+    append = 0 if b.k_new is None else 2 * 2 * b.k_new.size * es_kv
     return {"kv": kv, "attn": kv + q + o + lse + idx, "append": append, "layer": kv + q + o + lse + idx + append}
 
 
@@ -117,6 +118,7 @@ class Runner:
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
+        kv_bf = b.kv_dtype == "bf16"   # fp8 caches stay uint8 codes
         self.q = dev(b.q, bf)
         self.kv_indices = dev(b.kv_indices, False)
         if b.mode == "mla":
@@ -126,19 +128,20 @@ class Runner:
             self.out = torch.empty((b.batch_size, 128, 512), dtype=torch.bfloat16, device="cuda")
             self.lse = torch.empty((b.batch_size, 128), dtype=torch.float32, device="cuda")
         else:
-            k0, v0 = dev(b.k_cache, bf), dev(b.v_cache, bf)
+            k0, v0 = dev(b.k_cache, kv_bf), dev(b.v_cache, kv_bf)
             self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(layers - 1)]
             self.out = torch.empty_like(self.q)
             self.lse = torch.empty((b.nnz, b.num_qo_heads), dtype=torch.float32, device="cuda")
             if b.k_new is not None:
-                self.k_new, self.v_new = dev(b.k_new, bf), dev(b.v_new, bf)
+                self.k_new, self.v_new = dev(b.k_new, kv_bf), dev(b.v_new, kv_bf)
                 self.append_indptr = dev(b.append_indptr, False)
                 self.kv_indptr_d = dev(b.kv_indptr, False)
                 self.last_d = dev(b.kv_last_page_len, False)
         self.params = pkv.plan_params(
             mode=b.mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
             head_dim_qk=576 if b.mode == "mla" else b.head_dim, head_dim_vo=512 if b.mode == "mla" else b.head_dim,
-            page_size=b.page_size, causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages)
+            page_size=b.page_size, causal=b.causal, dtype=b.dtype, max_num_pages=b.max_num_pages,
+            kv_dtype=b.kv_dtype)
         info, _, _ = pkv.plan_compute(self.params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None,
                                       kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
                                       kv_last_page_len=b.kv_last_page_len)
@@ -293,7 +296,7 @@ def cpu_baseline(b, budget_s: float = 12.0) -> dict:
 
 
 COUNTER_KERNELS = {"decode": "attn_rows_kernel", "skewed": "attn_rows_kernel", "prefill": "prefill_mfma_kernel",
-                   "mla": "mla_decode_kernel", "cascade": "prefill_mfma_kernel"}
+                   "mla": "mla_decode_kernel", "cascade": "prefill_mfma_kernel", "fp8": "attn_rows_kernel"}
 
 
 def ingest_counters(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
@@ -362,7 +365,7 @@ def main():
     ap.add_argument("--secondary-layers", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla", "cascade"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla", "cascade", "fp8"], default=None,
                     help="time one workload (profiling runs)")
     ap.add_argument("--cascade-target", type=int, default=0,
                     help="planner target items per CU for every cascade level (0: the per-mode default)")
@@ -407,7 +410,7 @@ def main():
 
     result = {}
     which = [args.only] if args.only else ["decode"] + ([] if args.no_secondary else
-                                                        ["prefill", "skewed", "mla", "cascade"])
+                                                        ["prefill", "skewed", "mla", "cascade", "fp8"])
 
     if "decode" in which:
         b = wl.make("decode", with_append=True)
@@ -453,6 +456,18 @@ def main():
             f"({m['attn_ms_mean'] * 1e3:.1f} us)")
         del r
 
+    if "fp8" in which:
+        # The headline decode batch over an E4M3 cache (one byte per element).
+        b = wl.make("decode", with_append=True, kv_dtype="fp8")
+        layers = args.layers
+        r = Runner(b, layers)
+        m = measure(r, layers, args.steps, args.warmup)
+        nb = decode_bytes(b)
+        result["fp8"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
+                             step_gbs=nb["layer"] * layers / (m["ms_per_step"] * 1e-3) / 1e9)
+        log(f"fp8: attention {result['fp8']['gbs']:.1f} GB/s ({m['attn_ms_mean'] * 1e3:.1f} us), "
+            f"step {result['fp8']['step_gbs']:.1f} GB/s")
+        del r
     if "cascade" in which:
         b = wl.make("cascade")
         layers = args.secondary_layers
@@ -523,6 +538,12 @@ def main():
         line["mla_decode"] = {"value": round(mm["gbs"], 1), "unit": "GB/s", "frac": round(mm["gbs"] / HBM_PEAK_GBS, 4),
                               "tflops": round(mm["tflops"], 2), "run_us_mean": round(mm["attn_ms_mean"] * 1e3, 2),
                               "timed": "attention + merge"}
+    if "fp8" in result:
+        f = result["fp8"]
+        line["fp8_decode"] = {"value": round(f["gbs"], 1), "unit": "GB/s", "frac": round(f["gbs"] / HBM_PEAK_GBS, 4),
+                              "launch_us_mean": round(f["attn_ms_mean"] * 1e3, 2),
+                              "bytes_per_launch": f["bytes"]["attn"],
+                              "workload": "the decode batch with an E4M3 K/V cache (bf16 queries and outputs)"}
     if "cascade" in result:
         c = result["cascade"]
         run_s = c["attn_ms_mean"] * 1e-3
