@@ -531,9 +531,12 @@ pkv_status pkv_cascade_plan_destroy(pkv_cascade_plan* plan);
  * and bit-packed little-endian: element e is bit e % 8 of byte e / 8 (numpy
  * packbits order, which is what pkv_packbits writes).  Row i of request b
  * sees key j iff its element is 1; a row that sees no key gets (0, -inf).
- *   d_mask  device, at least ceil(info.mask_bits / 32) * 4 bytes (read in
- *           aligned 32-bit words)
- * Custom-masked plans run one query row per work item on the row kernel.
+ *   d_mask  device, 16-byte aligned, at least ceil(info.mask_bits / 8) + 32
+ *           bytes (the kernels read aligned words and 32-byte row windows
+ *           that may run past the last mask bit)
+ * bf16 plans with head_dim 128 and at least 2 query heads per kv head run
+ * the MFMA tile kernel (each tile's mask bits move into LDS with its keys);
+ * the others run one query row per work item on the row kernel.
  */
 pkv_status pkv_run_masked(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
                           const pkv_cache_desc* cache, const int32_t* d_kv_indices, const uint8_t* d_mask,
@@ -561,7 +564,8 @@ pkv_status pkv_run_ragged(const pkv_plan* plan, const void* q, int64_t q_stride_
 /*
  * Pack n device bytes (0 = false, anything else = true) into the
  * little-endian bit layout above: d_packed receives ceil(n / 32) 32-bit words
- * (ceil(n/32)*4 bytes; bits past n are 0).  Asynchronous on `stream`.
+ * (ceil(n/32)*4 bytes; bits past n are 0; allocate the 32 extra bytes that
+ * pkv_run_masked reads and zero them).  Asynchronous on `stream`.
  */
 pkv_status pkv_packbits(const uint8_t* d_bool, int64_t n, uint8_t* d_packed, void* stream);
 

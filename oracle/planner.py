@@ -50,9 +50,10 @@ RAGGED_PAGE = 16                # ragged keys are chunked as if in pages of this
 
 def rows_per_tile(mode: str, group: int, kv_dtype: str, masked: bool = False) -> int:
     """Query rows per work item: 1 for decode, MLA, float32 or fp8-cache
-    prefill and custom-masked prefill; for bfloat16 prefill as many rows as
-    fit a 256-high tile of (row, head) pairs."""
-    if mode != PREFILL or kv_dtype != "bf16" or masked:
+    prefill and custom-masked prefill with one query head per kv head; for
+    bfloat16 prefill as many rows as fit a 256-high tile of (row, head)
+    pairs."""
+    if mode != PREFILL or kv_dtype != "bf16" or (masked and group < 2):
         return 1
     return max(1, MFMA_TILE_ROWS // group)
 

@@ -517,7 +517,8 @@ def append_paged_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, kv_last_
 
 def packbits(mask_bool, stream=None):
     """pkv_packbits: a device bool/uint8 tensor -> device uint8 tensor of
-    ceil(n / 32) * 4 bytes, element e at bit e % 8 of byte e // 8."""
+    ceil(n / 32) * 4 + 32 bytes (the tail zeroed; the masked kernels read up
+    to 32 bytes past the last mask byte), element e at bit e % 8 of byte e // 8."""
     import torch
     m = mask_bool.contiguous()
     if m.dtype == torch.bool:
@@ -525,7 +526,7 @@ def packbits(mask_bool, stream=None):
     if m.dtype != torch.uint8:
         raise TypeError("mask must be bool or uint8")
     n = m.numel()
-    out = torch.zeros(max(4, (n + 31) // 32 * 4), dtype=torch.uint8, device=m.device)
+    out = torch.zeros((n + 31) // 32 * 4 + 32, dtype=torch.uint8, device=m.device)
     _check(lib().pkv_packbits(_dev(m, "mask"), n, _dev(out, "packed"), _stream(stream)))
     return out
 

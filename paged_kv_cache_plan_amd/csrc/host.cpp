@@ -150,7 +150,8 @@ constexpr int32_t kCascadeTargetPerCu = 1;
 constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
-  if (mode != PKV_MODE_PREFILL || kv_dtype != PKV_BF16 || mask_mode == PKV_MASK_CUSTOM) return 1;
+  if (mode != PKV_MODE_PREFILL || kv_dtype != PKV_BF16) return 1;
+  if (mask_mode == PKV_MASK_CUSTOM && group < 2) return 1;   // masked tiles need a head group of 2+
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
 
@@ -863,7 +864,7 @@ pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::A
   const int32_t group = p.num_qo_heads / p.num_kv_heads;
   bool supported = false;
   hipError_t e;
-  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16 && !a.mask)
+  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
     e = pkv::launch_prefill_mfma(p.head_dim_qk, group, a, st, &supported);
   else
     e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
@@ -968,7 +969,7 @@ pkv_status check_mask_arg(const pkv_plan* plan, const uint8_t* d_mask, pkv::Attn
     return PKV_OK;
   }
   if (!d_mask && plan->grid_items() > 0) return fail(PKV_ERR_INVALID_ARG, "null custom mask");
-  if (reinterpret_cast<uintptr_t>(d_mask) % 4 != 0) return fail(PKV_ERR_INVALID_ARG, "mask must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(d_mask) % 16 != 0) return fail(PKV_ERR_INVALID_ARG, "mask must be 16-byte aligned");
   a->mask = reinterpret_cast<const uint32_t*>(d_mask);
   a->mask_rows = plan->d_mask_rows;
   return PKV_OK;

@@ -42,6 +42,14 @@
 //
 // The epilogue writes the normalised rows (bf16) and base-2 LSE, or fp32
 // partial states for the split merge ("A worked split-KV example").
+//
+// Custom masks ("FlashInfer 中的 KV-Cache 布局", "掩码布局"): the kMask
+// variant moves, with every K tile, the tile's mask bits of each of its rows
+// into LDS by the same direct loads: 32 bytes per row, read from the 16-byte
+// boundary at or below the row's first key bit, which covers the 64 bits of
+// the tile.  The first waves issue these loads (one more per tile step, and a
+// correspondingly larger wait count at their barriers); every lane then reads
+// its row's 64 bits with a funnel shift and keeps the scores whose bit is 1.
 
 #include "device.h"
 #include "internal.h"
@@ -98,6 +106,12 @@ __device__ __forceinline__ void dma16(const void* src, uint16_t* lds_wave_base) 
 // Waits for every outstanding tile load of this wave.
 __device__ __forceinline__ void dma_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// 16 bytes into LDS (any LDS byte address, wave-uniform base) -- mask rows.
+__device__ __forceinline__ void dma16_bytes(const void* src, const void* lds_wave_base) {
+  const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+}
+
 // Pins a value in registers at this point of the instruction stream, so the
 // compiler cannot sink its computation into a later block.
 __device__ __forceinline__ void keep(const uint4& x) {
@@ -116,9 +130,16 @@ __device__ __forceinline__ void dma_barrier() {
   static_assert(kLoadsPerTile == 4, "the wait count below is written out");
   asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Waves that also load mask rows issue kLoadsPerTile + 1 loads per step.
+__device__ __forceinline__ void dma_barrier_mask_wave() {
+  asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-template <int G, bool kPow2>
+template <int G, bool kPow2, bool kMask>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArgs a) {
+  constexpr int kTileRows = 256 / G;                 // query rows of a work item
+  constexpr int kMaskInstr = kTileRows * 2 / 64;     // 16-byte mask pieces of a tile / 64 lanes
+  static_assert(!kMask || (kMaskInstr >= 1 && kMaskInstr <= kWaves), "mask rows per tile");
   // Ring slot i holds K(t+1) (first half) and V(t) (second half) for the
   // tile steps t with t % 4 == i: exactly what step t reads, and what step
   // t-3 loads.  Four separate arrays, so the compiler can tell the slot being
@@ -128,6 +149,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   __shared__ __attribute__((aligned(16))) uint16_t s_b2[2 * kTile];
   __shared__ __attribute__((aligned(16))) uint16_t s_b3[2 * kTile];
   __shared__ int32_t s_pages[kMaxChunkPages];
+  // Mask ring (kMask): slot i holds, for the tile whose K is in s_b<i>, 32
+  // bytes per tile row.
+  __shared__ uint4 s_mask[kMask ? 4 * kTileRows * 2 : 1];
 
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
@@ -149,6 +173,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   const int32_t limit = pair_ok ? min(it.kv_end - 1, it.diag + prow) : -1;   // last visible key
   // Smallest row limit in the wave: tiles ending at or before it need no mask.
   const int32_t wave_limit_min = min(it.kv_end - 1, it.diag + (wave * 32) / G);
+  // Custom mask: bit of (row, key 0) for this lane's row and for the row whose
+  // mask pieces this lane loads (lane l of mask wave w: row (64w + l) / 2).
+  int64_t mask_row_bit = 0, mask_dma_bit = 0;
+  const char* const mask_bytes = reinterpret_cast<const char*>(a.mask);
+  if constexpr (kMask) {
+    const MaskRow mr = a.mask_rows[it.batch];
+    const int32_t local0 = it.q_row0 - mr.q_start;
+    mask_row_bit = mr.bit0 + int64_t(local0 + (pair_ok ? prow : 0)) * mr.kv_len;
+    const int dma_r = (64 * min(wave, kMaskInstr - 1) + lane) >> 1;
+    mask_dma_bit = mr.bit0 + int64_t(local0 + (dma_r < it.num_rows ? dma_r : 0)) * mr.kv_len;
+  }
 
   const char* const kbase = static_cast<const char*>(a.k) + int64_t(kvh) * a.head_stride * 2;
   const char* const vbase = static_cast<const char*>(a.v) + int64_t(kvh) * a.head_stride * 2;
@@ -248,6 +283,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     if (tile_aligned(t0)) dma_aligned(vbase, lane_v, dst, off_next);
     else dma_general(vbase, cv, dst, t0);
   };
+  // Mask pieces of the tile starting at t0 (mask waves only): lane l of wave
+  // w fetches half l & 1 of row (64w + l) / 2's 32 bytes.  Tiles past the
+  // chunk end fetch the bits of its last key instead (never used).
+  auto load_m = [&](uint4* slot, int32_t t0) {
+    if constexpr (kMask) {
+      if (wave < kMaskInstr) {
+        const int64_t bit = mask_dma_bit + min(t0, kv_hi - 1);
+        const char* src = mask_bytes + ((bit >> 3) & ~int64_t(15)) + 16 * (lane & 1);
+        dma16_bytes(src, slot + 64 * wave);
+      }
+    }
+  };
+  auto barrier = [&]() {
+    if (kMask && wave < kMaskInstr) dma_barrier_mask_wave();
+    else dma_barrier();
+  };
 
   // S^T of the K tile in kbuf: two 32-key blocks.  Lane (col, h) reads row
   // 32kb + col, source chunk 2st + h, stored at chunk (2st + h) ^ (col & 15).
@@ -278,7 +329,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   // Causal / chunk-end mask of a score tile whose first key is t0: the key of
   // value v in block kb is t0 + 32kb + 8(v/4) + 4h + v%4.  Tiles that end at
   // or before every row limit of the wave need none.
-  auto mask_tile = [&](f32x16_t (&sc)[2], int32_t t0) {
+  auto mask_tile = [&](f32x16_t (&sc)[2], int32_t t0, const uint4* mslot) {
+    if constexpr (kMask) {
+      // This row's 64 bits for keys t0 .. t0 + 63: bit k of (lo, hi).
+      const int64_t bit = mask_row_bit + t0;
+      const int sh = int(bit & 127);
+      const uint32_t* words = reinterpret_cast<const uint32_t*>(mslot + 2 * (pair_ok ? prow : 0));
+      const int w0 = sh >> 5, s5 = sh & 31;
+      const uint32_t d0 = words[w0], d1 = words[w0 + 1], d2 = words[w0 + 2];
+      const uint32_t lo = __builtin_amdgcn_alignbit(d1, d0, s5);
+      const uint32_t hi = __builtin_amdgcn_alignbit(d2, d1, s5);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int k = 8 * (v >> 2) + 4 * h + (v & 3);
+          const int32_t j = t0 + 32 * kb + k;
+          const bool on = (((kb ? hi : lo) >> k) & 1u) != 0;
+          sc[kb][v] = (on && j <= limit) ? sc[kb][v] : -INFINITY;
+        }
+      return;
+    }
     if (t0 + kKeys - 1 > wave_limit_min) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -351,13 +422,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   // into m_used) and K(t+1), V(t) are (being) loaded into kread / vread;
   // V(t+3) -> vdma and K(t+4) -> kdma are issued here.
   auto body = [&](int32_t t, const uint16_t* kread, const uint16_t* vread, uint16_t* kdma, uint16_t* vdma,
-                  f32x16_t (&sc)[2]) {
+                  const uint4* mread, uint4* mdma, f32x16_t (&sc)[2]) {
     const int32_t t0 = kv_lo + t * kKeys;
     // K(t+1) and V(t) have landed for every wave, and every wave is done
     // reading the slot of step t-1, which now takes V(t+3) and K(t+4).
-    dma_barrier();
+    barrier();
     load_v(vdma, t0 + 3 * kKeys);
     load_k(kdma, t0 + 4 * kKeys);
+    load_m(mdma, t0 + 4 * kKeys);
     const float shift = m_used != -INFINITY ? m_used : 0.f;
     float ls0 = 0.f, ls1 = 0.f;
     uint4 pb[4];
@@ -368,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     for (int ks = 0; ks < 4; ++ks) pv_step(vread, ks, pb[ks]);
     if (t + 1 < ntiles) {
       scores(kread, sc);
-      mask_tile(sc, t0 + kKeys);
+      mask_tile(sc, t0 + kKeys, mread);
       update_max(tile_max(sc));
     }
   };
@@ -376,26 +448,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   // The prologue loads K(0) (slot 3), then V(s) and K(s+1) into slot s for
   // s = 0, 1, 2, and waits for all but the last two steps.
   f32x16_t sc[2];
+  // Mask slot i goes with K slot s_b<i> (K(j) and its mask bits sit in slot (j + 3) % 4).
+  constexpr int kMaskSlot = kMask ? kTileRows * 2 : 0;
+  uint4* const m0 = s_mask;
+  uint4* const m1 = s_mask + kMaskSlot;
+  uint4* const m2 = s_mask + 2 * kMaskSlot;
+  uint4* const m3 = s_mask + 3 * kMaskSlot;
   if (ntiles > 0) {
     load_k(s_b3, kv_lo);
+    load_m(m3, kv_lo);
     load_v(s_b0 + kTile, kv_lo);
     load_k(s_b0, kv_lo + kKeys);
+    load_m(m0, kv_lo + kKeys);
     load_v(s_b1 + kTile, kv_lo + kKeys);
     load_k(s_b1, kv_lo + 2 * kKeys);
+    load_m(m1, kv_lo + 2 * kKeys);
     load_v(s_b2 + kTile, kv_lo + 2 * kKeys);
     load_k(s_b2, kv_lo + 3 * kKeys);
-    dma_barrier();
+    load_m(m2, kv_lo + 3 * kKeys);
+    barrier();
     scores(s_b3, sc);
-    mask_tile(sc, kv_lo);
+    mask_tile(sc, kv_lo, m3);
     update_max(tile_max(sc));
     for (int32_t t = 0; t < ntiles; t += 4) {
-      body(t, s_b0, s_b0 + kTile, s_b3, s_b3 + kTile, sc);
+      body(t, s_b0, s_b0 + kTile, s_b3, s_b3 + kTile, m0, m3, sc);
       if (t + 1 >= ntiles) break;
-      body(t + 1, s_b1, s_b1 + kTile, s_b0, s_b0 + kTile, sc);
+      body(t + 1, s_b1, s_b1 + kTile, s_b0, s_b0 + kTile, m1, m0, sc);
       if (t + 2 >= ntiles) break;
-      body(t + 2, s_b2, s_b2 + kTile, s_b1, s_b1 + kTile, sc);
+      body(t + 2, s_b2, s_b2 + kTile, s_b1, s_b1 + kTile, m2, m1, sc);
       if (t + 3 >= ntiles) break;
-      body(t + 3, s_b3, s_b3 + kTile, s_b2, s_b2 + kTile, sc);
+      body(t + 3, s_b3, s_b3 + kTile, s_b2, s_b2 + kTile, m3, m2, sc);
     }
     // The last steps loaded tiles past the chunk end; they must land before
     // the workgroup can exit and its LDS be reused.
@@ -438,15 +520,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   }
 }
 
-template <int G>
-hipError_t launch_g(const AttnArgs& a, hipStream_t st) {
+template <int G, bool kMask>
+hipError_t launch_gm(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
   if (a.page_shift >= 0)
-    hipLaunchKernelGGL((prefill_mfma_kernel<G, true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<G, true, kMask>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<G, false>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<G, false, kMask>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_g(const AttnArgs& a, hipStream_t st) {
+  if constexpr (G >= 2) {
+    if (a.mask) return launch_gm<G, true>(a, st);
+  }
+  return launch_gm<G, false>(a, st);
 }
 
 }  // namespace
@@ -455,7 +546,9 @@ hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& 
                                bool* supported) {
   // The tile loader forms 16 rows of token stride as a 32-bit byte offset.
   const bool strides_ok = a.token_stride >= 0 && a.token_stride * 2 * 16 < (int64_t(1) << 31);
-  if (head_dim == kD && strides_ok) {
+  // A custom mask runs here for head groups of 2 or more (the mask tiles of
+  // 256 rows would not fit the LDS left over).
+  if (head_dim == kD && strides_ok && !(a.mask && group < 2)) {
     *supported = true;
     switch (group) {
       case 1: return launch_g<1>(a, st);

@@ -70,7 +70,10 @@ def _ragged_case(seed, dtype, hq, hkv, d, qo_lens, kv_extra):
     ("bf16", 32, 8, 128, True, False, 0),     # MFMA tile kernel
     ("bf16", 32, 8, 128, False, False, 3),
     ("f32", 8, 2, 64, True, False, 0),        # row kernel
-    ("bf16", 16, 4, 128, False, True, 0),     # custom mask (row kernel)
+    ("bf16", 16, 4, 128, False, True, 0),     # custom mask on the MFMA kernel (group 4)
+    ("bf16", 16, 8, 128, False, True, 2),     # group 2, forced splits
+    ("bf16", 64, 8, 128, False, True, 0),     # group 8
+    ("bf16", 8, 8, 128, False, True, 0),      # group 1: row kernel
     ("f32", 4, 4, 64, False, True, 1),
 ])
 def test_ragged_prefill(torch, pkv, dtype, hq, hkv, d, causal, masked, fixed):

@@ -420,4 +420,4 @@ def test_mask_and_ragged_parameter_rules():
                              **dict(meta, qo_indptr=None))
         assert e.value.status == _abi.ERR_UNSUPPORTED
     info = pkv.plan_compute(pkv.plan_params(mode="prefill", causal=False, custom_mask=True, **base), **meta)[0]
-    assert info["mask_bits"] == 2 * 3 and info["rows_per_tile"] == 1
+    assert info["mask_bits"] == 2 * 3 and info["rows_per_tile"] == 1   # float32: the row kernel

@@ -248,9 +248,12 @@ def test_cascade_plan_invariants():
             assert p["row_ptr"][r + 1] - p["row_ptr"][r] >= 3
 
 
-def test_masked_prefill_runs_one_row_per_tile():
-    assert pl.rows_per_tile("prefill", 4, "bf16", masked=True) == 1
+def test_masked_prefill_tile_rows():
+    assert pl.rows_per_tile("prefill", 4, "bf16", masked=True) == 64
     assert pl.rows_per_tile("prefill", 4, "bf16", masked=False) == 64
+    assert pl.rows_per_tile("prefill", 1, "bf16", masked=True) == 1
+    assert pl.rows_per_tile("prefill", 1, "bf16", masked=False) == 256
+    assert pl.rows_per_tile("prefill", 4, "f32", masked=True) == 1
 
 
 def test_hand_worked_ragged_plan():
