@@ -168,6 +168,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   const int pair = wave * 32 + col;
   const int prow = pair / G, phead = pair - (pair / G) * G;
   const bool pair_ok = prow < it.num_rows;
+  // Waves whose 32 pairs all lie past the tile's rows (short tiles: a
+  // request's last rows, small cascade nodes) only load and synchronise.
+  const bool wave_active = 32 * wave < it.num_rows * G;
   const int32_t qrow_idx = it.q_row0 + prow;
   const int32_t head = kvh * G + phead;
   const int32_t limit = pair_ok ? min(it.kv_end - 1, it.diag + prow) : -1;   // last visible key
@@ -430,6 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     load_v(vdma, t0 + 3 * kKeys);
     load_k(kdma, t0 + 4 * kKeys);
     load_m(mdma, t0 + 4 * kKeys);
+    if (!wave_active) return;
     const float shift = m_used != -INFINITY ? m_used : 0.f;
     float ls0 = 0.f, ls1 = 0.f;
     uint4 pb[4];
@@ -467,9 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     load_k(s_b2, kv_lo + 3 * kKeys);
     load_m(m2, kv_lo + 3 * kKeys);
     barrier();
-    scores(s_b3, sc);
-    mask_tile(sc, kv_lo, m3);
-    update_max(tile_max(sc));
+    if (wave_active) {
+      scores(s_b3, sc);
+      mask_tile(sc, kv_lo, m3);
+      update_max(tile_max(sc));
+    }
     for (int32_t t = 0; t < ntiles; t += 4) {
       body(t, s_b0, s_b0 + kTile, s_b3, s_b3 + kTile, m0, m3, sc);
       if (t + 1 >= ntiles) break;
