@@ -128,3 +128,38 @@ def test_one_level_cascade_matches_plain_run(torch, pkv):
     ro, rl = _oracle(b, k_exp, v_exp, levels=leaf)
     gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "one-level cascade o")
     gu.check_lse(lse, rl, "one-level cascade lse")
+
+
+def test_cascade_over_fp8_cache(torch, pkv):
+    """The bf16 tree above with its cache rounded to E4M3 (bf16 queries)."""
+    b = wl.make("cascade_small", seed=21, poison=True, dtype="bf16", hq=8, hkv=2, dim=128, page_size=16,
+                tree=[[12], [5, 7], [2, 3, 4, 3], [1] * 12], level_kv=[(300, 300), (40, 200), (1, 90), (1, 70)],
+                qo_range=(1, 9))
+    # Round the bf16 cache values to E4M3 codes (poisoned slots become the fp8 NaN code).
+    k8 = wl.to_fp8_codes(gu.as_f64(b.k_cache, "bf16").astype(np.float32))
+    v8 = wl.to_fp8_codes(gu.as_f64(b.v_cache, "bf16").astype(np.float32))
+    k8[np.isnan(gu.as_f64(b.k_cache, "bf16"))] = wl.FP8_NAN
+    v8[np.isnan(gu.as_f64(b.v_cache, "bf16"))] = wl.FP8_NAN
+    kn = wl.to_fp8_codes(gu.as_f64(b.k_new, "bf16").astype(np.float32))
+    vn = wl.to_fp8_codes(gu.as_f64(b.v_new, "bf16").astype(np.float32))
+    k_dev = torch.from_numpy(k8).cuda()
+    v_dev = torch.from_numpy(v8).cuda()
+    pkv.append_paged_kv(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(), gu.to_dev(b.append_indptr, "i32"),
+                        gu.to_dev(b.kv_indptr, "i32"), gu.to_dev(b.kv_indices, "i32"),
+                        gu.to_dev(b.kv_last_page_len, "i32"), k_dev, v_dev, layout=b.layout, page_size=b.page_size)
+    b8 = wl.Batch(**{**b.__dict__, "k_cache": k8, "v_cache": v8, "k_new": kn, "v_new": vn, "kv_dtype": "fp8"})
+    k_exp, v_exp = _leaf_append_host(b8)
+    levels = b.extra["levels"]
+    params = pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=8, num_kv_heads=2, head_dim_qk=128,
+                             page_size=16, causal=True, dtype="bf16", kv_dtype="fp8", max_num_pages=k_dev.shape[0])
+    plan = pkv.CascadePlan(params, levels)
+    q = gu.to_dev(b.q, "bf16")
+    out = gu.empty_like_out(q.shape, "bf16")
+    lse = torch.full((q.shape[0], 8), float("nan"), dtype=torch.float32, device="cuda")
+    idx = gu.to_dev(np.concatenate([lv["kv_indices"][:lv["kv_indptr"][-1]] for lv in levels]), "i32")
+    plan.run(q, k_dev, v_dev, idx, out, lse, layout=b.layout, sm_scale=b.sm_scale, k_scale=0.5, v_scale=2.0)
+    torch.cuda.synchronize()
+    ro, rl = occ.cascade_attention(b.q, k_exp, v_exp, levels=levels, page_size=16, layout=b.layout, num_kv_heads=2,
+                                   causal=True, sm_scale=b.sm_scale * 0.5, q_dtype="bf16", kv_dtype="fp8")
+    gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), 2.0 * ro, "bf16", "cascade fp8 o")
+    gu.check_lse(lse.cpu().numpy(), rl, "cascade fp8 lse")

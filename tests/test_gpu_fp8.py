@@ -106,3 +106,12 @@ def test_fp8_prefill_append_hnd(torch, pkv):
     ro, rl = _oracle(b, k_exp, v_exp, 1.0, 1.0)
     gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 prefill o")
     gu.check_lse(lse, rl, "fp8 prefill lse")
+
+
+def test_fp8_odd_page_size(torch, pkv):
+    """Page size 3 (no power of two: every key located through the page table)."""
+    b = wl.make("decode", kv_dtype="fp8", scale=0.1, batch=9, page_size=3, poison=True)
+    _, o, lse = _run(pkv, torch, b, _u8(torch, b.k_cache), _u8(torch, b.v_cache), k_scale=0.25, v_scale=4.0)
+    ro, rl = _oracle(b, b.k_cache, b.v_cache, 0.25, 4.0)
+    gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 page 3 o")
+    gu.check_lse(lse, rl, "fp8 page 3 lse")

@@ -188,3 +188,58 @@ def test_captured_mla_run_replays_across_updates(torch, pkv):
             gu.check_lse(lse.cpu().numpy(), rl, f"mla batch {i} lse")
             torch.zeros(1 << 20, device="cuda").add_(1.0)
             torch.cuda.synchronize()
+
+
+def test_captured_masked_prefill_replays_across_updates(torch, pkv):
+    """A fixed-capacity plan with a custom mask (the MFMA kernel's mask tiles)
+    captured once and replayed for three batches; the packed mask lives in a
+    fixed buffer whose contents change with each batch."""
+    rng = np.random.default_rng(77)
+    batches = [wl.make("prefill", seed=700 + i, batch=4, qo_range=r, prefix_range=(0, 700), pool=500)
+               for i, r in enumerate([(60, 250), (1, 50), (200, 260)])]
+    b0 = batches[0]
+    max_rows = 4 * 260
+    params = pkv.plan_params(mode="prefill", batch_size=4, num_qo_heads=32, num_kv_heads=8, head_dim_qk=128,
+                             page_size=16, causal=False, dtype="bf16", custom_mask=True, max_num_pages=500)
+    plan = pkv.GraphPlan(params, pkv.graph_caps(max_total_rows=max_rows, max_total_pages=500, max_partial_rows=8192))
+    buf = _Fixed(torch, b0, max_rows, 500)
+    max_bits = max_rows * 960
+    mask_dev = torch.zeros(max_bits // 8 + 64, dtype=torch.uint8, device="cuda")
+    masks = []
+    for b in batches:
+        segs = [(rng.random((q, k)) < 0.6).reshape(-1) for q, k in zip(b.qo_lens, b.kv_lens)]
+        masks.append(np.concatenate(segs))
+        assert len(masks[-1]) <= max_bits
+
+    def load(i):
+        b = batches[i]
+        plan.update(qo_indptr=b.qo_indptr, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
+                    kv_last_page_len=b.kv_last_page_len)
+        buf.load(torch, b)
+        packed = np.packbits(masks[i], bitorder="little")
+        mask_dev.zero_()
+        mask_dev[:len(packed)].copy_(torch.from_numpy(packed).cuda())
+
+    def run():
+        plan.run_masked(buf.q[:max_rows], buf.k, buf.v, buf.idx, mask_dev, buf.out[:max_rows], buf.lse[:max_rows],
+                        layout=b0.layout, sm_scale=b0.sm_scale)
+
+    load(0)
+    g = _capture(torch, run)
+    for i, b in enumerate(batches):
+        print(f"graph masked batch {i}", flush=True)
+        load(i)
+        buf.out.fill_(float("nan"))
+        for rep in range(2):
+            g.replay()
+            torch.cuda.synchronize()
+            n = int(b.qo_indptr[-1])
+            ro, rl = oat.paged_attention(b.q, b.k_cache, b.v_cache, qo_indptr=list(b.qo_indptr),
+                                         kv_indptr=list(b.kv_indptr), kv_indices=list(b.kv_indices),
+                                         kv_last_page_len=list(b.kv_last_page_len), page_size=16, layout=b.layout,
+                                         num_kv_heads=8, sm_scale=b.sm_scale, q_dtype="bf16", kv_dtype="bf16",
+                                         custom_mask=masks[i])
+            gu.check_close(gu.as_f64(gu.to_host(buf.out[:n], "bf16"), "bf16"), ro, "bf16", f"masked batch {i} o")
+            gu.check_lse(buf.lse[:n].cpu().numpy(), rl, f"masked batch {i} lse")
+            torch.zeros(1 << 20, device="cuda").add_(1.0)
+            torch.cuda.synchronize()
