@@ -30,14 +30,33 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
                                                      int64_t page_b, int64_t tok_b, int64_t head_b,
                                                      int32_t page_size, int32_t heads, int32_t row_chunks,
                                                      int32_t max_pages) {
+  __shared__ int32_t s_req;
   const int32_t t = blockIdx.x;
-  if (t >= append_indptr[batch]) return;
-  int32_t lo = 0, hi = batch - 1;   // last request b with append_indptr[b] <= t
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (append_indptr[mid] <= t) lo = mid; else hi = mid - 1;
+  const int32_t per = heads * row_chunks;
+  // The new row's bytes do not depend on where they go: load them first (the
+  // usual case, one 16-byte chunk per thread, keeps them in registers).
+  const int64_t src = int64_t(t) * new_st_b;
+  auto src_of = [&](int32_t i) {
+    const int32_t which = i >= per;
+    const int32_t j = i - which * per;
+    const int32_t h = j / row_chunks, c = j - (j / row_chunks) * row_chunks;
+    return (which ? v_new : k_new) + src + int64_t(h) * new_sh_b + int64_t(c) * 16;
+  };
+  const int32_t i0 = threadIdx.x;
+  uint4 first = make_uint4(0, 0, 0, 0);
+  if (i0 < 2 * per) first = *reinterpret_cast<const uint4*>(src_of(i0));
+  // Request of token t: the one b with append_indptr[b] <= t < append_indptr[b+1]
+  // (unique: empty requests never match), found by all threads in parallel.
+  if (threadIdx.x == 0) s_req = -1;
+  __syncthreads();
+  for (int32_t r0 = 0; r0 < batch; r0 += blockDim.x) {
+    const int32_t r = r0 + threadIdx.x;
+    if (r < batch && append_indptr[r] <= t && t < append_indptr[r + 1]) s_req = r;
+    __syncthreads();
+    if (s_req >= 0) break;   // uniform: read after the barrier
   }
-  const int32_t b = lo;
+  const int32_t b = s_req;
+  if (b < 0) return;
   const int32_t n_new = append_indptr[b + 1] - append_indptr[b];
   const int32_t n_pages = kv_indptr[b + 1] - kv_indptr[b];
   const int32_t kv_len = page_size * (n_pages - 1) + last[b];
@@ -46,16 +65,15 @@ __global__ __launch_bounds__(256) void append_kernel(const char* k_new, const ch
   const int32_t page = kv_indices[kv_indptr[b] + pos / page_size];
   if (page < 0 || page >= max_pages) return;
   const int64_t dst = int64_t(page) * page_b + int64_t(pos % page_size) * tok_b;
-  const int64_t src = int64_t(t) * new_st_b;
-  const int32_t per = heads * row_chunks;
-  for (int32_t i = threadIdx.x; i < 2 * per; i += blockDim.x) {
+  auto dst_of = [&](int32_t i) {
     const int32_t which = i >= per;
     const int32_t j = i - which * per;
     const int32_t h = j / row_chunks, c = j - (j / row_chunks) * row_chunks;
-    const char* s = (which ? v_new : k_new) + src + int64_t(h) * new_sh_b + int64_t(c) * 16;
-    char* d = (which ? v : k) + dst + int64_t(h) * head_b + int64_t(c) * 16;
-    *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(s);
-  }
+    return (which ? v : k) + dst + int64_t(h) * head_b + int64_t(c) * 16;
+  };
+  if (i0 < 2 * per) *reinterpret_cast<uint4*>(dst_of(i0)) = first;
+  for (int32_t i = i0 + blockDim.x; i < 2 * per; i += blockDim.x)
+    *reinterpret_cast<uint4*>(dst_of(i)) = *reinterpret_cast<const uint4*>(src_of(i));
 }
 
 template <typename T>
@@ -132,7 +150,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     // Waves per row: all four share one row (each a quarter of its dims) when
     // the block has one row, two share a row when it has two.
     const int32_t rows_here = r_hi - r_lo;
-    const int32_t wpr = rows_here == 1 ? 4 : (rows_here == 2 ? 2 : 1);
+    // Waves per row: up to four (one row) or two (two rows), at most one per
+    // 128 dims (a wave covers 128 dims with two per lane).
+    const int32_t by_dims = max(1, d_all / 128);
+    const int32_t wpr = rows_here == 1 ? min(4, by_dims) : (rows_here == 2 ? min(2, by_dims) : 1);
     const int32_t w = tid >> 6;
     const int32_t r = r_lo + w / wpr;
     const int32_t slice = w - (w / wpr) * wpr;
@@ -140,6 +161,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     if (r >= r_hi) return;
     const int32_t d_lo = slice * d_all / wpr, d_hi = (slice + 1) * d_all / wpr;
     const int64_t row_base = int64_t(mi.slot0) + r;
+    const float* pbase = a.part_o + (row_base * hq + h) * d_all;
+    const int64_t chunk_stride = int64_t(mi.num_rows) * hq * d_all;
+    // Up to 8 chunks and one 128-dim pass (split decode and MLA rows): the
+    // partial values are loaded together with the statistics, so the two
+    // memory latencies overlap.
+    const bool fast = kVec4 && n <= 8 && (d_hi - d_lo) <= 128 && ((d_hi - d_lo) & 1) == 0;
+    float2 pre[8];
+    if (fast) {
+      const int32_t d = d_lo + 2 * lane;
+      const float* src = pbase + (d < d_hi ? d : d_lo);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pre[j] = *reinterpret_cast<const float2*>(src + int64_t(min(j, n - 1)) * chunk_stride);
+    }
     const float sc = lane < n ? a.part_lse[(row_base + int64_t(lane) * mi.num_rows) * hq + h] : -INFINITY;
     const float mx = wave_max(sc);
     const float wl = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);   // mx finite whenever sc is
@@ -152,9 +186,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     // consecutive dims (8-byte loads); chunks go four at a time so four loads
     // are in flight, the steps past the last chunk re-reading it with weight 0.
     // Lanes past the slice end read dim d_lo and store nothing.
-    const float* pbase = a.part_o + (row_base * hq + h) * d_all;
-    const int64_t chunk_stride = int64_t(mi.num_rows) * hq * d_all;
-    if (kVec4 && ((d_hi - d_lo) & 1) == 0) {
+    if (fast) {
+      const int32_t d = d_lo + 2 * lane;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = j < n ? __shfl(scale, j) : 0.f;
+        acc0 = fmaf(w, pre[j].x, acc0);
+        acc1 = fmaf(w, pre[j].y, acc1);
+      }
+      if (d < d_hi) {
+        store_f<T>(orow, d, acc0);
+        store_f<T>(orow, d + 1, acc1);
+      }
+    } else if (kVec4 && ((d_hi - d_lo) & 1) == 0) {
       for (int32_t d0 = d_lo; d0 < d_hi; d0 += 128) {
         const int32_t d = d0 + 2 * lane;
         const bool own = d < d_hi;
