@@ -384,7 +384,7 @@ def main():
         path = os.path.join(ROOT, "profiles", "traffic.json")
         data = json.load(open(path)) if os.path.exists(path) else {}
         cmd = (f"rocprofv3 --pmc {{FETCH_SIZE|WRITE_SIZE}} -f csv -d <dir> -o p -- python3 bench.py --only {w} "
-               "--steps 2 --warmup 1 --layers 4 --secondary-layers 4 --no-cpu-baseline --calibrate-copy-mib 512")
+               "--steps 2 --warmup 1 --layers 4 --secondary-layers 4 --no-cpu-baseline --no-flat --calibrate-copy-mib 512")
         data[w] = ingest_counters(w, fcsv, wcsv, cmd)
         with open(path, "w") as f:
             json.dump(data, f, indent=1, sort_keys=True)
