@@ -115,6 +115,9 @@ class Runner:
         import paged_kv_cache_plan_amd as pkv
         self.b, self.torch, self.pkv = b, torch, pkv
         self.time_merge = time_merge
+        # Attention-only timing uses events that the kernel's own dispatch
+        # records (pkv_time_next_attention): no event packets in the stream.
+        self.kernel_events = not time_merge and b.mode != "mla"
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
@@ -174,11 +177,14 @@ class Runner:
             self.pkv.append_paged_kv(self.k_new, self.v_new, self.append_indptr, self.kv_indptr_d, self.kv_indices,
                                      self.last_d, k, v, layout=b.layout, page_size=b.page_size)
         if ev:
-            ev[0].record()
+            if self.kernel_events:
+                self.pkv.time_next_attention(ev[0], ev[1])
+            else:
+                ev[0].record()
         plan.run_attention(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
         if self.time_merge:
             plan.run_merge(self.out, self.lse)
-        if ev:
+        if ev and not self.kernel_events:
             ev[1].record()
         if not self.time_merge:
             plan.run_merge(self.out, self.lse)
@@ -193,6 +199,7 @@ class CascadeRunner(Runner):
         import paged_kv_cache_plan_amd as pkv
         self.b, self.torch, self.pkv = b, torch, pkv
         self.time_merge = True
+        self.kernel_events = False
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
@@ -234,10 +241,11 @@ class CascadeRunner(Runner):
 
 
 def measure(runner: Runner, layers: int, steps: int, warmup: int, ev_every: int = 1) -> dict:
-    """Time `steps` steps (plan + `layers` layers each).  The attention launches
-    of every `ev_every`-th layer are also bracketed by HIP events, inside the
-    same timed region (an event pair per launch costs about 7 us of stream
-    time, so the headline run samples every 4th layer)."""
+    """Time `steps` steps (plan + `layers` layers each).  The attention launch
+    of every `ev_every`-th layer is also timed with a pair of HIP events inside
+    the same timed region: recorded by the kernel's own dispatch when the
+    runner times attention alone, else recorded on the stream around the
+    timed launches (a stream event pair costs a few microseconds)."""
     torch = runner.torch
     for _ in range(warmup):
         runner.make_plan()
@@ -246,6 +254,10 @@ def measure(runner: Runner, layers: int, steps: int, warmup: int, ev_every: int 
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            if i % ev_every == 0 else None for _ in range(steps) for i in range(layers)]
+    for e in evs:                       # create the events outside the timed region
+        if e is not None:
+            e[0].record()
+            e[1].record()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     plan_host = []
     torch.cuda.synchronize()
@@ -374,6 +386,10 @@ def main():
     ap.add_argument("--cascade-target", type=int, default=0,
                     help="planner target items per CU for every cascade level (0: the per-mode default)")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat-page-table comparison run")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="time the attention launch of every N-th layer of the decode workloads")
+    ap.add_argument("--stream-events", action="store_true",
+                    help="record timing events on the stream around launches instead of by the dispatch")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
@@ -419,7 +435,8 @@ def main():
     if "decode" in which:
         b = wl.make("decode", with_append=True)
         r = Runner(b, args.layers)
-        m = measure(r, args.layers, args.steps, args.warmup, ev_every=4)
+        r.kernel_events = r.kernel_events and not args.stream_events
+        m = measure(r, args.layers, args.steps, args.warmup, ev_every=args.event_every)
         nb = decode_bytes(b)
         value = nb["layer"] * args.layers / (m["ms_per_step"] * 1e-3) / 1e9
         achieved = nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9
@@ -465,7 +482,8 @@ def main():
         b = wl.make("decode", with_append=True, kv_dtype="fp8")
         layers = args.layers
         r = Runner(b, layers)
-        m = measure(r, layers, args.steps, args.warmup, ev_every=4)
+        r.kernel_events = r.kernel_events and not args.stream_events
+        m = measure(r, layers, args.steps, args.warmup, ev_every=args.event_every)
         nb = decode_bytes(b)
         result["fp8"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
                              step_gbs=nb["layer"] * layers / (m["ms_per_step"] * 1e-3) / 1e9)

@@ -406,6 +406,23 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token,
                          int64_t o_stride_head, float* lse, void* stream);
 
 /*
+ * Kernel timing (measurement support, not an operation of the method): arms
+ * two events for the next attention kernel that this library launches from
+ * the calling host thread (pkv_run, pkv_run_attention, pkv_run_masked,
+ * pkv_run_ragged, pkv_run_mla, or a cascade level).  That launch passes them
+ * to hipExtLaunchKernel, so the dispatch itself records start_event when the
+ * kernel starts and stop_event when it ends: hipEventElapsedTime then gives
+ * the kernel's own duration, with no separate event packets in the stream
+ * around it.  The events are disarmed by that launch (one launch per arming;
+ * a run that launches no attention kernel leaves them armed).
+ *   start_event, stop_event  hipEvent_t handles created by the caller with
+ *                            timing enabled, or both NULL to disarm
+ * The library does not take ownership of the events.  Returns
+ * PKV_ERR_INVALID_ARG when exactly one of them is NULL.
+ */
+pkv_status pkv_time_next_attention(void* start_event, void* stop_event);
+
+/*
  * MLA decode run ([KVL] "多头潜在注意力页布局"): one latent row per token,
  * ckv (512) and kpe (64), shared by every query head; score =
  * sm_scale * (q_ckv . ckv + q_kpe . kpe); output = softmax-weighted ckv.

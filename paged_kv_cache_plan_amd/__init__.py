@@ -515,6 +515,22 @@ def append_paged_kv(k_new, v_new, append_indptr, kv_indptr, kv_indices, kv_last_
                                      k_new.shape[0], ctypes.byref(desc), _stream(stream)))
 
 
+def time_next_attention(start=None, stop=None):
+    """pkv_time_next_attention: the next attention kernel launched from this
+    thread records the two timing events (torch.cuda.Event(enable_timing=True))
+    at its own start and end; ``start.elapsed_time(stop)`` after a
+    synchronisation is then that kernel's duration.  No arguments disarm."""
+    if (start is None) != (stop is None):
+        raise ValueError("pass both events or neither")
+    if start is None:
+        _check(lib().pkv_time_next_attention(None, None))
+        return
+    for ev in (start, stop):
+        if not ev.cuda_event:          # torch creates the event on its first record
+            ev.record()
+    _check(lib().pkv_time_next_attention(ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)))
+
+
 def packbits(mask_bool, stream=None):
     """pkv_packbits: a device bool/uint8 tensor -> device uint8 tensor of
     ceil(n / 32) * 4 + 32 bytes (the tail zeroed; the masked kernels read up

@@ -491,14 +491,14 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
   if (a.mask) {
     if (aligned)
-      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, true, true>), grid, block, 0, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, true>, grid, block, st, a);
     else
-      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, false, true>), grid, block, 0, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, true>, grid, block, st, a);
   } else {
     if (aligned)
-      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, true, false>), grid, block, 0, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false>, grid, block, st, a);
     else
-      hipLaunchKernelGGL((attn_rows_kernel<T, TK, D, G, false, false>), grid, block, 0, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false>, grid, block, st, a);
   }
   return hipGetLastError();
 }

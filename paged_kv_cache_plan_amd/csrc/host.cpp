@@ -27,6 +27,15 @@
 using pkv::Item;
 using pkv::MergeItem;
 
+namespace pkv {
+
+LaunchEvents& armed_launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+
+}  // namespace pkv
+
 namespace {
 
 thread_local std::string g_error;
@@ -929,6 +938,15 @@ pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token, 
   m.lse = lse;
   hipError_t e = pkv::launch_merge_partials(p.q_dtype, m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+  return ok();
+}
+
+pkv_status pkv_time_next_attention(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "pass both timing events or neither");
+  pkv::LaunchEvents& ev = pkv::armed_launch_events();
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
   return ok();
 }
 

@@ -2,10 +2,34 @@
 // Not part of the C ABI (include/pkv.h is).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pkv {
+
+// Timing events armed for the next attention kernel launched from this host
+// thread (pkv_time_next_attention); null when none are armed.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& armed_launch_events();
+
+// Launches an attention kernel.  With events armed, the dispatch itself
+// records them at the kernel's start and end (hipExtLaunchKernelGGL), and
+// they are disarmed; otherwise a plain launch.
+template <typename Kernel, typename... Args>
+void launch_attention_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  LaunchEvents& ev = armed_launch_events();
+  if (ev.start || ev.stop) {
+    const LaunchEvents use = ev;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, use.start, use.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  }
+}
 
 // One unit of attention work: a tile of query rows of one request against one
 // chunk of its keys.  The device replicates it over kv heads (or MLA head

@@ -360,9 +360,9 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
   const int64_t blocks = (int64_t(a.num_items) + kXcds - 1) / kXcds * kXcds * a.head_groups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (a.page_shift >= 0)
-    hipLaunchKernelGGL((mla_decode_kernel<true>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+    launch_attention_kernel(mla_decode_kernel<true>, dim3(uint32_t(blocks)), dim3(kThreads), st, a);
   else
-    hipLaunchKernelGGL((mla_decode_kernel<false>), dim3(uint32_t(blocks)), dim3(kThreads), 0, st, a);
+    launch_attention_kernel(mla_decode_kernel<false>, dim3(uint32_t(blocks)), dim3(kThreads), st, a);
   return hipGetLastError();
 }
 

@@ -70,11 +70,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazyMax = 8.f;  // rescale only when a row max grows by more than this (log2 units)
 
-// Instruction classes for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
@@ -226,6 +221,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     const int32_t pg = pages[pg_lo + i];
     s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;
   }
+  // Q must have landed before the tile loop on every path: the compiler does
+  // not count the tile loads (inline assembly), so a Q load still pending at
+  // the loop would make it wait for every outstanding load before the first
+  // score product of each tile step.
+#pragma unroll
+  for (int s = 0; s < 8; ++s) keep(qreg[s]);
   __syncthreads();
 
   // Tile loads.  A tile is four groups of 16 rows.  Load instruction i (0, 1)
@@ -532,9 +533,9 @@ hipError_t launch_gm(const AttnArgs& a, hipStream_t st) {
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
   if (a.page_shift >= 0)
-    hipLaunchKernelGGL((prefill_mfma_kernel<G, true, kMask>), grid, block, 0, st, a);
+    launch_attention_kernel(prefill_mfma_kernel<G, true, kMask>, grid, block, st, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<G, false, kMask>), grid, block, 0, st, a);
+    launch_attention_kernel(prefill_mfma_kernel<G, false, kMask>, grid, block, st, a);
   return hipGetLastError();
 }
 

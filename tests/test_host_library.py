@@ -421,3 +421,15 @@ def test_mask_and_ragged_parameter_rules():
         assert e.value.status == _abi.ERR_UNSUPPORTED
     info = pkv.plan_compute(pkv.plan_params(mode="prefill", causal=False, custom_mask=True, **base), **meta)[0]
     assert info["mask_bits"] == 2 * 3 and info["rows_per_tile"] == 1   # float32: the row kernel
+
+
+def test_timing_events_are_armed_in_pairs():
+    """pkv_time_next_attention takes both events or neither (no GPU needed:
+    arming only stores the handles for the next launch)."""
+    lib = pkv.lib()
+    assert lib.pkv_time_next_attention(None, None) == _abi.OK
+    assert lib.pkv_time_next_attention(ctypes.c_void_p(16), None) == _abi.ERR_INVALID_ARG
+    assert lib.pkv_time_next_attention(None, ctypes.c_void_p(16)) == _abi.ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        pkv.time_next_attention(object(), None)
+    pkv.time_next_attention()          # disarm: both NULL
