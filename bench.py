@@ -115,9 +115,10 @@ class Runner:
         import paged_kv_cache_plan_amd as pkv
         self.b, self.torch, self.pkv = b, torch, pkv
         self.time_merge = time_merge
-        # Attention-only timing uses events that the kernel's own dispatch
+        # Decode attention is timed with events that the kernel's own dispatch
         # records (pkv_time_next_attention): no event packets in the stream.
-        self.kernel_events = not time_merge and b.mode != "mla"
+        # Other runs record events on the stream around the timed launches.
+        self.kernel_events = not time_merge and b.mode == "decode"
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"

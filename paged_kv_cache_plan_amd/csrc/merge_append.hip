@@ -98,8 +98,10 @@ __device__ __forceinline__ void store_f<uint16_t>(uint16_t* p, int64_t i, float 
 //     Lane c holds chunk c's statistic, so the shift (largest statistic) and
 //     the weight sum are wave reductions; then every lane accumulates its dims
 //     over the chunks, reading each chunk's scale from the lane that owns it.
-//   * More chunks (one long row split hundreds of ways): the workgroup merges
-//     its rows one at a time with the chunks spread over all threads: the shift
+//   * More chunks (one long row split many ways): the workgroup merges its
+//     rows one at a time.  Up to 256 chunks, thread c loads chunk c's
+//     statistic once, and every thread starts loading its share of the
+//     partial values before the reductions; beyond that, the shift
 //     and the weight sum are block reductions, the normalised scales of up to
 //     kMergeSeg chunks at a time are staged in LDS, and groups of threads
 //     accumulate disjoint chunk subsets of the output row (4 dims per thread)
@@ -108,6 +110,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeRows = kMergeThreads / 64;   // rows per workgroup
 constexpr int kMergeWaveChunks = 64;            // chunk count up to which one wave merges a row
 constexpr int kMergeSeg = 512;
+constexpr int kMergePre = 8;   // chunks of partial values per thread loaded ahead (long rows)
 
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -246,6 +249,64 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
   const int32_t tpr = min(nvec, kMergeThreads);   // threads per group (one vector each)
   const int32_t groups = kMergeThreads / tpr;
   const int32_t grp = tid / tpr, lv = tid - (tid / tpr) * tpr;
+  if (kVec4 && n <= kMergeThreads && nvec <= kMergeThreads) {
+    // Up to 256 chunks, output rows of at most 1024 dims: thread c holds chunk
+    // c's statistic (one load), and each group's first kMergePre chunks of
+    // partial values are loaded before the reductions, so their memory
+    // latency overlaps that of the statistics.
+    for (int32_t r = r_lo; r < r_hi; ++r) {
+      const int64_t row_base = int64_t(mi.slot0) + r;
+      const float sc = tid < n ? a.part_lse[(row_base + int64_t(tid) * mi.num_rows) * hq + h] : -INFINITY;
+      const bool own = lv < nvec;
+      const int32_t v = own ? lv : 0;
+      auto part = [&](int32_t c) {
+        return *reinterpret_cast<const float4*>(a.part_o + ((row_base + int64_t(c) * mi.num_rows) * hq + h) * d_all +
+                                                v * kVec);
+      };
+      float4 pre[kMergePre];
+#pragma unroll
+      for (int j = 0; j < kMergePre; ++j) pre[j] = part(min(grp + j * groups, n - 1));
+      const float mx = block_reduce(sc, s_red, true);
+      const float wl = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);   // mx finite whenever sc is
+      const float z = block_reduce(wl, s_red, false);
+      s_w[tid] = z > 0.f ? wl / z : 0.f;   // chunk tid's normalised scale (0 past n)
+      __syncthreads();
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      auto add = [&](float w, const float4& x) {
+        acc.x = fmaf(w, x.x, acc.x);
+        acc.y = fmaf(w, x.y, acc.y);
+        acc.z = fmaf(w, x.z, acc.z);
+        acc.w = fmaf(w, x.w, acc.w);
+      };
+#pragma unroll
+      for (int j = 0; j < kMergePre; ++j) {
+        const int32_t c = grp + j * groups;
+        if (c < n) add(s_w[c], pre[j]);
+      }
+      for (int32_t c = grp + kMergePre * groups; c < n; c += groups) add(s_w[c], part(c));
+      s_acc[tid] = acc;
+      __syncthreads();
+      const int32_t row = mi.q_row0 + r;
+      T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
+      if (grp == 0 && own) {
+        float4 t = acc;
+        for (int32_t g = 1; g < groups; ++g) {
+          const float4 u = s_acc[g * tpr + lv];
+          t.x += u.x;
+          t.y += u.y;
+          t.z += u.z;
+          t.w += u.w;
+        }
+        store_f<T>(orow, v * kVec, t.x);
+        store_f<T>(orow, v * kVec + 1, t.y);
+        store_f<T>(orow, v * kVec + 2, t.z);
+        store_f<T>(orow, v * kVec + 3, t.w);
+      }
+      if (tid == 0 && a.lse) a.lse[int64_t(row) * hq + h] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+      __syncthreads();   // s_w and s_acc are free for the next row
+    }
+    return;
+  }
   for (int32_t r = r_lo; r < r_hi; ++r) {
     const int64_t row_base = int64_t(mi.slot0) + r;   // partial row of chunk c: row_base + c * num_rows
     float mx = -INFINITY;

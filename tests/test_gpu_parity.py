@@ -137,6 +137,23 @@ def test_skewed_decode_split_and_merge(torch, pkv):
     gu.check_lse(lse, rl, "skewed lse")
 
 
+@pytest.mark.parametrize("fixed", [100, 30, 10])
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("f32", 64)])
+def test_split_merge_chunk_counts(torch, pkv, fixed, dtype, dim):
+    """A 4000-token request among short ones (page 1) split into about 40,
+    130 and 400 chunks: the merge's one-wave path (up to 64 chunks), its
+    prefetching block path (up to 256) and its segmented block path."""
+    print("case merge chunks", fixed, dtype, dim, flush=True)
+    b = wl.make("skewed", poison=True, long_len=4000, kv_range=(20, 300), dtype=dtype, dim=dim)
+    k_dev, v_dev = gu.to_dev(b.k_cache, dtype), gu.to_dev(b.v_cache, dtype)
+    plan, o, lse = _run_gqa(pkv, torch, b, k_cache=k_dev, v_cache=v_dev, fixed_split_pages=fixed, num_cus=64)
+    assert plan.info["num_merges"] >= 1
+    ro, rl = _oracle(b, b.k_cache, b.v_cache)
+    got = gu.as_f64(o, "bf16") if dtype == "bf16" else o
+    gu.check_close(got, ro, dtype, f"merge chunks {fixed} o")
+    gu.check_lse(lse, rl, f"merge chunks {fixed} lse", atol=1e-5 if dtype == "f32" else 1e-3)
+
+
 PREFILL_HEADS = [0, 5, 9, 14, 18, 23, 27, 31]     # one or more per kv head
 
 
@@ -198,6 +215,37 @@ def test_mla_decode_full_size(torch, pkv):
     rep = gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "mla o")
     gu.check_lse(lse.cpu().numpy(), rl, "mla lse")
     print("mla parity", rep, plan.info)
+
+
+@pytest.mark.parametrize("page_size,kv_range,batch,fixed,heads", [
+    (1, (1, 200), 6, 0, 128),      # one key per page: every key located through the page table
+    (3, (5, 300), 5, 7, 128),      # no power of two; forced 21-token chunks end inside tiles
+    (16, (30, 700), 4, 5, 64),     # pages shorter than a tile; one head group
+    (64, (1, 40), 9, 0, 128),      # requests shorter than one tile
+    (64, (32, 32), 3, 1, 128),     # exactly one tile per request; one-page chunks
+])
+def test_mla_decode_page_shapes_and_splits(torch, pkv, page_size, kv_range, batch, fixed, heads):
+    """MLA decode on small batches whose pages, chunk ends and lengths cut the
+    key tiles at every offset (NaN-poisoned caches)."""
+    print("case mla shapes", page_size, kv_range, batch, fixed, heads, flush=True)
+    b = wl.make("mla", poison=True, page_size=page_size, kv_range=kv_range, batch=batch, heads=heads)
+    cache = gu.to_dev(b.k_cache, "bf16")
+    params = pkv.plan_params(mode="mla", batch_size=b.batch_size, num_qo_heads=heads, num_kv_heads=1,
+                             head_dim_qk=576, head_dim_vo=512, page_size=page_size, dtype="bf16",
+                             fixed_split_pages=fixed, num_cus=16 if fixed else 0, max_num_pages=b.max_num_pages)
+    plan = pkv.Plan(params, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
+    out = gu.empty_like_out((b.batch_size, heads, 512), "bf16")
+    lse = torch.full((b.batch_size, heads), float("nan"), dtype=torch.float32, device="cuda")
+    plan.run_mla(gu.to_dev(b.q, "bf16"), gu.to_dev(b.q_kpe, "bf16"), cache[..., :512], cache[..., 512:],
+                 gu.to_dev(b.kv_indices, "i32"), out, lse, sm_scale=b.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oat.mla_decode(b.q, b.q_kpe, b.k_cache[..., :512], b.k_cache[..., 512:], kv_indptr=list(b.kv_indptr),
+                            kv_indices=list(b.kv_indices), kv_last_page_len=list(b.kv_last_page_len),
+                            page_size=page_size, sm_scale=b.sm_scale, dtype="bf16")
+    gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "mla o")
+    gu.check_lse(lse.cpu().numpy(), rl, "mla lse")
+    if fixed > 1:
+        assert plan.info["num_merges"] > 0
 
 
 def test_layouts_page_sizes_and_storage_forms_agree(torch, pkv):
