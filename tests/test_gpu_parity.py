@@ -372,3 +372,49 @@ def test_stale_plan_and_int64_rejection(torch, pkv):
     with pytest.raises(TypeError):
         pkv.Plan(params, qo_indptr=b.qo_indptr.astype(np.int64), kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
                  kv_last_page_len=b.kv_last_page_len)
+
+
+ROW_KERNEL_CASES = [
+    ("bf16", "bf16", 128, 1), ("bf16", "bf16", 128, 2), ("bf16", "bf16", 128, 8),
+    ("bf16", "bf16", 64, 1), ("bf16", "bf16", 64, 2), ("bf16", "bf16", 64, 4), ("bf16", "bf16", 64, 8),
+    ("f32", "f32", 128, 1), ("f32", "f32", 128, 2), ("f32", "f32", 128, 4),
+    ("f32", "f32", 64, 1), ("f32", "f32", 64, 4),
+    ("bf16", "fp8", 128, 1), ("bf16", "fp8", 128, 2), ("bf16", "fp8", 128, 8),
+]
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("dtype,kv_dtype,dim,group", ROW_KERNEL_CASES)
+def test_every_dtype_dim_and_group(torch, pkv, mode, dtype, kv_dtype, dim, group):
+    """Every (query dtype, cache dtype, head_dim, GQA group) the library builds,
+    in decode and prefill, on small batches (2 kv heads; HND for prefill):
+    each kernel instantiation against the oracle.  bf16 prefill with
+    head_dim 128 runs the MFMA tile kernel, the rest the row kernel."""
+    print("case kernel", mode, dtype, kv_dtype, dim, group, flush=True)
+    kw = dict(hq=2 * group, hkv=2, dim=dim, dtype=dtype, kv_dtype=kv_dtype, batch=5)
+    if mode == "decode":
+        b = wl.make("decode", kv_range=(1, 300), pool=128, poison=True, **kw)
+    else:
+        b = wl.make("prefill", qo_range=(1, 70), prefix_range=(0, 200), **kw)
+    fp8 = kv_dtype == "fp8"
+    to_kv = (lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()) if fp8 else (lambda x: gu.to_dev(x, dtype))
+    k_dev, v_dev = to_kv(b.k_cache), to_kv(b.v_cache)
+    params = pkv.plan_params(mode=mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads,
+                             num_kv_heads=2, head_dim_qk=dim, page_size=b.page_size, causal=b.causal,
+                             dtype=dtype, kv_dtype=kv_dtype, max_num_pages=b.max_num_pages)
+    plan = pkv.Plan(params, qo_indptr=b.qo_indptr if mode == "prefill" else None, kv_indptr=b.kv_indptr,
+                    kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
+    q = gu.to_dev(b.q, dtype)
+    out = gu.empty_like_out(q.shape, dtype)
+    lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    ks, vs = (0.5, 2.0) if fp8 else (1.0, 1.0)
+    plan.run(q, k_dev, v_dev, gu.to_dev(b.kv_indices, "i32"), out, lse, layout=b.layout, sm_scale=b.sm_scale,
+             k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ro, rl = oat.paged_attention(b.q, b.k_cache, b.v_cache, qo_indptr=list(b.qo_indptr), kv_indptr=list(b.kv_indptr),
+                                 kv_indices=list(b.kv_indices), kv_last_page_len=list(b.kv_last_page_len),
+                                 page_size=b.page_size, layout=b.layout, num_kv_heads=2, causal=b.causal,
+                                 sm_scale=b.sm_scale, q_dtype=dtype, kv_dtype=kv_dtype, k_scale=ks, v_scale=vs)
+    got = gu.to_host(out, dtype)
+    gu.check_close(gu.as_f64(got, "bf16") if dtype == "bf16" else got, ro, dtype, f"{mode} o")
+    gu.check_lse(lse.cpu().numpy(), rl, f"{mode} lse", atol=1e-5 if dtype == "f32" else 1e-3)
