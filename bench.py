@@ -313,7 +313,8 @@ def cpu_baseline(b, budget_s: float = 12.0) -> dict:
 
 
 COUNTER_KERNELS = {"decode": "attn_rows_kernel", "skewed": "attn_rows_kernel", "prefill": "prefill_mfma_kernel",
-                   "mla": "mla_decode_kernel", "cascade": "prefill_mfma_kernel", "fp8": "attn_rows_kernel"}
+                   "mla": "mla_decode_kernel", "cascade": "prefill_mfma_kernel", "fp8": "attn_rows_kernel",
+                   "fp8_prefill": "prefill_mfma_kernel"}
 
 
 def ingest_counters(workload: str, fetch_csv: str, write_csv: str, command: str) -> dict:
@@ -382,7 +383,8 @@ def main():
     ap.add_argument("--secondary-layers", type=int, default=4)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "skewed", "mla", "cascade", "fp8"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "fp8_prefill", "skewed", "mla", "cascade", "fp8"],
+                    default=None,
                     help="time one workload (profiling runs)")
     ap.add_argument("--cascade-target", type=int, default=0,
                     help="planner target items per CU for every cascade level (0: the per-mode default)")
@@ -431,7 +433,8 @@ def main():
 
     result = {}
     which = [args.only] if args.only else ["decode"] + ([] if args.no_secondary else
-                                                        ["prefill", "skewed", "mla", "cascade", "fp8"])
+                                                        ["prefill", "fp8_prefill", "skewed", "mla",
+                                                         "cascade", "fp8"])
 
     if "decode" in which:
         b = wl.make("decode", with_append=True)
@@ -456,6 +459,17 @@ def main():
         step_tf = fl * layers / (m["ms_per_step"] * 1e-3) / 1e12
         result["prefill"] = dict(m, tflops=tf, step_tflops=step_tf, flops=fl)
         log(f"prefill: attention {tf:.1f} TFLOP/s ({m['attn_ms_mean']:.3f} ms), step {step_tf:.1f} TFLOP/s")
+        del r
+    if "fp8_prefill" in which:
+        # The prefill batch over an E4M3 cache (bf16 queries and outputs).
+        b = wl.make("prefill", kv_dtype="fp8")
+        layers = args.secondary_layers
+        r = Runner(b, layers)
+        m = measure(r, layers, max(1, min(args.steps, 5)), 1)
+        fl = prefill_flops(b)
+        tf = fl / (m["attn_ms_mean"] * 1e-3) / 1e12
+        result["fp8_prefill"] = dict(m, tflops=tf, flops=fl)
+        log(f"fp8 prefill: attention {tf:.1f} TFLOP/s ({m['attn_ms_mean']:.3f} ms)")
         del r
     if "skewed" in which:
         b = wl.make("skewed")
@@ -552,6 +566,13 @@ def main():
                            "step_tflops_incl_append": round(p["step_tflops"], 2),
                            "workload": "chunked prefill/append: 8 requests, qo U[512,2048], prefix U[0,8192], "
                                        "page 16, HND, 32/8 heads, d128, bf16, causal"}
+    if "fp8_prefill" in result:
+        p = result["fp8_prefill"]
+        line["fp8_prefill"] = {"value": round(p["tflops"], 2), "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                               "frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
+                               "launch_ms_mean": round(p["attn_ms_mean"], 4),
+                               "workload": "the chunked prefill batch with an E4M3 K/V cache (bf16 queries and "
+                                           "outputs; the products run in bf16)"}
     if "skewed" in result:
         s = result["skewed"]
         line["skewed_decode"] = {"value": round(s["gbs"], 1), "unit": "GB/s", "frac": round(s["gbs"] / HBM_PEAK_GBS, 4),

@@ -159,8 +159,9 @@ constexpr int32_t kCascadeTargetPerCu = 1;
 constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
-  if (mode != PKV_MODE_PREFILL || kv_dtype != PKV_BF16) return 1;
-  if (mask_mode == PKV_MASK_CUSTOM && group < 2) return 1;   // masked tiles need a head group of 2+
+  if (mode != PKV_MODE_PREFILL || (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)) return 1;
+  if (mask_mode == PKV_MASK_CUSTOM && (group < 2 || kv_dtype != PKV_BF16))
+    return 1;   // masked tiles need a bf16 cache and a head group of 2+
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
 
@@ -873,8 +874,8 @@ pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::A
   const int32_t group = p.num_qo_heads / p.num_kv_heads;
   bool supported = false;
   hipError_t e;
-  if (mode == PKV_MODE_PREFILL && p.kv_dtype == PKV_BF16)
-    e = pkv::launch_prefill_mfma(p.head_dim_qk, group, a, st, &supported);
+  if (mode == PKV_MODE_PREFILL && (p.kv_dtype == PKV_BF16 || p.kv_dtype == PKV_FP8_E4M3))
+    e = pkv::launch_prefill_mfma(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
   else
     e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
   if (!supported)

@@ -147,8 +147,8 @@ struct MlaArgs {
 // Kernel launchers (each returns the launch error, if any).
 hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
                             hipStream_t stream, bool* supported);
-hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& a, hipStream_t stream,
-                               bool* supported);
+hipError_t launch_prefill_mfma(int32_t kv_dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
+                               hipStream_t stream, bool* supported);
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t stream);

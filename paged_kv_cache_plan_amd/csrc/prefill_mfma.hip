@@ -43,6 +43,16 @@
 // The epilogue writes the normalised rows (bf16) and base-2 LSE, or fp32
 // partial states for the split merge ("A worked split-KV example").
 //
+// fp8 caches ("FlashInfer 中的 KV-Cache 布局" names E4M3 caches): the kFp8
+// variant moves K and V tiles of E4M3 codes (128-byte rows, half the bytes)
+// through a ring of four fp8 slots by the same direct loads.  One tile step
+// ahead of its use, the waves expand each landed tile exactly into bf16
+// (v_cvt_scalef32_pk_bf16_fp8) and store it, with the bf16 swizzles, into one
+// of two bf16 work tiles, which the unchanged MFMA phases then read.  The
+// expansion of tile t+1 and the products of tile t share one barrier per step.
+// The K scale is folded into the logit scale, the V scale into the final
+// normalisation.
+//
 // Custom masks ("FlashInfer 中的 KV-Cache 布局", "掩码布局"): the kMask
 // variant moves, with every K tile, the tile's mask bits of each of its rows
 // into LDS by the same direct loads: 32 bytes per row, read from the 16-byte
@@ -125,24 +135,52 @@ __device__ __forceinline__ void dma_barrier() {
   static_assert(kLoadsPerTile == 4, "the wait count below is written out");
   asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// fp8 tiles: one load per thread for each of K and V per step, and the slot
+// expanded in step t was loaded in step t-2, so only the previous step's two
+// loads may still be outstanding.
+__device__ __forceinline__ void dma_barrier_fp8() {
+  asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 E4M3 codes -> two chunks of 8 bf16 values (exact conversion).
+__device__ __forceinline__ void expand_fp8(const uint4& raw, uint4& lo, uint4& hi) {
+  auto cv0 = [](uint32_t w) {   // codes in bytes 0, 1
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  };
+  auto cv1 = [](uint32_t w) {   // codes in bytes 2, 3
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  };
+  lo = make_uint4(cv0(raw.x), cv1(raw.x), cv0(raw.y), cv1(raw.y));
+  hi = make_uint4(cv0(raw.z), cv1(raw.z), cv0(raw.w), cv1(raw.w));
+}
+
 // Waves that also load mask rows issue kLoadsPerTile + 1 loads per step.
 __device__ __forceinline__ void dma_barrier_mask_wave() {
   asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int G, bool kPow2, bool kMask>
+template <int G, bool kPow2, bool kMask, bool kFp8>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArgs a) {
   constexpr int kTileRows = 256 / G;                 // query rows of a work item
   constexpr int kMaskInstr = kTileRows * 2 / 64;     // 16-byte mask pieces of a tile / 64 lanes
   static_assert(!kMask || (kMaskInstr >= 1 && kMaskInstr <= kWaves), "mask rows per tile");
+  static_assert(!(kMask && kFp8), "custom masks over fp8 caches run the row kernel");
+  constexpr int kEs = kFp8 ? 1 : 2;                  // bytes per stored K/V element
   // Ring slot i holds K(t+1) (first half) and V(t) (second half) for the
   // tile steps t with t % 4 == i: exactly what step t reads, and what step
   // t-3 loads.  Four separate arrays, so the compiler can tell the slot being
-  // read from the slots being loaded.
-  __shared__ __attribute__((aligned(16))) uint16_t s_b0[2 * kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b1[2 * kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b2[2 * kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b3[2 * kTile];
+  // read from the slots being loaded.  (kFp8: the ring holds E4M3 codes in
+  // s_f<i>, and step t reads the bf16 work tile s_w<t % 2>.)
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[kFp8 ? 8 : 2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[kFp8 ? 8 : 2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b2[kFp8 ? 8 : 2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b3[kFp8 ? 8 : 2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t s_f0[kFp8 ? 2 * kTile : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_f1[kFp8 ? 2 * kTile : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_f2[kFp8 ? 2 * kTile : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_f3[kFp8 ? 2 * kTile : 16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w0[kFp8 ? 2 * kTile : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w1[kFp8 ? 2 * kTile : 8];
   __shared__ int32_t s_pages[kMaxChunkPages];
   // Mask ring (kMask): slot i holds, for the tile whose K is in s_b<i>, 32
   // bytes per tile row.
@@ -183,13 +221,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     mask_dma_bit = mr.bit0 + int64_t(local0 + (dma_r < it.num_rows ? dma_r : 0)) * mr.kv_len;
   }
 
-  const char* const kbase = static_cast<const char*>(a.k) + int64_t(kvh) * a.head_stride * 2;
-  const char* const vbase = static_cast<const char*>(a.v) + int64_t(kvh) * a.head_stride * 2;
+  const char* const kbase = static_cast<const char*>(a.k) + int64_t(kvh) * a.head_stride * kEs;
+  const char* const vbase = static_cast<const char*>(a.v) + int64_t(kvh) * a.head_stride * kEs;
   const int32_t* pages = a.kv_indices + it.page_base;
   const int32_t psz = a.page_size, pshift = a.page_shift;
   const uint32_t max_pages = uint32_t(a.max_num_pages);
-  const int64_t page_bytes = a.page_stride * 2;
-  const uint32_t tok_bytes = uint32_t(a.token_stride) * 2;   // the launcher bounds 16 rows of it below 2^31
+  const int64_t page_bytes = a.page_stride * kEs;
+  const uint32_t tok_bytes = uint32_t(a.token_stride) * kEs;   // the launcher bounds 16 rows of it below 2^31
 
   // Q^T as the B operand: k-step s covers dims [16s, 16s+16); this lane holds dims 16s + 8h + [0, 8).
   uint4 qreg[8];
@@ -450,6 +488,74 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     }
   };
 
+  // fp8 tiles: 64 rows of 128 codes (8 KiB).  Wave w's single load
+  // instruction of a tile fills rows 8w + l/8, chunk l%8 (lane l), unswizzled;
+  // keys past the chunk end re-read the last key.  On pages of >= 8 keys (a
+  // power of two) the 8 rows of an instruction share a page.
+  const bool aligned8 = kPow2 && pshift >= 3;
+  const uint32_t lane8 = uint32_t(lane >> 3) * tok_bytes + uint32_t(lane & 7) * 16;
+  auto load8 = [&](const char* base, uint8_t* dst, int32_t t0) {
+    if constexpr (kFp8) {
+      const int32_t r0 = t0 + 8 * wave;
+      const char* src;
+      if (aligned8 && t0 + kKeys <= kv_hi) {
+        const int32_t pg = __builtin_amdgcn_readfirstlane(s_pages[(r0 >> pshift) - pg_lo]);
+        src = base + (int64_t(pg) * page_bytes + int64_t(r0 & (psz - 1)) * tok_bytes) + lane8;
+      } else {
+        const int32_t j = min(r0 + (lane >> 3), kv_hi - 1);
+        const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
+        const int32_t sl = kPow2 ? (j & (psz - 1)) : (j - pi * psz);
+        const int32_t pg = s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
+        src = base + (int64_t(pg) * page_bytes + int64_t(sl) * tok_bytes) + (lane & 7) * 16;
+      }
+      dma16_bytes(src, dst + 1024 * wave);
+    }
+  };
+  // Expands an fp8 slot (K half, V half) into a bf16 work tile with the bf16
+  // swizzles: thread c expands chunk c (row c/8, dims 16(c%8) + [0, 16)) of
+  // each half into bf16 chunks 2(c%8) and 2(c%8) + 1 of that row.
+  auto expand_tile = [&](const uint8_t* src, uint16_t* dst) {
+    if constexpr (kFp8) {
+      const int row = tid >> 3, c2 = 2 * (tid & 7);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src + half * kTile + 16 * tid);
+        uint4 lo, hi;
+        expand_fp8(raw, lo, hi);
+        const int swz = half == 0 ? (row & 15) : 4 * (row & 3);
+        uint16_t* drow = dst + half * kTile + row * kD;
+        *reinterpret_cast<uint4*>(drow + (c2 ^ swz) * 8) = lo;
+        *reinterpret_cast<uint4*>(drow + ((c2 + 1) ^ swz) * 8) = hi;
+      }
+    }
+  };
+  // fp8 tile step t: fp8 slot (t+1) % 4 (K(t+2), V(t+1)) landed for every wave
+  // and is expanded into work tile (t+1) % 2 for the next step; this step's
+  // products read work tile t % 2 (K(t+1), V(t)), expanded during step t-1.
+  // Slot (t+3) % 4, expanded during step t-2, takes V(t+3) and K(t+4).
+  auto body8 = [&](int32_t t, uint8_t* fdma, const uint8_t* fexp, uint16_t* wexp, const uint16_t* wread,
+                   f32x16_t (&sc)[2]) {
+    const int32_t t0 = kv_lo + t * kKeys;
+    dma_barrier_fp8();
+    load8(vbase, fdma + kTile, t0 + 3 * kKeys);
+    load8(kbase, fdma, t0 + 4 * kKeys);
+    expand_tile(fexp, wexp);
+    if (!wave_active) return;
+    const float shift = m_used != -INFINITY ? m_used : 0.f;
+    float ls0 = 0.f, ls1 = 0.f;
+    uint4 pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pb[ks] = weights(sc, ks, shift, ls0, ls1);
+    lsum += ls0 + ls1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pv_step(wread + kTile, ks, pb[ks]);
+    if (t + 1 < ntiles) {
+      scores(wread, sc);
+      mask_tile(sc, t0 + kKeys, nullptr);
+      update_max(tile_max(sc));
+    }
+  };
+
   // The prologue loads K(0) (slot 3), then V(s) and K(s+1) into slot s for
   // s = 0, 1, 2, and waits for all but the last two steps.
   f32x16_t sc[2];
@@ -459,7 +565,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   uint4* const m1 = s_mask + kMaskSlot;
   uint4* const m2 = s_mask + 2 * kMaskSlot;
   uint4* const m3 = s_mask + 3 * kMaskSlot;
-  if (ntiles > 0) {
+  if constexpr (kFp8) {
+   if (ntiles > 0) {
+    // fp8 prologue: K(0) -> slot 3, then V(s), K(s+1) -> slot s for s = 0, 1,
+    // 2 (one load per thread each); K(0), V(0) and K(1) land (four loads stay
+    // in flight), are expanded into work tiles 1 (K(0)) and 0, and the scores
+    // of tile 0 come from work tile 1.
+    load8(kbase, s_f3, kv_lo);
+    load8(vbase, s_f0 + kTile, kv_lo);
+    load8(kbase, s_f0, kv_lo + kKeys);
+    load8(vbase, s_f1 + kTile, kv_lo + kKeys);
+    load8(kbase, s_f1, kv_lo + 2 * kKeys);
+    load8(vbase, s_f2 + kTile, kv_lo + 2 * kKeys);
+    load8(kbase, s_f2, kv_lo + 3 * kKeys);
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    expand_tile(s_f3, s_w1);   // its V half is never read
+    expand_tile(s_f0, s_w0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave_active) {
+      scores(s_w1, sc);
+      mask_tile(sc, kv_lo, nullptr);
+      update_max(tile_max(sc));
+    }
+    for (int32_t t = 0; t < ntiles; t += 4) {
+      body8(t, s_f3, s_f1, s_w1, s_w0, sc);
+      if (t + 1 >= ntiles) break;
+      body8(t + 1, s_f0, s_f2, s_w0, s_w1, sc);
+      if (t + 2 >= ntiles) break;
+      body8(t + 2, s_f1, s_f3, s_w1, s_w0, sc);
+      if (t + 3 >= ntiles) break;
+      body8(t + 3, s_f2, s_f0, s_w0, s_w1, sc);
+    }
+    dma_drain();
+   }
+  } else if (ntiles > 0) {
     load_k(s_b3, kv_lo);
     load_m(m3, kv_lo);
     load_v(s_b0 + kTile, kv_lo);
@@ -495,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (!pair_ok) return;
   const bool empty = !(ltot > 0.f);
-  const float inv = empty ? 0.f : 1.f / ltot;
+  const float inv = empty ? 0.f : (kFp8 ? a.v_scale : 1.f) / ltot;
   const float lse2 = empty ? -INFINITY : m_used + __log2f(ltot);
   const int32_t hq = a.num_qo_heads;
   if (it.out_slot < 0) {
@@ -527,46 +666,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   }
 }
 
-template <int G, bool kMask>
+template <int G, bool kMask, bool kFp8>
 hipError_t launch_gm(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
   if (a.page_shift >= 0)
-    launch_attention_kernel(prefill_mfma_kernel<G, true, kMask>, grid, block, st, a);
+    launch_attention_kernel(prefill_mfma_kernel<G, true, kMask, kFp8>, grid, block, st, a);
   else
-    launch_attention_kernel(prefill_mfma_kernel<G, false, kMask>, grid, block, st, a);
+    launch_attention_kernel(prefill_mfma_kernel<G, false, kMask, kFp8>, grid, block, st, a);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_g(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_g(const AttnArgs& a, bool fp8, hipStream_t st) {
+  if (fp8) return launch_gm<G, false, true>(a, st);
   if constexpr (G >= 2) {
-    if (a.mask) return launch_gm<G, true>(a, st);
+    if (a.mask) return launch_gm<G, true, false>(a, st);
   }
-  return launch_gm<G, false>(a, st);
+  return launch_gm<G, false, false>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(int32_t head_dim, int32_t group, const AttnArgs& a, hipStream_t st,
-                               bool* supported) {
+hipError_t launch_prefill_mfma(int32_t kv_dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
+                               hipStream_t st, bool* supported) {
   // The tile loader forms 16 rows of token stride as a 32-bit byte offset.
   const bool strides_ok = a.token_stride >= 0 && a.token_stride * 2 * 16 < (int64_t(1) << 31);
+  const bool fp8 = kv_dtype == kFP8;
   // A custom mask runs here for head groups of 2 or more (the mask tiles of
-  // 256 rows would not fit the LDS left over).
-  if (head_dim == kD && strides_ok && !(a.mask && group < 2)) {
+  // 256 rows would not fit the LDS left over), and not over fp8 caches.
+  const bool mask_ok = !a.mask || (group >= 2 && !fp8);
+  if (head_dim == kD && strides_ok && mask_ok && (fp8 || kv_dtype == kBF16)) {
     *supported = true;
     switch (group) {
-      case 1: return launch_g<1>(a, st);
-      case 2: return launch_g<2>(a, st);
-      case 4: return launch_g<4>(a, st);
-      case 8: return launch_g<8>(a, st);
+      case 1: return launch_g<1>(a, fp8, st);
+      case 2: return launch_g<2>(a, fp8, st);
+      case 4: return launch_g<4>(a, fp8, st);
+      case 8: return launch_g<8>(a, fp8, st);
       default: break;
     }
   }
   // Other shapes run the row kernel (same results, VALU arithmetic).
-  return launch_attn_rows(kBF16, head_dim, group, a, st, supported);
+  return launch_attn_rows(kv_dtype, head_dim, group, a, st, supported);
 }
 
 }  // namespace pkv

@@ -87,7 +87,8 @@ def test_fp8_every_finite_code(torch, pkv, fixed):
 def test_fp8_prefill_append_hnd(torch, pkv):
     """Chunked prefill (a quarter of the prefill workload, HND, causal) over an
     fp8 cache: the new fp8 rows are appended first (byte copies), then the
-    row kernel runs every query row."""
+    MFMA tile kernel runs 64-row tiles, expanding the fp8 tiles to bf16 in
+    LDS."""
     print("case fp8 prefill", flush=True)
     b = wl.make("prefill", kv_dtype="fp8", scale=0.25, batch=4, poison=True)
     k_dev, v_dev = _u8(torch, b.k_cache), _u8(torch, b.v_cache)
@@ -102,7 +103,7 @@ def test_fp8_prefill_append_hnd(torch, pkv):
         k_exp[page, :, slot], v_exp[page, :, slot] = b.k_new[t], b.v_new[t]
     assert np.array_equal(k_dev.cpu().numpy(), k_exp) and np.array_equal(v_dev.cpu().numpy(), v_exp)
     plan, o, lse = _run(pkv, torch, b, k_dev, v_dev, k_scale=1.0, v_scale=1.0)
-    assert plan.info["rows_per_tile"] == 1
+    assert plan.info["rows_per_tile"] == 64
     ro, rl = _oracle(b, k_exp, v_exp, 1.0, 1.0)
     gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 prefill o")
     gu.check_lse(lse, rl, "fp8 prefill lse")
@@ -115,3 +116,32 @@ def test_fp8_odd_page_size(torch, pkv):
     ro, rl = _oracle(b, b.k_cache, b.v_cache, 0.25, 4.0)
     gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 page 3 o")
     gu.check_lse(lse, rl, "fp8 page 3 lse")
+
+
+@pytest.mark.parametrize("layout,page_size,fixed,group", [
+    ("NHD", 3, 0, 4),      # no power of two: every key located through the page table
+    ("HND", 8, 2, 4),      # 8-key pages (one page per load instruction); forced splits
+    ("NHD", 16, 1, 2),
+    ("HND", 1, 0, 8),
+    ("NHD", 32, 3, 1),     # 256-row tiles
+])
+def test_fp8_prefill_mfma_shapes(torch, pkv, layout, page_size, fixed, group):
+    """Prefill over an fp8 cache on the MFMA tile kernel across page sizes,
+    layouts, head groups and forced splits, with non-unit K and V scales (the
+    V scale reaches split rows before their merge)."""
+    print("case fp8 prefill", layout, page_size, fixed, group, flush=True)
+    b = wl.make("prefill", kv_dtype="fp8", layout=layout, page_size=page_size, batch=4, qo_range=(1, 150),
+                prefix_range=(0, 400), hq=2 * group, hkv=2, poison=True)
+    k_dev, v_dev = _u8(torch, b.k_cache), _u8(torch, b.v_cache)
+    pkv.append_paged_kv(_u8(torch, b.k_new), _u8(torch, b.v_new), gu.to_dev(b.append_indptr, "i32"),
+                        gu.to_dev(b.kv_indptr, "i32"), gu.to_dev(b.kv_indices, "i32"),
+                        gu.to_dev(b.kv_last_page_len, "i32"), k_dev, v_dev, layout=layout, page_size=page_size)
+    torch.cuda.synchronize()
+    k_exp, v_exp = k_dev.cpu().numpy(), v_dev.cpu().numpy()
+    plan, o, lse = _run(pkv, torch, b, k_dev, v_dev, k_scale=0.5, v_scale=2.0, fixed=fixed, num_cus=8 if fixed else 0)
+    assert plan.info["rows_per_tile"] == 256 // group
+    if fixed > 1:
+        assert plan.info["num_merges"] > 0
+    ro, rl = _oracle(b, k_exp, v_exp, 0.5, 2.0)
+    gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 prefill o")
+    gu.check_lse(lse, rl, "fp8 prefill lse")
