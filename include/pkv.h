@@ -567,7 +567,9 @@ pkv_status pkv_run_masked(const pkv_plan* plan, const void* q, int64_t q_stride_
  * kv_indptr[b] + j of the data tensors.
  *   k, v         device, element (token t, kv head h, dim d) at
  *                k + t*kv_stride_token + h*kv_stride_head + d (NHD: strides
- *                Hkv*D and D), dtype of the plan
+ *                Hkv*D and D), the plan's kv_dtype (an fp8 plan reads E4M3
+ *                codes with unit scales: fold a K scale into sm_scale and
+ *                apply a V scale to the output)
  *   d_kv_indptr  device int32, B+1 entries, the same values the plan was built on
  *   d_mask       device bit-packed custom mask (as for pkv_run_masked) for a
  *                custom-masked plan, else NULL

@@ -328,8 +328,9 @@ class Plan:
             raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
             raise TypeError("lse must be contiguous float32")
-        _check(lib().pkv_run_ragged(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), _dev(k, "k", q.dtype),
-                                    _dev(v, "v", q.dtype), k.stride(0), k.stride(1),
+        kv_dt = torch.uint8 if self.params.kv_dtype == FP8_E4M3 else q.dtype   # fp8: E4M3 codes
+        _check(lib().pkv_run_ragged(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), _dev(k, "k", kv_dt),
+                                    _dev(v, "v", kv_dt), k.stride(0), k.stride(1),
                                     _dev(kv_indptr, "kv_indptr", torch.int32),
                                     None if mask_packed is None else _dev(mask_packed, "mask", torch.uint8),
                                     _dev(out, "out", q.dtype), out.stride(0), out.stride(1),

@@ -1024,8 +1024,9 @@ pkv_status pkv_run_ragged(const pkv_plan* plan, const void* q, int64_t q_stride_
   if (p.kv_format != PKV_KV_RAGGED) return fail(PKV_ERR_INVALID_ARG, "not a ragged plan");
   // The ragged tensors as a cache of one unbounded page per request: page b
   // starts at token kv_indptr[b] (page stride = token stride), so key j is
-  // slot j of that page.
-  pkv_cache_desc desc;
+  // slot j of that page.  Scales stay at zero, i.e. 1 (an fp8 ragged run
+  // takes unit scales).
+  pkv_cache_desc desc{};
   desc.k = const_cast<void*>(k);
   desc.v = const_cast<void*>(v);
   desc.page_stride = kv_stride_token;

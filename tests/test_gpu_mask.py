@@ -101,6 +101,38 @@ def test_ragged_prefill(torch, pkv, dtype, hq, hkv, d, causal, masked, fixed):
     gu.check_lse(lse.cpu().numpy(), rl, "ragged lse", atol=1e-5 if dtype == "f32" else 1e-3)
 
 
+@pytest.mark.parametrize("hq,causal,fixed", [(16, True, 0), (8, False, 3), (16, False, 0)])
+def test_ragged_prefill_fp8(torch, pkv, hq, causal, fixed):
+    """Ragged keys and values stored as E4M3 codes (bf16 queries and outputs):
+    the MFMA tile kernel expands the tiles to bf16 in LDS; with a custom mask
+    (the last case) the row kernel runs instead."""
+    print("case ragged fp8", hq, causal, fixed, flush=True)
+    masked = not causal and not fixed
+    rng = np.random.default_rng(17)
+    qo_lens, kv_extra = [37, 0, 300, 129, 64, 5], [0, 9, 700, 0, 33, 1]
+    kv_lens = [q + e for q, e in zip(qo_lens, kv_extra)]
+    qo = np.array([0] + list(np.cumsum(qo_lens)), np.int32)
+    kv = np.array([0] + list(np.cumsum(kv_lens)), np.int32)
+    q = _payload(rng, (int(qo[-1]), hq, 128), "bf16")
+    k = wl.to_fp8_codes(rng.standard_normal((int(kv[-1]), 8, 128)).astype(np.float32))
+    v = wl.to_fp8_codes(rng.standard_normal((int(kv[-1]), 8, 128)).astype(np.float32))
+    mask = _mask(rng, qo_lens, kv_lens) if masked else None
+    params = pkv.plan_params(mode="prefill", batch_size=len(qo_lens), num_qo_heads=hq, num_kv_heads=8,
+                             head_dim_qk=128, page_size=16, causal=causal, dtype="bf16", kv_dtype="fp8",
+                             ragged=True, custom_mask=masked, fixed_split_pages=fixed, num_cus=16 if fixed else 0)
+    plan = pkv.Plan(params, qo_indptr=qo, kv_indptr=kv, kv_last_page_len=None)
+    qd = gu.to_dev(q, "bf16")
+    out = gu.empty_like_out(qd.shape, "bf16")
+    lse = torch.full((qd.shape[0], hq), float("nan"), dtype=torch.float32, device="cuda")
+    plan.run_ragged(qd, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), gu.to_dev(kv, "i32"), out, lse,
+                    mask_packed=_packed(torch, pkv, mask) if masked else None, sm_scale=1.0 / math.sqrt(128))
+    torch.cuda.synchronize()
+    ro, rl = omask.ragged_attention(q, k, v, qo_indptr=list(qo), kv_indptr=list(kv), num_kv_heads=8, causal=causal,
+                                    custom_mask=mask, sm_scale=1.0 / math.sqrt(128), q_dtype="bf16", kv_dtype="fp8")
+    gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "ragged fp8 o")
+    gu.check_lse(lse.cpu().numpy(), rl, "ragged fp8 lse")
+
+
 @pytest.mark.parametrize("fixed", [0, 1, 2])
 def test_paged_custom_mask(torch, pkv, fixed):
     """The pages' three-request batch shape on a paged cache (page 4) with a
