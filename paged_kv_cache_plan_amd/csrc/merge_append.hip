@@ -174,8 +174,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(const Mer
     if (fast) {
       const int32_t d = d_lo + 2 * lane;
       const float* src = pbase + (d < d_hi ? d : d_lo);
+      // Only the row's own chunks are loaded (n is uniform over the wave).
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pre[j] = *reinterpret_cast<const float2*>(src + int64_t(min(j, n - 1)) * chunk_stride);
+      for (int j = 0; j < 8; ++j)
+        pre[j] = j < n ? *reinterpret_cast<const float2*>(src + int64_t(j) * chunk_stride) : make_float2(0.f, 0.f);
     }
     const float sc = lane < n ? a.part_lse[(row_base + int64_t(lane) * mi.num_rows) * hq + h] : -INFINITY;
     const float mx = wave_max(sc);
