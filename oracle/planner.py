@@ -49,13 +49,13 @@ RAGGED_PAGE = 16                # ragged keys are chunked as if in pages of this
 
 
 def rows_per_tile(mode: str, group: int, kv_dtype: str, masked: bool = False) -> int:
-    """Query rows per work item: 1 for decode, MLA and float32 prefill, for
-    custom-masked prefill over an fp8 cache and for custom-masked prefill with
-    one query head per kv head; for prefill over a bfloat16 or fp8 cache as
-    many rows as fit a 256-high tile of (row, head) pairs."""
+    """Query rows per work item: 1 for decode, MLA and float32 prefill and for
+    custom-masked prefill with one query head per kv head; for prefill over a
+    bfloat16 or fp8 cache as many rows as fit a 256-high tile of (row, head)
+    pairs."""
     if mode != PREFILL or kv_dtype not in ("bf16", "fp8"):
         return 1
-    if masked and (group < 2 or kv_dtype != "bf16"):
+    if masked and group < 2:
         return 1
     return max(1, MFMA_TILE_ROWS // group)
 

@@ -160,8 +160,7 @@ constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages 
 
 int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
   if (mode != PKV_MODE_PREFILL || (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)) return 1;
-  if (mask_mode == PKV_MASK_CUSTOM && (group < 2 || kv_dtype != PKV_BF16))
-    return 1;   // masked tiles need a bf16 cache and a head group of 2+
+  if (mask_mode == PKV_MASK_CUSTOM && group < 2) return 1;   // masked tiles need a head group of 2+
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
 

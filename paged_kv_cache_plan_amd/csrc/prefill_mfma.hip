@@ -141,6 +141,10 @@ __device__ __forceinline__ void dma_barrier() {
 __device__ __forceinline__ void dma_barrier_fp8() {
   asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// ... and for the waves that also load mask rows (three loads per step).
+__device__ __forceinline__ void dma_barrier_fp8_mask_wave() {
+  asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // 16 E4M3 codes -> two chunks of 8 bf16 values (exact conversion).
 __device__ __forceinline__ void expand_fp8(const uint4& raw, uint4& lo, uint4& hi) {
@@ -164,7 +168,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   constexpr int kTileRows = 256 / G;                 // query rows of a work item
   constexpr int kMaskInstr = kTileRows * 2 / 64;     // 16-byte mask pieces of a tile / 64 lanes
   static_assert(!kMask || (kMaskInstr >= 1 && kMaskInstr <= kWaves), "mask rows per tile");
-  static_assert(!(kMask && kFp8), "custom masks over fp8 caches run the row kernel");
   constexpr int kEs = kFp8 ? 1 : 2;                  // bytes per stored K/V element
   // Ring slot i holds K(t+1) (first half) and V(t) (second half) for the
   // tile steps t with t % 4 == i: exactly what step t reads, and what step
@@ -534,11 +537,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   // products read work tile t % 2 (K(t+1), V(t)), expanded during step t-1.
   // Slot (t+3) % 4, expanded during step t-2, takes V(t+3) and K(t+4).
   auto body8 = [&](int32_t t, uint8_t* fdma, const uint8_t* fexp, uint16_t* wexp, const uint16_t* wread,
-                   f32x16_t (&sc)[2]) {
+                   const uint4* mread, uint4* mdma, f32x16_t (&sc)[2]) {
     const int32_t t0 = kv_lo + t * kKeys;
-    dma_barrier_fp8();
+    if (kMask && wave < kMaskInstr) dma_barrier_fp8_mask_wave();
+    else dma_barrier_fp8();
     load8(vbase, fdma + kTile, t0 + 3 * kKeys);
     load8(kbase, fdma, t0 + 4 * kKeys);
+    load_m(mdma, t0 + 4 * kKeys);
     expand_tile(fexp, wexp);
     if (!wave_active) return;
     const float shift = m_used != -INFINITY ? m_used : 0.f;
@@ -551,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
     for (int ks = 0; ks < 4; ++ks) pv_step(wread + kTile, ks, pb[ks]);
     if (t + 1 < ntiles) {
       scores(wread, sc);
-      mask_tile(sc, t0 + kKeys, nullptr);
+      mask_tile(sc, t0 + kKeys, mread);
       update_max(tile_max(sc));
     }
   };
@@ -568,33 +573,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(const AttnArg
   if constexpr (kFp8) {
    if (ntiles > 0) {
     // fp8 prologue: K(0) -> slot 3, then V(s), K(s+1) -> slot s for s = 0, 1,
-    // 2 (one load per thread each); K(0), V(0) and K(1) land (four loads stay
-    // in flight), are expanded into work tiles 1 (K(0)) and 0, and the scores
-    // of tile 0 come from work tile 1.
+    // 2 (one load per thread each, plus the mask rows of each K on the mask
+    // waves); K(0), V(0) and K(1) (and their masks) land while the loads of
+    // slots 1 and 2 stay in flight, are expanded into work tiles 1 (K(0)) and
+    // 0, and the scores of tile 0 come from work tile 1.
     load8(kbase, s_f3, kv_lo);
+    load_m(m3, kv_lo);
     load8(vbase, s_f0 + kTile, kv_lo);
     load8(kbase, s_f0, kv_lo + kKeys);
+    load_m(m0, kv_lo + kKeys);
     load8(vbase, s_f1 + kTile, kv_lo + kKeys);
     load8(kbase, s_f1, kv_lo + 2 * kKeys);
+    load_m(m1, kv_lo + 2 * kKeys);
     load8(vbase, s_f2 + kTile, kv_lo + 2 * kKeys);
     load8(kbase, s_f2, kv_lo + 3 * kKeys);
-    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    load_m(m2, kv_lo + 3 * kKeys);
+    if (kMask && wave < kMaskInstr) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     expand_tile(s_f3, s_w1);   // its V half is never read
     expand_tile(s_f0, s_w0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (wave_active) {
       scores(s_w1, sc);
-      mask_tile(sc, kv_lo, nullptr);
+      mask_tile(sc, kv_lo, m3);
       update_max(tile_max(sc));
     }
     for (int32_t t = 0; t < ntiles; t += 4) {
-      body8(t, s_f3, s_f1, s_w1, s_w0, sc);
+      body8(t, s_f3, s_f1, s_w1, s_w0, m0, m3, sc);
       if (t + 1 >= ntiles) break;
-      body8(t + 1, s_f0, s_f2, s_w0, s_w1, sc);
+      body8(t + 1, s_f0, s_f2, s_w0, s_w1, m1, m0, sc);
       if (t + 2 >= ntiles) break;
-      body8(t + 2, s_f1, s_f3, s_w1, s_w0, sc);
+      body8(t + 2, s_f1, s_f3, s_w1, s_w0, m2, m1, sc);
       if (t + 3 >= ntiles) break;
-      body8(t + 3, s_f2, s_f0, s_w0, s_w1, sc);
+      body8(t + 3, s_f2, s_f0, s_w0, s_w1, m3, m2, sc);
     }
     dma_drain();
    }
@@ -680,11 +691,10 @@ hipError_t launch_gm(const AttnArgs& a, hipStream_t st) {
 
 template <int G>
 hipError_t launch_g(const AttnArgs& a, bool fp8, hipStream_t st) {
-  if (fp8) return launch_gm<G, false, true>(a, st);
   if constexpr (G >= 2) {
-    if (a.mask) return launch_gm<G, true, false>(a, st);
+    if (a.mask) return fp8 ? launch_gm<G, true, true>(a, st) : launch_gm<G, true, false>(a, st);
   }
-  return launch_gm<G, false, false>(a, st);
+  return fp8 ? launch_gm<G, false, true>(a, st) : launch_gm<G, false, false>(a, st);
 }
 
 }  // namespace
@@ -695,8 +705,8 @@ hipError_t launch_prefill_mfma(int32_t kv_dtype, int32_t head_dim, int32_t group
   const bool strides_ok = a.token_stride >= 0 && a.token_stride * 2 * 16 < (int64_t(1) << 31);
   const bool fp8 = kv_dtype == kFP8;
   // A custom mask runs here for head groups of 2 or more (the mask tiles of
-  // 256 rows would not fit the LDS left over), and not over fp8 caches.
-  const bool mask_ok = !a.mask || (group >= 2 && !fp8);
+  // 256 rows would not fit the LDS left over).
+  const bool mask_ok = !a.mask || group >= 2;
   if (head_dim == kD && strides_ok && mask_ok && (fp8 || kv_dtype == kBF16)) {
     *supported = true;
     switch (group) {

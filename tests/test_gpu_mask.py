@@ -101,13 +101,14 @@ def test_ragged_prefill(torch, pkv, dtype, hq, hkv, d, causal, masked, fixed):
     gu.check_lse(lse.cpu().numpy(), rl, "ragged lse", atol=1e-5 if dtype == "f32" else 1e-3)
 
 
-@pytest.mark.parametrize("hq,causal,fixed", [(16, True, 0), (8, False, 3), (16, False, 0)])
-def test_ragged_prefill_fp8(torch, pkv, hq, causal, fixed):
+@pytest.mark.parametrize("hq,causal,fixed,masked", [(16, True, 0, False), (8, False, 3, False), (16, False, 0, True),
+                                                    (32, False, 2, True), (8, False, 0, True)])
+def test_ragged_prefill_fp8(torch, pkv, hq, causal, fixed, masked):
     """Ragged keys and values stored as E4M3 codes (bf16 queries and outputs):
-    the MFMA tile kernel expands the tiles to bf16 in LDS; with a custom mask
-    (the last case) the row kernel runs instead."""
-    print("case ragged fp8", hq, causal, fixed, flush=True)
-    masked = not causal and not fixed
+    the MFMA tile kernel expands the tiles to bf16 in LDS, custom masks
+    included (head groups 2 and 4); with one query head per kv head a masked
+    plan runs the row kernel."""
+    print("case ragged fp8", hq, causal, fixed, masked, flush=True)
     rng = np.random.default_rng(17)
     qo_lens, kv_extra = [37, 0, 300, 129, 64, 5], [0, 9, 700, 0, 33, 1]
     kv_lens = [q + e for q, e in zip(qo_lens, kv_extra)]
@@ -185,6 +186,34 @@ def test_paged_custom_mask_bf16_prefill_workload(torch, pkv):
                                  kv_dtype="bf16", custom_mask=mask)
     gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "masked prefill o")
     gu.check_lse(lse.cpu().numpy(), rl, "masked prefill lse")
+
+
+def test_paged_custom_mask_fp8_prefill_workload(torch, pkv):
+    """The chunked-prefill workload (scaled to a quarter) over an E4M3 cache
+    with a random mask, HND: the masked MFMA tile kernel on fp8 tiles, with
+    non-unit K and V scales."""
+    b = wl.make("prefill", scale=0.25, batch=4, poison=False, kv_dtype="fp8")
+    rng = np.random.default_rng(19)
+    mask = _mask(rng, b.qo_lens, b.kv_lens, p=0.7, empty_rows=3)
+    params = pkv.plan_params(mode="prefill", batch_size=4, num_qo_heads=32, num_kv_heads=8, head_dim_qk=128,
+                             page_size=16, causal=False, dtype="bf16", kv_dtype="fp8", custom_mask=True,
+                             max_num_pages=b.max_num_pages)
+    plan = pkv.Plan(params, qo_indptr=b.qo_indptr, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
+                    kv_last_page_len=b.kv_last_page_len)
+    assert plan.info["rows_per_tile"] == 64
+    qd = gu.to_dev(b.q, "bf16")
+    out = gu.empty_like_out(qd.shape, "bf16")
+    lse = torch.full((qd.shape[0], 32), float("nan"), dtype=torch.float32, device="cuda")
+    plan.run_masked(qd, torch.from_numpy(b.k_cache).cuda(), torch.from_numpy(b.v_cache).cuda(),
+                    gu.to_dev(b.kv_indices, "i32"), _packed(torch, pkv, mask), out, lse, layout="HND",
+                    sm_scale=b.sm_scale, k_scale=0.5, v_scale=2.0)
+    torch.cuda.synchronize()
+    ro, rl = oat.paged_attention(b.q, b.k_cache, b.v_cache, qo_indptr=list(b.qo_indptr), kv_indptr=list(b.kv_indptr),
+                                 kv_indices=list(b.kv_indices), kv_last_page_len=list(b.kv_last_page_len),
+                                 page_size=16, layout="HND", num_kv_heads=8, sm_scale=b.sm_scale, q_dtype="bf16",
+                                 kv_dtype="fp8", custom_mask=mask, k_scale=0.5, v_scale=2.0)
+    gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "masked fp8 prefill o")
+    gu.check_lse(lse.cpu().numpy(), rl, "masked fp8 prefill lse")
 
 
 def test_masked_and_ragged_plans_need_their_entry_points(torch, pkv):

@@ -153,7 +153,8 @@ def test_rows_per_tile_rule():
     assert pl.rows_per_tile("prefill", 512, "bf16") == 1
     assert pl.rows_per_tile("prefill", 4, "fp8") == 64
     assert pl.rows_per_tile("decode", 4, "fp8") == 1
-    assert pl.rows_per_tile("prefill", 4, "fp8", masked=True) == 1
+    assert pl.rows_per_tile("prefill", 4, "fp8", masked=True) == 64
+    assert pl.rows_per_tile("prefill", 1, "fp8", masked=True) == 1
     assert pl.rows_per_tile("prefill", 4, "bf16", masked=True) == 64
     assert pl.rows_per_tile("prefill", 1, "bf16", masked=True) == 1
 
