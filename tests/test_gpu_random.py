@@ -126,3 +126,68 @@ def test_random_mla_batch(torch, pkv, i):
                             page_size=b.page_size, sm_scale=b.sm_scale, dtype="bf16")
     gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", f"random mla {i} o")
     gu.check_lse(lse.cpu().numpy(), rl, f"random mla {i} lse")
+
+
+N_CASCADE_CASES = 16
+
+
+def _partition(rng, parts):
+    """Random refinement of a list of group sizes: every group splits into 1..3 consecutive groups."""
+    out = []
+    for n in parts:
+        k = int(rng.integers(1, min(3, n) + 1))
+        cuts = sorted(rng.choice(np.arange(1, n), size=k - 1, replace=False).tolist()) if k > 1 else []
+        edges = [0] + cuts + [n]
+        out += [edges[j + 1] - edges[j] for j in range(k)]
+    return out
+
+
+def _cascade_case(i):
+    rng = np.random.default_rng(9800 + i)
+    batch = int(rng.integers(2, 11))
+    depth = int(rng.integers(2, 5))
+    tree = [[batch]]
+    for _ in range(depth - 2):
+        tree.append(_partition(rng, tree[-1]))
+    tree.append([1] * batch)
+    level_kv = [(int(lo), int(lo + rng.integers(0, 60))) for lo in rng.integers(1, 80, size=depth)]
+    bf16 = bool(rng.integers(0, 2))
+    kw = dict(tree=tree, level_kv=level_kv, qo_range=(1, int(rng.integers(1, 6))),
+              page_size=int(rng.choice([1, 4, 16])), layout=str(rng.choice(["NHD", "HND"])),
+              causal=bool(rng.integers(0, 2)), seed=8800 + i, poison=True)
+    if bf16:
+        kw.update(hq=8, hkv=2, dim=128, dtype="bf16")
+    b = wl.make("cascade_small", **kw)
+    return b, int(rng.choice([0, 0, 1, 3]))
+
+
+@pytest.mark.parametrize("i", range(N_CASCADE_CASES))
+def test_random_cascade(torch, pkv, i):
+    from oracle import cascade as occ
+    from oracle import metadata as omd
+    b, fixed = _cascade_case(i)
+    levels = b.extra["levels"]
+    print(f"case random cascade {i}: {b.dtype} page {b.page_size} {b.layout} causal={b.causal} fixed={fixed} "
+          f"tree={[len(lv['kv_lens']) for lv in levels]} qo={list(b.qo_lens)}", flush=True)
+    k_dev, v_dev = gu.to_dev(b.k_cache, b.dtype), gu.to_dev(b.v_cache, b.dtype)
+    pkv.append_paged_kv(gu.to_dev(b.k_new, b.dtype), gu.to_dev(b.v_new, b.dtype), gu.to_dev(b.append_indptr, "i32"),
+                        gu.to_dev(b.kv_indptr, "i32"), gu.to_dev(b.kv_indices, "i32"),
+                        gu.to_dev(b.kv_last_page_len, "i32"), k_dev, v_dev, layout=b.layout, page_size=b.page_size)
+    torch.cuda.synchronize()
+    k_host, v_host = gu.to_host(k_dev, b.dtype), gu.to_host(v_dev, b.dtype)
+    params = pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads,
+                             head_dim_qk=b.head_dim, page_size=b.page_size, causal=b.causal, dtype=b.dtype,
+                             num_cus=8 if fixed else 0, fixed_split_pages=fixed, max_num_pages=k_dev.shape[0])
+    plan = pkv.CascadePlan(params, levels)
+    q = gu.to_dev(b.q, b.dtype)
+    out = gu.empty_like_out(q.shape, b.dtype)
+    lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
+    idx = gu.to_dev(np.concatenate([lv["kv_indices"][:lv["kv_indptr"][-1]] for lv in levels]), "i32")
+    plan.run(q, k_dev, v_dev, idx, out, lse, layout=b.layout, sm_scale=b.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = occ.cascade_attention(b.q, k_host, v_host, levels=levels, page_size=b.page_size, layout=b.layout,
+                                   num_kv_heads=b.num_kv_heads, causal=b.causal, sm_scale=b.sm_scale,
+                                   q_dtype=b.dtype, kv_dtype=b.dtype)
+    got = gu.to_host(out, b.dtype)
+    gu.check_close(gu.as_f64(got, "bf16") if b.dtype == "bf16" else got, ro, b.dtype, f"random cascade {i} o")
+    gu.check_lse(lse.cpu().numpy(), rl, f"random cascade {i} lse", atol=1e-5 if b.dtype == "f32" else 1e-3)
