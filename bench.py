@@ -417,7 +417,7 @@ def main():
         print(json.dumps(data[w]))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path; run with --gpus 1",
+        print("bench.py measures one GPU only: the library has no multi-GPU path; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

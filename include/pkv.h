@@ -43,7 +43,7 @@ enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,  /* null pointer, bad size/stride/alignment, plan/call mismatch */
   PKV_ERR_METADATA = 2,     /* page-table metadata breaks a rule (see pkv_meta_reason) */
-  PKV_ERR_UNSUPPORTED = 3,  /* a head dim, group size, dtype or mode this build has no kernel for */
+  PKV_ERR_UNSUPPORTED = 3,  /* a head dim, group size, dtype or mode the library has no kernel for */
   PKV_ERR_WORKSPACE = 4,    /* workspace or staging buffer too small */
   PKV_ERR_STALE_PLAN = 5,   /* pkv_plan_check: metadata differs from what the plan was built on */
   PKV_ERR_HIP = 6           /* a HIP runtime call failed (message has the HIP error string) */
