@@ -433,3 +433,36 @@ def test_timing_events_are_armed_in_pairs():
     with pytest.raises(ValueError):
         pkv.time_next_attention(object(), None)
     pkv.time_next_attention()          # disarm: both NULL
+
+
+def test_binding_rejects_bad_host_and_device_arguments():
+    """Argument checks of the Python binding that run before any C call: host
+    metadata must be int32 (never silently cast), device arguments must be
+    device tensors of the right dtype, and metadata lengths must match the
+    batch size the plan was made for."""
+    import torch
+    from paged_kv_cache_plan_amd import _check_batch, _dev, _dtype_code, _host_i32
+    assert _host_i32(None, "x") == (None, None)
+    arr, ptr = _host_i32([0, 3, 4], "x")
+    assert arr.dtype == np.int32 and list(arr) == [0, 3, 4] and ptr is not None
+    for bad in (np.array([0, 1], np.int64), torch.tensor([0, 1], dtype=torch.int64), [0.5, 1.0]):
+        with pytest.raises(TypeError):
+            _host_i32(bad if not isinstance(bad, list) else np.asarray(bad), "x")
+    with pytest.raises(TypeError):
+        _dev(torch.zeros(4), "q")                       # a host tensor where a device one is needed
+    with pytest.raises(TypeError):
+        _dev(np.zeros(4), "q")
+    assert _dtype_code(torch.zeros(1, dtype=torch.bfloat16)) == _abi.BF16
+    assert _dtype_code(torch.zeros(1, dtype=torch.uint8)) == _abi.FP8_E4M3
+    with pytest.raises(TypeError):
+        _dtype_code(torch.zeros(1, dtype=torch.float16))
+    p = pkv.plan_params(mode="prefill", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                        page_size=4, dtype="f32")
+    _check_batch(p, [0, 1, 2], [0, 1, 2], [1, 1])
+    for qo, kvp, last in (([0, 1], [0, 1, 2], [1, 1]), ([0, 1, 2], [0, 1], [1, 1]), ([0, 1, 2], [0, 1, 2], [1]),
+                          ([0, 1, 2], None, [1, 1]), ([0, 1, 2], [0, 1, 2], None)):
+        with pytest.raises(ValueError):
+            _check_batch(p, qo, kvp, last)
+    r = pkv.plan_params(mode="prefill", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                        page_size=4, dtype="f32", ragged=True)
+    _check_batch(r, [0, 1, 2], [0, 3, 5], None)          # ragged plans take no tail lengths
