@@ -3,6 +3,9 @@ inputs and the tolerance checks.  Imports torch lazily."""
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # Tolerances: float32 paths within 1e-5 max-abs; bfloat16 outputs within
@@ -10,6 +13,20 @@ import numpy as np
 F32_ATOL = 1e-5
 BF16_ATOL, BF16_RTOL = 1.5e-2, 1e-2
 LSE_ATOL = 1e-3
+
+# Regression guard, tighter than the pass bar above and asserted beside it on
+# the bf16 workloads.  The GPU forms every score from exact bf16 products
+# accumulated in fp32 and sums the weights in fp32, so its base-2 LSE differs
+# from the float64 oracle by ~1e-6; its two coarse roundings (the weights to
+# bf16 before the value product, the output to bf16) each add a relative error
+# of at most 2^-9 per element, about 1.6e-3 relative L2 error per (row, head)
+# together.  Removing (or duplicating) one key of median weight out of K moves
+# the LSE by about 0.6 / (K ln 2), >= 1e-4 for K <= 8192, and the output row by
+# about 1 / sqrt(e K) relative L2.  tests/test_guard.py plants such a key in
+# the oracle and checks that these bounds reject it at the full decode and
+# prefill sizes.
+GUARD_O_REL_L2 = 4e-3
+GUARD_LSE = 5e-5
 
 
 def require_gpu():
@@ -83,3 +100,58 @@ def check_lse(got, ref, what: str, atol=LSE_ATOL, mask=None):
     assert np.all(np.isfinite(err)), f"{what}: non-finite LSE mismatch"
     assert err.max(initial=0.0) <= atol, f"{what}: LSE max err {err.max()}"
     return float(err.max(initial=0.0))
+
+
+def guard_stats(got, ref, lse_got, lse_ref):
+    """Per (row, head): relative L2 error of the output and absolute LSE
+    error, on [rows, heads, dim] / [rows, heads] arrays.  Entries the caller
+    did not compute (NaN in ref) are NaN; empty rows (ref LSE -inf) are 0
+    when got is empty too, else inf."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    lg = np.asarray(lse_got, dtype=np.float64)
+    lr = np.asarray(lse_ref, dtype=np.float64)
+    num = np.sqrt(np.sum((got - ref) ** 2, axis=-1))
+    den = np.sqrt(np.sum(ref ** 2, axis=-1))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(den > 0, num / den, num)
+        lerr = np.abs(lg - lr)
+    empty = np.isneginf(lr)
+    lerr = np.where(empty, np.where(np.isneginf(lg), 0.0, np.inf), lerr)
+    rel = np.where(empty, np.where(np.isneginf(lg), 0.0, np.inf), rel)
+    return rel, lerr
+
+
+def check_guard(got, ref, lse_got, lse_ref, what: str, o_rel_l2: float = GUARD_O_REL_L2,
+                lse_atol: float = GUARD_LSE):
+    """Regression guard on [rows, heads, dim] outputs and [rows, heads] LSEs:
+    every computed (row, head) must have ||got - ref||_2 <= o_rel_l2 *
+    ||ref||_2 and |lse_got - lse_ref| <= lse_atol (an empty reference row
+    must be empty).  Returns the largest of each statistic."""
+    rel, lerr = guard_stats(got, ref, lse_got, lse_ref)
+    live = ~np.isnan(np.asarray(lse_ref, dtype=np.float64))
+    rel, lerr = rel[live], lerr[live]
+    rep = {"o_rel_l2_max": float(rel.max(initial=0.0)), "lse_max": float(lerr.max(initial=0.0)),
+           "pairs": int(live.sum())}
+    assert not np.isnan(rel).any() and rel.max(initial=0.0) <= o_rel_l2, \
+        f"{what}: guard: {np.count_nonzero(~(rel <= o_rel_l2))} (row, head) outputs past {o_rel_l2} relative L2, {rep}"
+    assert not np.isnan(lerr).any() and lerr.max(initial=0.0) <= lse_atol, \
+        f"{what}: guard: {np.count_nonzero(~(lerr <= lse_atol))} LSEs past {lse_atol}, {rep}"
+    return rep
+
+
+def oracle_in_threads(fn, head_groups, workers=None):
+    """Run ``fn(heads=group)`` (an oracle call that fills only the listed
+    heads, NaN elsewhere) for every group in parallel threads (numpy releases
+    the GIL in its kernels; BLAS runs one thread per call) and combine the
+    results.  Returns (o, lse) as the oracle call does."""
+    from threadpoolctl import threadpool_limits
+    workers = workers or min(16, os.cpu_count() or 1, len(head_groups))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda g: fn(heads=list(g)), head_groups))
+    o, lse = parts[0]
+    o, lse = o.copy(), lse.copy()
+    for po, pl in parts[1:]:
+        o = np.where(np.isnan(po), o, po)
+        lse = np.where(np.isnan(pl), lse, pl)
+    return o, lse

@@ -63,7 +63,8 @@ def test_fp8_decode_full_size(torch, pkv, layout):
     ro, rl = _oracle(b, b.k_cache, b.v_cache, 0.5, 2.0)
     rep = gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "fp8 decode o")
     gu.check_lse(lse, rl, "fp8 decode lse")
-    print("fp8 decode parity", rep, plan.info["num_items"])
+    grd = gu.check_guard(gu.as_f64(o, "bf16"), ro, lse, rl, "fp8 decode")
+    print("fp8 decode parity", rep, grd, plan.info["num_items"])
 
 
 @pytest.mark.parametrize("fixed", [0, 1, 5])

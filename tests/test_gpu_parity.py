@@ -111,7 +111,8 @@ def test_decode_full_size(torch, pkv):
     ro, rl = _oracle(b, b.k_cache, b.v_cache)
     rep = gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "decode o")
     gu.check_lse(lse, rl, "decode lse")
-    print("decode parity", rep, plan.info["num_items"], plan.info["split"])
+    grd = gu.check_guard(gu.as_f64(o, "bf16"), ro, lse, rl, "decode")
+    print("decode parity", rep, grd, plan.info["num_items"], plan.info["split"])
 
 
 @pytest.mark.parametrize("fixed", [1, 2, 7])
@@ -135,6 +136,7 @@ def test_skewed_decode_split_and_merge(torch, pkv):
     ro, rl = _oracle(b, b.k_cache, b.v_cache)
     gu.check_close(gu.as_f64(o, "bf16"), ro, "bf16", "skewed o")
     gu.check_lse(lse, rl, "skewed lse")
+    print("skewed guard", gu.check_guard(gu.as_f64(o, "bf16"), ro, lse, rl, "skewed"))
 
 
 @pytest.mark.parametrize("fixed", [100, 30, 10])
@@ -154,45 +156,56 @@ def test_split_merge_chunk_counts(torch, pkv, fixed, dtype, dim):
     gu.check_lse(lse, rl, f"merge chunks {fixed} lse", atol=1e-5 if dtype == "f32" else 1e-3)
 
 
-PREFILL_HEADS = [0, 5, 9, 14, 18, 23, 27, 31]     # one or more per kv head
-
-
-def test_prefill_full_size_append_then_run(torch, pkv):
-    """8 requests, 512-2048 new rows after a 0-8192 prefix, page 16, HND,
-    causal, bf16: append (bit-exact) then prefill, checked on 8 heads that
-    cover every kv head."""
+@pytest.fixture(scope="module")
+def prefill_full():
+    """The full-size prefill batch, its cache after the append (host), and the
+    oracle over every query head, computed once for the module (one thread per
+    kv head's 4 query heads)."""
     b = wl.make("prefill", poison=True)
+    k_exp, v_exp = _expected_after_append(b, b.k_cache, b.v_cache)
+    print("prefill oracle: 32 heads in threads", flush=True)
+    ro, rl = gu.oracle_in_threads(lambda heads: _oracle(b, k_exp, v_exp, heads=heads),
+                                  [list(range(g * 4, g * 4 + 4)) for g in range(8)])
+    assert not np.isnan(ro).any() and not np.isnan(rl).any()
+    return b, k_exp, v_exp, ro, rl
+
+
+def test_prefill_full_size_append_then_run(torch, pkv, prefill_full):
+    """8 requests, 512-2048 new rows after a 0-8192 prefix, page 16, HND,
+    causal, bf16: append (bit-exact) then prefill, every output element and
+    LSE against the oracle, plus the regression guard."""
+    b, k_exp, v_exp, ro, rl = prefill_full
     k_dev, v_dev = gu.to_dev(b.k_cache, "bf16"), gu.to_dev(b.v_cache, "bf16")
     _append_on_gpu(pkv, b, k_dev, v_dev)
     torch.cuda.synchronize()
-    k_exp, v_exp = _expected_after_append(b, b.k_cache, b.v_cache)
     assert np.array_equal(gu.to_host(k_dev, "bf16"), k_exp)
     assert np.array_equal(gu.to_host(v_dev, "bf16"), v_exp)
     plan, o, lse = _run_gqa(pkv, torch, b, k_cache=k_dev, v_cache=v_dev)
-    ro, rl = _oracle(b, k_exp, v_exp, heads=PREFILL_HEADS)
-    rep = gu.check_close(gu.as_f64(o[:, PREFILL_HEADS], "bf16"), ro[:, PREFILL_HEADS], "bf16", "prefill o")
-    gu.check_lse(lse[:, PREFILL_HEADS], rl[:, PREFILL_HEADS], "prefill lse")
-    print("prefill parity", rep)
+    got = gu.as_f64(o, "bf16")
+    rep = gu.check_close(got, ro, "bf16", "prefill o")
+    gu.check_lse(lse, rl, "prefill lse")
+    grd = gu.check_guard(got, ro, lse, rl, "prefill")
+    assert rep["n"] == b.nnz * b.num_qo_heads * b.head_dim
+    print("prefill parity", rep, grd)
 
 
 @pytest.mark.parametrize("fixed", [4, 12, 64])
-def test_prefill_forced_chunk_lengths(torch, pkv, fixed):
+def test_prefill_forced_chunk_lengths(torch, pkv, prefill_full, fixed):
     """The full-size prefill batch split into chunks of 4, 12 and 64 pages
     (1, 3 and 16 key tiles): every tile pipeline depth, each chunk's partial
-    last tile, and the merge of up to ~40 partial states per row.  Checked on
-    the first head of two kv heads; the LSE bar catches a stale key tile that
-    the output tolerance alone can miss."""
-    b = wl.make("prefill", poison=True)
-    k_dev, v_dev = gu.to_dev(b.k_cache, "bf16"), gu.to_dev(b.v_cache, "bf16")
-    _append_on_gpu(pkv, b, k_dev, v_dev)
-    torch.cuda.synchronize()
-    k_exp, v_exp = _expected_after_append(b, b.k_cache, b.v_cache)
-    heads = [0, 9]
-    plan, o, lse = _run_gqa(pkv, torch, b, k_cache=k_dev, v_cache=v_dev, fixed_split_pages=fixed)
-    ro, rl = _oracle(b, k_exp, v_exp, heads=heads)
-    gu.check_close(gu.as_f64(o[:, heads], "bf16"), ro[:, heads], "bf16", f"prefill o fixed={fixed}")
-    gu.check_lse(lse[:, heads], rl[:, heads], f"prefill lse fixed={fixed}")
+    last tile, and the merge of up to ~40 partial states per row.  Every head
+    against the oracle; the guard's LSE bound catches a stale or missing key
+    tile that the output tolerance alone can miss."""
+    print("case prefill forced chunk", fixed, flush=True)
+    b, k_exp, v_exp, ro, rl = prefill_full
+    plan, o, lse = _run_gqa(pkv, torch, b, k_cache=gu.to_dev(k_exp, "bf16"), v_cache=gu.to_dev(v_exp, "bf16"),
+                            fixed_split_pages=fixed)
+    got = gu.as_f64(o, "bf16")
+    gu.check_close(got, ro, "bf16", f"prefill o fixed={fixed}")
+    gu.check_lse(lse, rl, f"prefill lse fixed={fixed}")
+    grd = gu.check_guard(got, ro, lse, rl, f"prefill fixed={fixed}")
     assert plan.info["num_merges"] > 0
+    print("prefill forced chunk guard", fixed, grd)
 
 
 def test_mla_decode_full_size(torch, pkv):
@@ -212,9 +225,11 @@ def test_mla_decode_full_size(torch, pkv):
     ro, rl = oat.mla_decode(b.q, b.q_kpe, b.k_cache[..., :512], b.k_cache[..., 512:], kv_indptr=list(b.kv_indptr),
                             kv_indices=list(b.kv_indices), kv_last_page_len=list(b.kv_last_page_len),
                             page_size=b.page_size, sm_scale=b.sm_scale, dtype="bf16")
-    rep = gu.check_close(gu.as_f64(gu.to_host(out, "bf16"), "bf16"), ro, "bf16", "mla o")
+    got = gu.as_f64(gu.to_host(out, "bf16"), "bf16")
+    rep = gu.check_close(got, ro, "bf16", "mla o")
     gu.check_lse(lse.cpu().numpy(), rl, "mla lse")
-    print("mla parity", rep, plan.info)
+    grd = gu.check_guard(got, ro, lse.cpu().numpy(), rl, "mla")
+    print("mla parity", rep, grd, plan.info)
 
 
 @pytest.mark.parametrize("page_size,kv_range,batch,fixed,heads", [

@@ -126,3 +126,46 @@ def test_mask_length_is_checked():
     with pytest.raises(md.MetadataError) as e:
         mk.ragged_attention(q, k, v, qo_indptr=qo, kv_indptr=kv, num_kv_heads=2, custom_mask=np.ones(9, bool))
     assert e.value.reason == "mask_length"
+
+
+def _ragged_reason(**kw):
+    with pytest.raises(md.MetadataError) as e:
+        mk.validate_ragged(**kw)
+    return e.value.reason
+
+
+def test_validate_ragged_rules_by_hand():
+    """Each rule of the ragged metadata ("FlashInfer 中的 KV-Cache 布局", "Ragged
+    Tensor": num_requests + 1 entries, the first one zero, request i's length
+    indptr[i+1] - indptr[i]) and the qo_len <= kv_len completion, with the
+    expected reason written out by hand, and the rule order checked where two
+    rules are broken at once."""
+    # The pages' three-request batch as ragged tensors: qo 3/1/4, kv 6/2/9.
+    assert mk.validate_ragged(qo_indptr=[0, 3, 4, 8], kv_indptr=[0, 6, 8, 17]) == [6, 2, 9]
+    # A request with no keys and no rows is allowed; qo_len == kv_len is allowed.
+    assert mk.validate_ragged(qo_indptr=[0, 2, 2, 7], kv_indptr=[0, 3, 3, 8], num_qo_heads=4,
+                              num_kv_heads=2) == [3, 0, 5]
+    assert mk.validate_ragged(qo_indptr=[0], kv_indptr=[0]) == []
+    # Heads must group evenly (checked first, even when the indptrs are also bad).
+    assert _ragged_reason(qo_indptr=[0, 1], kv_indptr=[0, 1], num_qo_heads=3, num_kv_heads=2) == "head_group"
+    assert _ragged_reason(qo_indptr=[0, 1], kv_indptr=[0, 1], num_qo_heads=4, num_kv_heads=0) == "head_group"
+    assert _ragged_reason(qo_indptr=[0, 1], kv_indptr=[0, 1], num_qo_heads=0, num_kv_heads=1) == "head_group"
+    assert _ragged_reason(qo_indptr=[1, 2], kv_indptr=[0, 1], num_qo_heads=6, num_kv_heads=4) == "head_group"
+    # Both indptrs cover the same requests; an empty kv_indptr is no batch at all.
+    assert _ragged_reason(qo_indptr=[0, 1], kv_indptr=[0, 1, 2]) == "batch_size"
+    assert _ragged_reason(qo_indptr=[], kv_indptr=[]) == "batch_size"
+    # The first entry is zero, qo_indptr before kv_indptr.
+    assert _ragged_reason(qo_indptr=[1, 2, 3], kv_indptr=[0, 2, 4]) == "indptr_start"
+    assert _ragged_reason(qo_indptr=[0, 1, 2], kv_indptr=[2, 4, 6]) == "indptr_start"
+    with pytest.raises(md.MetadataError, match="qo_indptr"):
+        mk.validate_ragged(qo_indptr=[1, 2], kv_indptr=[1, 2])
+    # Lengths are differences of consecutive entries, so an indptr never decreases.
+    assert _ragged_reason(qo_indptr=[0, 2, 1], kv_indptr=[0, 2, 4]) == "indptr_order"
+    assert _ragged_reason(qo_indptr=[0, 1, 1], kv_indptr=[0, 3, 2]) == "indptr_order"
+    # Order before lengths: request 0 has qo 3 > kv 2, but kv_indptr decreases later.
+    assert _ragged_reason(qo_indptr=[0, 3, 4], kv_indptr=[0, 2, 1]) == "indptr_order"
+    # Completion: a request's keys include its new tokens, so qo_len <= kv_len.
+    assert _ragged_reason(qo_indptr=[0, 3], kv_indptr=[0, 2]) == "qo_exceeds_kv"
+    assert _ragged_reason(qo_indptr=[0, 1, 2], kv_indptr=[0, 5, 5]) == "qo_exceeds_kv"
+    with pytest.raises(md.MetadataError, match="request 2"):
+        mk.validate_ragged(qo_indptr=[0, 1, 2, 6], kv_indptr=[0, 1, 9, 12])
