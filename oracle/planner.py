@@ -39,6 +39,7 @@ DEFAULT_TARGET_PER_CU = {DECODE: 3, PREFILL: 4, MLA: 1}
 DEFAULT_TAIL_SPLIT = {DECODE: 2, PREFILL: 1, MLA: 1}
 CASCADE_TARGET_PER_CU = 1       # cascade levels run one launch each: one item per CU by default
 MFMA_TILE_ROWS = 256            # prefill tile height counted in (row, head) pairs
+MFMA_HEAD_DIM = 128             # the head dim whose prefill runs 256-pair tiles
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -48,12 +49,14 @@ def _cdiv(a: int, b: int) -> int:
 RAGGED_PAGE = 16                # ragged keys are chunked as if in pages of this many tokens
 
 
-def rows_per_tile(mode: str, group: int, kv_dtype: str, masked: bool = False) -> int:
-    """Query rows per work item: 1 for decode, MLA and float32 prefill and for
-    custom-masked prefill with one query head per kv head; for prefill over a
-    bfloat16 or fp8 cache as many rows as fit a 256-high tile of (row, head)
-    pairs."""
+def rows_per_tile(mode: str, group: int, kv_dtype: str, masked: bool = False, head_dim: int = 128) -> int:
+    """Query rows per work item: for prefill over a bfloat16 or fp8 cache at
+    head_dim 128 as many rows as fit a 256-high tile of (row, head) pairs;
+    1 otherwise (decode, MLA, float32 prefill, other head dims, and
+    custom-masked prefill with one query head per kv head)."""
     if mode != PREFILL or kv_dtype not in ("bf16", "fp8"):
+        return 1
+    if head_dim != MFMA_HEAD_DIM:
         return 1
     if masked and group < 2:
         return 1
@@ -181,7 +184,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
 
 def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: int, causal: bool,
                  num_cus: int, fixed_split_pages: int = 0, target_per_cu: int = 0,
-                 tail_split: int = 0) -> dict:
+                 tail_split: int = 0, head_dim: int = 128) -> dict:
     """Work list of a multi-level cascade ("FlashInfer 中的 KV-Cache 布局",
     multi-level cascade layout: each level has its own qo_indptr and page
     table over the shared queries and cache).
@@ -214,7 +217,7 @@ def plan_cascade(*, levels, page_size: int, group: int, kv_dtype: str, heads_y: 
         qo = [int(x) for x in lv["qo_indptr"]]
         nodes = len(qo) - 1
         mode = DECODE if nodes > 0 and all(qo[n + 1] - qo[n] == 1 for n in range(nodes)) else PREFILL
-        rows = rows_per_tile(mode, group, kv_dtype)
+        rows = rows_per_tile(mode, group, kv_dtype, head_dim=head_dim)
         p = plan(mode=mode, qo_indptr=None if mode == DECODE else qo, kv_indptr=[int(x) for x in lv["kv_indptr"]],
                  kv_last_page_len=[int(x) for x in lv["kv_last_page_len"]], page_size=page_size, heads_y=heads_y,
                  rows=rows, causal=causal and li == len(levels) - 1, num_cus=num_cus,

@@ -157,9 +157,15 @@ constexpr int32_t kMlaHeadsPerGroup = 64;   // the MLA kernel's head-group width
 constexpr int32_t kCascadeTargetPerCu = 1;
 
 constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
+constexpr int32_t kMfmaHeadDim = 128;  // the head dim the MFMA prefill kernel is built for
 
-int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode) {
+// Query rows per work item.  Prefill over a bf16 or fp8 cache at the MFMA
+// kernel's head dim gets a tile of 256 (row, head) pairs; every other case is
+// one row per item, because the row kernel that runs it streams an item's
+// keys once per row (a tall tile would serialise its rows in one workgroup).
+int32_t rows_per_tile(int32_t mode, int32_t group, int32_t kv_dtype, int32_t mask_mode, int32_t head_dim) {
   if (mode != PKV_MODE_PREFILL || (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3)) return 1;
+  if (head_dim != kMfmaHeadDim) return 1;
   if (mask_mode == PKV_MASK_CUSTOM && group < 2) return 1;   // masked tiles need a head group of 2+
   return std::max<int32_t>(1, kMfmaTileRows / group);
 }
@@ -295,7 +301,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
     if (e != hipSuccess) return hip_fail(e, "querying the compute-unit count");
   }
   const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
-  const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode);
+  const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode, prm->head_dim_qk);
   int32_t heads_y = prm->num_kv_heads;
   if (mla) {
     heads_y = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
@@ -574,35 +580,44 @@ pkv_status cascade_impl(const pkv_plan_params* prm, int32_t num_levels, const pk
 }
 
 // Pinned staging buffers remember the event of the last upload made from
-// them, so a later plan does not overwrite bytes still being copied.
+// them and the plan that made it, so a later plan does not overwrite bytes
+// still being copied.  An entry lives as long as that plan: destroying the
+// plan waits for its upload and drops the entry (and its event) unless a
+// later plan has reused the buffer since.  A buffer whose address is reused
+// after its last plan is gone therefore starts without a stale event.
+struct StagingSlot {
+  hipEvent_t event;
+  const void* owner;   // the plan whose upload the event records
+};
 std::mutex g_staging_mu;
-std::unordered_map<void*, hipEvent_t> g_staging_events;
+std::unordered_map<void*, StagingSlot> g_staging;
 
 // Copies a plan's host-built tables to the start of the device workspace.
 // With a pinned staging buffer the copy is asynchronous; the buffer's event
 // records it, and a later upload from the same buffer first waits for that
 // event.  Without one, the bytes go through a temporary host vector and the
 // stream is synchronised before it is freed.
-hipError_t upload_staging(void* h_staging, void* ws, int64_t bytes, hipStream_t st,
+hipError_t upload_staging(void* h_staging, void* ws, int64_t bytes, hipStream_t st, const void* owner,
                           const std::function<void(char*)>& fill) {
   hipError_t e;
   if (h_staging) {
     std::lock_guard<std::mutex> lock(g_staging_mu);
-    auto it = g_staging_events.find(h_staging);
-    if (it == g_staging_events.end()) {
+    auto it = g_staging.find(h_staging);
+    if (it == g_staging.end()) {
       hipEvent_t ev;
       e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
       if (e != hipSuccess) return e;
-      it = g_staging_events.emplace(h_staging, ev).first;
+      it = g_staging.emplace(h_staging, StagingSlot{ev, owner}).first;
     } else {
-      e = hipEventSynchronize(it->second);   // the previous upload from this buffer
+      e = hipEventSynchronize(it->second.event);   // the previous upload from this buffer
       if (e != hipSuccess) return e;
     }
+    it->second.owner = owner;
     char* hs = static_cast<char*>(h_staging);
     std::memset(hs, 0, size_t(bytes));
     fill(hs);
     e = hipMemcpyAsync(ws, hs, size_t(bytes), hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipEventRecord(it->second, st);
+    if (e == hipSuccess) e = hipEventRecord(it->second.event, st);
     return e;
   }
   std::vector<char> tmp(size_t(bytes), 0);
@@ -610,6 +625,28 @@ hipError_t upload_staging(void* h_staging, void* ws, int64_t bytes, hipStream_t 
   e = hipMemcpyAsync(ws, tmp.data(), tmp.size(), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e;
+}
+
+// Called when `owner` is destroyed: if it made the last upload from
+// h_staging, wait for that upload and release the buffer's event.
+void release_staging(void* h_staging, const void* owner) {
+  if (!h_staging) return;
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  auto it = g_staging.find(h_staging);
+  if (it == g_staging.end() || it->second.owner != owner) return;
+  (void)hipEventSynchronize(it->second.event);
+  (void)hipEventDestroy(it->second.event);
+  g_staging.erase(it);
+}
+
+// Plans that lead to a run must bound the page ids they will dereference.
+// The MLA run takes raw cache pointers without a descriptor, so its plan
+// carries the pool size.
+pkv_status check_runnable(const pkv_plan_params* p) {
+  if (p && p->mode == PKV_MODE_MLA_DECODE && p->max_num_pages <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "MLA plans need max_num_pages (the pool size): pkv_run_mla has no "
+                                     "cache descriptor to bound page ids by");
+  return PKV_OK;
 }
 
 }  // namespace
@@ -630,7 +667,7 @@ struct pkv_plan {
   pkv_graph_caps caps{};
   int32_t* d_counts = nullptr;   // [0] live items, [1] live merge items
   char* d_ws = nullptr;
-  void* h_staging = nullptr;
+  void* h_staging = nullptr;   // pinned staging of the uploads (fixed-capacity plans: also of updates)
   int64_t staging_bytes = 0;
 
   int32_t grid_items() const { return graph ? caps.max_items : info.num_items; }
@@ -720,6 +757,7 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
   *plan_out = nullptr;
   PlanResult r;
   pkv_status s = plan_impl(params, qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len, &r);
+  if (!s) s = check_runnable(params);
   if (s) return s;
   const pkv_plan_info& in = r.info;
   if (in.workspace_bytes > 0 && (!d_workspace || int64_t(ws_bytes) < in.workspace_bytes))
@@ -749,13 +787,15 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
     delete plan;
     return hip_fail(e, "hipGetDevice");
   }
+  plan->h_staging = h_staging;
   if (in.staging_bytes > 0) {
-    e = upload_staging(h_staging, ws, in.staging_bytes, st, [&](char* hs) {
+    e = upload_staging(h_staging, ws, in.staging_bytes, st, plan, [&](char* hs) {
       std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
       std::memcpy(hs + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
       std::memcpy(hs + items_bytes + merges_bytes, r.mask_rows.data(), r.mask_rows.size() * sizeof(pkv::MaskRow));
     });
     if (e != hipSuccess) {
+      release_staging(h_staging, plan);
       delete plan;
       return hip_fail(e, "uploading the plan");
     }
@@ -788,6 +828,7 @@ pkv_status pkv_plan_check(const pkv_plan* plan, const int32_t* qo_indptr, const 
 }
 
 pkv_status pkv_plan_destroy(pkv_plan* plan) {
+  if (plan) release_staging(plan->h_staging, plan);
   delete plan;
   return ok();
 }
@@ -1090,7 +1131,7 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
   a.token_stride = token_stride;
   a.page_size = p.page_size;
   a.page_shift = page_shift_of(p.page_size);
-  a.max_num_pages = p.max_num_pages > 0 ? p.max_num_pages : INT32_MAX;
+  a.max_num_pages = p.max_num_pages;   // > 0: check_runnable at plan creation
   a.kv_indices = d_kv_indices;
   a.o = o;
   a.lse = lse;
@@ -1211,7 +1252,7 @@ pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, Gr
   const int32_t group = prm->num_qo_heads / prm->num_kv_heads;
   if (prm->kv_format == PKV_KV_RAGGED)
     return fail(PKV_ERR_UNSUPPORTED, "fixed-capacity plans are built for paged caches");
-  const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode);
+  const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode, prm->head_dim_qk);
   int64_t hy = prm->num_kv_heads;
   if (mla) {
     hy = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
@@ -1271,6 +1312,7 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
   *plan_out = nullptr;
   GraphLayout g;
   pkv_status s = graph_layout(params, caps, &g);
+  if (!s) s = check_runnable(params);
   if (s) return s;
   if (!d_workspace || int64_t(ws_bytes) < g.workspace_bytes)
     return fail(PKV_ERR_WORKSPACE, fmt("workspace %lld bytes < %lld needed", int64_t(ws_bytes), g.workspace_bytes));
@@ -1301,8 +1343,9 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
   plan->staging_bytes = g.staging_bytes;
   hipError_t e = hipGetDevice(&plan->device);
   if (e == hipSuccess)   // counters (and lists) start at zero: a run before the first update does nothing
-    e = upload_staging(h_staging, ws, 256, static_cast<hipStream_t>(stream), [](char*) {});
+    e = upload_staging(h_staging, ws, 256, static_cast<hipStream_t>(stream), plan, [](char*) {});
   if (e != hipSuccess) {
+    release_staging(h_staging, plan);
     delete plan;
     return hip_fail(e, "initialising the fixed-capacity plan");
   }
@@ -1335,7 +1378,7 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
   const int64_t mask_off = merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
   const int64_t upload = r.mask_rows.empty() ? merges_off + int64_t(r.merges.size()) * sizeof(MergeItem)
                                              : mask_off + int64_t(r.mask_rows.size()) * sizeof(pkv::MaskRow);
-  hipError_t e = upload_staging(plan->h_staging, plan->d_ws, upload, static_cast<hipStream_t>(stream),
+  hipError_t e = upload_staging(plan->h_staging, plan->d_ws, upload, static_cast<hipStream_t>(stream), plan,
                                 [&](char* hs) {
                                   int32_t* counts = reinterpret_cast<int32_t*>(hs);
                                   counts[0] = r.info.num_items;
@@ -1368,6 +1411,7 @@ struct pkv_cascade_plan {
   float* d_part_lse;
   float* d_part_o;
   int device;
+  void* h_staging = nullptr;
 };
 
 extern "C" {
@@ -1433,14 +1477,16 @@ pkv_status pkv_cascade_plan_create(const pkv_plan_params* params, int32_t num_le
   plan->d_slots = reinterpret_cast<int32_t*>(ws + items_bytes + rp_bytes);
   plan->d_part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
   plan->d_part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
+  plan->h_staging = h_staging;
   hipError_t e = hipGetDevice(&plan->device);
   if (e == hipSuccess && in.staging_bytes > 0)
-    e = upload_staging(h_staging, ws, in.staging_bytes, static_cast<hipStream_t>(stream), [&](char* hs) {
+    e = upload_staging(h_staging, ws, in.staging_bytes, static_cast<hipStream_t>(stream), plan, [&](char* hs) {
       std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
       std::memcpy(hs + items_bytes, r.row_ptr.data(), r.row_ptr.size() * 4);
       std::memcpy(hs + items_bytes + rp_bytes, r.slots.data(), r.slots.size() * 4);
     });
   if (e != hipSuccess) {
+    release_staging(h_staging, plan);
     delete plan;
     return hip_fail(e, "uploading the cascade plan");
   }
@@ -1495,6 +1541,7 @@ pkv_status pkv_cascade_run(const pkv_cascade_plan* plan, const void* q, int64_t 
 }
 
 pkv_status pkv_cascade_plan_destroy(pkv_cascade_plan* plan) {
+  if (plan) release_staging(plan->h_staging, plan);
   delete plan;
   return ok();
 }

@@ -21,59 +21,101 @@
 namespace pkv {
 namespace {
 
-// One workgroup per appended token: find its request by binary search over
-// append_indptr, locate (page, slot), copy K and V rows in 16-byte chunks.
-__global__ __launch_bounds__(256) void append_kernel(const char* k_new, const char* v_new, int64_t new_st_b,
-                                                     int64_t new_sh_b, const int32_t* append_indptr,
-                                                     const int32_t* kv_indptr, const int32_t* kv_indices,
-                                                     const int32_t* last, int32_t batch, char* k, char* v,
-                                                     int64_t page_b, int64_t tok_b, int64_t head_b,
-                                                     int32_t page_size, int32_t heads, int32_t row_chunks,
-                                                     int32_t max_pages) {
-  __shared__ int32_t s_req;
-  const int32_t t = blockIdx.x;
-  const int32_t per = heads * row_chunks;
-  // The new row's bytes do not depend on where they go: load them first (the
-  // usual case, one 16-byte chunk per thread, keeps them in registers).
-  const int64_t src = int64_t(t) * new_st_b;
-  auto src_of = [&](int32_t i) {
-    const int32_t which = i >= per;
-    const int32_t j = i - which * per;
-    const int32_t h = j / row_chunks, c = j - (j / row_chunks) * row_chunks;
-    return (which ? v_new : k_new) + src + int64_t(h) * new_sh_b + int64_t(c) * 16;
+// Append: workgroup w copies the new rows of tokens [w*tpb, w*tpb + tpb)
+// (tpb = tokens per block, chosen by the launcher).  Three phases, two
+// barriers, both reached by every thread:
+//   1. every thread issues the loads of its 16-byte chunks of those rows
+//      (they do not depend on where the rows go), then scans requests
+//      r = tid, tid + 256, ...: request r owns tokens [append_indptr[r],
+//      append_indptr[r+1]); a request that owns some of the block's tokens
+//      computes their logical positions kv_len_r - n_r + i, reads their page
+//      ids and stores each token's destination offset in LDS (its page-table
+//      entries are loaded with append_indptr, before the test, so the scan
+//      costs one dependent load plus the page-id load);
+//   2. every thread stores its chunks at their token's destination (rows
+//      wider than 8 chunks per thread, one token per block then, copy the
+//      rest in a loop).
+// A token no request owns, or whose page id lies outside the pool, is
+// skipped.
+constexpr int kAppendThreads = 256;
+constexpr int kAppendMaxTok = 16;     // tokens per block at most
+constexpr int kAppendMaxChunks = 8;   // 16-byte chunks per thread at most
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(const char* k_new, const char* v_new, int64_t new_st_b,
+                                                                int64_t new_sh_b, const int32_t* append_indptr,
+                                                                const int32_t* kv_indptr, const int32_t* kv_indices,
+                                                                const int32_t* last, int32_t batch, int32_t nnz,
+                                                                int32_t tpb, char* k, char* v, int64_t page_b,
+                                                                int64_t tok_b, int64_t head_b, int32_t page_size,
+                                                                int32_t heads, int32_t row_chunks, int32_t max_pages) {
+  __shared__ int64_t s_dst[kAppendMaxTok];   // byte offset of each token's slot, -1: skip
+  const int tid = threadIdx.x;
+  const int32_t t0 = int32_t(blockIdx.x) * tpb;
+  const int32_t n = min(tpb, nnz - t0);
+  const int32_t per = heads * row_chunks;    // chunks of one K (or V) row
+  const int32_t total = n * 2 * per;
+  // Chunk i: token i / (2 per); then K or V; then head and 16-byte chunk.
+  auto locate = [&](int32_t i, int32_t& j, int32_t& which, int64_t& inner_src, int64_t& inner_dst) {
+    j = i / (2 * per);
+    const int32_t rem = i - j * 2 * per;
+    which = rem >= per;
+    const int32_t q = rem - which * per;
+    const int32_t h = q / row_chunks, c = q - (q / row_chunks) * row_chunks;
+    inner_src = int64_t(h) * new_sh_b + int64_t(c) * 16;
+    inner_dst = int64_t(h) * head_b + int64_t(c) * 16;
   };
-  const int32_t i0 = threadIdx.x;
-  uint4 first = make_uint4(0, 0, 0, 0);
-  if (i0 < 2 * per) first = *reinterpret_cast<const uint4*>(src_of(i0));
-  // Request of token t: the one b with append_indptr[b] <= t < append_indptr[b+1]
-  // (unique: empty requests never match), found by all threads in parallel.
-  if (threadIdx.x == 0) s_req = -1;
-  __syncthreads();
-  for (int32_t r0 = 0; r0 < batch; r0 += blockDim.x) {
-    const int32_t r = r0 + threadIdx.x;
-    if (r < batch && append_indptr[r] <= t && t < append_indptr[r + 1]) s_req = r;
-    __syncthreads();
-    if (s_req >= 0) break;   // uniform: read after the barrier
+  uint4 data[kAppendMaxChunks];
+#pragma unroll
+  for (int x = 0; x < kAppendMaxChunks; ++x) {
+    const int32_t i = tid + x * kAppendThreads;
+    if (i < total) {
+      int32_t j, which;
+      int64_t is, id;
+      locate(i, j, which, is, id);
+      data[x] = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);
+    }
   }
-  const int32_t b = s_req;
-  if (b < 0) return;
-  const int32_t n_new = append_indptr[b + 1] - append_indptr[b];
-  const int32_t n_pages = kv_indptr[b + 1] - kv_indptr[b];
-  const int32_t kv_len = page_size * (n_pages - 1) + last[b];
-  const int32_t pos = kv_len - n_new + (t - append_indptr[b]);
-  if (n_pages < 1 || pos < 0 || pos >= kv_len) return;
-  const int32_t page = kv_indices[kv_indptr[b] + pos / page_size];
-  if (page < 0 || page >= max_pages) return;
-  const int64_t dst = int64_t(page) * page_b + int64_t(pos % page_size) * tok_b;
-  auto dst_of = [&](int32_t i) {
-    const int32_t which = i >= per;
-    const int32_t j = i - which * per;
-    const int32_t h = j / row_chunks, c = j - (j / row_chunks) * row_chunks;
-    return (which ? v : k) + dst + int64_t(h) * head_b + int64_t(c) * 16;
-  };
-  if (i0 < 2 * per) *reinterpret_cast<uint4*>(dst_of(i0)) = first;
-  for (int32_t i = i0 + blockDim.x; i < 2 * per; i += blockDim.x)
-    *reinterpret_cast<uint4*>(dst_of(i)) = *reinterpret_cast<const uint4*>(src_of(i));
+  if (tid < kAppendMaxTok) s_dst[tid] = -1;
+  __syncthreads();
+  for (int32_t r = tid; r < batch; r += kAppendThreads) {
+    const int32_t a0 = append_indptr[r], a1 = append_indptr[r + 1];
+    const int32_t p0 = kv_indptr[r], p1 = kv_indptr[r + 1], lst = last[r];
+    const int32_t lo = max(a0, t0), hi = min(a1, t0 + n);
+    if (lo >= hi) continue;
+    const int32_t n_pages = p1 - p0;
+    const int32_t kv_len = page_size * (n_pages - 1) + lst;
+    for (int32_t t = lo; t < hi; ++t) {
+      const int32_t pos = kv_len - (a1 - a0) + (t - a0);
+      int64_t dst = -1;
+      if (n_pages >= 1 && pos >= 0 && pos < kv_len) {
+        const int32_t page = kv_indices[p0 + pos / page_size];
+        if (page >= 0 && page < max_pages) dst = int64_t(page) * page_b + int64_t(pos % page_size) * tok_b;
+      }
+      s_dst[t - t0] = dst;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < kAppendMaxChunks; ++x) {
+    const int32_t i = tid + x * kAppendThreads;
+    if (i < total) {
+      int32_t j, which;
+      int64_t is, id;
+      locate(i, j, which, is, id);
+      const int64_t dst = s_dst[j];
+      if (dst >= 0) *reinterpret_cast<uint4*>((which ? v : k) + dst + id) = data[x];
+    }
+  }
+  // Rows wider than the preloaded chunks (one token per block then): the rest.
+  for (int32_t i = tid + kAppendMaxChunks * kAppendThreads; i < total; i += kAppendThreads) {
+    int32_t j, which;
+    int64_t is, id;
+    locate(i, j, which, is, id);
+    const int64_t dst = s_dst[j];
+    if (dst >= 0)
+      *reinterpret_cast<uint4*>((which ? v : k) + dst + id) =
+          *reinterpret_cast<const uint4*>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);
+  }
 }
 
 template <typename T>
@@ -539,10 +581,19 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
                          int32_t num_heads, int32_t head_dim, int32_t max_num_pages, hipStream_t st) {
   const int64_t es = dtype == kF32 ? 4 : (dtype == kFP8 ? 1 : 2);
   const int32_t row_chunks = int32_t(head_dim * es / 16);
-  hipLaunchKernelGGL(append_kernel, dim3(uint32_t(nnz)), dim3(256), 0, st, static_cast<const char*>(k_new),
-                     static_cast<const char*>(v_new), new_st * es, new_sh * es, append_indptr, kv_indptr, kv_indices,
-                     last_page_len, batch, static_cast<char*>(k), static_cast<char*>(v), page_stride * es,
-                     token_stride * es, head_stride * es, page_size, num_heads, row_chunks, max_num_pages);
+  const int64_t token_chunks = 2 * int64_t(num_heads) * row_chunks;   // K and V rows of one token
+  // Tokens per block: as many as the per-thread chunk registers hold, but
+  // keep at least ~4 blocks per CU-sized group of 256 tokens so that small
+  // batches (decode: one token per request) still spread over the GPU.
+  const int64_t cap = std::max<int64_t>(1, int64_t(kAppendThreads) * kAppendMaxChunks / token_chunks);
+  int64_t tpb = std::min<int64_t>({cap, int64_t(kAppendMaxTok), std::max<int64_t>(1, nnz / 1024)});
+  const int64_t blocks = (nnz + tpb - 1) / tpb;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(append_kernel, dim3(uint32_t(blocks)), dim3(kAppendThreads), 0, st,
+                     static_cast<const char*>(k_new), static_cast<const char*>(v_new), new_st * es, new_sh * es,
+                     append_indptr, kv_indptr, kv_indices, last_page_len, batch, nnz, int32_t(tpb),
+                     static_cast<char*>(k), static_cast<char*>(v), page_stride * es, token_stride * es,
+                     head_stride * es, page_size, num_heads, row_chunks, max_num_pages);
   return hipGetLastError();
 }
 

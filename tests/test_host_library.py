@@ -466,3 +466,115 @@ def test_binding_rejects_bad_host_and_device_arguments():
     r = pkv.plan_params(mode="prefill", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
                         page_size=4, dtype="f32", ragged=True)
     _check_batch(r, [0, 1, 2], [0, 3, 5], None)          # ragged plans take no tail lengths
+
+
+def _p32(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+# A 256-byte aligned address that is never dereferenced: every call below
+# fails its size check before it touches device memory or the device.
+FAKE_DEVICE_PTR = ctypes.c_void_p(1 << 20)
+
+
+def test_plan_create_rejects_small_workspace_and_staging():
+    """pkv_plan_create refuses a workspace or pinned staging buffer smaller
+    than the plan needs (PKV_ERR_WORKSPACE) before any upload, and a missing
+    workspace when the plan needs one."""
+    lib = pkv.lib()
+    params = pkv.plan_params(mode="decode", batch_size=3, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                             page_size=4, dtype="f32", num_cus=4, fixed_split_pages=1, max_num_pages=16)
+    kvp, idx = np.array([0, 2, 3, 6], np.int32), np.array([7, 2, 11, 3, 14, 6], np.int32)
+    last = np.array([2, 2, 1], np.int32)
+    info = pkv.plan_compute(params, qo_indptr=None, kv_indptr=kvp, kv_indices=idx, kv_last_page_len=last)[0]
+    ws, st = info["workspace_bytes"], info["staging_bytes"]
+    assert ws > st > 0 and info["num_partial_rows"] > 0
+    staging = np.zeros(st + 256, np.uint8)
+    handle = ctypes.c_void_p()
+
+    def create(ws_ptr, ws_bytes, st_ptr, st_bytes):
+        return lib.pkv_plan_create(ctypes.byref(params), None, _p32(kvp), _p32(idx), len(idx), _p32(last), ws_ptr,
+                                   ws_bytes, st_ptr, st_bytes, None, ctypes.byref(handle))
+
+    stp = ctypes.c_void_p(staging.ctypes.data)
+    assert create(FAKE_DEVICE_PTR, ws - 1, stp, st) == _abi.ERR_WORKSPACE
+    assert b"workspace" in lib.pkv_last_error()
+    assert create(None, ws, stp, st) == _abi.ERR_WORKSPACE
+    assert create(FAKE_DEVICE_PTR, ws, stp, st - 1) == _abi.ERR_WORKSPACE
+    assert b"staging" in lib.pkv_last_error()
+    assert create(ctypes.c_void_p((1 << 20) + 16), ws, stp, st) == _abi.ERR_INVALID_ARG   # not 256-aligned
+    assert not handle.value
+
+
+def test_graph_and_cascade_plans_reject_small_workspace():
+    lib = pkv.lib()
+    params = pkv.plan_params(mode="decode", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                             page_size=4, dtype="f32", num_cus=4, max_num_pages=16)
+    caps = pkv.graph_caps(max_total_pages=8)
+    _, ws, st = pkv.graph_plan_size(params, caps)
+    staging = np.zeros(st, np.uint8)
+    handle = ctypes.c_void_p()
+    assert lib.pkv_graph_plan_create(ctypes.byref(params), ctypes.byref(caps), FAKE_DEVICE_PTR, ws - 1,
+                                     ctypes.c_void_p(staging.ctypes.data), st, None,
+                                     ctypes.byref(handle)) == _abi.ERR_WORKSPACE
+    assert lib.pkv_graph_plan_create(ctypes.byref(params), ctypes.byref(caps), FAKE_DEVICE_PTR, ws,
+                                     ctypes.c_void_p(staging.ctypes.data), st - 1, None,
+                                     ctypes.byref(handle)) == _abi.ERR_WORKSPACE
+    levels = [dict(qo_indptr=[0, 2], kv_indptr=[0, 2], kv_indices=[1, 2], kv_last_page_len=[4]),
+              dict(qo_indptr=[0, 1, 2], kv_indptr=[0, 1, 2], kv_indices=[3, 4], kv_last_page_len=[2, 3])]
+    cparams = pkv.plan_params(mode="prefill", batch_size=0, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                              page_size=4, dtype="f32", num_cus=4, max_num_pages=16)
+    info = pkv.cascade_plan_compute(cparams, levels)[0]
+    arr, keep = pkv._cascade_levels(levels)
+    cst = np.zeros(info["staging_bytes"], np.uint8)
+    chandle = ctypes.c_void_p()
+    assert lib.pkv_cascade_plan_create(ctypes.byref(cparams), 2, arr, FAKE_DEVICE_PTR, info["workspace_bytes"] - 1,
+                                       ctypes.c_void_p(cst.ctypes.data), cst.size, None,
+                                       ctypes.byref(chandle)) == _abi.ERR_WORKSPACE
+    assert not handle.value and not chandle.value
+
+
+def test_mla_plans_that_run_need_the_pool_size():
+    """An MLA run bounds page ids by the plan's max_num_pages (pkv_run_mla
+    takes no cache descriptor), so creating an MLA plan without it is refused;
+    host-only planning (pkv_plan_compute) does not need it."""
+    lib = pkv.lib()
+    params = pkv.plan_params(mode="mla", batch_size=1, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
+                             head_dim_vo=512, page_size=64, dtype="bf16", num_cus=4)
+    kvp, last, idx = np.array([0, 2], np.int32), np.array([10], np.int32), np.array([5, 9], np.int32)
+    info = pkv.plan_compute(params, qo_indptr=None, kv_indptr=kvp, kv_indices=idx, kv_last_page_len=last)[0]
+    staging = np.zeros(max(256, info["staging_bytes"]), np.uint8)
+    handle = ctypes.c_void_p()
+    st = lib.pkv_plan_create(ctypes.byref(params), None, _p32(kvp), _p32(idx), len(idx), _p32(last),
+                             FAKE_DEVICE_PTR, 1 << 30, ctypes.c_void_p(staging.ctypes.data), staging.size, None,
+                             ctypes.byref(handle))
+    assert st == _abi.ERR_INVALID_ARG and b"max_num_pages" in lib.pkv_last_error()
+    caps = pkv.graph_caps(max_total_pages=4)
+    gst = lib.pkv_graph_plan_create(ctypes.byref(params), ctypes.byref(caps), FAKE_DEVICE_PTR, 1 << 30,
+                                    ctypes.c_void_p(staging.ctypes.data), staging.size, None, ctypes.byref(handle))
+    assert gst == _abi.ERR_INVALID_ARG and not handle.value
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefill_at_head_dim_64_plans_one_row_tiles(dtype):
+    """bf16 / fp8 prefill at a head dim the MFMA tile kernel is not built for
+    runs on the row kernel, which streams an item's keys once per row: the
+    planner gives it one-row tiles, as the oracle's planner spec does."""
+    rng = np.random.default_rng(11)
+    kv_lens = [int(x) for x in rng.integers(40, 300, size=5)]
+    qo_lens = [int(rng.integers(1, k + 1)) for k in kv_lens]
+    page = 16
+    pages = [(k + page - 1) // page for k in kv_lens]
+    kvp = np.array(md.indptr_from_lengths(pages), np.int32)
+    last = np.array([k - page * (n - 1) for k, n in zip(kv_lens, pages)], np.int32)
+    qo = np.array(md.indptr_from_lengths(qo_lens), np.int32)
+    params = pkv.plan_params(mode="prefill", batch_size=5, num_qo_heads=8, num_kv_heads=2, head_dim_qk=64,
+                             page_size=page, dtype="bf16", kv_dtype=dtype, num_cus=16)
+    info, items, merges = pkv.plan_compute(params, qo_indptr=qo, kv_indptr=kvp, kv_indices=None,
+                                           kv_last_page_len=last)
+    rows = pl.rows_per_tile("prefill", 4, dtype, head_dim=64)
+    assert rows == 1 and info["rows_per_tile"] == 1
+    spec = pl.plan(mode="prefill", qo_indptr=list(qo), kv_indptr=list(kvp), kv_last_page_len=list(last),
+                   page_size=page, heads_y=2, rows=rows, causal=True, num_cus=16)
+    assert items.tolist() == spec["items"] and merges.tolist() == spec["merges"]
+    assert info["num_items"] >= sum(qo_lens)

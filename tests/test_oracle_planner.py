@@ -157,6 +157,10 @@ def test_rows_per_tile_rule():
     assert pl.rows_per_tile("prefill", 1, "fp8", masked=True) == 1
     assert pl.rows_per_tile("prefill", 4, "bf16", masked=True) == 64
     assert pl.rows_per_tile("prefill", 1, "bf16", masked=True) == 1
+    # Head dims other than 128 run one row per item (no MFMA tile instantiation).
+    assert pl.rows_per_tile("prefill", 4, "bf16", head_dim=64) == 1
+    assert pl.rows_per_tile("prefill", 2, "fp8", head_dim=256) == 1
+    assert pl.rows_per_tile("prefill", 4, "bf16", head_dim=128) == 64
 
 
 def test_empty_batch_and_empty_requests():
