@@ -17,15 +17,19 @@ LSE_ATOL = 1e-3
 # Regression guard, tighter than the pass bar above and asserted beside it on
 # the bf16 workloads.  The GPU forms every score from exact bf16 products
 # accumulated in fp32 and sums the weights in fp32, so its base-2 LSE differs
-# from the float64 oracle by ~1e-6; its two coarse roundings (the weights to
-# bf16 before the value product, the output to bf16) each add a relative error
-# of at most 2^-9 per element, about 1.6e-3 relative L2 error per (row, head)
-# together.  Removing (or duplicating) one key of median weight out of K moves
-# the LSE by about 0.6 / (K ln 2), >= 1e-4 for K <= 8192, and the output row by
-# about 1 / sqrt(e K) relative L2.  tests/test_guard.py plants such a key in
-# the oracle and checks that these bounds reject it at the full decode and
-# prefill sizes.
-GUARD_O_REL_L2 = 4e-3
+# from the float64 oracle by ~1e-6 (measured at most 2.2e-6 over the full
+# decode, prefill and MLA batches).  Its two coarse roundings (the weights to
+# bf16 before the value product, the output to bf16) each add a relative
+# error of at most 2^-9 per element; in rows dominated by a few keys the
+# weight rounding does not average out, and the relative L2 error per
+# (row, head) reaches 3.7e-3 on the prefill batch.  Removing (or duplicating)
+# one key of median weight out of K moves the LSE by about 0.6 / (K ln 2),
+# >= 1e-4 for K <= 8192 (the LSE bound catches it); a wrong value row of a
+# key of about average weight moves the output by about sqrt(2 / (e K)) relative L2,
+# >= 1e-2 for K <= 8192 (the output bound catches it).  tests/test_guard.py
+# plants such a key in the oracle and checks that the bounds reject it at
+# the full decode and prefill sizes.
+GUARD_O_REL_L2 = 6e-3
 GUARD_LSE = 5e-5
 
 

@@ -29,11 +29,16 @@ def _bf16_round(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def _median_key(q_row, keys, visible, sm_scale):
-    """Index of the visible key whose softmax weight is the median one."""
+def _quantile_key(q_row, keys, visible, sm_scale, frac):
+    """Index of the visible key whose softmax weight has rank frac among the
+    row's visible keys (0.5: the median weight)."""
     s = sm_scale * (keys[visible] @ q_row)
     idx = np.flatnonzero(visible)
-    return int(idx[np.argsort(s)[len(idx) // 2]])
+    return int(idx[np.argsort(s)[int(frac * len(idx))]])
+
+
+def _median_key(q_row, keys, visible, sm_scale):
+    return _quantile_key(q_row, keys, visible, sm_scale, 0.5)
 
 
 def test_guard_rejects_one_dropped_key_at_decode_size():
@@ -66,6 +71,34 @@ def test_guard_rejects_one_dropped_key_at_decode_size():
               np.all(np.abs(do[r, 0] - ro[r, 0]) <= gu.BF16_ATOL + gu.BF16_RTOL * np.abs(ro[r, 0]))
               for r in range(b.batch_size)]
     assert sum(passes) >= b.batch_size // 2, sum(passes)
+
+
+def test_guard_rejects_one_wrong_value_row_at_decode_size():
+    """The output bound: in every request of the full decode batch, the value
+    row of a key of about average weight for head 0 (rank 0.7 of the row's
+    weights: with these scores the mean weight lies above the median)
+    replaced by another key's row
+    -- a wrong value gather that leaves the scores and the LSE exact -- moves
+    head 0's output past the guard."""
+    b = wl.make("decode")
+    kw = dict(qo_indptr=list(b.qo_indptr), kv_indptr=list(b.kv_indptr), kv_indices=list(b.kv_indices),
+              kv_last_page_len=list(b.kv_last_page_len), page_size=b.page_size, layout=b.layout,
+              num_kv_heads=b.num_kv_heads, sm_scale=b.sm_scale, q_dtype="bf16", kv_dtype="bf16", heads=[0])
+    ro, rl = oat.paged_attention(b.q, b.k_cache, b.v_cache, **kw)
+    v_bad = b.v_cache.copy()
+    for r in range(b.batch_size):
+        k_len = b.kv_lens[r]
+        keys = oat.upcast(oat.gather_request(b.k_cache, b.layout, b.kv_indptr, b.kv_indices, b.page_size, r,
+                                             k_len), "bf16")[:, 0]
+        j = _quantile_key(oat.upcast(b.q[r, 0], "bf16"), keys, np.ones(k_len, bool), b.sm_scale, 0.7)
+        src = (j + k_len // 2) % k_len                 # another key of the same request
+        pages = b.kv_indices[b.kv_indptr[r]:b.kv_indptr[r + 1]]
+        v_bad[pages[j // b.page_size], j % b.page_size, 0] = b.v_cache[pages[src // b.page_size],
+                                                                      src % b.page_size, 0]
+    do, dl = oat.paged_attention(b.q, b.k_cache, v_bad, **kw)
+    rel, lerr = gu.guard_stats(do, ro, dl, rl)
+    assert np.all(lerr[:, 0] == 0.0)                   # the scores did not move
+    assert np.all(rel[:, 0] > gu.GUARD_O_REL_L2), np.sort(rel[:, 0])[:4]
 
 
 def test_guard_rejects_one_dropped_key_at_prefill_size():
@@ -108,7 +141,7 @@ def test_guard_flags_empty_row_mismatch_and_bad_outputs():
     lse = np.array([[1.0], [-np.inf]])
     gu.check_guard(ref, ref, lse, lse, "identical")
     got = ref.copy()
-    got[0, 0, 0] += 0.01                               # relative L2 0.005
+    got[0, 0, 0] += 0.02                               # relative L2 0.01
     with pytest.raises(AssertionError, match="relative L2"):
         gu.check_guard(got, ref, lse, lse, "bad")
     bad_lse = np.array([[1.0], [0.0]])                 # an empty row reported as non-empty
