@@ -437,6 +437,41 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
                        int64_t token_stride, const int32_t* d_kv_indices, void* o, float* lse,
                        float sm_scale, void* stream);
 
+/* ------------------------------------------------ run without allocation -- */
+
+/* Bytes of the per-device array that pkv_run_noalloc works in. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pkv_run
+ * without a plan object, workspace or staging buffer.  One call plans the
+ * batch on the host (as pkv_plan_create does, same work list), copies the
+ * work list into a device array that the library holds (one array of
+ * PKV_NOALLOC_SCRATCH_BYTES per device, for the life of the process), and
+ * runs attention and the split merge with the partial states in that array.  It calls no device or
+ * pinned-host allocation routine; planning uses ordinary host memory only.
+ *   params, host metadata        as for pkv_plan_create (paged decode or
+ *                                prefill; MLA, ragged and custom-masked
+ *                                plans are PKV_ERR_INVALID_ARG)
+ *   q, cache, d_kv_indices, o, lse, sm_scale, stream   as for pkv_run
+ * The array is shared by every call on a device and keeps the last call's
+ * contents (nothing in it has to start at zero: each call writes the work
+ * list and every partial state before reading them).  Calls on one device
+ * must therefore not overlap: two calls on different streams of one device
+ * race on the array, and a call on a stream is ordered after the earlier
+ * ones only on that stream.  Returns PKV_ERR_WORKSPACE, with the size needed,
+ * for a batch whose work list and partial states exceed the array (plan it
+ * with pkv_plan_create and a workspace instead); the metadata and argument
+ * errors of pkv_plan_create and pkv_run otherwise.
+ */
+pkv_status pkv_run_noalloc(const pkv_plan_params* params, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, int64_t num_indices, const int32_t* kv_last_page_len,
+                           const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                           const pkv_cache_desc* cache, const int32_t* d_kv_indices, void* o,
+                           int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
+                           void* stream);
+
 /* --------------------------------------------------------------- cascade -- */
 
 /*

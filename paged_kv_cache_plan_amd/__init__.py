@@ -358,6 +358,36 @@ class Plan:
             self._handle = None
 
 
+# ---------------------------------------------------- run without allocation --
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def run_noalloc(params: PlanParams, q, k_cache, v_cache, kv_indices, out, lse=None, *, kv_indptr, kv_last_page_len,
+                kv_indices_host=None, qo_indptr=None, layout, sm_scale=0.0, stream=None, k_scale=1.0, v_scale=1.0):
+    """pkv_run_noalloc: plan this batch on the host and run it with the work
+    list and partial states in the library's per-device array (no workspace,
+    staging or plan object).  Host metadata as for ``Plan``; device tensors as
+    for ``Plan.run``."""
+    import torch
+    meta = [_host_i32(x, n) for x, n in ((qo_indptr, "qo_indptr"), (kv_indptr, "kv_indptr"),
+                                          (kv_indices_host, "kv_indices_host"),
+                                          (kv_last_page_len, "kv_last_page_len"))]
+    (qo, qo_p), (kvp, kvp_p), (idx, idx_p), (last, last_p) = meta
+    _check_batch(params, qo, kvp, last)
+    desc = cache_desc(k_cache, v_cache, layout, params.page_size, params.num_kv_heads, params.head_dim_qk,
+                      k_scale, v_scale)
+    if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise TypeError("lse must be contiguous float32")
+    _check(lib().pkv_run_noalloc(ctypes.byref(params), qo_p, kvp_p, idx_p, 0 if idx is None else len(idx), last_p,
+                                 _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
+                                 _dev(kv_indices, "kv_indices", torch.int32), _dev(out, "out", q.dtype),
+                                 out.stride(0), out.stride(1), None if lse is None else _dev(lse, "lse"),
+                                 ctypes.c_float(sm_scale), _stream(stream)))
+
+
 # --------------------------------------------------- fixed-capacity plans --
 
 def graph_caps(*, max_total_rows=0, max_total_pages, max_items=0, max_merges=0, max_partial_rows=0) -> GraphCaps:

@@ -107,6 +107,8 @@ SIGNATURES = {
     "pkv_run_merge": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "pkv_time_next_attention": (_i32, [_vp, _vp]),
     "pkv_run_mla": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.c_float, _vp]),
+    "pkv_run_noalloc": (_i32, [ctypes.POINTER(PlanParams), _i32p, _i32p, _i32p, _i64, _i32p, _vp, _i64, _i64,
+                               ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp, ctypes.c_float, _vp]),
     "pkv_cascade_plan_compute": (_i32, [ctypes.POINTER(PlanParams), _i32, ctypes.POINTER(CascadeLevel),
                                         ctypes.POINTER(CascadeInfo), ctypes.POINTER(PlanInfo), _i32p, _i64, _i32p,
                                         _i64, _i32p, _i64]),

@@ -1226,6 +1226,111 @@ pkv_status pkv_merge_states(const void* v, const float* s, void* v_out, float* s
 
 }  // extern "C"
 
+// ------------------------------------------------ run without allocation --
+
+// The device memory of pkv_run_noalloc: one array per device, part of this
+// library's code object (loading the library on a device reserves it until
+// the process ends).  Host code never takes the array's name as a device
+// address: the first call on each device asks the runtime for the array's
+// address on that device (hipGetSymbolAddress, with that device current) and
+// every later use -- the work-list copy and the kernel arguments -- goes
+// through that pointer.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices] = {};
+
+hipError_t scratch_on_device(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_run_noalloc(const pkv_plan_params* params, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, int64_t num_indices, const int32_t* kv_last_page_len,
+                           const void* q, int64_t q_stride_token, int64_t q_stride_head, const pkv_cache_desc* cache,
+                           const int32_t* d_kv_indices, void* o, int64_t o_stride_token, int64_t o_stride_head,
+                           float* lse, float sm_scale, void* stream) {
+  pkv_status s = check_params(params);
+  if (s) return s;
+  if (params->mode == PKV_MODE_MLA_DECODE || params->kv_format != PKV_KV_PAGED ||
+      params->mask_mode != PKV_MASK_NONE)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_run_noalloc runs paged decode and prefill without a custom mask");
+  PlanResult r;
+  s = plan_impl(params, qo_indptr, kv_indptr, kv_indices, num_indices, kv_last_page_len, &r);
+  if (s) return s;
+  const pkv_plan_info& in = r.info;
+  if (in.workspace_bytes > int64_t(PKV_NOALLOC_SCRATCH_BYTES))
+    return fail(PKV_ERR_WORKSPACE, fmt("the batch needs %lld bytes of work list and partial states; "
+                                       "pkv_run_noalloc has %lld (use pkv_plan_create with a workspace)",
+                                       in.workspace_bytes, int64_t(PKV_NOALLOC_SCRATCH_BYTES)));
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  pkv::AttnArgs a;
+  s = prepare_attn(*params, dev, in.num_items > 0, q, q_stride_token, q_stride_head, cache, d_kv_indices, o,
+                   o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (s) return s;
+  if (in.num_items == 0) return ok();
+  char* ws = nullptr;
+  e = scratch_on_device(dev, &ws);
+  if (e != hipSuccess) return hip_fail(e, "locating the scratch array");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The work list and merge list go to the start of the array, the partial
+  // states after them, in the layout of a plan's workspace.  The copy is
+  // from ordinary (pageable) host memory, which the runtime has consumed
+  // when hipMemcpyAsync returns; it is ordered after earlier work on `stream`.
+  const int64_t items_bytes = align256(int64_t(r.items.size()) * sizeof(Item));
+  const int64_t lse_bytes = align256(int64_t(in.num_partial_rows) * params->num_qo_heads * 4);
+  std::vector<char> tables(size_t(in.staging_bytes), 0);
+  std::memcpy(tables.data(), r.items.data(), r.items.size() * sizeof(Item));
+  std::memcpy(tables.data() + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+  e = hipMemcpyAsync(ws, tables.data(), tables.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "copying the work list");
+  a.items = reinterpret_cast<const Item*>(ws);
+  a.num_items = in.num_items;
+  a.live_items = nullptr;
+  a.part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
+  a.part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
+  s = launch_attn_mode(params->mode, *params, a, st);
+  if (s) return s;
+  if (in.num_merges > 0) {
+    pkv::MergePartialArgs m;
+    m.merges = reinterpret_cast<const MergeItem*>(ws + items_bytes);
+    m.num_merges = in.num_merges;
+    m.live_merges = nullptr;
+    m.max_rows = in.rows_per_tile;
+    m.num_heads = params->num_qo_heads;
+    m.head_dim = params->head_dim_vo;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.o = o;
+    m.o_stride_token = o_stride_token;
+    m.o_stride_head = o_stride_head;
+    m.lse = lse;
+    e = pkv::launch_merge_partials(params->q_dtype, m, st);
+    if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+  }
+  return ok();
+}
+
+}  // extern "C"
+
 // ------------------------------------------------- fixed-capacity plans --
 
 namespace {

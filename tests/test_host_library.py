@@ -578,3 +578,31 @@ def test_prefill_at_head_dim_64_plans_one_row_tiles(dtype):
                    page_size=page, heads_y=2, rows=rows, causal=True, num_cus=16)
     assert items.tolist() == spec["items"] and merges.tolist() == spec["merges"]
     assert info["num_items"] >= sum(qo_lens)
+
+
+def test_noalloc_run_rejects_batches_beyond_its_array():
+    """pkv_run_noalloc refuses, with the size it needed, a batch whose work
+    list and partial states exceed PKV_NOALLOC_SCRATCH_BYTES (before any
+    device call), and the plan kinds it does not run."""
+    lib = pkv.lib()
+    batch, pages = 512, 8
+    params = pkv.plan_params(mode="decode", batch_size=batch, num_qo_heads=64, num_kv_heads=8, head_dim_qk=128,
+                             page_size=16, dtype="bf16", num_cus=256, fixed_split_pages=1, max_num_pages=batch * pages)
+    kvp = np.arange(0, batch * pages + 1, pages, dtype=np.int32)
+    last = np.full(batch, 16, np.int32)
+    info = pkv.plan_compute(params, qo_indptr=None, kv_indptr=kvp, kv_indices=None, kv_last_page_len=last)[0]
+    assert info["workspace_bytes"] > pkv.NOALLOC_SCRATCH_BYTES
+    assert "#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(os.path.join(ROOT, "include", "pkv.h")).read()
+    assert pkv.NOALLOC_SCRATCH_BYTES == 32 << 20
+    desc = _abi.CacheDesc()
+    st = lib.pkv_run_noalloc(ctypes.byref(params), None, _p32(kvp), None, 0, _p32(last), FAKE_DEVICE_PTR, 64 * 128,
+                             128, ctypes.byref(desc), FAKE_DEVICE_PTR, FAKE_DEVICE_PTR, 64 * 128, 128, None,
+                             ctypes.c_float(0.0), None)
+    assert st == _abi.ERR_WORKSPACE
+    assert str(info["workspace_bytes"]).encode() in lib.pkv_last_error()
+    mla = pkv.plan_params(mode="mla", batch_size=1, num_qo_heads=128, num_kv_heads=1, head_dim_qk=576,
+                          head_dim_vo=512, page_size=64, dtype="bf16", num_cus=4, max_num_pages=4)
+    st = lib.pkv_run_noalloc(ctypes.byref(mla), None, _p32(np.array([0, 1], np.int32)), None, 0,
+                             _p32(np.array([3], np.int32)), FAKE_DEVICE_PTR, 0, 0, ctypes.byref(desc),
+                             FAKE_DEVICE_PTR, FAKE_DEVICE_PTR, 0, 0, None, ctypes.c_float(0.0), None)
+    assert st == _abi.ERR_INVALID_ARG
