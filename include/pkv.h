@@ -223,7 +223,7 @@ typedef struct pkv_plan_params {
   int32_t causal;            /* prefill: bottom-right causal mask ([DD] "Causality uses
                                 logical positions, not page numbers"); ignored by decode */
   int32_t q_dtype;           /* pkv_dtype of q and o; equals kv_dtype, or bf16 over an fp8 cache */
-  int32_t kv_dtype;          /* an fp8 cache runs decode / prefill (head_dim 128) on the row kernel */
+  int32_t kv_dtype;          /* pkv_dtype of the cache (fp8: E4M3 codes, bf16 queries) */
   int32_t num_cus;           /* 0: query the current device */
   int32_t fixed_split_pages; /* > 0 forces this chunk size in pages */
   int32_t target_per_cu;     /* 0: default (decode 3, prefill 4, MLA 1) */
