@@ -32,7 +32,7 @@ def lib():
     return _lib
 
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+from ._abi import LIB_PATH  # noqa: E402  (PKV_LIB_PATH may name another build)
 
 
 class PkvError(RuntimeError):

@@ -5,7 +5,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# The in-tree library; PKV_LIB_PATH names another build of the same sources
+# (the CPU sanitizer test loads a host-sanitized one this way).
+LIB_PATH = os.environ.get("PKV_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 # pkv_status
 OK, ERR_INVALID_ARG, ERR_METADATA, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_STALE_PLAN, ERR_HIP = range(7)

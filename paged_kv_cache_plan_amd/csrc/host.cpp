@@ -70,6 +70,13 @@ std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// Copies a host table; an empty one may have a null data pointer, which
+// memcpy must not be given even for zero bytes.
+template <typename T>
+void copy_table(void* dst, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(T));
+}
+
 int page_shift_of(int32_t p) {
   if (p <= 0 || (p & (p - 1)) != 0) return -1;
   int s = 0;
@@ -739,12 +746,12 @@ pkv_status pkv_plan_compute(const pkv_plan_params* params, const int32_t* qo_ind
   if (items_out) {
     if (items_capacity < int64_t(r.items.size()) * PKV_ITEM_WORDS)
       return fail(PKV_ERR_WORKSPACE, "work-item buffer too small");
-    std::memcpy(items_out, r.items.data(), r.items.size() * sizeof(Item));
+    copy_table(items_out, r.items);
   }
   if (merges_out) {
     if (merges_capacity < int64_t(r.merges.size()) * PKV_MERGE_WORDS)
       return fail(PKV_ERR_WORKSPACE, "merge buffer too small");
-    std::memcpy(merges_out, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+    copy_table(merges_out, r.merges);
   }
   return ok();
 }
@@ -790,9 +797,9 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
   plan->h_staging = h_staging;
   if (in.staging_bytes > 0) {
     e = upload_staging(h_staging, ws, in.staging_bytes, st, plan, [&](char* hs) {
-      std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
-      std::memcpy(hs + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
-      std::memcpy(hs + items_bytes + merges_bytes, r.mask_rows.data(), r.mask_rows.size() * sizeof(pkv::MaskRow));
+      copy_table(hs, r.items);
+      copy_table(hs + items_bytes, r.merges);
+      copy_table(hs + items_bytes + merges_bytes, r.mask_rows);
     });
     if (e != hipSuccess) {
       release_staging(h_staging, plan);
@@ -1298,8 +1305,8 @@ pkv_status pkv_run_noalloc(const pkv_plan_params* params, const int32_t* qo_indp
   const int64_t items_bytes = align256(int64_t(r.items.size()) * sizeof(Item));
   const int64_t lse_bytes = align256(int64_t(in.num_partial_rows) * params->num_qo_heads * 4);
   std::vector<char> tables(size_t(in.staging_bytes), 0);
-  std::memcpy(tables.data(), r.items.data(), r.items.size() * sizeof(Item));
-  std::memcpy(tables.data() + items_bytes, r.merges.data(), r.merges.size() * sizeof(MergeItem));
+  copy_table(tables.data(), r.items);
+  copy_table(tables.data() + items_bytes, r.merges);
   e = hipMemcpyAsync(ws, tables.data(), tables.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "copying the work list");
   a.items = reinterpret_cast<const Item*>(ws);
@@ -1488,10 +1495,9 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
                                   int32_t* counts = reinterpret_cast<int32_t*>(hs);
                                   counts[0] = r.info.num_items;
                                   counts[1] = r.info.num_merges;
-                                  std::memcpy(hs + items_off, r.items.data(), r.items.size() * sizeof(Item));
-                                  std::memcpy(hs + merges_off, r.merges.data(), r.merges.size() * sizeof(MergeItem));
-                                  std::memcpy(hs + mask_off, r.mask_rows.data(),
-                                              r.mask_rows.size() * sizeof(pkv::MaskRow));
+                                  copy_table(hs + items_off, r.items);
+                                  copy_table(hs + merges_off, r.merges);
+                                  copy_table(hs + mask_off, r.mask_rows);
                                 });
   if (e != hipSuccess) return hip_fail(e, "uploading the plan");
   const int64_t ws_bytes = plan->info.workspace_bytes, st_bytes = plan->info.staging_bytes;
@@ -1536,15 +1542,15 @@ pkv_status pkv_cascade_plan_compute(const pkv_plan_params* params, int32_t num_l
   if (items_out) {
     if (items_capacity < int64_t(r.items.size()) * PKV_ITEM_WORDS)
       return fail(PKV_ERR_WORKSPACE, "work-item buffer too small");
-    std::memcpy(items_out, r.items.data(), r.items.size() * sizeof(Item));
+    copy_table(items_out, r.items);
   }
   if (row_ptr_out) {
     if (row_ptr_capacity < int64_t(r.row_ptr.size())) return fail(PKV_ERR_WORKSPACE, "row pointer buffer too small");
-    std::memcpy(row_ptr_out, r.row_ptr.data(), r.row_ptr.size() * 4);
+    copy_table(row_ptr_out, r.row_ptr);
   }
   if (slots_out) {
     if (slots_capacity < int64_t(r.slots.size())) return fail(PKV_ERR_WORKSPACE, "slot buffer too small");
-    std::memcpy(slots_out, r.slots.data(), r.slots.size() * 4);
+    copy_table(slots_out, r.slots);
   }
   return ok();
 }
@@ -1586,9 +1592,9 @@ pkv_status pkv_cascade_plan_create(const pkv_plan_params* params, int32_t num_le
   hipError_t e = hipGetDevice(&plan->device);
   if (e == hipSuccess && in.staging_bytes > 0)
     e = upload_staging(h_staging, ws, in.staging_bytes, static_cast<hipStream_t>(stream), plan, [&](char* hs) {
-      std::memcpy(hs, r.items.data(), r.items.size() * sizeof(Item));
-      std::memcpy(hs + items_bytes, r.row_ptr.data(), r.row_ptr.size() * 4);
-      std::memcpy(hs + items_bytes + rp_bytes, r.slots.data(), r.slots.size() * 4);
+      copy_table(hs, r.items);
+      copy_table(hs + items_bytes, r.row_ptr);
+      copy_table(hs + items_bytes + rp_bytes, r.slots);
     });
   if (e != hipSuccess) {
     release_staging(h_staging, plan);

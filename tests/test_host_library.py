@@ -130,7 +130,7 @@ def _compare_plans(mode, qo_indptr, kv_indptr, kv_indices, last, page_size, hq, 
     ("mla", {}),
 ])
 def test_planner_matches_spec_on_workloads(name, kw):
-    b = wl.make(name, **kw, **({} if name == "worked" else {"scale": 1.0}))
+    b = wl.make(name, payload=False, **kw, **({} if name == "worked" else {"scale": 1.0}))
     mode = b.mode
     hkv = b.num_kv_heads
     for num_cus in (256, 80):
@@ -223,7 +223,7 @@ def _compare_cascade(levels, page, hq, hkv, dtype, causal, num_cus, fixed=0, tar
 
 @pytest.mark.parametrize("name", ["cascade", "cascade_small"])
 def test_cascade_planner_matches_spec_on_workloads(name):
-    b = wl.make(name)
+    b = wl.make(name, payload=False)
     for num_cus in (256, 80):
         info = _compare_cascade(b.extra["levels"], b.page_size, b.num_qo_heads, b.num_kv_heads, b.dtype,
                                 b.causal, num_cus)

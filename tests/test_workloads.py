@@ -61,3 +61,20 @@ def test_poison_marks_only_unowned_slots():
         for slot in range(4):
             finite = np.isfinite(b.k_cache[page, slot]).all()
             assert finite == ((page, slot) in hist)
+
+
+@pytest.mark.parametrize("name,kw", [("worked", {}), ("decode", {"scale": 0.1}), ("skewed", {"scale": 0.05}),
+                                     ("prefill", {"scale": 0.1}), ("mla", {"scale": 0.1}),
+                                     ("cascade", {"scale": 0.05}), ("cascade_small", {})])
+def test_metadata_only_batches_match(name, kw):
+    """payload=False stops after the metadata draws, which come first: the
+    metadata equals that of the full batch and no tensor is drawn."""
+    full = wl.make(name, **kw)
+    meta = wl.make(name, payload=False, **kw)
+    for f in ("qo_indptr", "kv_indptr", "kv_indices", "kv_last_page_len"):
+        assert np.array_equal(getattr(full, f), getattr(meta, f)), f
+    assert full.kv_lens == meta.kv_lens and full.qo_lens == meta.qo_lens and full.max_num_pages == meta.max_num_pages
+    assert meta.q is None and meta.k_cache is None
+    if "levels" in full.extra:
+        for a, b in zip(full.extra["levels"], meta.extra["levels"]):
+            assert all(np.array_equal(np.asarray(a[k]), np.asarray(b[k])) for k in a)

@@ -170,12 +170,18 @@ def _slots(kv_indptr, kv_indices, page_size, b, lo, hi):
 
 
 def _gqa_batch(name, rng, *, mode, qo_lens, kv_lens, page_size, pool, pages_for_request, hq, hkv,
-               dim, dtype, layout, causal, sm_scale, with_append, poison, kv_dtype=None):
+               dim, dtype, layout, causal, sm_scale, with_append, poison, kv_dtype=None, payload=True):
     kv_dtype = dtype if kv_dtype is None else kv_dtype
     n_pages, kv_indptr, kv_indices, last = _csr(kv_lens, page_size, pages_for_request)
     qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int32)
     qo_indptr[1:] = np.cumsum(qo_lens)
     nnz = int(qo_indptr[-1])
+    if not payload:
+        return Batch(name=name, mode=mode, dtype=dtype, kv_dtype=kv_dtype, layout=layout, page_size=page_size,
+                     num_qo_heads=hq, num_kv_heads=hkv, head_dim=dim, causal=causal, sm_scale=sm_scale,
+                     qo_lens=list(qo_lens), kv_lens=list(kv_lens), qo_indptr=qo_indptr,
+                     kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last, max_num_pages=pool,
+                     append_indptr=qo_indptr.copy() if with_append else None)
     q = _payload(rng, (nnz, hq, dim), dtype)
     shape = _cache_shape(layout, pool, page_size, hkv, dim)
     k_cache = _pool(rng, shape, kv_dtype, kv_indices)
@@ -202,12 +208,14 @@ def _gqa_batch(name, rng, *, mode, qo_lens, kv_lens, page_size, pool, pages_for_
 
 
 def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pages: bool = False,
-         scale: float = 1.0, **overrides) -> Batch:
+         scale: float = 1.0, payload: bool = True, **overrides) -> Batch:
     """Build workload ``name`` (one of WORKLOADS).
 
     ``scale`` < 1 shrinks lengths/batch for quick CPU tests while keeping the
     workload's structure; ``overrides`` replace individual knobs (e.g.
-    ``layout="HND"``, ``page_size=1``, ``batch=4``).
+    ``layout="HND"``, ``page_size=1``, ``batch=4``).  ``payload=False``
+    stops after the metadata draws (which come first, so the metadata is the
+    same) and leaves every tensor None: for planner and validator checks.
     """
     rng = np.random.default_rng(SEEDS[name] if seed is None else seed)
     o = dict(overrides)
@@ -225,7 +233,8 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                           page_size=page_size, pool=pool, pages_for_request=pages_for,
                           hq=o.get("hq", 4), hkv=o.get("hkv", 2), dim=o.get("dim", 64),
                           dtype=o.get("dtype", "f32"), layout=o.get("layout", "NHD"), causal=True,
-                          sm_scale=o.get("sm_scale", 1.0 / 8.0), with_append=True, poison=poison)
+                          sm_scale=o.get("sm_scale", 1.0 / 8.0), with_append=True, poison=poison,
+                          payload=payload)
     if name in ("decode", "skewed"):
         if name == "decode":
             batch = o.get("batch", max(1, int(round(64 * scale))))
@@ -250,7 +259,8 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                           hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=o.get("dim", 128),
                           dtype=o.get("dtype", "bf16"), layout=layout, causal=True,
                           sm_scale=o.get("sm_scale", 1.0 / math.sqrt(o.get("dim", 128))),
-                          with_append=o.get("with_append", False), poison=poison, kv_dtype=o.get("kv_dtype"))
+                          with_append=o.get("with_append", False), poison=poison, kv_dtype=o.get("kv_dtype"),
+                          payload=payload)
     if name == "prefill":
         batch = o.get("batch", 8)
         qlo, qhi = o.get("qo_range", (max(1, int(512 * scale)), max(1, int(2048 * scale))))
@@ -270,7 +280,7 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                           hq=o.get("hq", 32), hkv=o.get("hkv", 8), dim=dim,
                           dtype=o.get("dtype", "bf16"), layout=o.get("layout", "HND"),
                           causal=o.get("causal", True), sm_scale=o.get("sm_scale", 1.0 / math.sqrt(dim)),
-                          with_append=True, poison=poison, kv_dtype=o.get("kv_dtype"))
+                          with_append=True, poison=poison, kv_dtype=o.get("kv_dtype"), payload=payload)
     if name == "mla":
         batch = o.get("batch", max(1, int(round(32 * scale))))
         lo, hi = o.get("kv_range", (max(1, int(1024 * scale)), max(1, int(8192 * scale))))
@@ -284,6 +294,13 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
             kv_lens, page_size, lambda b, n: perm[starts[b]:starts[b] + n])
         heads = o.get("heads", 128)
         d_ckv, d_kpe = 512, 64
+        qo_indptr = np.arange(batch + 1, dtype=np.int32)
+        if not payload:
+            return Batch(name="mla", mode="mla", dtype="bf16", layout="NHD", page_size=page_size,
+                         num_qo_heads=heads, num_kv_heads=1, head_dim=d_ckv + d_kpe, causal=False,
+                         sm_scale=o.get("sm_scale", 1.0 / math.sqrt(d_ckv + d_kpe)), qo_lens=[1] * batch,
+                         kv_lens=kv_lens, qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices,
+                         kv_last_page_len=last, max_num_pages=pool)
         q_ckv = _payload(rng, (batch, heads, d_ckv), "bf16")
         q_kpe = _payload(rng, (batch, heads, d_kpe), "bf16")
         cache = _pool(rng, (pool, page_size, d_ckv + d_kpe), "bf16", kv_indices)
@@ -301,11 +318,11 @@ def make(name: str, *, seed: int | None = None, poison: bool = False, literal_pa
                      kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
                      max_num_pages=pool, q=q_ckv, q_kpe=q_kpe, k_cache=cache, v_cache=None)
     if name in ("cascade", "cascade_small"):
-        return _cascade(name, rng, o, scale, poison)
+        return _cascade(name, rng, o, scale, poison, payload)
     raise KeyError(name)
 
 
-def _cascade(name, rng, o, scale, poison):
+def _cascade(name, rng, o, scale, poison, payload=True):
     """A request tree as levels of nodes over one page pool.
 
     ``tree`` lists, per level, how many consecutive requests each node holds
@@ -366,6 +383,14 @@ def _cascade(name, rng, o, scale, poison):
     qo_indptr = np.zeros(batch + 1, dtype=np.int32)
     qo_indptr[1:] = np.cumsum(qo_lens)
     nnz = int(qo_indptr[-1])
+    leaf = levels[-1]
+    if not payload:
+        return Batch(name=name, mode="cascade", dtype=dtype, layout=layout, page_size=page_size,
+                     num_qo_heads=hq, num_kv_heads=hkv, head_dim=dim, causal=o.get("causal", True),
+                     sm_scale=o.get("sm_scale", 1.0 / math.sqrt(dim)), qo_lens=qo_lens,
+                     kv_lens=list(leaf["kv_lens"]), qo_indptr=qo_indptr, kv_indptr=leaf["kv_indptr"],
+                     kv_indices=leaf["kv_indices"], kv_last_page_len=leaf["kv_last_page_len"],
+                     max_num_pages=pool, append_indptr=qo_indptr.copy(), extra={"levels": levels})
     q = _payload(rng, (nnz, hq, dim), dtype)
     shape = _cache_shape(layout, pool, page_size, hkv, dim)
     all_pages = np.concatenate([lv["kv_indices"] for lv in levels])
