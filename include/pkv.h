@@ -227,7 +227,8 @@ typedef struct pkv_plan_params {
   int32_t num_cus;           /* 0: query the current device */
   int32_t fixed_split_pages; /* > 0 forces this chunk size in pages */
   int32_t target_per_cu;     /* 0: default (decode 3, prefill 4, MLA 1) */
-  int32_t mla_head_groups;   /* MLA only; 0: default */
+  int32_t mla_head_groups;   /* MLA only: head groups of 64 or 128 heads each; 0: groups of 128 when
+                                the head count allows, else of 64 */
   int32_t max_num_pages;     /* pool size, for the page-id range check */
   int32_t tail_split;        /* 0: default (decode 2, prefill 1, MLA 1); 1: off */
   int32_t kv_format;         /* pkv_kv_format; ragged needs PKV_MODE_PREFILL */
@@ -431,6 +432,7 @@ pkv_status pkv_time_next_attention(void* start_event, void* stop_event);
  *   kpe    device bf16, same strides (zero-copy slices of one [pages, P, 576] tensor work)
  *   o      device bf16 [B, H, 512] contiguous; lse device float [B, H] or NULL
  *   sm_scale <= 0 selects 1/sqrt(576)
+ * token_stride must stay below 2^26 elements (PKV_ERR_UNSUPPORTED otherwise).
  */
 pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kpe,
                        const void* ckv, const void* kpe, int64_t page_stride,

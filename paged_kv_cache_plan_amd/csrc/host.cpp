@@ -160,7 +160,18 @@ int32_t default_target(int32_t mode) {
   return mode == PKV_MODE_MLA_DECODE ? 1 : (mode == PKV_MODE_DECODE ? 3 : 4);
 }
 int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 1; }
-constexpr int32_t kMlaHeadsPerGroup = 64;   // the MLA kernel's head-group width
+// MLA head groups: the kernel runs groups of 128 heads (one wave per 32
+// heads) or of 64 heads (two waves per 32 heads).  By default the heads form
+// groups of 128 when their count allows it, else groups of 64.
+int32_t mla_head_groups(const pkv_plan_params* p) {
+  if (p->mla_head_groups > 0) return p->mla_head_groups;
+  return p->num_qo_heads % 128 == 0 ? p->num_qo_heads / 128 : p->num_qo_heads / 64;
+}
+bool mla_groups_ok(const pkv_plan_params* p, int64_t groups) {
+  if (groups < 1 || p->num_qo_heads % groups != 0) return false;
+  const int64_t width = p->num_qo_heads / groups;
+  return width == 128 || width == 64;
+}
 constexpr int32_t kCascadeTargetPerCu = 1;
 
 constexpr int32_t kRaggedPage = 16;   // ragged keys are chunked as if in pages of this many tokens
@@ -311,9 +322,8 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   const int32_t rows = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode, prm->head_dim_qk);
   int32_t heads_y = prm->num_kv_heads;
   if (mla) {
-    heads_y = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
-    if (heads_y < 1 || prm->num_qo_heads != heads_y * kMlaHeadsPerGroup)
-      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 heads");
+    heads_y = mla_head_groups(prm);
+    if (!mla_groups_ok(prm, heads_y)) return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 or 128 heads");
   }
   const int32_t target_per_cu = prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode);
   const int32_t tail_split = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);
@@ -1119,6 +1129,8 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
     return s;
   if (!stride_ok(page_stride, 2) || !stride_ok(token_stride, 2))
     return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (token_stride >= pkv::kMlaMaxTokenStride)
+    return fail(PKV_ERR_UNSUPPORTED, "MLA token_stride must stay below 2^26 elements");
   if (!d_kv_indices && plan->grid_items() > 0) return fail(PKV_ERR_INVALID_ARG, "null kv_indices");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
@@ -1163,8 +1175,8 @@ pkv_status pkv_run_mla(const pkv_plan* plan, const void* q_ckv, const void* q_kp
     m.o_stride_token = int64_t(p.num_qo_heads) * 512;
     m.o_stride_head = 512;
     m.lse = lse;
-    e = pkv::launch_merge_partials(PKV_BF16, m, st);
-    if (e != hipSuccess) return hip_fail(e, "launching the split merge");
+    e = pkv::launch_mla_merge(m, st);
+    if (e != hipSuccess) return hip_fail(e, "launching the MLA split merge");
   }
   return ok();
 }
@@ -1367,9 +1379,8 @@ pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, Gr
   const int64_t R = rows_per_tile(prm->mode, group, prm->kv_dtype, prm->mask_mode, prm->head_dim_qk);
   int64_t hy = prm->num_kv_heads;
   if (mla) {
-    hy = prm->mla_head_groups > 0 ? prm->mla_head_groups : prm->num_qo_heads / kMlaHeadsPerGroup;
-    if (hy < 1 || prm->num_qo_heads != hy * kMlaHeadsPerGroup)
-      return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 heads");
+    hy = mla_head_groups(prm);
+    if (!mla_groups_ok(prm, hy)) return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 or 128 heads");
   }
   int32_t num_cus = prm->num_cus;
   if (num_cus <= 0) {

@@ -139,7 +139,7 @@ struct MlaArgs {
   const int32_t* kv_indices;
   void* o;             // [B, H, 512]
   float* lse;          // [B, H] or null
-  float* part_o;       // [partial rows, H, 512]
+  float* part_o;       // [partial rows, H, 512] as bf16 (the fp32-sized region holds them)
   float* part_lse;     // [partial rows, H]
   float scale_log2;
 };
@@ -149,7 +149,12 @@ hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, cons
                             hipStream_t stream, bool* supported);
 hipError_t launch_prefill_mfma(int32_t kv_dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
                                hipStream_t stream, bool* supported);
+// The MLA kernel addresses the 8 rows one wave loads with 32-bit offsets:
+// token_stride (elements) must stay below this.
+constexpr int64_t kMlaMaxTokenStride = int64_t(1) << 26;
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+// Merge of MLA partial rows (bf16 rows of 512 dims, float LSE) into o (bf16).
+hipError_t launch_mla_merge(const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t stream);
 hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st,

@@ -263,6 +263,46 @@ def test_mla_decode_page_shapes_and_splits(torch, pkv, page_size, kv_range, batc
         assert plan.info["num_merges"] > 0
 
 
+@pytest.mark.parametrize("heads", [128, 64])
+def test_mla_decode_score_jump_past_the_first_tile(torch, pkv, heads):
+    """A key far into a chunk whose score for some heads exceeds the max of
+    the chunk's first tile by far more than the weights may grow (a latent row
+    equal to 4x one head's query: a score gap of about 96 for that head), so
+    the kernel's second pass with the chunk's largest max runs."""
+    print("case mla score jump", heads, flush=True)
+    b = wl.make("mla", poison=True, page_size=16, kv_range=(150, 400), batch=3, heads=heads)
+    lat = gu.as_f64(b.k_cache, "bf16").astype(np.float32)
+    q = gu.as_f64(b.q, "bf16").astype(np.float32)
+    qk = gu.as_f64(b.q_kpe, "bf16").astype(np.float32)
+    # chunks of 64 keys, tiles of 32: keys 100 and 300 sit in a chunk's second
+    # tile (the second pass runs), 140 and 7 in a first tile (it need not)
+    for r, j, h in [(0, 100, 0), (0, 300, heads // 2), (1, 140, heads - 1), (2, 7, 5)]:
+        page, slot = omd.token_address(list(b.kv_indptr), list(b.kv_indices), b.page_size, r, j)
+        lat[page, slot, :512] = 4 * q[r, h]
+        lat[page, slot, 512:] = 4 * qk[r, h]
+    b.k_cache = wl.to_bf16_bits(lat)
+    cache = gu.to_dev(b.k_cache, "bf16")
+    params = pkv.plan_params(mode="mla", batch_size=b.batch_size, num_qo_heads=heads, num_kv_heads=1,
+                             head_dim_qk=576, head_dim_vo=512, page_size=b.page_size, dtype="bf16",
+                             fixed_split_pages=4, num_cus=16, max_num_pages=b.max_num_pages)
+    plan = pkv.Plan(params, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
+    out = gu.empty_like_out((b.batch_size, heads, 512), "bf16")
+    lse = torch.full((b.batch_size, heads), float("nan"), dtype=torch.float32, device="cuda")
+    plan.run_mla(gu.to_dev(b.q, "bf16"), gu.to_dev(b.q_kpe, "bf16"), cache[..., :512], cache[..., 512:],
+                 gu.to_dev(b.kv_indices, "i32"), out, lse, sm_scale=b.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oat.mla_decode(b.q, b.q_kpe, b.k_cache[..., :512], b.k_cache[..., 512:], kv_indptr=list(b.kv_indptr),
+                            kv_indices=list(b.kv_indices), kv_last_page_len=list(b.kv_last_page_len),
+                            page_size=b.page_size, sm_scale=b.sm_scale, dtype="bf16")
+    got = gu.as_f64(gu.to_host(out, "bf16"), "bf16")
+    gu.check_close(got, ro, "bf16", "mla jump o")
+    gu.check_lse(lse.cpu().numpy(), rl, "mla jump lse")
+    gu.check_guard(got, ro, lse.cpu().numpy(), rl, "mla jump")
+    assert plan.info["num_merges"] > 0
+    # the planted keys dominate their heads: those rows are (nearly) 4 q
+    assert rl[0, 0] > np.median(rl[0]) + 20
+
+
 def test_layouts_page_sizes_and_storage_forms_agree(torch, pkv):
     """The same logical decode batch stored NHD and HND, at page sizes 1, 3
     and 16, and as a 5-D [pages, 2, ...] tensor: each matches the oracle."""

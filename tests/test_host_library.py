@@ -340,7 +340,7 @@ def test_graph_capacities_bound_every_plan(mode):
             else:
                 qo = None
             spec = pl.plan(mode=mode, qo_indptr=qo, kv_indptr=list(np.cumsum([0] + n)), kv_last_page_len=last,
-                           page_size=page, heads_y=hkv if mode != "mla" else 2, rows=pl.rows_per_tile(mode, hq // hkv,
+                           page_size=page, heads_y=hkv if mode != "mla" else 1, rows=pl.rows_per_tile(mode, hq // hkv,
                                                                                                       dtype),
                            causal=bool(trial % 2), num_cus=num_cus, fixed_split_pages=fixed, target_per_cu=target,
                            tail_split=tail)
