@@ -227,6 +227,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
   const uint32_t max_pages = uint32_t(a.max_num_pages);
   const int64_t page_bytes = a.page_stride * 2, tok_bytes = a.token_stride * 2;
 
+  // The chunk's page ids are staged in LDS; their loads go out first, then
+  // those of Q, whose latency then overlaps the staging and the first tile
+  // loads (loads complete in order, so the first tile barrier also covers Q).
+  const int32_t kv_lo = it.kv_start, kv_hi = it.kv_end;
+  const int32_t ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kKeys - 1) / kKeys : 0;
+  const int32_t pg_lo = kv_hi > kv_lo ? (kPow2 ? kv_lo >> pshift : kv_lo / psz) : 0;
+  const int32_t pg_n =
+      kv_hi > kv_lo ? min(kMaxChunkPages, (kPow2 ? (kv_hi - 1) >> pshift : (kv_hi - 1) / psz) - pg_lo + 1) : 0;
+  int32_t pg_first = 0;
+  if (tid < pg_n) pg_first = pages[pg_lo + tid];
+  asm volatile("" ::: "memory");
+
   // Q^T as the B operand: k-step s covers dims [16s, 16s+16); this lane holds
   // dims 16s + 8hk + [0, 8) of its head (ckv dims first, then kpe).
   bf16x8_t qreg[kSteps];
@@ -240,20 +252,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
       qreg[s] = d < kDimCkv ? *reinterpret_cast<const bf16x8_t*>(qc + d)
                             : *reinterpret_cast<const bf16x8_t*>(qp + d - kDimCkv);
     }
-    // Wait for Q here, before any tile load is in flight (otherwise the
-    // compiler's wait before the first MFMA would also drain the tile loads).
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) asm volatile("" ::"v"(qreg[s]));
   }
+  asm volatile("" ::: "memory");
 
-  const int32_t kv_lo = it.kv_start, kv_hi = it.kv_end;
-  const int32_t ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kKeys - 1) / kKeys : 0;
-  const int32_t pg_lo = kv_hi > kv_lo ? (kPow2 ? kv_lo >> pshift : kv_lo / psz) : 0;
-  const int32_t pg_n =
-      kv_hi > kv_lo ? min(kMaxChunkPages, (kPow2 ? (kv_hi - 1) >> pshift : (kv_hi - 1) / psz) - pg_lo + 1) : 0;
-  for (int i = tid; i < pg_n; i += kThreads) {
+  if (tid < pg_n) s_pages[tid] = uint32_t(pg_first) < max_pages ? pg_first : 0;   // ids outside the pool read page 0
+  for (int i = tid + kThreads; i < pg_n; i += kThreads) {
     const int32_t pg = pages[pg_lo + i];
-    s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;   // ids outside the pool read page 0
+    s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;
   }
   if (tid == 0) s_restart = 0;
   __syncthreads();
@@ -274,7 +279,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
     return s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
   };
   auto slot_of_key = [&](int32_t j) { return kPow2 ? (j & (psz - 1)) : (j - (j / psz) * psz); };
-  auto load_tile = [&](int32_t t) {
+  // The page of the wave's first row of tile t (read ahead of load_tile, so
+  // that the LDS latency of the lookup is hidden).
+  auto first_page = [&](int32_t t) { return page_of_key(min(kv_lo + t * kKeys + r_w, kv_hi - 1)); };
+  auto load_tile = [&](int32_t t, int32_t page0) {
     const int32_t t0 = kv_lo + t * kKeys;
     const uint32_t slot = ring_lds + uint32_t((t & (kRing - 1)) * kSlot);
     const uint32_t lds_ckv = slot + uint32_t(r_w * kCkvRow), lds_kpe = slot + uint32_t(kKpeOff + r_w * kKpeRow);
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
     if (kPow2 && pshift >= 3 && j0 + kRowsPerWave <= kv_hi) {
       // The 8 rows lie on one page (pages of 8+ keys; chunks start on page
       // boundaries and the 8 rows on an 8-key boundary within them).
-      const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(page_of_key(j0))) * page_bytes +
+      const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(page0)) * page_bytes +
                           int64_t(j0 & (psz - 1)) * tok_bytes;
       uint32_t cvoff[kRowsPerWave];
 #pragma unroll
@@ -403,9 +411,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
   auto pass = [&](auto first_pass) {
     constexpr bool kFirst = decltype(first_pass)::value;
     // Prologue: tiles 0-2 in flight, S(0) and its max.
-    load_tile(0);
-    if (ntiles > 1) load_tile(1);
-    if (ntiles > 2) load_tile(2);
+    load_tile(0, first_page(0));
+    if (ntiles > 1) load_tile(1, first_page(1));
+    if (ntiles > 2) load_tile(2, first_page(2));
     if (ntiles > 2) tile_barrier<2 * kLoadsPerTile>();
     else if (ntiles > 1) tile_barrier<kLoadsPerTile>();
     else tile_barrier<0>();
@@ -428,27 +436,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
     // tile t+1 and is done with the slot of tile t-1, which takes tile t+3.
     // Then S(t+1) is computed while the weights of tile t are formed, and
     // O += V(t) P(t) while the max of S(t+1) is formed.
+    int32_t page_next = first_page(3);   // page of tile t+3 (looked up one step ahead)
     for (int32_t t = 0; t < ntiles; ++t) {
       const bool more = t + 1 < ntiles;
       if (t + 2 < ntiles) tile_barrier<kLoadsPerTile>();
       else tile_barrier<0>();
-      if (t + 3 < ntiles) load_tile(t + 3);
+      const bool load_next = t + 3 < ntiles;
+      if (load_next) load_tile(t + 3, page_next);
+      page_next = first_page(t + 4);
       // Weights of tile t, one per k-step 0-15 (exp2(-inf) = 0 covers masked
-      // keys), packed in pairs into the B operands of the two value k-steps.
+      // keys), summed and packed in pairs two k-steps later (so that no
+      // instruction waits on an exponential between the MFMAs) into the B
+      // operands of the two value k-steps.
       uint4 pb[2];
-      float p_even = 0.f;
+      float e[16];
       auto weights = [&](int s) {
         if (s < 16) {
-          float p = dev::fast_exp2(fmaf(sc_cur[s], c, -m_used));
-          asm volatile("" : "+v"(p));   // here, between the MFMAs (not sunk to its use)
-          lsum += p;
-          if ((s & 1) == 0) {
-            p_even = p;
-          } else {
-            // pair q = s / 2 holds keys 8 (q / 2) + 4 hk + 2 (q % 2) + {0, 1}:
+          e[s] = dev::fast_exp2(fmaf(sc_cur[s], c, -m_used));
+          asm volatile("" : "+v"(e[s]));   // here, between the MFMAs (not sunk to its use)
+        }
+        const int u = s - 2;
+        if (u >= 0 && u < 16) {
+          lsum += e[u];
+          if (u & 1) {
+            // pair q = u / 2 holds keys 8 (q / 2) + 4 hk + 2 (q % 2) + {0, 1}:
             // value k-step (q / 2) % 2, lower or upper half by q / 4
-            const uint32_t v = pack2(p_even, p);
-            const int q = s >> 1, ks = (q >> 1) & 1, w = 2 * (q >> 2) + (q & 1);
+            const uint32_t v = pack2(e[u - 1], e[u]);
+            const int q = u >> 1, ks = (q >> 1) & 1, w = 2 * (q >> 2) + (q & 1);
             if (w == 0) pb[ks].x = v;
             if (w == 1) pb[ks].y = v;
             if (w == 2) pb[ks].z = v;
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
         mask_tile(sc_nxt, kv_lo + (t + 1) * kKeys);
       } else {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) weights(s);
+        for (int s = 0; s < 18; ++s) weights(s);
       }
       float mx = -INFINITY;
       auto tmax = [&](int v) {   // steps 4-11: two scores of S(t+1) each (unused on the last tile)

@@ -99,13 +99,14 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 // 16 bytes from global memory straight into LDS: lane l of the wave writes
 // lds_wave_base + 16 l (the LDS address goes in M0, so it must be
-// wave-uniform).  Issued as inline assembly so that the compiler neither
+// wave-uniform; a write of M0 needs one wait state, the s_nop, before a load
+// that reads it).  Issued as inline assembly so that the compiler neither
 // reorders it nor inserts waits for it: the kernel's own protocol orders these
 // loads (each tile barrier waits until only the latest tile step's loads are
 // outstanding, and the kernel drains them all before its epilogue).
 __device__ __forceinline__ void dma16(const void* src, uint16_t* lds_wave_base) {
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
 }
 
 // Waits for every outstanding tile load of this wave.
@@ -114,7 +115,7 @@ __device__ __forceinline__ void dma_drain() { asm volatile("s_waitcnt vmcnt(0)" 
 // 16 bytes into LDS (any LDS byte address, wave-uniform base) -- mask rows.
 __device__ __forceinline__ void dma16_bytes(const void* src, const void* lds_wave_base) {
   const uint32_t lds = uint32_t(reinterpret_cast<uintptr_t>(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
 }
 
 // Pins a value in registers at this point of the instruction stream, so the
