@@ -577,38 +577,53 @@ __global__ __launch_bounds__(64 * kMergeWaves) void mla_merge_kernel(const Merge
   for (int32_t r = 0; r < mi.num_rows; ++r) {
     const int64_t row0 = int64_t(mi.slot0) + r;
     auto stat = [&](int32_t c) { return a.part_lse[(row0 + int64_t(c) * mi.num_rows) * hq + h]; };
-    float mx = -INFINITY;
-    for (int32_t c = lane; c < n; c += 64) mx = fmaxf(mx, stat(c));
+    auto row_of = [&](int32_t c) {
+      return reinterpret_cast<const uint4*>(part + ((row0 + int64_t(c) * mi.num_rows) * hq + h) * kDimCkv + 8 * lane);
+    };
+    // The first eight chunks' rows and (lane c) chunk c's statistic are
+    // loaded together, so their latencies overlap.
+    uint4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *row_of(min(j, n - 1));
+    const float sc_lane = lane < n ? stat(lane) : -INFINITY;
+    float mx = sc_lane;
+    for (int32_t c = lane + 64; c < n; c += 64) mx = fmaxf(mx, stat(c));
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float z = 0.f;
-    for (int32_t c = lane; c < n; c += 64) {
+    const float wl_lane = sc_lane == -INFINITY ? 0.f : dev::fast_exp2(sc_lane - mx);   // mx finite whenever sc is
+    float z = wl_lane;
+    for (int32_t c = lane + 64; c < n; c += 64) {
       const float sc = stat(c);
-      z += sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);   // mx finite whenever sc is
+      z += sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);
     }
     for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
     const float inv_z = z > 0.f ? 1.f / z : 0.f;
+    const float w_lane = wl_lane * inv_z;
+    auto weight = [&](int32_t c) {   // normalised weight of chunk c (0 past the last)
+      if (c >= n) return 0.f;
+      if (c < 64) return __shfl(w_lane, c);
+      const float sc = stat(c);
+      return sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx) * inv_z;
+    };
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // Eight chunks at a time, so that eight 16-byte loads per lane are in
-    // flight; steps past the last chunk re-read it with weight 0.
-    for (int32_t c0 = 0; c0 < n; c0 += 8) {
-      uint4 x[8];
-      float w[8];
+    auto fold = [&](const uint4 (&xs)[8], int32_t c0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int32_t c = min(c0 + j, n - 1);
-        const float sc = stat(c);
-        w[j] = (c0 + j < n && sc != -INFINITY) ? dev::fast_exp2(sc - mx) * inv_z : 0.f;
-        x[j] = *reinterpret_cast<const uint4*>(part + ((row0 + int64_t(c) * mi.num_rows) * hq + h) * kDimCkv + 8 * lane);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t u[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+        const float w = weight(c0 + j);
+        const uint32_t u[4] = {xs[j].x, xs[j].y, xs[j].z, xs[j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(w[j], dev::bf16_lo(u[e]), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(w[j], dev::bf16_hi(u[e]), acc[2 * e + 1]);
+          acc[2 * e] = fmaf(w, dev::bf16_lo(u[e]), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(w, dev::bf16_hi(u[e]), acc[2 * e + 1]);
         }
       }
+    };
+    fold(x, 0);
+    // Further chunks eight at a time (eight 16-byte loads per lane in
+    // flight); steps past the last chunk re-read it with weight 0.
+    for (int32_t c0 = 8; c0 < n; c0 += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = *row_of(min(c0 + j, n - 1));
+      fold(x, c0);
     }
     const int32_t row = mi.q_row0 + r;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(h) * a.o_stride_head;
