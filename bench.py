@@ -65,7 +65,11 @@ def decode_bytes(b) -> dict:
     lse = b.nnz * b.num_qo_heads * 4
     idx = int(b.kv_indptr[-1]) * 4
     append = 0 if b.k_new is None else 2 * 2 * b.k_new.size * es_kv
-    return {"kv": kv, "attn": kv + q + o + lse + idx, "append": append, "layer": kv + q + o + lse + idx + append}
+    attn = kv + q + o + lse + idx
+    # With the append fused into the attention launch the new rows are read
+    # once (as keys, already in kv) and written once into the cache.
+    return {"kv": kv, "attn": attn, "append": append, "layer": attn + append,
+            "attn_fused": attn + append // 2, "layer_fused": attn + append // 2}
 
 
 def prefill_flops(b) -> int:
@@ -119,6 +123,12 @@ class Runner:
         # records (pkv_time_next_attention): no event packets in the stream.
         # Other runs record events on the stream around the timed launches.
         self.kernel_events = not time_merge and b.mode == "decode"
+        # Decode batches with new rows append them inside the attention launch
+        # (pkv_run_append) unless a separate append kernel is asked for.
+        self.fused_append = b.mode == "decode" and b.k_new is not None
+        # Decode runs fold the split rows inside the attention launch when the
+        # plan allows it (pkv_plan_info.merge_in_launch), unless asked not to.
+        self.separate_merge = False
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
@@ -181,19 +191,28 @@ class Runner:
                 ev[1].record()
             return
         k, v = self.pools[i % len(self.pools)]
-        if b.k_new is not None:
+        if b.k_new is not None and not self.fused_append:
             self.append(i)
         if ev:
             if self.kernel_events:
                 self.pkv.time_next_attention(ev[0], ev[1])
             else:
                 ev[0].record()
-        plan.run_attention(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
-        if self.time_merge:
+        merged = b.mode == "decode" and not self.separate_merge   # o final after the attention call
+        if self.fused_append:
+            plan.run_append(self.q, k, v, self.kv_indices, self.out, self.lse, k_new=self.k_new, v_new=self.v_new,
+                            append_indptr=self.append_indptr, kv_indptr=self.kv_indptr_d,
+                            kv_last_page_len=self.last_d, layout=b.layout, sm_scale=b.sm_scale, with_merge=merged)
+        elif merged:
+            plan.run(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout, sm_scale=b.sm_scale)
+        else:
+            plan.run_attention(self.q, k, v, self.kv_indices, self.out, self.lse, layout=b.layout,
+                               sm_scale=b.sm_scale)
+        if self.time_merge and not merged:
             plan.run_merge(self.out, self.lse)
         if ev and not self.kernel_events:
             ev[1].record()
-        if not self.time_merge:
+        if not self.time_merge and not merged:
             plan.run_merge(self.out, self.lse)
 
 
@@ -536,6 +555,12 @@ def main():
                     help="time the attention launch of every N-th layer of the decode workloads")
     ap.add_argument("--stream-events", action="store_true",
                     help="record timing events on the stream around launches instead of by the dispatch")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode workloads: launch append_paged_kv on its own before each attention launch "
+                         "instead of fusing it into the attention launch (pkv_run_append)")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="decode workloads: merge split rows in their own launch after attention instead of "
+                         "inside the attention launch (when the plan allows that)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
@@ -593,13 +618,18 @@ def main():
         b = host["decode"]
         r = Runner(b, args.layers)
         r.kernel_events = r.kernel_events and not args.stream_events
+        r.fused_append = r.fused_append and not args.separate_append
+        r.separate_merge = args.separate_merge
         m = measure(r, args.layers, args.steps, args.warmup, ev_every=args.event_every)
         m["append"] = measure_append(r, args.layers)
         nb = decode_bytes(b)
-        value = nb["layer"] * args.layers / (m["ms_per_step"] * 1e-3) / 1e9
-        achieved = nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9
-        traffic = read_traffic("decode")
-        result["decode"] = dict(m, value=value, bytes=nb, achieved=achieved)
+        fused = r.fused_append
+        merge_in = bool(r.plan.info["merge_in_launch"]) and not r.separate_merge
+        value = nb["layer_fused" if fused else "layer"] * args.layers / (m["ms_per_step"] * 1e-3) / 1e9
+        launch_bytes = nb["attn_fused" if fused else "attn"]
+        achieved = launch_bytes / (m["attn_ms_mean"] * 1e-3) / 1e9
+        result["decode"] = dict(m, value=value, bytes=nb, achieved=achieved, fused=fused, merge_in=merge_in,
+                                launch_bytes=launch_bytes)
         log(f"decode: {value:.1f} GB/s per step, attention kernel {achieved:.1f} GB/s "
             f"({m['attn_ms_mean'] * 1e3:.1f} us), plan {m['plan_host_ms']:.3f} ms host")
         del r
@@ -633,6 +663,7 @@ def main():
         b = host["skewed"]
         layers = args.secondary_layers
         r = Runner(b, layers, time_merge=True)
+        r.separate_merge = args.separate_merge
         m = measure(r, layers, args.steps, args.warmup)
         nb = decode_bytes(b)
         result["skewed"] = dict(m, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9, bytes=nb)
@@ -656,10 +687,14 @@ def main():
         layers = args.layers
         r = Runner(b, layers)
         r.kernel_events = r.kernel_events and not args.stream_events
+        r.fused_append = r.fused_append and not args.separate_append
+        r.separate_merge = args.separate_merge
         m = measure(r, layers, args.steps, args.warmup, ev_every=args.event_every)
         nb = decode_bytes(b)
-        result["fp8"] = dict(m, bytes=nb, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9,
-                             step_gbs=nb["layer"] * layers / (m["ms_per_step"] * 1e-3) / 1e9)
+        fz = "_fused" if r.fused_append else ""
+        result["fp8"] = dict(m, bytes=nb, gbs=nb["attn" + fz] / (m["attn_ms_mean"] * 1e-3) / 1e9,
+                             step_gbs=nb["layer" + fz] * layers / (m["ms_per_step"] * 1e-3) / 1e9,
+                             launch_bytes=nb["attn" + fz])
         log(f"fp8: attention {result['fp8']['gbs']:.1f} GB/s ({m['attn_ms_mean'] * 1e3:.1f} us), "
             f"step {result['fp8']['step_gbs']:.1f} GB/s")
         del r
@@ -704,11 +739,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "batch paged decode: 64 requests, qo_len 1, kv_len U[512,4096], page_size 16, "
                                "20000-page shuffled pool, 32 qo / 8 kv heads, head_dim 128, bf16, NHD; "
-                               f"step = plan + {args.layers} layers x (append + attention + merge)",
+                               f"step = plan + {args.layers} layers x ("
+                               + ("one attention launch with the append fused in" if d["fused"]
+                                  else "append + attention")
+                               + (" and the split merge folded in)" if d["merge_in"] else " + merge)"),
                    "layers": args.layers, "batch": 64, "page_size": 16, "heads": [32, 8], "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": round(d["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["achieved"] / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode"),
-                     "kernel": "attention (decode)", "bytes_per_launch": d["bytes"]["attn"],
+                     "kernel": "attention (decode)" + (", append fused in" if d["fused"] else "")
+                               + (", split merge folded in" if d["merge_in"] else ""),
+                     "bytes_per_launch": d["launch_bytes"],
                      "launch_us_mean": round(d["attn_ms_mean"] * 1e3, 2),
                      "launch_us_median": round(d["attn_ms_median"] * 1e3, 2),
                      "launch_us_p10_p90": [round(d["attn_ms_p10"] * 1e3, 2), round(d["attn_ms_p90"] * 1e3, 2)],
@@ -761,8 +801,10 @@ def main():
         line["fp8_decode"] = {"value": round(f["gbs"], 1), "unit": "GB/s", "frac": round(f["gbs"] / HBM_PEAK_GBS, 4),
                               "launch_us_mean": round(f["attn_ms_mean"] * 1e3, 2),
                               "launch_us_median": round(f["attn_ms_median"] * 1e3, 2),
-                              "bytes_per_launch": f["bytes"]["attn"],
-                              "workload": "the decode batch with an E4M3 K/V cache (bf16 queries and outputs)"}
+                              "bytes_per_launch": f["launch_bytes"],
+                              "step_gbs": round(f["step_gbs"], 1),
+                              "workload": "the decode batch with an E4M3 K/V cache (bf16 queries and outputs), "
+                                          "the append fused into the attention launch as in the decode step"}
     if "cascade" in result:
         c = result["cascade"]
         run_s = c["attn_ms_mean"] * 1e-3

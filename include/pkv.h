@@ -252,6 +252,9 @@ typedef struct pkv_plan_info {
   int64_t staging_bytes;     /* pinned staging this plan needs */
   uint64_t fingerprint;      /* hash of params + metadata (staleness check) */
   int64_t mask_bits;         /* custom mask: sum over requests of qo_len * kv_len */
+  int32_t merge_in_launch;   /* 1: pkv_run / pkv_run_append fold split rows inside the
+                                attention launch (set by plan creation, see pkv_run) */
+  int32_t reserved;
 } pkv_plan_info;
 
 /* Work item / merge item sizes in int32 words (layout documented in the
@@ -284,6 +287,11 @@ pkv_status pkv_plan_compute(const pkv_plan_params* params, const int32_t* qo_ind
  * (host memory, owned by the library) stays valid only for this exact batch
  * ([DD] "Plan then run"; a plan reused after the page table changes gives
  * plausible output for the wrong sequence) and until pkv_plan_destroy.
+ * The first split decode plan made on a device (here or by
+ * pkv_graph_plan_create) also checks, once per device and process, which
+ * XCD runs each workgroup: a 1024-workgroup probe launch on the null stream,
+ * a 4 KiB device buffer and a synchronous copy back.  The answer decides
+ * merge_in_launch (PKV_MERGE_IN_ATTENTION=0 in the environment: never).
  */
 pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indptr,
                            const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -381,7 +389,13 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
  *   lse    device float [nnz, Hq] (contiguous), base-2, or NULL
  *   sm_scale  logit scale; <= 0 selects 1/sqrt(head_dim_qk)
  * Enqueues one attention kernel and, if the plan split any tile, one merge
- * kernel on `stream`.  No host synchronisation, no allocation, no host copy.
+ * kernel on `stream`, unless the plan folds the split rows inside the
+ * attention launch (pkv_plan_info.merge_in_launch): paged decode plans whose
+ * kv heads are a multiple of 8, on a device that runs workgroups i and i + 8
+ * on one XCD, where the last workgroup to finish a row's chunks merges them
+ * ([DD] "A worked split-KV example").  No host synchronisation, no
+ * allocation, no host copy.  Runs of one plan must not overlap in time: they
+ * share its workspace (partial states and merge counters).
  */
 pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token,
                    int64_t q_stride_head, const pkv_cache_desc* cache,
@@ -405,6 +419,39 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
                              int64_t o_stride_head, float* lse, float sm_scale, void* stream);
 pkv_status pkv_run_merge(const pkv_plan* plan, void* o, int64_t o_stride_token,
                          int64_t o_stride_head, float* lse, void* stream);
+
+/*
+ * append_paged_kv fused into a decode run: the result of
+ * pkv_append_paged_kv(k_new, v_new, ..., d_kv_indptr, d_kv_indices,
+ * d_kv_last_page_len, batch_size, nnz, cache) followed by pkv_run (with_merge
+ * != 0) or pkv_run_attention (with_merge == 0) with one launch fewer: the
+ * cache bit for bit, o and lse up to fp32 rounding (the block holding the
+ * new keys is summed first).  [KVL], FlashInfer API note under the MLA page
+ * layout (pages allocated first, then appended) and [DD] "Why inference
+ * attention becomes irregular" (kv_len counts the new rows): the n_b new rows
+ * of request b are its keys [kv_len_b - n_b, kv_len_b).  The attention kernel
+ * reads those keys from k_new / v_new, and the workgroup whose key chunk holds
+ * them stores them into the cache for its kv head.
+ *   plan              a paged decode plan (one query row per request) without
+ *                     a custom mask; other plans: PKV_ERR_UNSUPPORTED
+ *   q ... sm_scale    as for pkv_run; cache is written (the new rows) and read
+ *   k_new, v_new      device [nnz, num_kv_heads, head_dim], cache dtype,
+ *                     strides in elements as for pkv_append_paged_kv
+ *   d_append_indptr, d_kv_indptr, d_kv_last_page_len   device, B+1, B+1 and B
+ *                     entries: the post-append metadata the plan was built on
+ *   nnz               rows of k_new / v_new (0: a plain run)
+ * Asynchronous on `stream`, no allocation.  The metadata is read only on the
+ * device: inconsistent values give undefined rows, never an access outside
+ * k_new, v_new or the pool (page ids outside it are skipped).
+ */
+pkv_status pkv_run_append(const pkv_plan* plan, const void* q, int64_t q_stride_token,
+                          int64_t q_stride_head, const pkv_cache_desc* cache,
+                          const int32_t* d_kv_indices, const void* k_new, const void* v_new,
+                          int64_t new_stride_token, int64_t new_stride_head,
+                          const int32_t* d_append_indptr, const int32_t* d_kv_indptr,
+                          const int32_t* d_kv_last_page_len, int32_t nnz, void* o,
+                          int64_t o_stride_token, int64_t o_stride_head, float* lse,
+                          float sm_scale, int32_t with_merge, void* stream);
 
 /*
  * Kernel timing (measurement support, not an operation of the method): arms

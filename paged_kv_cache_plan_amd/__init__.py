@@ -298,6 +298,29 @@ class Plan:
         self.run(q, k_cache, v_cache, kv_indices, out, lse, layout=layout, sm_scale=sm_scale, stream=stream,
                  _entry="pkv_run_attention", k_scale=k_scale, v_scale=v_scale)
 
+    def run_append(self, q, k_cache, v_cache, kv_indices, out, lse=None, *, k_new, v_new, append_indptr, kv_indptr,
+                   kv_last_page_len, layout, sm_scale=0.0, with_merge=True, stream=None, k_scale=1.0, v_scale=1.0):
+        """pkv_run_append: append_paged_kv of k_new/v_new [nnz, Hkv, D] fused into this decode run
+        (with_merge False: the attention launch only, like run_attention).  Metadata device int32."""
+        import torch
+        p = self.params
+        desc = cache_desc(k_cache, v_cache, layout, p.page_size, p.num_kv_heads, p.head_dim_qk, k_scale, v_scale)
+        if q.dim() != 3 or out.dim() != 3 or q.stride(2) != 1 or out.stride(2) != 1:
+            raise ValueError("q and out must be [tokens, heads, dim] with contiguous dim")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        if k_new.shape != v_new.shape or k_new.stride() != v_new.stride() or k_new.stride(2) != 1:
+            raise ValueError("k_new and v_new must be [nnz, heads, dim] with equal strides")
+        i32 = torch.int32
+        _check(lib().pkv_run_append(self._handle, _dev(q, "q"), q.stride(0), q.stride(1), ctypes.byref(desc),
+                                    _dev(kv_indices, "kv_indices", i32), _dev(k_new, "k_new", k_cache.dtype),
+                                    _dev(v_new, "v_new", k_cache.dtype), k_new.stride(0), k_new.stride(1),
+                                    _dev(append_indptr, "append_indptr", i32), _dev(kv_indptr, "kv_indptr", i32),
+                                    _dev(kv_last_page_len, "kv_last_page_len", i32), k_new.shape[0],
+                                    _dev(out, "out", q.dtype), out.stride(0), out.stride(1),
+                                    None if lse is None else _dev(lse, "lse"), ctypes.c_float(sm_scale),
+                                    1 if with_merge else 0, _stream(stream)))
+
     def run_merge(self, out, lse=None, *, stream=None):
         """pkv_run_merge: merge the split tiles' partial states into out / lse."""
         _check(lib().pkv_run_merge(self._handle, _dev(out, "out"), out.stride(0), out.stride(1),

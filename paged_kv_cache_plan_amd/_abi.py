@@ -46,10 +46,10 @@ class PlanInfo(ctypes.Structure):
         "mode", "batch_size", "num_items", "num_merges", "num_partial_rows", "chunk_pages", "split",
         "rows_per_tile", "heads_y", "num_cus", "target", "total_rows")] + [
         ("workspace_bytes", ctypes.c_int64), ("staging_bytes", ctypes.c_int64), ("fingerprint", ctypes.c_uint64),
-        ("mask_bits", ctypes.c_int64)]
+        ("mask_bits", ctypes.c_int64), ("merge_in_launch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_}
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
 
 
 class GraphCaps(ctypes.Structure):
@@ -107,6 +107,8 @@ SIGNATURES = {
     "pkv_run_attention": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _i64, _i64, _vp,
                                  ctypes.c_float, _vp]),
     "pkv_run_merge": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "pkv_run_append": (_i32, [_vp, _vp, _i64, _i64, ctypes.POINTER(CacheDesc), _vp, _vp, _vp, _i64, _i64, _vp, _vp,
+                              _vp, _i32, _vp, _i64, _i64, _vp, ctypes.c_float, _i32, _vp]),
     "pkv_time_next_attention": (_i32, [_vp, _vp]),
     "pkv_run_mla": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, ctypes.c_float, _vp]),
     "pkv_run_noalloc": (_i32, [ctypes.POINTER(PlanParams), _i32p, _i32p, _i32p, _i64, _i32p, _vp, _i64, _i64,

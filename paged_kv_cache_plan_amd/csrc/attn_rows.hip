@@ -149,9 +149,122 @@ __device__ __forceinline__ void expand_fp8(const uint4& raw, uint4& lo, uint4& h
   hi = make_uint4(cv0(raw.z), cv1(raw.z), cv0(raw.w), cv1(raw.w));
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Split merge inside the decode launch ("Deep Dive - FlashInfer", "A worked
+// split-KV example": shift by the largest base-2 statistic, weights
+// 2^(s - shift) normalised by their sum, LSE = shift + log2 sum).  Called by
+// every thread of a workgroup that has just written the partial state of one
+// chunk of (row, kv head): it counts the chunk in merge_ctr, and the
+// workgroup that finishes the last chunk folds all of them into o and lse.
+// All chunks of one (merge item, kv head) run on the same XCD, so the partial
+// states stored by the others are in its L2 once each writer has waited for
+// its stores; the reader drops its own L1 lines first.  The arithmetic and
+// its order are those of the separate merge kernel.
+template <typename T, int D, int G>
+__device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& mi, int32_t row, int32_t kvh) {
+  __shared__ int32_t s_last;
+  const int32_t hq = a.num_qo_heads;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are in L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* ctr = a.merge_ctr + int64_t(m) * a.num_kv_heads + kvh;
+    const int32_t done = atomicAdd(ctr, 1) + 1;
+    const bool last = done == mi.num_chunks;
+    if (last) atomicExch(ctr, 0);   // zero again for the next launch
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;   // uniform: another workgroup finishes this row
+  asm volatile("buffer_inv sc0" ::: "memory");
+  const int32_t n = mi.num_chunks, slot0 = mi.slot0;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int32_t hh = wave; hh < G; hh += kWaves) {
+    const int32_t head = kvh * G + hh;
+    const float* pbase = a.part_o + (int64_t(slot0) * hq + head) * D;
+    const int64_t cstride = int64_t(hq) * D;   // partial rows of one merge item's chunks are consecutive
+    auto stat = [&](int32_t c) { return a.part_lse[(int64_t(slot0) + c) * hq + head]; };
+    const bool pre = n <= 8 && D <= 128;
+    float2 x8[8];
+    const int32_t d_first = min(2 * lane, D - 2);
+    if (pre) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x8[j] = j < n ? *reinterpret_cast<const float2*>(pbase + int64_t(j) * cstride + d_first)
+                      : make_float2(0.f, 0.f);
+    }
+    const float sc = lane < n ? stat(lane) : -INFINITY;
+    float mx = sc;
+    for (int32_t c = lane + 64; c < n; c += 64) mx = fmaxf(mx, stat(c));
+    mx = wave_max(mx);
+    const float wl = sc == -INFINITY ? 0.f : dev::fast_exp2(sc - mx);   // mx finite whenever sc is
+    float zp = wl;
+    for (int32_t c = lane + 64; c < n; c += 64) {
+      const float s2 = stat(c);
+      zp += s2 == -INFINITY ? 0.f : dev::fast_exp2(s2 - mx);
+    }
+    const float z = wave_sum(zp);
+    const float scale = z > 0.f ? wl / z : 0.f;
+    auto weight = [&](int32_t c) {   // chunk c's normalised weight
+      if (c < 64) return __shfl(scale, c);
+      const float s2 = stat(c);
+      return s2 == -INFINITY || !(z > 0.f) ? 0.f : dev::fast_exp2(s2 - mx) / z;
+    };
+    T* orow = static_cast<T*>(a.o) + int64_t(row) * a.o_stride_token + int64_t(head) * a.o_stride_head;
+    if (pre) {
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = j < n ? __shfl(scale, j) : 0.f;
+        acc0 = fmaf(w, x8[j].x, acc0);
+        acc1 = fmaf(w, x8[j].y, acc1);
+      }
+      if (2 * lane < D) {
+        store_out<T>(orow + 2 * lane, acc0);
+        store_out<T>(orow + 2 * lane + 1, acc1);
+      }
+    } else {
+      for (int32_t d0 = 0; d0 < D; d0 += 128) {
+        const int32_t d = d0 + 2 * lane;
+        const float* src = pbase + min(d, D - 2);
+        float acc0 = 0.f, acc1 = 0.f;
+        for (int32_t c = 0; c < n; c += 4) {
+          float2 x[4];
+          float w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int32_t cc = min(c + j, n - 1);
+            w[j] = weight(cc);
+            if (c + j >= n) w[j] = 0.f;
+            x[j] = *reinterpret_cast<const float2*>(src + int64_t(cc) * cstride);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc0 = fmaf(w[j], x[j].x, acc0);
+            acc1 = fmaf(w[j], x[j].y, acc1);
+          }
+        }
+        if (d < D) {
+          store_out<T>(orow + d, acc0);
+          store_out<T>(orow + d + 1, acc1);
+        }
+      }
+    }
+    if (lane == 0 && a.lse) a.lse[int64_t(row) * hq + head] = z > 0.f ? mx + __log2f(z) : -INFINITY;
+  }
+}
+
 // T: query / output elements (bf16 bits or float).  TK: stored K/V elements
 // (T itself, or uint8_t E4M3 codes with T = bf16).
-template <typename T, typename TK, int D, int G, bool kAligned, bool kMask>
+template <typename T, typename TK, int D, int G, bool kAligned, bool kMask, bool kAppend>
 __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr bool kFp8 = sizeof(TK) == 1;
@@ -176,9 +289,22 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
 
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
-  const int32_t kvh = blockIdx.x - item_idx * hkv;
   if (a.live_items && item_idx >= *a.live_items) return;   // fixed-capacity grid: whole workgroup
   const Item it = a.items[item_idx];
+  // Workgroup item * Hkv + j takes kv head (j + b) mod Hkv of request b:
+  // workgroups run on XCD (blockIdx mod 8), so every XCD serves a mix of kv
+  // heads (heads whose rows sit at some offsets in the token rows stream
+  // more slowly than others), while all chunks of one (request, kv head)
+  // still share an XCD.
+  const int32_t kvh = (int32_t(blockIdx.x) - item_idx * hkv + it.batch % hkv) % hkv;
+  // A chunk of a split decode row, with the merge inside the launch: its
+  // merge item, read now so that the end of the workgroup waits on no load.
+  int32_t merge_m = -1;
+  MergeItem merge_item{0, 0, 0, 0};
+  if (a.merge_ctr && it.out_slot >= 0) {
+    merge_m = a.tile_merge[it.batch];
+    merge_item = a.merges[merge_m];
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // Group vg of the wave holds key u * VT + vg of each 16-key block (u < NU);
@@ -197,6 +323,26 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   auto slot_of = [&](int32_t j) {
     return kAligned ? (j & (psz - 1)) : (pshift >= 0 ? (j & (psz - 1)) : (j - (j / psz) * psz));
   };
+
+  // Fused append: the request's n_b new rows are its keys [kv_len - n_b,
+  // kv_len) (kv_len already counts them), read from k_new / v_new and stored
+  // into their cache slots for this kv head by the workgroup whose chunk
+  // holds them, as the append kernel would (each key of a decode row lies in
+  // one item).  Key j >= new_lo is row j + new_off of k_new (clamped into the
+  // nnz_new rows, so that inconsistent metadata never reads outside them).
+  int32_t new_lo = INT32_MAX, new_off = 0;
+  const TK* knew = nullptr;
+  const TK* vnew = nullptr;
+  if constexpr (kAppend) {
+    const int32_t b = it.batch;
+    const int32_t a0 = a.append_indptr[b], a1 = a.append_indptr[b + 1];
+    const int32_t np = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    const int32_t kvlen = np > 0 ? (np - 1) * psz + a.kv_last[b] : 0;
+    new_lo = max(kvlen - (a1 - a0), 0);
+    new_off = a1 - kvlen;
+    knew = static_cast<const TK*>(a.k_new) + int64_t(kvh) * a.new_stride_head;
+    vnew = static_cast<const TK*>(a.v_new) + int64_t(kvh) * a.new_stride_head;
+  }
 
   for (int r = 0; r < it.num_rows; ++r) {
     const int32_t row = it.q_row0 + r;
@@ -234,16 +380,19 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       __syncthreads();
       for (int i = threadIdx.x; i < np; i += kThreads) {
         const int32_t pg = pages[sp + i];
-        s_pages[i] = uint32_t(pg) < max_pages ? pg : 0;
+        // Ids outside the pool read page 0; with a fused append they keep the
+        // sign bit as a mark, so that no new row is stored through them.
+        s_pages[i] = uint32_t(pg) < max_pages ? pg : (kAppend ? INT32_MIN : 0);
       }
       __syncthreads();
+      auto page_id = [&](int32_t i) { return kAppend ? (s_pages[i] & INT32_MAX) : s_pages[i]; };
       const int32_t tlo = max(lo, sp * psz);
-      const int32_t thi = min(hi, (sp + np) * psz);
+      int32_t thi = min(hi, (sp + np) * psz);   // lowered below past a fused append's new keys
 
       // Element offset of key j's row; keys at or past thi re-read key thi-1.
       auto row_off = [&](int32_t j) -> int64_t {
         j = min(j, thi - 1);
-        return int64_t(s_pages[page_of(j) - sp]) * a.page_stride + int64_t(slot_of(j)) * a.token_stride;
+        return int64_t(page_id(page_of(j) - sp)) * a.page_stride + int64_t(slot_of(j)) * a.token_stride;
       };
       // K and V rows of one block: instruction u moves key rows u*VT + g, each
       // read by VL lanes as contiguous 16-byte chunks (whole rows per request).
@@ -251,7 +400,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         int64_t off[NU];
         if constexpr (kAligned) {
           // A 16-key block never crosses a page: one page id for the block.
-          const int64_t base = int64_t(s_pages[(blk >> pshift) - sp]) * a.page_stride;
+          const int64_t base = int64_t(page_id((blk >> pshift) - sp)) * a.page_stride;
           const int32_t last = thi - 1 - blk;
           const int32_t s0 = blk & (psz - 1);
 #pragma unroll
@@ -270,7 +419,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           for (int c = 0; c < VCR; ++c) vr[u][c] = dev::load16<kStreamKV>(vbase + off[u] + (vi + VL * c) * RE);
       };
 
-      auto compute = [&](int32_t blk, uint4 (&kraw)[NU][VCR], uint4 (&vraw)[NU][VCR]) {
+      auto compute = [&](int32_t blk, uint4 (&kraw)[NU][VCR], uint4 (&vraw)[NU][VCR]) __attribute__((always_inline)) {
         // K and V rows as bf16 / f32 chunks (fp8 codes expanded in registers).
         uint4 kr[NU][VC], vr[NU][VC];
 #pragma unroll
@@ -367,19 +516,103 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         }
       };
 
+      constexpr int32_t kStride = kWaves * kBlockKeys;
+      // Fused append: the blocks from the one holding the segment's first new
+      // key nlo onward (the boundary blocks) mix cached keys (below nlo) and
+      // rows of k_new / v_new.  Each goes to the wave that owns it in the
+      // loop's interleave; the wave loads its first one here, ahead of the
+      // loop's loads, and computes it first (the online softmax is
+      // order-free, so only the fp32 rounding differs from the order without
+      // the append).  The loop below covers the cached blocks [tlo, nb0).
+      const int32_t thi_all = thi;
+      int32_t nlo = thi, nb0 = thi, bb = thi, bb0 = thi;
+      // float32 rows keep no boundary block across the loop (its registers
+      // would spill): they load and compute it after the loop.
+      constexpr bool kPreBoundary = kBF16;
+      uint4 kbn[NU][VCR], vbn[NU][VCR];   // the wave's boundary block
+      auto load_mixed = [&](int32_t blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int32_t key = min(blk + u * VT + vg, thi_all - 1);
+          const int64_t row = min(max(int64_t(new_off) + key, int64_t(0)), int64_t(a.nnz_new) - 1);
+          const bool fresh = key >= nlo;
+          const int64_t off = fresh ? row * a.new_stride_token
+                                    : int64_t(page_id(page_of(key) - sp)) * a.page_stride +
+                                          int64_t(slot_of(key)) * a.token_stride;
+          const TK* kp = (fresh ? knew : kbase) + off;
+          const TK* vp = (fresh ? vnew : vbase) + off;
+#pragma unroll
+          for (int c = 0; c < VCR; ++c) {
+            kbn[u][c] = dev::load16<kStreamKV>(kp + (vi + VL * c) * RE);
+            vbn[u][c] = dev::load16<kStreamKV>(vp + (vi + VL * c) * RE);
+          }
+        }
+      };
+      if constexpr (kAppend) {
+        nlo = max(tlo, new_lo);
+        if (nlo < thi) {
+          nb0 = tlo + (nlo - tlo) / kBlockKeys * kBlockKeys;
+          const int32_t k0 = (nb0 - tlo) / kBlockKeys;
+          bb = nb0 + ((wave - k0) % kWaves + kWaves) % kWaves * kBlockKeys;
+          bb0 = bb;
+          if (kPreBoundary && bb < thi_all) load_mixed(bb);
+          thi = nb0;
+        }
+      }
+
       // Register sets: the loads of the next block(s) are in flight while a
       // block computes.  The prefetch is unconditional (past the end it
       // re-reads the last block, which the caches serve) so that every path
       // through the loop has the same loads outstanding and the wait before a
       // block's compute covers only that block's own loads.
-      constexpr int32_t kStride = kWaves * kBlockKeys;
       const int32_t blk_max = kAligned ? ((thi - 1) & ~(kBlockKeys - 1)) : thi - 1;
       int32_t blk = tlo + wave * kBlockKeys;
+      // The wave's boundary block bb: its new rows go into their cache slots
+      // (first row only), then the block is computed against the segment's
+      // full key range.  The first one runs while the loop's first loads are
+      // in flight (its own were issued before them).
+      // The new rows of boundary block blk (loaded into kbn / vbn) into their
+      // cache slots (first row only).  Issued after the wave's last load:
+      // a store counts like a load in the wave's memory counter, and one
+      // between the loop's loads would make every later wait cover it too.
+      auto store_new = [&](int32_t blk) __attribute__((always_inline)) {
+        if (r != 0) return;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int32_t key = blk + u * VT + vg;
+          const int32_t pg = key >= nlo && key < thi_all ? s_pages[page_of(key) - sp] : -1;
+          if (pg >= 0) {   // a marked (outside the pool) page stores nothing
+            // The cache is the caller's writable pool (const only for the plain run).
+            const int64_t off = int64_t(pg) * a.page_stride + int64_t(slot_of(key)) * a.token_stride;
+            TK* kd = const_cast<TK*>(kbase) + off;
+            TK* vd = const_cast<TK*>(vbase) + off;
+#pragma unroll
+            for (int c = 0; c < VCR; ++c) {
+              *reinterpret_cast<uint4*>(kd + (vi + VL * c) * RE) = kbn[u][c];
+              *reinterpret_cast<uint4*>(vd + (vi + VL * c) * RE) = vbn[u][c];
+            }
+          }
+        }
+      };
+      // Block bb against the segment's full key range.
+      auto boundary = [&]() __attribute__((always_inline)) {
+        const int32_t thi_loop = thi;
+        thi = thi_all;
+        compute(bb, kbn, vbn);
+        thi = thi_loop;
+      };
+      bool first_done = false;   // the prefetched first boundary block is computed
       if constexpr (kDepth == 3) {
         uint4 ka[NU][VCR], kb[NU][VCR], kc[NU][VCR], va[NU][VCR], vb[NU][VCR], vc[NU][VCR];
         if (blk < thi) {
           load(blk, ka, va);
           load(min(blk + kStride, blk_max), kb, vb);
+          if constexpr (kAppend && kPreBoundary) {
+            if (bb < thi_all) {
+              boundary();
+              first_done = true;
+            }
+          }
           while (true) {
             load(min(blk + 2 * kStride, blk_max), kc, vc);
             compute(blk, ka, va);
@@ -399,6 +632,12 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         uint4 ka[NU][VCR], kb[NU][VCR], va[NU][VCR], vb[NU][VCR];
         if (blk < thi) {
           load(blk, ka, va);
+          if constexpr (kAppend && kPreBoundary) {
+            if (bb < thi_all) {
+              boundary();
+              first_done = true;
+            }
+          }
           while (true) {
             load(min(blk + kStride, blk_max), kb, vb);
             compute(blk, ka, va);
@@ -409,6 +648,16 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
             blk += kStride;
             if (blk >= thi) break;
           }
+        }
+      }
+      if constexpr (kAppend) {
+        // A wave without cached blocks takes its first boundary block here;
+        // appends that reach past one block per wave take the rest here.
+        for (; bb < thi_all; bb += kStride) {
+          const bool pre = kPreBoundary && bb == bb0;   // already in kbn / vbn
+          if (!pre) load_mixed(bb);
+          if (!(pre && first_done)) boundary();
+          store_new(bb);
         }
       }
     }
@@ -479,6 +728,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         if (d == 0) a.part_lse[prow] = lse2;
       }
     }
+    if (merge_m >= 0) merge_in_launch<T, D, G>(a, merge_m, merge_item, row, kvh);
     __syncthreads();
   }
 }
@@ -489,16 +739,22 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const bool aligned = a.page_shift >= 4;   // a power-of-two page of at least 16 keys
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
+  if (a.mask && a.append_indptr) return hipErrorInvalidValue;   // no fused append over a custom mask
   if (a.mask) {
     if (aligned)
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, true>, grid, block, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, true, false>, grid, block, st, a);
     else
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, true>, grid, block, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, true, false>, grid, block, st, a);
+  } else if (a.append_indptr) {
+    if (aligned)
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false, true>, grid, block, st, a);
+    else
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false, true>, grid, block, st, a);
   } else {
     if (aligned)
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false>, grid, block, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false, false>, grid, block, st, a);
     else
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false>, grid, block, st, a);
+      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false, false>, grid, block, st, a);
   }
   return hipGetLastError();
 }

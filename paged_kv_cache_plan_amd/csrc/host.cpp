@@ -192,8 +192,16 @@ struct PlanResult {
   std::vector<Item> items;
   std::vector<MergeItem> merges;
   std::vector<pkv::MaskRow> mask_rows;   // custom-masked plans: one per request
+  std::vector<int32_t> tile_merge;       // decode plans: merge item of request b's tile, or -1
   pkv_plan_info info;
 };
+
+// Paged decode plans carry the tables of the split merge inside the
+// attention launch: per request its merge item (int32), and per (merge item,
+// kv head) a counter of finished chunks (int32, zero between launches).
+bool has_merge_tables(const pkv_plan_params* p) {
+  return p->mode == PKV_MODE_DECODE && p->kv_format == PKV_KV_PAGED && p->mask_mode == PKV_MASK_NONE;
+}
 
 // Ragged metadata, in the oracle's order: heads, qo_indptr, kv_indptr, then
 // qo_len <= kv_len per request.
@@ -449,6 +457,12 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
     }
   }
 
+  out->tile_merge.clear();
+  if (has_merge_tables(prm)) {   // a decode tile is one request: merge item q_row0 == b
+    out->tile_merge.assign(size_t(batch), -1);
+    for (size_t m = 0; m < out->merges.size(); ++m) out->tile_merge[size_t(out->merges[m].q_row0)] = int32_t(m);
+  }
+
   pkv_plan_info& in = out->info;
   std::memset(&in, 0, sizeof in);
   in.mode = prm->mode;
@@ -465,9 +479,11 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   in.total_rows = int32_t(total_rows);
   const int64_t hq = prm->num_qo_heads;
   in.mask_bits = mask_bits;
+  const int64_t merge_ctrs = out->tile_merge.empty() ? 0 : int64_t(out->merges.size()) * prm->num_kv_heads;
   const int64_t staging = align256(int64_t(out->items.size()) * sizeof(Item)) +
                           align256(int64_t(out->merges.size()) * sizeof(MergeItem)) +
-                          align256(int64_t(out->mask_rows.size()) * sizeof(pkv::MaskRow));
+                          align256(int64_t(out->mask_rows.size()) * sizeof(pkv::MaskRow)) +
+                          align256(int64_t(out->tile_merge.size()) * 4) + align256(merge_ctrs * 4);
   in.staging_bytes = staging;
   in.workspace_bytes = staging + align256(slot * hq * 4) + align256(slot * hq * prm->head_dim_vo * 4);
   in.fingerprint = fingerprint(*prm, qo_indptr, user_kv_indptr, kv_indices, num_indices, user_last);
@@ -659,6 +675,46 @@ void release_staging(void* h_staging, const void* owner) {
 // Plans that lead to a run must bound the page ids they will dereference.
 // The MLA run takes raw cache pointers without a descriptor, so its plan
 // carries the pool size.
+// Whether workgroups i and i + 8 of a launch run on one XCD on `device`
+// (the order in which the command processor hands workgroups to the XCDs),
+// checked once per device with a small probe launch: the split merge inside
+// the decode launch relies on it.  A failed check (or PKV_MERGE_IN_ATTENTION=0)
+// leaves the merge to its own launch.
+bool xcd_groups_ok(int device) {
+  static std::mutex mu;
+  static std::unordered_map<int, bool> known;
+  std::lock_guard<std::mutex> lock(mu);
+  auto f = known.find(device);
+  if (f != known.end()) return f->second;
+  bool ok = false;
+  const char* env = std::getenv("PKV_MERGE_IN_ATTENTION");
+  if (!(env && env[0] == '0')) {
+    constexpr int32_t kBlocks = 1024;
+    int32_t* d = nullptr;
+    std::vector<int32_t> h(kBlocks, -1);
+    if (hipMalloc(&d, kBlocks * sizeof(int32_t)) == hipSuccess) {
+      if (pkv::launch_xcd_probe(d, kBlocks, nullptr) == hipSuccess &&
+          hipMemcpy(h.data(), d, kBlocks * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess) {
+        ok = true;
+        for (int32_t i = 0; i < kBlocks; ++i) ok = ok && h[i] >= 0 && h[i] == h[i % 8];
+      }
+      (void)hipFree(d);
+    }
+    (void)hipGetLastError();   // a failed probe only turns the fused merge off
+  }
+  known[device] = ok;
+  return ok;
+}
+
+// Whether run() folds a plan's split rows inside the attention launch: a
+// paged decode plan (one row per tile, each chunk of it one workgroup per kv
+// head: workgroup item * Hkv + j serves head (j + b) mod Hkv of request b),
+// kv heads a multiple of 8 so that every chunk of one (request, kv head)
+// lands on the same XCD.
+bool merge_in_launch_ok(const pkv_plan_params* p, int device) {
+  return has_merge_tables(p) && p->num_kv_heads % 8 == 0 && xcd_groups_ok(device);
+}
+
 pkv_status check_runnable(const pkv_plan_params* p) {
   if (p && p->mode == PKV_MODE_MLA_DECODE && p->max_num_pages <= 0)
     return fail(PKV_ERR_INVALID_ARG, "MLA plans need max_num_pages (the pool size): pkv_run_mla has no "
@@ -677,6 +733,12 @@ struct pkv_plan {
   float* d_part_lse;
   float* d_part_o;
   int device;
+  // Split merge inside the attention launch (decode plans whose kv heads
+  // are a multiple of 8 on a device that runs workgroups i and i + 8 on one
+  // XCD): the tables, and whether run() uses them.
+  int32_t* d_tile_merge = nullptr;
+  int32_t* d_merge_ctr = nullptr;
+  bool merge_in = false;
   // Fixed-capacity plans (pkv_graph_plan_create): every run launches grids
   // sized by the capacities and the kernels read the live counts from
   // d_counts, so one captured graph serves every later update.
@@ -799,17 +861,28 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
   plan->d_mask_rows = reinterpret_cast<pkv::MaskRow*>(ws + items_bytes + merges_bytes);
   plan->d_part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
   plan->d_part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
+  const int64_t tm_off = items_bytes + merges_bytes + align256(int64_t(r.mask_rows.size()) * sizeof(pkv::MaskRow));
+  const int64_t ctr_off = tm_off + align256(int64_t(r.tile_merge.size()) * 4);
+  const int64_t ctr_bytes = r.tile_merge.empty() ? 0 : int64_t(r.merges.size()) * params->num_kv_heads * 4;
   hipError_t e = hipGetDevice(&plan->device);
   if (e != hipSuccess) {
     delete plan;
     return hip_fail(e, "hipGetDevice");
   }
+  if (!r.tile_merge.empty()) {
+    plan->d_tile_merge = reinterpret_cast<int32_t*>(ws + tm_off);
+    plan->d_merge_ctr = reinterpret_cast<int32_t*>(ws + ctr_off);
+    plan->merge_in = !r.merges.empty() && merge_in_launch_ok(params, plan->device);
+  }
+  plan->info.merge_in_launch = plan->merge_in ? 1 : 0;
   plan->h_staging = h_staging;
   if (in.staging_bytes > 0) {
     e = upload_staging(h_staging, ws, in.staging_bytes, st, plan, [&](char* hs) {
       copy_table(hs, r.items);
       copy_table(hs + items_bytes, r.merges);
       copy_table(hs + items_bytes + merges_bytes, r.mask_rows);
+      copy_table(hs + tm_off, r.tile_merge);
+      std::memset(hs + ctr_off, 0, size_t(ctr_bytes));   // counters start at zero
     });
     if (e != hipSuccess) {
       release_staging(h_staging, plan);
@@ -918,6 +991,17 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(float(p.head_dim_qk));
   a->scale_log2 = scale * 1.4426950408889634f;
   a->v_scale = 1.f;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  a->new_stride_token = 0;
+  a->new_stride_head = 0;
+  a->append_indptr = nullptr;
+  a->kv_indptr = nullptr;
+  a->kv_last = nullptr;
+  a->nnz_new = 0;
+  a->merges = nullptr;
+  a->tile_merge = nullptr;
+  a->merge_ctr = nullptr;
   if (p.kv_dtype == PKV_FP8_E4M3) {   // the key scale multiplies every logit
     if (cache->k_scale > 0.f) a->scale_log2 *= cache->k_scale;
     if (cache->v_scale > 0.f) a->v_scale = cache->v_scale;
@@ -1012,10 +1096,70 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int64_t q_stride_token, 
                    const pkv_cache_desc* cache, const int32_t* d_kv_indices, void* o,
                    int64_t o_stride_token, int64_t o_stride_head, float* lse, float sm_scale,
                    void* stream) {
+  if (plan && plan->merge_in)   // one launch: the split rows are folded inside it
+    return pkv_run_append(plan, q, q_stride_token, q_stride_head, cache, d_kv_indices, nullptr, nullptr, 0, 0,
+                          nullptr, nullptr, nullptr, 0, o, o_stride_token, o_stride_head, lse, sm_scale, 1, stream);
   pkv_status s = pkv_run_attention(plan, q, q_stride_token, q_stride_head, cache, d_kv_indices, o, o_stride_token,
                                    o_stride_head, lse, sm_scale, stream);
   if (s) return s;
   if (plan->params.mode == PKV_MODE_MLA_DECODE) return ok();
+  return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
+}
+
+pkv_status pkv_run_append(const pkv_plan* plan, const void* q, int64_t q_stride_token, int64_t q_stride_head,
+                          const pkv_cache_desc* cache, const int32_t* d_kv_indices, const void* k_new,
+                          const void* v_new, int64_t new_stride_token, int64_t new_stride_head,
+                          const int32_t* d_append_indptr, const int32_t* d_kv_indptr,
+                          const int32_t* d_kv_last_page_len, int32_t nnz, void* o, int64_t o_stride_token,
+                          int64_t o_stride_head, float* lse, float sm_scale, int32_t with_merge, void* stream) {
+  if (!plan || !cache) return fail(PKV_ERR_INVALID_ARG, "null plan or cache");
+  const pkv_plan_params& p = plan->params;
+  if (p.mode != PKV_MODE_DECODE || p.kv_format == PKV_KV_RAGGED || p.mask_mode == PKV_MASK_CUSTOM)
+    return fail(PKV_ERR_UNSUPPORTED, "the fused append runs with paged decode plans without a custom mask");
+  if (nnz < 0) return fail(PKV_ERR_INVALID_ARG, "negative nnz");
+  pkv::AttnArgs a;
+  const int32_t grid_items = plan->grid_items();
+  pkv_status s = prepare_attn(p, plan->device, grid_items > 0, q, q_stride_token, q_stride_head, cache,
+                              d_kv_indices, o, o_stride_token, o_stride_head, lse, sm_scale, &a);
+  if (s) return s;
+  if (nnz > 0) {
+    const size_t es = dtype_size(p.kv_dtype);
+    if ((s = check_ptr16(k_new, "k_new")) || (s = check_ptr16(v_new, "v_new"))) return s;
+    if (!d_append_indptr || !d_kv_indptr || !d_kv_last_page_len)
+      return fail(PKV_ERR_INVALID_ARG, "null append metadata");
+    if (!stride_ok(new_stride_token, es) || !stride_ok(new_stride_head, es))
+      return fail(PKV_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  }
+  if (grid_items == 0) {
+    // No attention work: the rows still go into the cache.
+    if (nnz == 0) return ok();
+    return pkv_append_paged_kv(k_new, v_new, new_stride_token, new_stride_head, d_append_indptr, d_kv_indptr,
+                               d_kv_indices, d_kv_last_page_len, p.batch_size, nnz, cache, stream);
+  }
+  a.items = plan->d_items;
+  a.num_items = grid_items;
+  a.live_items = plan->live_items();
+  a.part_o = plan->d_part_o;
+  a.part_lse = plan->d_part_lse;
+  if (nnz > 0) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_stride_token = new_stride_token;
+    a.new_stride_head = new_stride_head;
+    a.append_indptr = d_append_indptr;
+    a.kv_indptr = d_kv_indptr;
+    a.kv_last = d_kv_last_page_len;
+    a.nnz_new = nnz;
+  }
+  const bool merge_in = with_merge && plan->merge_in;
+  if (merge_in) {
+    a.merges = plan->d_merges;
+    a.tile_merge = plan->d_tile_merge;
+    a.merge_ctr = plan->d_merge_ctr;
+  }
+  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream));
+  if (s) return s;
+  if (!with_merge || merge_in) return ok();
   return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
 }
 
@@ -1357,7 +1501,8 @@ namespace {
 struct GraphLayout {
   pkv_graph_caps caps;
   int32_t rows_per_tile;
-  int64_t items_off, merges_off, mask_off, staging_bytes, lse_off, o_off, workspace_bytes;
+  int64_t items_off, merges_off, mask_off, tm_off, ctr_off, ctr_bytes, staging_bytes, lse_off, o_off,
+      workspace_bytes;
 };
 
 pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, GraphLayout* g) {
@@ -1406,7 +1551,11 @@ pkv_status graph_layout(const pkv_plan_params* prm, const pkv_graph_caps* in, Gr
   g->items_off = 256;   // the two counters
   g->merges_off = g->items_off + align256(int64_t(c.max_items) * sizeof(Item));
   g->mask_off = g->merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
-  g->staging_bytes = g->mask_off + (prm->mask_mode == PKV_MASK_CUSTOM ? align256(B * sizeof(pkv::MaskRow)) : 0);
+  g->tm_off = g->mask_off + (prm->mask_mode == PKV_MASK_CUSTOM ? align256(B * sizeof(pkv::MaskRow)) : 0);
+  const bool tables = has_merge_tables(prm);
+  g->ctr_off = g->tm_off + (tables ? align256(B * 4) : 0);
+  g->ctr_bytes = tables ? int64_t(c.max_merges) * prm->num_kv_heads * 4 : 0;
+  g->staging_bytes = g->ctr_off + align256(g->ctr_bytes);
   g->lse_off = g->staging_bytes;
   g->o_off = g->lse_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * 4);
   g->workspace_bytes = g->o_off + align256(int64_t(c.max_partial_rows) * prm->num_qo_heads * prm->head_dim_vo * 4);
@@ -1465,8 +1614,17 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
   plan->h_staging = h_staging;
   plan->staging_bytes = g.staging_bytes;
   hipError_t e = hipGetDevice(&plan->device);
-  if (e == hipSuccess)   // counters (and lists) start at zero: a run before the first update does nothing
-    e = upload_staging(h_staging, ws, 256, static_cast<hipStream_t>(stream), plan, [](char*) {});
+  if (e == hipSuccess && has_merge_tables(params)) {
+    plan->d_tile_merge = reinterpret_cast<int32_t*>(ws + g.tm_off);
+    plan->d_merge_ctr = reinterpret_cast<int32_t*>(ws + g.ctr_off);
+    plan->merge_in = g.caps.max_merges > 0 && merge_in_launch_ok(params, plan->device);
+  }
+  plan->info.merge_in_launch = plan->merge_in ? 1 : 0;
+  // The live counts (and the merge counters) start at zero: a run before the
+  // first update does nothing.
+  if (e == hipSuccess)
+    e = upload_staging(h_staging, ws, g.ctr_bytes > 0 ? g.ctr_off + g.ctr_bytes : 256,
+                       static_cast<hipStream_t>(stream), plan, [](char*) {});
   if (e != hipSuccess) {
     release_staging(h_staging, plan);
     delete plan;
@@ -1499,8 +1657,14 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
   const int64_t items_off = 256;
   const int64_t merges_off = items_off + align256(int64_t(c.max_items) * sizeof(Item));
   const int64_t mask_off = merges_off + align256(int64_t(c.max_merges) * sizeof(MergeItem));
-  const int64_t upload = r.mask_rows.empty() ? merges_off + int64_t(r.merges.size()) * sizeof(MergeItem)
-                                             : mask_off + int64_t(r.mask_rows.size()) * sizeof(pkv::MaskRow);
+  GraphLayout g;
+  pkv_status gs = graph_layout(&plan->params, &plan->caps, &g);
+  if (gs) return gs;
+  int64_t upload = r.mask_rows.empty() ? merges_off + int64_t(r.merges.size()) * sizeof(MergeItem)
+                                       : mask_off + int64_t(r.mask_rows.size()) * sizeof(pkv::MaskRow);
+  // Decode plans: the merge table of the live batch, and the counters zeroed
+  // again (a run that failed part-way must not leave counts behind).
+  if (!r.tile_merge.empty()) upload = g.ctr_off + g.ctr_bytes;
   hipError_t e = upload_staging(plan->h_staging, plan->d_ws, upload, static_cast<hipStream_t>(stream), plan,
                                 [&](char* hs) {
                                   int32_t* counts = reinterpret_cast<int32_t*>(hs);
@@ -1509,12 +1673,15 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
                                   copy_table(hs + items_off, r.items);
                                   copy_table(hs + merges_off, r.merges);
                                   copy_table(hs + mask_off, r.mask_rows);
+                                  copy_table(hs + g.tm_off, r.tile_merge);
                                 });
   if (e != hipSuccess) return hip_fail(e, "uploading the plan");
   const int64_t ws_bytes = plan->info.workspace_bytes, st_bytes = plan->info.staging_bytes;
+  const int32_t merge_in = plan->info.merge_in_launch;
   plan->info = r.info;
   plan->info.workspace_bytes = ws_bytes;
   plan->info.staging_bytes = st_bytes;
+  plan->info.merge_in_launch = merge_in;
   return ok();
 }
 

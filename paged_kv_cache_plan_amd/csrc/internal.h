@@ -91,6 +91,26 @@ struct AttnArgs {
   const uint32_t* mask;        // packed custom mask (little-endian bits), or null
   const MaskRow* mask_rows;    // per request, when mask is set
   float v_scale;               // fp8 caches: factor applied to the normalised output
+  // Append fused into a decode launch (null append_indptr: none).  Request b's
+  // new rows k_new/v_new[append_indptr[b] .. append_indptr[b+1]) are its last
+  // keys (kv_len from kv_indptr and kv_last): the kernel reads them from there
+  // and the workgroup whose chunk holds them also writes them into the cache.
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride_token, new_stride_head;   // elements
+  const int32_t* append_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* kv_last;
+  int32_t nnz_new;             // rows of k_new / v_new
+  // Split merge inside the decode launch (null merge_ctr: a separate merge
+  // launch folds the partial states).  tile_merge[b]: merge item of request
+  // b's tile or -1; merge_ctr[m * num_kv_heads + h]: chunks of merge item m
+  // finished for kv head h (zero between launches).  Every chunk of one
+  // (merge item, kv head) runs on one XCD (workgroup order), so their
+  // partial states meet in that XCD's L2.
+  const MergeItem* merges;
+  const int32_t* tile_merge;
+  int32_t* merge_ctr;
 };
 
 struct MergePartialArgs {
@@ -157,6 +177,8 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_mla_merge(const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_partials(int32_t dtype, const MergePartialArgs& a, hipStream_t stream);
 hipError_t launch_merge_rows(int32_t dtype, const MergeRowsArgs& a, hipStream_t stream);
+// out[i] = the XCD that ran workgroup i, for i < blocks (64 threads each).
+hipError_t launch_xcd_probe(int32_t* d_out, int32_t blocks, hipStream_t st);
 hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st,
                          int64_t new_sh, const int32_t* append_indptr, const int32_t* kv_indptr,
                          const int32_t* kv_indices, const int32_t* last_page_len, int32_t batch,

@@ -572,7 +572,22 @@ __global__ __launch_bounds__(256) void merge_many_kernel(const T* v, const float
   if (lane == 0) so[rh] = z > 0.f ? mx + __log2f(z) : -INFINITY;
 }
 
+// The XCD (accelerator complex die) that runs each workgroup, from the
+// hardware register that names it: the library checks once per device that
+// workgroups i and i + 8 share one XCD before it relies on that for the
+// split merge inside the decode launch.
+__global__ void xcd_probe_kernel(int32_t* out) {
+  int32_t id;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+  if (threadIdx.x == 0) out[blockIdx.x] = id & 0xf;
+}
+
 }  // namespace
+
+hipError_t launch_xcd_probe(int32_t* d_out, int32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(uint32_t(blocks)), dim3(64), 0, st, d_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, int64_t new_st, int64_t new_sh,
                          const int32_t* append_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
