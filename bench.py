@@ -126,9 +126,9 @@ class Runner:
         # Decode batches with new rows append them inside the attention launch
         # (pkv_run_append) unless a separate append kernel is asked for.
         self.fused_append = b.mode == "decode" and b.k_new is not None
-        # Decode runs fold the split rows inside the attention launch when the
-        # plan allows it (pkv_plan_info.merge_in_launch), unless asked not to.
-        self.separate_merge = False
+        # Decode plans may fold the split merge into the attention launch
+        # (plan_params merge_in_launch); set before make_plan.
+        self.separate_merge = True
         dev = lambda x, bf: (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
                              if bf else torch.from_numpy(np.ascontiguousarray(x)).cuda())
         bf = b.dtype == "bf16"
@@ -168,6 +168,9 @@ class Runner:
         self.plan = self.pkv.Plan(self.params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None,
                                   kv_indptr=b.kv_indptr, kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len,
                                   workspace=self.workspace, staging=self.staging)
+        # o is final after the attention call (the split merge inside it)
+        self.merged = (b.mode == "decode" and not self.separate_merge
+                       and bool(self.plan.info["merge_in_launch"]))
         return self.plan
 
     def append(self, i: int):
@@ -198,7 +201,7 @@ class Runner:
                 self.pkv.time_next_attention(ev[0], ev[1])
             else:
                 ev[0].record()
-        merged = b.mode == "decode" and not self.separate_merge   # o final after the attention call
+        merged = self.merged
         if self.fused_append:
             plan.run_append(self.q, k, v, self.kv_indices, self.out, self.lse, k_new=self.k_new, v_new=self.v_new,
                             append_indptr=self.append_indptr, kv_indptr=self.kv_indptr_d,
@@ -558,9 +561,9 @@ def main():
     ap.add_argument("--separate-append", action="store_true",
                     help="decode workloads: launch append_paged_kv on its own before each attention launch "
                          "instead of fusing it into the attention launch (pkv_run_append)")
-    ap.add_argument("--separate-merge", action="store_true",
-                    help="decode workloads: merge split rows in their own launch after attention instead of "
-                         "inside the attention launch (when the plan allows that)")
+    ap.add_argument("--merge-in-launch", action="store_true",
+                    help="decode workloads: plans with merge_in_launch = 1, which fold the split merge into the "
+                         "attention launch where they can (default: a merge launch of its own)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
@@ -619,7 +622,8 @@ def main():
         r = Runner(b, args.layers)
         r.kernel_events = r.kernel_events and not args.stream_events
         r.fused_append = r.fused_append and not args.separate_append
-        r.separate_merge = args.separate_merge
+        r.separate_merge = not args.merge_in_launch
+        r.params.merge_in_launch = int(args.merge_in_launch)
         m = measure(r, args.layers, args.steps, args.warmup, ev_every=args.event_every)
         m["append"] = measure_append(r, args.layers)
         nb = decode_bytes(b)
@@ -663,7 +667,8 @@ def main():
         b = host["skewed"]
         layers = args.secondary_layers
         r = Runner(b, layers, time_merge=True)
-        r.separate_merge = args.separate_merge
+        r.separate_merge = not args.merge_in_launch
+        r.params.merge_in_launch = int(args.merge_in_launch)
         m = measure(r, layers, args.steps, args.warmup)
         nb = decode_bytes(b)
         result["skewed"] = dict(m, gbs=nb["attn"] / (m["attn_ms_mean"] * 1e-3) / 1e9, bytes=nb)
@@ -688,7 +693,8 @@ def main():
         r = Runner(b, layers)
         r.kernel_events = r.kernel_events and not args.stream_events
         r.fused_append = r.fused_append and not args.separate_append
-        r.separate_merge = args.separate_merge
+        r.separate_merge = not args.merge_in_launch
+        r.params.merge_in_launch = int(args.merge_in_launch)
         m = measure(r, layers, args.steps, args.warmup, ev_every=args.event_every)
         nb = decode_bytes(b)
         fz = "_fused" if r.fused_append else ""

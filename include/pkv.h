@@ -233,6 +233,8 @@ typedef struct pkv_plan_params {
   int32_t tail_split;        /* 0: default (decode 2, prefill 1, MLA 1); 1: off */
   int32_t kv_format;         /* pkv_kv_format; ragged needs PKV_MODE_PREFILL */
   int32_t mask_mode;         /* pkv_mask_mode; custom needs PKV_MODE_PREFILL and causal == 0 */
+  int32_t merge_in_launch;   /* 1: fold the split merge into the attention launch where the plan
+                                allows it (see pkv_run); 0: a merge launch of its own */
 } pkv_plan_params;
 
 typedef struct pkv_plan_info {
@@ -287,8 +289,9 @@ pkv_status pkv_plan_compute(const pkv_plan_params* params, const int32_t* qo_ind
  * (host memory, owned by the library) stays valid only for this exact batch
  * ([DD] "Plan then run"; a plan reused after the page table changes gives
  * plausible output for the wrong sequence) and until pkv_plan_destroy.
- * The first split decode plan made on a device (here or by
- * pkv_graph_plan_create) also checks, once per device and process, which
+ * The first split decode plan made with merge_in_launch = 1 on a device
+ * (here or by pkv_graph_plan_create) also checks, once per device and
+ * process, which
  * XCD runs each workgroup: a 1024-workgroup probe launch on the null stream,
  * a 4 KiB device buffer and a synchronous copy back.  The answer decides
  * merge_in_launch (PKV_MERGE_IN_ATTENTION=0 in the environment: never).
@@ -390,10 +393,13 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
  *   sm_scale  logit scale; <= 0 selects 1/sqrt(head_dim_qk)
  * Enqueues one attention kernel and, if the plan split any tile, one merge
  * kernel on `stream`, unless the plan folds the split rows inside the
- * attention launch (pkv_plan_info.merge_in_launch): paged decode plans whose
- * kv heads are a multiple of 8, on a device that runs workgroups i and i + 8
- * on one XCD, where the last workgroup to finish a row's chunks merges them
- * ([DD] "A worked split-KV example").  No host synchronisation, no
+ * attention launch (pkv_plan_info.merge_in_launch): plans made with
+ * params.merge_in_launch = 1 in paged decode mode whose kv heads are a
+ * multiple of 8, on a device that runs workgroups i and i + 8 on one XCD,
+ * where the last workgroup to finish a row's chunks merges them ([DD] "A
+ * worked split-KV example"); plans from pkv_plan_create only when no row has
+ * more than 16 chunks (one workgroup merging many chunks at the end of the
+ * launch costs more than a merge launch).  No host synchronisation, no
  * allocation, no host copy.  Runs of one plan must not overlap in time: they
  * share its workspace (partial states and merge counters).
  */

@@ -38,7 +38,7 @@ class PlanParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "batch_size", "num_qo_heads", "num_kv_heads", "head_dim_qk", "head_dim_vo", "page_size", "causal",
         "q_dtype", "kv_dtype", "num_cus", "fixed_split_pages", "target_per_cu", "mla_head_groups",
-        "max_num_pages", "tail_split", "kv_format", "mask_mode")]
+        "max_num_pages", "tail_split", "kv_format", "mask_mode", "merge_in_launch")]
 
 
 class PlanInfo(ctypes.Structure):

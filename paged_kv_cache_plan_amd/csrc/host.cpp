@@ -268,6 +268,8 @@ pkv_status check_params(const pkv_plan_params* p) {
     return fail(PKV_ERR_INVALID_ARG, fmt("unknown kv_format %lld", p->kv_format));
   if (p->mask_mode != PKV_MASK_NONE && p->mask_mode != PKV_MASK_CUSTOM)
     return fail(PKV_ERR_INVALID_ARG, fmt("unknown mask_mode %lld", p->mask_mode));
+  if (p->merge_in_launch != 0 && p->merge_in_launch != 1)
+    return fail(PKV_ERR_INVALID_ARG, "merge_in_launch must be 0 or 1");
   if ((p->kv_format == PKV_KV_RAGGED || p->mask_mode == PKV_MASK_CUSTOM) && p->mode != PKV_MODE_PREFILL)
     return fail(PKV_ERR_UNSUPPORTED, "ragged KV and custom masks need prefill mode");
   if (p->mask_mode == PKV_MASK_CUSTOM && p->causal)
@@ -711,8 +713,10 @@ bool xcd_groups_ok(int device) {
 // head: workgroup item * Hkv + j serves head (j + b) mod Hkv of request b),
 // kv heads a multiple of 8 so that every chunk of one (request, kv head)
 // lands on the same XCD.
+constexpr int32_t kMergeInMaxChunks = 16;   // plans whose rows have more chunks merge in their own launch
+
 bool merge_in_launch_ok(const pkv_plan_params* p, int device) {
-  return has_merge_tables(p) && p->num_kv_heads % 8 == 0 && xcd_groups_ok(device);
+  return p->merge_in_launch == 1 && has_merge_tables(p) && p->num_kv_heads % 8 == 0 && xcd_groups_ok(device);
 }
 
 pkv_status check_runnable(const pkv_plan_params* p) {
@@ -872,7 +876,12 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
   if (!r.tile_merge.empty()) {
     plan->d_tile_merge = reinterpret_cast<int32_t*>(ws + tm_off);
     plan->d_merge_ctr = reinterpret_cast<int32_t*>(ws + ctr_off);
-    plan->merge_in = !r.merges.empty() && merge_in_launch_ok(params, plan->device);
+    // One workgroup merges a row's chunks at the end of the launch: with
+    // many chunks (one long request split many ways) that serial tail costs
+    // more than a merge launch of its own.
+    int32_t most = 0;
+    for (const MergeItem& mi : r.merges) most = std::max(most, mi.num_chunks);
+    plan->merge_in = !r.merges.empty() && most <= kMergeInMaxChunks && merge_in_launch_ok(params, plan->device);
   }
   plan->info.merge_in_launch = plan->merge_in ? 1 : 0;
   plan->h_staging = h_staging;
