@@ -264,7 +264,7 @@ __device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& m
 
 // T: query / output elements (bf16 bits or float).  TK: stored K/V elements
 // (T itself, or uint8_t E4M3 codes with T = bf16).
-template <typename T, typename TK, int D, int G, bool kAligned, bool kMask, bool kAppend>
+template <typename T, typename TK, int D, int G, bool kAligned, bool kMask, bool kAppend, bool kMergeIn>
 __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr bool kFp8 = sizeof(TK) == 1;
@@ -286,6 +286,10 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_acc[kWaves][G][D];
+  // Fused append: the first boundary block's K and V rows of each wave
+  // (bf16 and fp8 rows; float32 rows load their boundary block after the loop).
+  constexpr bool kPreBoundary = kBF16 && kDepth == 2;
+  __shared__ uint4 s_new[(kAppend && kPreBoundary) ? kWaves * NU * VCR * 128 : 1];
 
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   // merge item, read now so that the end of the workgroup waits on no load.
   int32_t merge_m = -1;
   MergeItem merge_item{0, 0, 0, 0};
-  if (a.merge_ctr && it.out_slot >= 0) {
+  if (kMergeIn && it.out_slot >= 0) {
     merge_m = a.tile_merge[it.batch];
     merge_item = a.merges[merge_m];
   }
@@ -528,11 +532,9 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       // the append).  The loop below covers the cached blocks [tlo, nb0).
       const int32_t thi_all = thi;
       int32_t nlo = thi, nb0 = thi, bb = thi, bb0 = thi;
-      // float32 rows keep no boundary block across the loop (its registers
-      // would spill): they load and compute it after the loop.
-      constexpr bool kPreBoundary = kBF16;
-      uint4 kbn[NU][VCR], vbn[NU][VCR];   // the wave's boundary block
-      auto load_mixed = [&](int32_t blk) __attribute__((always_inline)) {
+      // The boundary block blk (cached keys through the page ids, new keys
+      // from k_new / v_new) into the register set kx / vx.
+      auto load_mixed = [&](int32_t blk, uint4 (&kx)[NU][VCR], uint4 (&vx)[NU][VCR]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const int32_t key = min(blk + u * VT + vg, thi_all - 1);
@@ -545,8 +547,8 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           const TK* vp = (fresh ? vnew : vbase) + off;
 #pragma unroll
           for (int c = 0; c < VCR; ++c) {
-            kbn[u][c] = dev::load16<kStreamKV>(kp + (vi + VL * c) * RE);
-            vbn[u][c] = dev::load16<kStreamKV>(vp + (vi + VL * c) * RE);
+            kx[u][c] = dev::load16<kStreamKV>(kp + (vi + VL * c) * RE);
+            vx[u][c] = dev::load16<kStreamKV>(vp + (vi + VL * c) * RE);
           }
         }
       };
@@ -557,7 +559,6 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           const int32_t k0 = (nb0 - tlo) / kBlockKeys;
           bb = nb0 + ((wave - k0) % kWaves + kWaves) % kWaves * kBlockKeys;
           bb0 = bb;
-          if (kPreBoundary && bb < thi_all) load_mixed(bb);
           thi = nb0;
         }
       }
@@ -569,15 +570,11 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       // block's compute covers only that block's own loads.
       const int32_t blk_max = kAligned ? ((thi - 1) & ~(kBlockKeys - 1)) : thi - 1;
       int32_t blk = tlo + wave * kBlockKeys;
-      // The wave's boundary block bb: its new rows go into their cache slots
-      // (first row only), then the block is computed against the segment's
-      // full key range.  The first one runs while the loop's first loads are
-      // in flight (its own were issued before them).
-      // The new rows of boundary block blk (loaded into kbn / vbn) into their
-      // cache slots (first row only).  Issued after the wave's last load:
-      // a store counts like a load in the wave's memory counter, and one
-      // between the loop's loads would make every later wait cover it too.
-      auto store_new = [&](int32_t blk) __attribute__((always_inline)) {
+      // The new rows of boundary block blk (in kx / vx) into their cache
+      // slots, first row only.  Issued after the wave's last load: a store
+      // counts like a load in the wave's memory counter, and one between the
+      // loop's loads would make every later wait cover it too.
+      auto store_new = [&](int32_t blk, uint4 (&kx)[NU][VCR], uint4 (&vx)[NU][VCR]) __attribute__((always_inline)) {
         if (r != 0) return;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -590,31 +587,44 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
             TK* vd = const_cast<TK*>(vbase) + off;
 #pragma unroll
             for (int c = 0; c < VCR; ++c) {
-              *reinterpret_cast<uint4*>(kd + (vi + VL * c) * RE) = kbn[u][c];
-              *reinterpret_cast<uint4*>(vd + (vi + VL * c) * RE) = vbn[u][c];
+              *reinterpret_cast<uint4*>(kd + (vi + VL * c) * RE) = kx[u][c];
+              *reinterpret_cast<uint4*>(vd + (vi + VL * c) * RE) = vx[u][c];
             }
           }
         }
       };
       // Block bb against the segment's full key range.
-      auto boundary = [&]() __attribute__((always_inline)) {
+      auto boundary = [&](uint4 (&kx)[NU][VCR], uint4 (&vx)[NU][VCR]) __attribute__((always_inline)) {
         const int32_t thi_loop = thi;
         thi = thi_all;
-        compute(bb, kbn, vbn);
+        compute(bb, kx, vx);
         thi = thi_loop;
       };
-      bool first_done = false;   // the prefetched first boundary block is computed
+      // The first boundary block's rows wait in LDS (which takes no part in
+      // the memory counter) from its compute, ahead of the loop, to their
+      // stores after it.
+      auto stash = [&](uint4 (&kx)[NU][VCR], uint4 (&vx)[NU][VCR], bool put) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int c = 0; c < VCR; ++c) {
+            uint4* sk = &s_new[((wave * NU + u) * VCR + c) * 128 + lane];
+            if (put) {
+              sk[0] = kx[u][c];
+              sk[64] = vx[u][c];
+            } else {
+              kx[u][c] = sk[0];
+              vx[u][c] = sk[64];
+            }
+          }
+      };
+      bool first_done = false;   // the first boundary block is computed (rows in s_new)
+      uint4 ka[NU][VCR], kb[NU][VCR], va[NU][VCR], vb[NU][VCR];
       if constexpr (kDepth == 3) {
-        uint4 ka[NU][VCR], kb[NU][VCR], kc[NU][VCR], va[NU][VCR], vb[NU][VCR], vc[NU][VCR];
+        uint4 kc[NU][VCR], vc[NU][VCR];
         if (blk < thi) {
           load(blk, ka, va);
           load(min(blk + kStride, blk_max), kb, vb);
-          if constexpr (kAppend && kPreBoundary) {
-            if (bb < thi_all) {
-              boundary();
-              first_done = true;
-            }
-          }
           while (true) {
             load(min(blk + 2 * kStride, blk_max), kc, vc);
             compute(blk, ka, va);
@@ -631,12 +641,16 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
           }
         }
       } else {
-        uint4 ka[NU][VCR], kb[NU][VCR], va[NU][VCR], vb[NU][VCR];
+        // A wave that owns a boundary block loads it first, into kb (free
+        // until the loop's first prefetch), and computes it while the loop's
+        // first loads are in flight.
+        if (kAppend && kPreBoundary && bb < thi_all) load_mixed(bb, kb, vb);
         if (blk < thi) {
           load(blk, ka, va);
           if constexpr (kAppend && kPreBoundary) {
             if (bb < thi_all) {
-              boundary();
+              boundary(kb, vb);
+              stash(kb, vb, true);
               first_done = true;
             }
           }
@@ -653,13 +667,18 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         }
       }
       if constexpr (kAppend) {
-        // A wave without cached blocks takes its first boundary block here;
-        // appends that reach past one block per wave take the rest here.
+        if (first_done) {
+          stash(ka, va, false);
+          store_new(bb, ka, va);
+          bb += kStride;
+        }
+        // A wave without cached blocks takes its first boundary block here
+        // (already in kb when prefetched); appends that reach past one block
+        // per wave take the rest here.
         for (; bb < thi_all; bb += kStride) {
-          const bool pre = kPreBoundary && bb == bb0;   // already in kbn / vbn
-          if (!pre) load_mixed(bb);
-          if (!(pre && first_done)) boundary();
-          store_new(bb);
+          if (!(kPreBoundary && kDepth == 2 && bb == bb0)) load_mixed(bb, kb, vb);
+          boundary(kb, vb);
+          store_new(bb, kb, vb);
         }
       }
     }
@@ -730,7 +749,9 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         if (d == 0) a.part_lse[prow] = lse2;
       }
     }
-    if (merge_m >= 0) merge_in_launch<T, D, G>(a, merge_m, merge_item, row, kvh);
+    if constexpr (kMergeIn) {
+      if (merge_m >= 0) merge_in_launch<T, D, G>(a, merge_m, merge_item, row, kvh);
+    }
     __syncthreads();
   }
 }
@@ -741,22 +762,26 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const bool aligned = a.page_shift >= 4;   // a power-of-two page of at least 16 keys
   const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
-  if (a.mask && a.append_indptr) return hipErrorInvalidValue;   // no fused append over a custom mask
+  if (a.mask && (a.append_indptr || a.merge_ctr)) return hipErrorInvalidValue;   // masks run plain launches
+  // Each variant is its own kernel, so that the plain decode launch carries
+  // neither the append nor the in-launch merge code (their registers cost
+  // the plain kernel about 1 us on the decode batch).
+  auto go = [&](auto kernel) { launch_attention_kernel(kernel, grid, block, st, a); };
   if (a.mask) {
-    if (aligned)
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, true, false>, grid, block, st, a);
-    else
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, true, false>, grid, block, st, a);
+    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, true, false, false>);
+    else go(attn_rows_kernel<T, TK, D, G, false, true, false, false>);
+  } else if (a.append_indptr && a.merge_ctr) {
+    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, true, true>);
+    else go(attn_rows_kernel<T, TK, D, G, false, false, true, true>);
   } else if (a.append_indptr) {
-    if (aligned)
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false, true>, grid, block, st, a);
-    else
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false, true>, grid, block, st, a);
+    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, true, false>);
+    else go(attn_rows_kernel<T, TK, D, G, false, false, true, false>);
+  } else if (a.merge_ctr) {
+    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, false, true>);
+    else go(attn_rows_kernel<T, TK, D, G, false, false, false, true>);
   } else {
-    if (aligned)
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, true, false, false>, grid, block, st, a);
-    else
-      launch_attention_kernel(attn_rows_kernel<T, TK, D, G, false, false, false>, grid, block, st, a);
+    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, false, false>);
+    else go(attn_rows_kernel<T, TK, D, G, false, false, false, false>);
   }
   return hipGetLastError();
 }
