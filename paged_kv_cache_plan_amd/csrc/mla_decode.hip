@@ -88,6 +88,7 @@ constexpr int kMaxChunkPages = 1024;
 constexpr int kAheadK = 2;                         // K operand reads issued this many k-steps ahead
 constexpr int kAheadV = 2;                         // V operand reads issued this many steps ahead
 constexpr float kMaxGap = 32.f;                 // weights stay below 2^kMaxGap
+static_assert(4 * kRowsPerWave + 1 < kSteps, "a tile's loads are spread one per four score k-steps");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 // MFMAs from inline assembly, so that O stays in the acc registers it fills
@@ -227,14 +228,67 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
   const uint32_t max_pages = uint32_t(a.max_num_pages);
   const int64_t page_bytes = a.page_stride * 2, tok_bytes = a.token_stride * 2;
 
-  // The chunk's page ids are staged in LDS; their loads go out first, then
-  // those of Q, whose latency then overlaps the staging and the first tile
-  // loads (loads complete in order, so the first tile barrier also covers Q).
   const int32_t kv_lo = it.kv_start, kv_hi = it.kv_end;
   const int32_t ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kKeys - 1) / kKeys : 0;
   const int32_t pg_lo = kv_hi > kv_lo ? (kPow2 ? kv_lo >> pshift : kv_lo / psz) : 0;
   const int32_t pg_n =
       kv_hi > kv_lo ? min(kMaxChunkPages, (kPow2 ? (kv_hi - 1) >> pshift : (kv_hi - 1) / psz) - pg_lo + 1) : 0;
+
+  // Tile loads: wave w fills rows [8w, 8w + 8) of a slot.  Row r's stored
+  // chunk p holds source chunk p ^ s(r) (s(r) < 8: within its group of 8).
+  // Lane l of a ckv row load writes stored chunk l; lane l of the kpe load
+  // writes stored chunk l & 7 of row 8w + l / 8.  Keys past the chunk end
+  // re-read the last key (their scores are masked to -inf).
+  const uint32_t tokb = uint32_t(tok_bytes);   // the host keeps 8 rows of offsets below 2^31
+  const uint32_t lane16 = uint32_t(lane * 16);
+  const uint32_t kchunk = uint32_t(((lane & 7) ^ (swz(8 * wave + (lane >> 3)) & 7)) * 16);
+  const uint32_t kvoff = uint32_t(lane >> 3) * tokb + kchunk;
+  const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>(s_ring));
+  const int32_t r_w = kRowsPerWave * wave;
+  auto page_of_key = [&](int32_t j) {   // page id of key j of the chunk (from the staged list)
+    const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
+    return s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
+  };
+  auto slot_of_key = [&](int32_t j) { return kPow2 ? (j & (psz - 1)) : (j - (j / psz) * psz); };
+  // The page of the wave's first row of tile t (read ahead of load_tile, so
+  // that the LDS latency of the lookup is hidden).
+  auto first_page = [&](int32_t t) { return page_of_key(min(kv_lo + t * kKeys + r_w, kv_hi - 1)); };
+  // The wave's 8 rows of tile t lie on one page (pages of 8+ keys; chunks
+  // start on page boundaries and the 8 rows on an 8-key boundary within
+  // them): one scalar base (tile_base) and fixed per-lane offsets (cvoff).
+  auto one_page = [&](int32_t t) { return kPow2 && pshift >= 3 && kv_lo + t * kKeys + r_w + kRowsPerWave <= kv_hi; };
+  auto tile_base = [&](int32_t t, int32_t page0) {
+    return int64_t(__builtin_amdgcn_readfirstlane(page0)) * page_bytes +
+           int64_t((kv_lo + t * kKeys + r_w) & (psz - 1)) * tok_bytes;
+  };
+  uint32_t cvoff[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) cvoff[j] = (lane16 ^ uint32_t(16 * swz(r_w + j))) + uint32_t(j) * tokb;
+  auto lds_ckv_of = [&](int32_t t) { return ring_lds + uint32_t((t & (kRing - 1)) * kSlot + r_w * kCkvRow); };
+  auto lds_kpe_of = [&](int32_t t) { return ring_lds + uint32_t((t & (kRing - 1)) * kSlot + kKpeOff + r_w * kKpeRow); };
+  auto load_tile = [&](int32_t t, int32_t page0) {
+    const uint32_t lds_ckv = lds_ckv_of(t), lds_kpe = lds_kpe_of(t);
+    const int32_t j0 = kv_lo + t * kKeys + r_w;
+    if (one_page(t)) {
+      const int64_t off = tile_base(t, page0);
+      dma_rows(ckv + off, cvoff, kpe + off, kvoff, lds_ckv, lds_kpe);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) {
+        const int32_t jk = min(j0 + j, kv_hi - 1);
+        const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(page_of_key(jk))) * page_bytes +
+                            int64_t(slot_of_key(jk)) * tok_bytes;
+        dma_row(ckv + off, lane16 ^ uint32_t(16 * swz(r_w + j)), lds_ckv + uint32_t(j * kCkvRow));
+      }
+      const int32_t jk = min(j0 + (lane >> 3), kv_hi - 1);
+      dma_lane(kpe + int64_t(page_of_key(jk)) * page_bytes + int64_t(slot_of_key(jk)) * tok_bytes + kchunk,
+               lds_kpe);
+    }
+  };
+
+  // The chunk's page ids are staged in LDS; their loads go out first, then
+  // those of Q, whose latency then overlaps the staging and the first tile
+  // loads (loads complete in order, so the first tile barrier also covers Q).
   int32_t pg_first = 0;
   if (tid < pg_n) pg_first = pages[pg_lo + tid];
   asm volatile("" ::: "memory");
@@ -263,53 +317,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
   if (tid == 0) s_restart = 0;
   __syncthreads();
 
-  // Tile loads: wave w fills rows [8w, 8w + 8) of a slot.  Row r's stored
-  // chunk p holds source chunk p ^ s(r) (s(r) < 8: within its group of 8).
-  // Lane l of a ckv row load writes stored chunk l; lane l of the kpe load
-  // writes stored chunk l & 7 of row 8w + l / 8.  Keys past the chunk end
-  // re-read the last key (their scores are masked to -inf).
-  const uint32_t tokb = uint32_t(tok_bytes);   // the host keeps 8 rows of offsets below 2^31
-  const uint32_t lane16 = uint32_t(lane * 16);
-  const uint32_t kchunk = uint32_t(((lane & 7) ^ (swz(8 * wave + (lane >> 3)) & 7)) * 16);
-  const uint32_t kvoff = uint32_t(lane >> 3) * tokb + kchunk;
-  const uint32_t ring_lds = uint32_t(reinterpret_cast<uintptr_t>(s_ring));
-  const int32_t r_w = kRowsPerWave * wave;
-  auto page_of_key = [&](int32_t j) {   // page id of key j of the chunk (from the staged list)
-    const int32_t pi = kPow2 ? (j >> pshift) : (j / psz);
-    return s_pages[min(pi - pg_lo, kMaxChunkPages - 1)];
-  };
-  auto slot_of_key = [&](int32_t j) { return kPow2 ? (j & (psz - 1)) : (j - (j / psz) * psz); };
-  // The page of the wave's first row of tile t (read ahead of load_tile, so
-  // that the LDS latency of the lookup is hidden).
-  auto first_page = [&](int32_t t) { return page_of_key(min(kv_lo + t * kKeys + r_w, kv_hi - 1)); };
-  auto load_tile = [&](int32_t t, int32_t page0) {
-    const int32_t t0 = kv_lo + t * kKeys;
-    const uint32_t slot = ring_lds + uint32_t((t & (kRing - 1)) * kSlot);
-    const uint32_t lds_ckv = slot + uint32_t(r_w * kCkvRow), lds_kpe = slot + uint32_t(kKpeOff + r_w * kKpeRow);
-    const int32_t j0 = t0 + r_w;
-    if (kPow2 && pshift >= 3 && j0 + kRowsPerWave <= kv_hi) {
-      // The 8 rows lie on one page (pages of 8+ keys; chunks start on page
-      // boundaries and the 8 rows on an 8-key boundary within them).
-      const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(page0)) * page_bytes +
-                          int64_t(j0 & (psz - 1)) * tok_bytes;
-      uint32_t cvoff[kRowsPerWave];
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j)
-        cvoff[j] = (lane16 ^ uint32_t(16 * swz(r_w + j))) + uint32_t(j) * tokb;
-      dma_rows(ckv + off, cvoff, kpe + off, kvoff, lds_ckv, lds_kpe);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j) {
-        const int32_t jk = min(j0 + j, kv_hi - 1);
-        const int64_t off = int64_t(__builtin_amdgcn_readfirstlane(page_of_key(jk))) * page_bytes +
-                            int64_t(slot_of_key(jk)) * tok_bytes;
-        dma_row(ckv + off, lane16 ^ uint32_t(16 * swz(r_w + j)), lds_ckv + uint32_t(j * kCkvRow));
-      }
-      const int32_t jk = min(j0 + (lane >> 3), kv_hi - 1);
-      dma_lane(kpe + int64_t(page_of_key(jk)) * page_bytes + int64_t(slot_of_key(jk)) * tok_bytes + kchunk,
-               lds_kpe);
-    }
-  };
 
   // K operand reads: lane (n, hk) reads row n, source chunk 2s + hk, stored
   // at (2s + hk) ^ g(n) = 16 (s / 8) + ((2 (s % 8) + hk) ^ g(n)).  Relative
@@ -441,8 +448,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
       const bool more = t + 1 < ntiles;
       if (t + 2 < ntiles) tile_barrier<kLoadsPerTile>();
       else tile_barrier<0>();
+      // Tile t+3's loads.  When the wave's rows lie on one page they are
+      // spread over the score k-steps below, one load per four MFMAs: issued
+      // back to back, each load waits for the CU's memory pipeline to take
+      // the one before (a tile is 36 KiB per CU), and the wave stalls.
       const bool load_next = t + 3 < ntiles;
-      if (load_next) load_tile(t + 3, page_next);
+      const bool spread = load_next && more && one_page(t + 3);
+      if (load_next && !spread) load_tile(t + 3, page_next);
+      const int64_t off_next = spread ? tile_base(t + 3, page_next) : 0;
+      const uint32_t ckv_next = lds_ckv_of(t + 3), kpe_next = lds_kpe_of(t + 3);
       page_next = first_page(t + 4);
       // Weights of tile t, one per k-step 0-15 (exp2(-inf) = 0 covers masked
       // keys), summed and packed in pairs two k-steps later (so that no
@@ -470,8 +484,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_kernel(const MlaArgs a
           }
         }
       };
+      auto weights_loads = [&](int s) {
+        weights(s);
+        if (spread && (s & 3) == 1) {
+          const int j = s >> 2;
+          if (j < kRowsPerWave) dma_row(ckv + off_next, cvoff[j], ckv_next + uint32_t(j * kCkvRow));
+          else dma_row(kpe + off_next, kvoff, kpe_next);
+        }
+      };
       if (more) {
-        scores(slot_of(t + 1), sc_nxt, weights);
+        scores(slot_of(t + 1), sc_nxt, weights_loads);
         mask_tile(sc_nxt, kv_lo + (t + 1) * kKeys);
       } else {
 #pragma unroll
