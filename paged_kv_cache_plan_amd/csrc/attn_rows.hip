@@ -232,25 +232,39 @@ __device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& m
         store_out<T>(orow + 2 * lane + 1, acc1);
       }
     } else {
+      // Many chunks: the partial rows come in groups of kFold, the loads of
+      // the next group issued before the current one is folded, so that the
+      // row waits for about n / kFold L2 round trips (it waited for n / 4).
+      // The fold keeps the chunk order.
+      constexpr int kFold = 16;
       for (int32_t d0 = 0; d0 < D; d0 += 128) {
         const int32_t d = d0 + 2 * lane;
         const float* src = pbase + min(d, D - 2);
         float acc0 = 0.f, acc1 = 0.f;
-        for (int32_t c = 0; c < n; c += 4) {
-          float2 x[4];
-          float w[4];
+        float2 x[kFold], y[kFold];
+        auto fetch = [&](float2 (&dst)[kFold], int32_t c0) {   // chunks past the last re-read it
+          const float* pj = src + int64_t(c0) * cstride;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int32_t cc = min(c + j, n - 1);
-            w[j] = weight(cc);
-            if (c + j >= n) w[j] = 0.f;
-            x[j] = *reinterpret_cast<const float2*>(src + int64_t(cc) * cstride);
+          for (int j = 0; j < kFold; ++j) {
+            dst[j] = *reinterpret_cast<const float2*>(pj);
+            pj += c0 + j + 1 < n ? cstride : 0;
           }
+        };
+        auto fold = [&](const float2 (&xs)[kFold], int32_t c0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc0 = fmaf(w[j], x[j].x, acc0);
-            acc1 = fmaf(w[j], x[j].y, acc1);
+          for (int j = 0; j < kFold; ++j) {
+            const float w = c0 + j < n ? weight(c0 + j) : 0.f;
+            acc0 = fmaf(w, xs[j].x, acc0);
+            acc1 = fmaf(w, xs[j].y, acc1);
           }
+        };
+        fetch(x, 0);
+        for (int32_t c0 = 0; c0 < n; c0 += 2 * kFold) {
+          if (c0 + kFold < n) fetch(y, c0 + kFold);
+          fold(x, c0);
+          if (c0 + kFold >= n) break;
+          if (c0 + 2 * kFold < n) fetch(x, c0 + 2 * kFold);
+          fold(y, c0 + kFold);
         }
         if (d < D) {
           store_out<T>(orow + d, acc0);
