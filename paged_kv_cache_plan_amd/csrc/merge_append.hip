@@ -597,11 +597,14 @@ hipError_t launch_append(int32_t dtype, const void* k_new, const void* v_new, in
   const int64_t es = dtype == kF32 ? 4 : (dtype == kFP8 ? 1 : 2);
   const int32_t row_chunks = int32_t(head_dim * es / 16);
   const int64_t token_chunks = 2 * int64_t(num_heads) * row_chunks;   // K and V rows of one token
-  // Tokens per block: as many as the per-thread chunk registers hold, but
-  // keep at least ~4 blocks per CU-sized group of 256 tokens so that small
-  // batches (decode: one token per request) still spread over the GPU.
+  // Tokens per block: one.  Blocks of several tokens (up to what the
+  // per-thread chunk registers hold) read all their rows before they write
+  // any, and with every block resident at once the copy's reads and writes
+  // then hardly overlap: on the prefill batch (9680 new tokens, 8 kv heads,
+  // head_dim 128) one token per block took 23.2 us, two 24.6, four 27.2 and
+  // eight 26.5.  The kernel keeps the general form (tpb tokens per block).
   const int64_t cap = std::max<int64_t>(1, int64_t(kAppendThreads) * kAppendMaxChunks / token_chunks);
-  int64_t tpb = std::min<int64_t>({cap, int64_t(kAppendMaxTok), std::max<int64_t>(1, nnz / 1024)});
+  const int64_t tpb = std::min<int64_t>({cap, int64_t(kAppendMaxTok), int64_t(1)});
   const int64_t blocks = (nnz + tpb - 1) / tpb;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(append_kernel, dim3(uint32_t(blocks)), dim3(kAppendThreads), 0, st,
