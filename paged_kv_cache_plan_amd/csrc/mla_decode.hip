@@ -146,6 +146,8 @@ __device__ __forceinline__ float sum_halves(float x) {
 // M0 must hold a wave-uniform LDS address, and a write of M0 needs one wait
 // state before a load that reads it (the s_nop).  Inline assembly: the kernel
 // waits for these loads itself (vmcnt before each tile barrier and the exit).
+// Every latent row is read once per launch, so the loads are non-temporal
+// (nt): the MLA batch ran about 4 % faster than with cached loads.
 //
 // The wave's 8 ckv rows of a tile from one scalar base (row j at
 // base + voff[j], stored 1 KiB apart from lds_ckv on), then the kpe parts of
@@ -155,35 +157,35 @@ __device__ __forceinline__ void dma_rows(const void* base, const uint32_t (&voff
                                          uint32_t lds_kpe) {
   asm volatile(
       "s_mov_b32 m0, %10\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %8\n\t"
+      "global_load_lds_dwordx4 %0, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %8\n\t"
+      "global_load_lds_dwordx4 %1, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %8\n\t"
+      "global_load_lds_dwordx4 %2, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %8\n\t"
+      "global_load_lds_dwordx4 %3, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %8\n\t"
+      "global_load_lds_dwordx4 %4, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %5, %8\n\t"
+      "global_load_lds_dwordx4 %5, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %6, %8\n\t"
+      "global_load_lds_dwordx4 %6, %8 nt\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %7, %8\n\t"
+      "global_load_lds_dwordx4 %7, %8 nt\n\t"
       "s_mov_b32 m0, %11\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %9, %12" ::"v"(voff[0]),
+      "global_load_lds_dwordx4 %9, %12 nt" ::"v"(voff[0]),
       "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]), "v"(voff[7]), "s"(base),
       "v"(voff_kpe), "s"(lds_ckv), "s"(lds_kpe), "s"(base_kpe)
       : "m0", "scc");
 }
 // One ckv row from a scalar base (rows on different pages).
 __device__ __forceinline__ void dma_row(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds)
                : "m0");
 }
 // 16 bytes from a per-lane address.
 __device__ __forceinline__ void dma_lane(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds) : "m0");
 }
 // At most N of this wave's tile loads still in flight and its LDS reads
 // returned, then the workgroup barrier.  The memory clobber keeps LDS
