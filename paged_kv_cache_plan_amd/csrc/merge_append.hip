@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const char* k_ne
       int32_t j, which;
       int64_t is, id;
       locate(i, j, which, is, id);
-      data[x] = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);
+      data[x] = dev::load16<true>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);   // read once: nt
     }
   }
   if (tid < kAppendMaxTok) s_dst[tid] = -1;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(const char* k_ne
     const int64_t dst = s_dst[j];
     if (dst >= 0)
       *reinterpret_cast<uint4*>((which ? v : k) + dst + id) =
-          *reinterpret_cast<const uint4*>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);
+          dev::load16<true>((which ? v_new : k_new) + int64_t(t0 + j) * new_st_b + is);
   }
 }
 
