@@ -37,6 +37,7 @@ MIN_SPLIT_TOKENS = 256          # a chunk holds at least this many tokens
 MAX_CHUNK_PAGES = 1024          # and at most this many pages (a kernel stages a chunk's page ids on chip)
 DEFAULT_TARGET_PER_CU = {DECODE: 3, PREFILL: 4, MLA: 1}
 DEFAULT_TAIL_SPLIT = {DECODE: 2, PREFILL: 1, MLA: 1}
+TAIL_SPLIT_MAX_PER_CU = 5       # the default tail split applies up to this many (item, head) units per CU
 CASCADE_TARGET_PER_CU = 1       # cascade levels run one launch each: one item per CU by default
 MFMA_TILE_ROWS = 256            # prefill tile height counted in (row, head) pairs
 MFMA_HEAD_DIM = 128             # the head dim whose prefill runs 256-pair tiles
@@ -84,11 +85,14 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
        diag = K_b - q_b + l0 (non-causal: diag = K_b); a chunk whose first key
        exceeds diag + rows - 1 is dropped, and kv_end is clipped to
        diag + rows.
-    5b. Tail split S (default 2 for decode, else 1 = off): if S > 1, the
-       tile's last kept chunk, when it spans more than one page, is replaced
-       by pieces of ceil(pages / S) pages from its first key on (the last
-       piece ends where the chunk ended).  The longest-first order of step 7
-       then finishes on small items.
+    5b. Tail split S: if S > 1, the tile's last kept chunk, when it spans
+       more than one page, is replaced by pieces of ceil(pages / S) pages
+       from its first key on (the last piece ends where the chunk ended).
+       The longest-first order of step 7 then finishes on small items.  An
+       explicit tail_split is used as given.  The default is 1 (off) except
+       for decode, where it is 2 when the kept chunks of step 5 times heads_y
+       number at most TAIL_SPLIT_MAX_PER_CU * num_cus; past that the batch
+       already ends on small items, and the extra items and merges only cost.
     6. A tile with one kept chunk writes directly (unless ``all_partial``,
        used by cascades, where every tile's rows must be merged later);
        otherwise its chunks get consecutive partial rows and one merge item.
@@ -104,8 +108,6 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
         causal = True        # a single decode row sees every key; diag = K - 1
     if target_per_cu <= 0:
         target_per_cu = DEFAULT_TARGET_PER_CU[mode]
-    if tail_split <= 0:
-        tail_split = DEFAULT_TAIL_SPLIT[mode]
     n_pages = [kv_indptr[b + 1] - kv_indptr[b] for b in range(batch)]
     k_lens = [page_size * (n_pages[b] - 1) + kv_last_page_len[b] for b in range(batch)]
     q_lens = [qo_indptr[b + 1] - qo_indptr[b] for b in range(batch)]
@@ -134,6 +136,24 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
             chunk = MAX_CHUNK_PAGES
     chunk_tokens = chunk * page_size
 
+    def kept_chunks(b, t):
+        """Steps 4-5: the (kv_start, kv_end) chunks that tile t of request b sees."""
+        diag = (k_lens[b] - q_lens[b] + t * rows) if causal else k_lens[b]
+        limit = min(k_lens[b], diag + min(rows, q_lens[b] - t * rows))   # keys < limit are seen by some row
+        kept = []
+        for c in range(_cdiv(n_pages[b], chunk)):
+            lo = c * chunk_tokens
+            if lo >= limit:
+                continue
+            kept.append((lo, min(lo + chunk_tokens, k_lens[b], limit)))
+        return kept
+
+    if tail_split <= 0:
+        tail_split = DEFAULT_TAIL_SPLIT[mode]
+        units = heads_y * sum(len(kept_chunks(b, t)) for b in range(batch) for t in range(tiles[b]))
+        if units > TAIL_SPLIT_MAX_PER_CU * num_cus:
+            tail_split = 1
+
     raw = []          # (key count, b, t, c_kept, fields) before slot assignment
     merges = []
     slot = 0
@@ -144,14 +164,7 @@ def plan(*, mode: str, qo_indptr, kv_indptr, kv_last_page_len, page_size: int, h
             l0 = t * rows
             n_rows = min(rows, q_lens[b] - l0)
             diag = (k_len - q_lens[b] + l0) if causal else k_len
-            limit = min(k_len, diag + n_rows)          # keys < limit are seen by some row
-            kept = []
-            for c in range(_cdiv(n_pages[b], chunk)):
-                lo = c * chunk_tokens
-                hi = min(lo + chunk_tokens, k_len)
-                if lo >= limit:
-                    continue
-                kept.append((lo, min(hi, limit)))
+            kept = kept_chunks(b, t)
             if tail_split > 1 and kept:
                 lo, hi = kept[-1]
                 pages = _cdiv(hi - lo, page_size)

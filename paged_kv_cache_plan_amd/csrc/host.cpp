@@ -160,6 +160,11 @@ int32_t default_target(int32_t mode) {
   return mode == PKV_MODE_MLA_DECODE ? 1 : (mode == PKV_MODE_DECODE ? 3 : 4);
 }
 int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 1; }
+// The default tail split applies only while the kept chunks times the head
+// slices number at most this many per CU: beyond that the longest-first order
+// already ends on small items, and the extra items and merge rows only cost
+// (2048 decode requests of 1-96 keys: 188 us unsplit against 349 us split).
+constexpr int64_t kTailSplitMaxPerCu = 5;
 // MLA head groups: the kernel runs groups of 128 heads (one wave per 32
 // heads) or of 64 heads (two waves per 32 heads).  By default the heads form
 // groups of 128 when their count allows it, else groups of 64.
@@ -336,7 +341,7 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
     if (!mla_groups_ok(prm, heads_y)) return fail(PKV_ERR_UNSUPPORTED, "MLA decode runs head groups of 64 or 128 heads");
   }
   const int32_t target_per_cu = prm->target_per_cu > 0 ? prm->target_per_cu : default_target(prm->mode);
-  const int32_t tail_split = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);
+  int32_t tail_split = prm->tail_split > 0 ? prm->tail_split : default_tail_split(prm->mode);
   const bool causal = prefill ? prm->causal != 0 : true;
 
   // Step 1-3: tiles, page work, chunk size.
@@ -377,6 +382,20 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
     }
   }
   const int64_t chunk_tokens = chunk * page_size;
+  // Keys of tile t of request b that some row of the tile sees: [0, limit).
+  auto tile_limit = [&](int32_t b, int64_t t) {
+    const int64_t k = kv_len[b];
+    const int64_t l0 = t * rows;
+    const int64_t diag = causal ? k - q_len[b] + l0 : k;
+    return std::min<int64_t>(k, diag + std::min<int64_t>(rows, q_len[b] - l0));
+  };
+  if (prm->tail_split <= 0 && tail_split > 1) {
+    int64_t units = 0;   // kept chunks of every tile (step 5) before any tail split
+    for (int32_t b = 0; b < batch; ++b)
+      for (int64_t t = 0; t < tiles[b]; ++t)
+        units += std::min(cdiv(n_pages[b], chunk), std::max<int64_t>(0, cdiv(tile_limit(b, t), chunk_tokens)));
+    if (units * heads_y > kTailSplitMaxPerCu * num_cus) tail_split = 1;
+  }
 
   // Step 4-6: chunks per tile, causal pruning, partial-row assignment.
   struct Raw {

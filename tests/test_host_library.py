@@ -125,6 +125,7 @@ def _compare_plans(mode, qo_indptr, kv_indptr, kv_indices, last, page_size, hq, 
 @pytest.mark.parametrize("name,kw", [
     ("worked", dict(literal_pages=True)),
     ("decode", {}),
+    ("decode", dict(batch=2048, kv_range=(1, 96), seed=4104)),   # past the default tail split's reach
     ("skewed", {}),
     ("prefill", {}),
     ("mla", {}),

@@ -49,6 +49,30 @@ def test_hand_worked_tail_split():
     assert [(i[2], i[3]) for i in p["items"]] == [(0, 256), (256, 261)]
 
 
+def test_default_tail_split_needs_few_units_per_cu():
+    """The default decode tail split applies while the kept chunks times
+    heads_y are at most 5 per CU.  The two requests above keep 3 + 1 = 4
+    chunks: with one head slice on one CU (4 <= 5) the default is the split
+    plan above; with two head slices (8 > 5) it is off, so request 0 keeps its
+    three chunks [0,256), [256,512), [512,600) (slots 0..2) and request 1 its
+    one [0,100), written directly; on two CUs (8 <= 10) it is on again.  An
+    explicit tail_split is used as given, and prefill never splits by
+    default."""
+    kw = dict(mode="decode", qo_indptr=None, kv_indptr=[0, 38, 45], kv_last_page_len=[8, 4], page_size=16,
+              rows=1, causal=True, fixed_split_pages=16)
+    split = pl.plan(heads_y=1, num_cus=1, tail_split=2, **kw)
+    assert pl.plan(heads_y=1, num_cus=1, **kw) == split
+    off = pl.plan(heads_y=2, num_cus=1, **kw)
+    assert off["merges"] == [[0, 1, 0, 3]] and off["num_partial_rows"] == 3
+    assert off["items"] == [[0, 1, 0, 256, 599, 0, 0, 0], [0, 1, 256, 512, 599, 0, 1, 0],
+                            [1, 1, 0, 100, 99, 38, -1, 1], [0, 1, 512, 600, 599, 0, 2, 0]]
+    assert pl.plan(heads_y=2, num_cus=1, tail_split=2, **kw)["items"] == split["items"]
+    assert pl.plan(heads_y=2, num_cus=2, **kw)["items"] == split["items"]
+    assert pl.plan(heads_y=2, num_cus=1, tail_split=1, **kw) == off
+    pre = dict(kw, mode="prefill", qo_indptr=[0, 1, 2])
+    assert pl.plan(heads_y=1, num_cus=1, **pre) == pl.plan(heads_y=1, num_cus=1, tail_split=1, **pre)
+
+
 def test_order_follows_key_count_not_rows():
     """One prefill request, 6 new rows after a 26-token prefix (K = 32), page
     4, tiles of 4 rows, one chunk.  Tile 0 (4 rows) sees keys < 30, tile 1
