@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0                  # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6              # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
 METRIC = "paged decode KV-read GB/s + prefill TFLOP/s, each as fraction of MI355X peak"
-KERNEL_SOURCES = ["attn_rows.hip", "prefill_mfma.hip", "mla_decode.hip", "merge_append.hip", "device.h"]
+KERNEL_SOURCES = ["attn_rows.hip", "attn_rows_one_wave.hip", "prefill_mfma.hip", "mla_decode.hip", "merge_append.hip",
+                  "device.h"]
 
 
 def log(*a):

@@ -235,6 +235,12 @@ typedef struct pkv_plan_params {
   int32_t mask_mode;         /* pkv_mask_mode; custom needs PKV_MODE_PREFILL and causal == 0 */
   int32_t merge_in_launch;   /* 1: fold the split merge into the attention launch where the plan
                                 allows it (see pkv_run); 0: a merge launch of its own */
+  int32_t row_waves;         /* decode only: waves per workgroup of the row kernel, 4 or 1; 0: the
+                                plan picks 1 when its work items average at most 384 keys and,
+                                times the kv heads, number at least 24 per CU (many short
+                                requests: one-wave workgroups put four times as many items on a
+                                CU), else 4.  One-wave plans fold no merge into the launch;
+                                fixed-capacity plans run 4. */
 } pkv_plan_params;
 
 typedef struct pkv_plan_info {
@@ -256,7 +262,8 @@ typedef struct pkv_plan_info {
   int64_t mask_bits;         /* custom mask: sum over requests of qo_len * kv_len */
   int32_t merge_in_launch;   /* 1: pkv_run / pkv_run_append fold split rows inside the
                                 attention launch (set by plan creation, see pkv_run) */
-  int32_t reserved;
+  int32_t row_waves;         /* waves per workgroup of the row kernel (4, or 1: see row_waves in
+                                pkv_plan_params); the MFMA and MLA kernels ignore it */
 } pkv_plan_info;
 
 /* Work item / merge item sizes in int32 words (layout documented in the

@@ -187,7 +187,7 @@ _DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, head_dim_vo=None, page_size,
                 causal=True, dtype="bf16", num_cus=0, fixed_split_pages=0, target_per_cu=0,
                 mla_head_groups=0, max_num_pages=0, tail_split=0, ragged=False, custom_mask=False,
-                kv_dtype=None, merge_in_launch=False) -> PlanParams:
+                kv_dtype=None, merge_in_launch=False, row_waves=0) -> PlanParams:
     p = PlanParams()
     p.mode = _MODES[mode] if isinstance(mode, str) else mode
     p.batch_size = batch_size
@@ -205,6 +205,7 @@ def plan_params(*, mode, batch_size, num_qo_heads, num_kv_heads, head_dim_qk, he
     p.kv_format = KV_RAGGED if ragged else KV_PAGED
     p.mask_mode = MASK_CUSTOM if custom_mask else MASK_NONE
     p.merge_in_launch = int(merge_in_launch)
+    p.row_waves = row_waves
     return p
 
 

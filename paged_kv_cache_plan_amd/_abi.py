@@ -38,7 +38,7 @@ class PlanParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "batch_size", "num_qo_heads", "num_kv_heads", "head_dim_qk", "head_dim_vo", "page_size", "causal",
         "q_dtype", "kv_dtype", "num_cus", "fixed_split_pages", "target_per_cu", "mla_head_groups",
-        "max_num_pages", "tail_split", "kv_format", "mask_mode", "merge_in_launch")]
+        "max_num_pages", "tail_split", "kv_format", "mask_mode", "merge_in_launch", "row_waves")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -46,10 +46,10 @@ class PlanInfo(ctypes.Structure):
         "mode", "batch_size", "num_items", "num_merges", "num_partial_rows", "chunk_pages", "split",
         "rows_per_tile", "heads_y", "num_cus", "target", "total_rows")] + [
         ("workspace_bytes", ctypes.c_int64), ("staging_bytes", ctypes.c_int64), ("fingerprint", ctypes.c_uint64),
-        ("mask_bits", ctypes.c_int64), ("merge_in_launch", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        ("mask_bits", ctypes.c_int64), ("merge_in_launch", ctypes.c_int32), ("row_waves", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class GraphCaps(ctypes.Structure):

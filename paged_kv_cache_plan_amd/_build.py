@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
-SOURCES = ["host.cpp", "attn_rows.hip", "prefill_mfma.hip", "mla_decode.hip", "merge_append.hip"]
+SOURCES = ["host.cpp", "attn_rows.hip", "attn_rows_one_wave.hip", "prefill_mfma.hip", "mla_decode.hip",
+           "merge_append.hip"]
 
 # Packed fp32 VALU ops stay off: the compiler would otherwise form
 # v_pk_{add,mul,fma}_f32 from ordinary float code.

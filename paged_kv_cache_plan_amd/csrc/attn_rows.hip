@@ -29,6 +29,15 @@
 // final output (dtype of Q, plus base-2 LSE) or as an fp32 partial state for
 // the split merge ("Deep Dive - FlashInfer", "A worked split-KV example").
 //
+// One-wave workgroups: this file compiled with PKV_ROWS_WAVES = 1 (the
+// translation unit attn_rows_one_wave.hip) gives the same kernel with one wave
+// per workgroup, which takes every 16-key block of its item itself.  Batches
+// of many short items (a few blocks each) leave most waves of a 4-wave
+// workgroup idle and pay one workgroup start per (item, kv head); one-wave
+// workgroups put up to four times as many items on a CU at once.  Plans pick
+// it for decode batches of many short items (the rule and its measurements
+// are in the host planner).
+//
 // Loads are branch-free: a key past the end of the row's range re-reads the
 // last valid key (its weight is zero), and a page id outside the pool is
 // replaced by page 0 so no access leaves the cache allocation (the host
@@ -49,8 +58,12 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup of this translation unit's kernels: 4, or 1 (see above).
+#ifndef PKV_ROWS_WAVES
+#define PKV_ROWS_WAVES 4
+#endif
+constexpr int kWaves = PKV_ROWS_WAVES;
+static_assert(kWaves == 4 || kWaves == 1, "row kernel workgroups of 4 or 1 waves");
 constexpr int kBlockKeys = 16;
 constexpr int kSegPages = 1024;   // page ids staged in LDS per segment
 // K and V rows are read once per launch: non-temporal loads (compile-time tunable).
@@ -168,7 +181,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // states stored by the others are in its L2 once each writer has waited for
 // its stores; the reader drops its own L1 lines first.  The arithmetic and
 // its order are those of the separate merge kernel.
-template <typename T, int D, int G>
+template <int W, typename T, int D, int G>
 __device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& mi, int32_t row, int32_t kvh) {
   __shared__ int32_t s_last;
   const int32_t hq = a.num_qo_heads;
@@ -187,7 +200,7 @@ __device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& m
   const int32_t n = mi.num_chunks, slot0 = mi.slot0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int32_t hh = wave; hh < G; hh += kWaves) {
+  for (int32_t hh = wave; hh < G; hh += W) {
     const int32_t head = kvh * G + hh;
     const float* pbase = a.part_o + (int64_t(slot0) * hq + head) * D;
     const int64_t cstride = int64_t(hq) * D;   // partial rows of one merge item's chunks are consecutive
@@ -276,10 +289,11 @@ __device__ void merge_in_launch(const AttnArgs& a, int32_t m, const MergeItem& m
   }
 }
 
-// T: query / output elements (bf16 bits or float).  TK: stored K/V elements
-// (T itself, or uint8_t E4M3 codes with T = bf16).
-template <typename T, typename TK, int D, int G, bool kAligned, bool kMask, bool kAppend, bool kMergeIn>
-__global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
+// W: waves per workgroup (4 or 1).  T: query / output elements (bf16 bits or
+// float).  TK: stored K/V elements (T itself, or uint8_t E4M3 codes with T = bf16).
+template <int W, typename T, typename TK, int D, int G, bool kAligned, bool kMask, bool kAppend, bool kMergeIn>
+__global__ __launch_bounds__(64 * W, (rows_min_waves<T, D, G>())) void attn_rows_kernel(const AttnArgs a) {
+  constexpr int kThreads = 64 * W;
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr bool kFp8 = sizeof(TK) == 1;
   static_assert(!kFp8 || kBF16, "fp8 caches compute on the bf16 path");
@@ -297,13 +311,13 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
   constexpr int kDepth = (kBF16 && G <= 4) ? PKV_DECODE_DEPTH : 2;
 
   __shared__ int32_t s_pages[kSegPages];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_m[W][G];
+  __shared__ float s_l[W][G];
+  __shared__ float s_acc[W][G][D];
   // Fused append: the first boundary block's K and V rows of each wave
   // (bf16 and fp8 rows; float32 rows load their boundary block after the loop).
   constexpr bool kPreBoundary = kBF16 && kDepth == 2;
-  __shared__ uint4 s_new[(kAppend && kPreBoundary) ? kWaves * NU * VCR * 128 : 1];
+  __shared__ uint4 s_new[(kAppend && kPreBoundary) ? W * NU * VCR * 128 : 1];
 
   const int32_t hkv = a.num_kv_heads;
   const int32_t item_idx = blockIdx.x / hkv;
@@ -536,7 +550,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         }
       };
 
-      constexpr int32_t kStride = kWaves * kBlockKeys;
+      constexpr int32_t kStride = W * kBlockKeys;
       // Fused append: the blocks from the one holding the segment's first new
       // key nlo onward (the boundary blocks) mix cached keys (below nlo) and
       // rows of k_new / v_new.  Each goes to the wave that owns it in the
@@ -571,7 +585,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
         if (nlo < thi) {
           nb0 = tlo + (nlo - tlo) / kBlockKeys * kBlockKeys;
           const int32_t k0 = (nb0 - tlo) / kBlockKeys;
-          bb = nb0 + ((wave - k0) % kWaves + kWaves) % kWaves * kBlockKeys;
+          bb = nb0 + ((wave - k0) % W + W) % W * kBlockKeys;
           bb0 = bb;
           thi = nb0;
         }
@@ -740,10 +754,10 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       const int h = idx / D, d = idx - (idx / D) * D;
       float mm = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w][h]);
+      for (int w = 0; w < W; ++w) mm = fmaxf(mm, s_m[w][h]);
       float ll = 0.f, oo = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float f = s_m[w][h] == -INFINITY ? 0.f : dev::fast_exp2(s_m[w][h] - mm);
         ll += f * s_l[w][h];
         oo += f * s_acc[w][h][d];
@@ -764,7 +778,7 @@ __global__ __launch_bounds__(kThreads, (rows_min_waves<T, D, G>())) void attn_ro
       }
     }
     if constexpr (kMergeIn) {
-      if (merge_m >= 0) merge_in_launch<T, D, G>(a, merge_m, merge_item, row, kvh);
+      if (merge_m >= 0) merge_in_launch<W, T, D, G>(a, merge_m, merge_item, row, kvh);
     }
     __syncthreads();
   }
@@ -775,27 +789,38 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int64_t blocks = int64_t(a.num_items) * a.num_kv_heads;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const bool aligned = a.page_shift >= 4;   // a power-of-two page of at least 16 keys
-  const dim3 grid{static_cast<uint32_t>(blocks)}, block{kThreads};
+  const dim3 grid{static_cast<uint32_t>(blocks)}, block{64 * kWaves};
   if (a.mask && (a.append_indptr || a.merge_ctr)) return hipErrorInvalidValue;   // masks run plain launches
   // Each variant is its own kernel, so that the plain decode launch carries
   // neither the append nor the in-launch merge code (their registers cost
   // the plain kernel about 1 us on the decode batch).
   auto go = [&](auto kernel) { launch_attention_kernel(kernel, grid, block, st, a); };
-  if (a.mask) {
-    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, true, false, false>);
-    else go(attn_rows_kernel<T, TK, D, G, false, true, false, false>);
+  if constexpr (kWaves == 1) {
+    // One-wave workgroups serve decode plans only: plain runs and runs with a
+    // fused append (no masks, no merge inside the launch).
+    if (a.mask || a.merge_ctr) return hipErrorInvalidValue;
+    if (a.append_indptr) {
+      if (aligned) go(attn_rows_kernel<1, T, TK, D, G, true, false, true, false>);
+      else go(attn_rows_kernel<1, T, TK, D, G, false, false, true, false>);
+    } else {
+      if (aligned) go(attn_rows_kernel<1, T, TK, D, G, true, false, false, false>);
+      else go(attn_rows_kernel<1, T, TK, D, G, false, false, false, false>);
+    }
+  } else if (a.mask) {
+    if (aligned) go(attn_rows_kernel<4, T, TK, D, G, true, true, false, false>);
+    else go(attn_rows_kernel<4, T, TK, D, G, false, true, false, false>);
   } else if (a.append_indptr && a.merge_ctr) {
-    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, true, true>);
-    else go(attn_rows_kernel<T, TK, D, G, false, false, true, true>);
+    if (aligned) go(attn_rows_kernel<4, T, TK, D, G, true, false, true, true>);
+    else go(attn_rows_kernel<4, T, TK, D, G, false, false, true, true>);
   } else if (a.append_indptr) {
-    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, true, false>);
-    else go(attn_rows_kernel<T, TK, D, G, false, false, true, false>);
+    if (aligned) go(attn_rows_kernel<4, T, TK, D, G, true, false, true, false>);
+    else go(attn_rows_kernel<4, T, TK, D, G, false, false, true, false>);
   } else if (a.merge_ctr) {
-    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, false, true>);
-    else go(attn_rows_kernel<T, TK, D, G, false, false, false, true>);
+    if (aligned) go(attn_rows_kernel<4, T, TK, D, G, true, false, false, true>);
+    else go(attn_rows_kernel<4, T, TK, D, G, false, false, false, true>);
   } else {
-    if (aligned) go(attn_rows_kernel<T, TK, D, G, true, false, false, false>);
-    else go(attn_rows_kernel<T, TK, D, G, false, false, false, false>);
+    if (aligned) go(attn_rows_kernel<4, T, TK, D, G, true, false, false, false>);
+    else go(attn_rows_kernel<4, T, TK, D, G, false, false, false, false>);
   }
   return hipGetLastError();
 }
@@ -818,8 +843,13 @@ hipError_t launch_g(int32_t group, const AttnArgs& a, hipStream_t st, bool* ok) 
 
 }  // namespace
 
+#if PKV_ROWS_WAVES == 1
+hipError_t launch_attn_rows_one_wave(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
+                                     hipStream_t st, bool* supported) {
+#else
 hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
                             hipStream_t st, bool* supported) {
+#endif
   *supported = false;
   if (dtype == kBF16) {
     if (head_dim == 128) return launch_g<uint16_t, uint16_t, 128>(group, a, st, supported);

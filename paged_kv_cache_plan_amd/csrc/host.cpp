@@ -165,6 +165,15 @@ int32_t default_tail_split(int32_t mode) { return mode == PKV_MODE_DECODE ? 2 : 
 // already ends on small items, and the extra items and merge rows only cost
 // (2048 decode requests of 1-96 keys: 188 us unsplit against 349 us split).
 constexpr int64_t kTailSplitMaxPerCu = 5;
+// Decode plans run one-wave workgroups by default when their items average at
+// most kOneWaveMaxKeys keys and number (times the kv heads) at least
+// kOneWaveMinPerCu per CU.  Measured, attention + merge with 4-wave / one-wave
+// workgroups (items x kv heads per CU, mean keys per item): 2048 requests of
+// 1-96 keys (64, 47) 196 / 95 us; 1024 of 16-256 (32, 136) 144 / 110 us; 512
+// of 64-512 (16, 291) 107 / 106 us; 384 of 128-1024 (12, 589) 146 / 169 us;
+// the skewed batch (3.75, 355) 43 / 50 us; 64 of 512-4096 (5.9, 734) 94 / 123 us.
+constexpr int64_t kOneWaveMaxKeys = 384;
+constexpr int64_t kOneWaveMinPerCu = 24;
 // MLA head groups: the kernel runs groups of 128 heads (one wave per 32
 // heads) or of 64 heads (two waves per 32 heads).  By default the heads form
 // groups of 128 when their count allows it, else groups of 64.
@@ -275,6 +284,10 @@ pkv_status check_params(const pkv_plan_params* p) {
     return fail(PKV_ERR_INVALID_ARG, fmt("unknown mask_mode %lld", p->mask_mode));
   if (p->merge_in_launch != 0 && p->merge_in_launch != 1)
     return fail(PKV_ERR_INVALID_ARG, "merge_in_launch must be 0 or 1");
+  if (p->row_waves != 0 && p->row_waves != 1 && p->row_waves != 4)
+    return fail(PKV_ERR_INVALID_ARG, "row_waves must be 0, 1 or 4");
+  if (p->row_waves == 1 && p->mode != PKV_MODE_DECODE)
+    return fail(PKV_ERR_UNSUPPORTED, "one-wave row workgroups run decode plans only");
   if ((p->kv_format == PKV_KV_RAGGED || p->mask_mode == PKV_MASK_CUSTOM) && p->mode != PKV_MODE_PREFILL)
     return fail(PKV_ERR_UNSUPPORTED, "ragged KV and custom masks need prefill mode");
   if (p->mask_mode == PKV_MASK_CUSTOM && p->causal)
@@ -498,6 +511,15 @@ pkv_status plan_impl(const pkv_plan_params* prm, const int32_t* qo_indptr, const
   in.num_cus = num_cus;
   in.target = int32_t(std::min<int64_t>(target, INT32_MAX));
   in.total_rows = int32_t(total_rows);
+  in.row_waves = 4;
+  if (prm->row_waves > 0) {
+    in.row_waves = prm->row_waves;
+  } else if (prm->mode == PKV_MODE_DECODE && !out->items.empty()) {
+    int64_t keys = 0;
+    for (const Item& it : out->items) keys += int64_t(it.kv_end) - it.kv_start;
+    const int64_t n = int64_t(out->items.size());
+    if (keys <= kOneWaveMaxKeys * n && n * heads_y >= kOneWaveMinPerCu * num_cus) in.row_waves = 1;
+  }
   const int64_t hq = prm->num_qo_heads;
   in.mask_bits = mask_bits;
   const int64_t merge_ctrs = out->tile_merge.empty() ? 0 : int64_t(out->merges.size()) * prm->num_kv_heads;
@@ -900,7 +922,9 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, const int32_t* qo_indp
     // more than a merge launch of its own.
     int32_t most = 0;
     for (const MergeItem& mi : r.merges) most = std::max(most, mi.num_chunks);
-    plan->merge_in = !r.merges.empty() && most <= kMergeInMaxChunks && merge_in_launch_ok(params, plan->device);
+    // One-wave workgroups fold no merge inside the launch.
+    plan->merge_in = r.info.row_waves == 4 && !r.merges.empty() && most <= kMergeInMaxChunks &&
+                     merge_in_launch_ok(params, plan->device);
   }
   plan->info.merge_in_launch = plan->merge_in ? 1 : 0;
   plan->h_staging = h_staging;
@@ -1039,12 +1063,15 @@ pkv_status prepare_attn(const pkv_plan_params& p, int plan_device, bool has_item
 
 // The attention kernel for a plan's mode: the MFMA tile kernel for bf16
 // prefill, the row kernel otherwise.
-pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::AttnArgs& a, hipStream_t st) {
+pkv_status launch_attn_mode(int32_t mode, const pkv_plan_params& p, const pkv::AttnArgs& a, hipStream_t st,
+                            int32_t row_waves = 4) {
   const int32_t group = p.num_qo_heads / p.num_kv_heads;
   bool supported = false;
   hipError_t e;
   if (mode == PKV_MODE_PREFILL && (p.kv_dtype == PKV_BF16 || p.kv_dtype == PKV_FP8_E4M3))
     e = pkv::launch_prefill_mfma(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
+  else if (row_waves == 1)
+    e = pkv::launch_attn_rows_one_wave(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
   else
     e = pkv::launch_attn_rows(p.kv_dtype, p.head_dim_qk, group, a, st, &supported);
   if (!supported)
@@ -1078,7 +1105,7 @@ pkv_status pkv_run_attention(const pkv_plan* plan, const void* q, int64_t q_stri
   a.live_items = plan->live_items();
   a.part_o = plan->d_part_o;
   a.part_lse = plan->d_part_lse;
-  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream));
+  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream), plan->info.row_waves);
   if (s) return s;
   return ok();
 }
@@ -1185,7 +1212,7 @@ pkv_status pkv_run_append(const pkv_plan* plan, const void* q, int64_t q_stride_
     a.tile_merge = plan->d_tile_merge;
     a.merge_ctr = plan->d_merge_ctr;
   }
-  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream));
+  s = launch_attn_mode(p.mode, p, a, static_cast<hipStream_t>(stream), plan->info.row_waves);
   if (s) return s;
   if (!with_merge || merge_in) return ok();
   return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
@@ -1205,7 +1232,8 @@ pkv_status run_with_args(const pkv_plan* plan, pkv::AttnArgs& a, void* o, int64_
     a.live_items = plan->live_items();
     a.part_o = plan->d_part_o;
     a.part_lse = plan->d_part_lse;
-    pkv_status s = launch_attn_mode(plan->params.mode, plan->params, a, static_cast<hipStream_t>(stream));
+    pkv_status s = launch_attn_mode(plan->params.mode, plan->params, a, static_cast<hipStream_t>(stream),
+                                    plan->info.row_waves);
     if (s) return s;
   }
   return pkv_run_merge(plan, o, o_stride_token, o_stride_head, lse, stream);
@@ -1498,7 +1526,7 @@ pkv_status pkv_run_noalloc(const pkv_plan_params* params, const int32_t* qo_indp
   a.live_items = nullptr;
   a.part_lse = reinterpret_cast<float*>(ws + in.staging_bytes);
   a.part_o = reinterpret_cast<float*>(ws + in.staging_bytes + lse_bytes);
-  s = launch_attn_mode(params->mode, *params, a, st);
+  s = launch_attn_mode(params->mode, *params, a, st, in.row_waves);
   if (s) return s;
   if (in.num_merges > 0) {
     pkv::MergePartialArgs m;
@@ -1614,6 +1642,8 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
   pkv_status s = graph_layout(params, caps, &g);
   if (!s) s = check_runnable(params);
   if (s) return s;
+  if (params->row_waves == 1)
+    return fail(PKV_ERR_UNSUPPORTED, "fixed-capacity plans run 4-wave row workgroups (row_waves 0 or 4)");
   if (!d_workspace || int64_t(ws_bytes) < g.workspace_bytes)
     return fail(PKV_ERR_WORKSPACE, fmt("workspace %lld bytes < %lld needed", int64_t(ws_bytes), g.workspace_bytes));
   if (reinterpret_cast<uintptr_t>(d_workspace) % 256 != 0)
@@ -1648,6 +1678,7 @@ pkv_status pkv_graph_plan_create(const pkv_plan_params* params, const pkv_graph_
     plan->merge_in = g.caps.max_merges > 0 && merge_in_launch_ok(params, plan->device);
   }
   plan->info.merge_in_launch = plan->merge_in ? 1 : 0;
+  plan->info.row_waves = 4;   // the captured launch keeps one kernel for every later batch
   // The live counts (and the merge counters) start at zero: a run before the
   // first update does nothing.
   if (e == hipSuccess)
@@ -1710,6 +1741,7 @@ pkv_status pkv_plan_update(pkv_plan* plan, const int32_t* qo_indptr, const int32
   plan->info.workspace_bytes = ws_bytes;
   plan->info.staging_bytes = st_bytes;
   plan->info.merge_in_launch = merge_in;
+  plan->info.row_waves = 4;
   return ok();
 }
 

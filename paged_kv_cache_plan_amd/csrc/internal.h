@@ -167,6 +167,10 @@ struct MlaArgs {
 // Kernel launchers (each returns the launch error, if any).
 hipError_t launch_attn_rows(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
                             hipStream_t stream, bool* supported);
+// The same row kernel with one wave per workgroup (decode plans of many short
+// items; plain runs and fused appends only).
+hipError_t launch_attn_rows_one_wave(int32_t dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
+                                     hipStream_t stream, bool* supported);
 hipError_t launch_prefill_mfma(int32_t kv_dtype, int32_t head_dim, int32_t group, const AttnArgs& a,
                                hipStream_t stream, bool* supported);
 // The MLA kernel addresses the 8 rows one wave loads with 32-bit offsets:

@@ -75,11 +75,11 @@ def _bits(x):
     return x.view(np.uint32) if x.dtype == np.float32 else x
 
 
-def _plan(pkv, b, kv_dtype, fixed, max_pages):
+def _plan(pkv, b, kv_dtype, fixed, max_pages, waves=0):
     params = pkv.plan_params(mode="decode", batch_size=b.batch_size, num_qo_heads=b.num_qo_heads,
                              num_kv_heads=b.num_kv_heads, head_dim_qk=b.head_dim, page_size=b.page_size,
                              causal=True, dtype=b.dtype, kv_dtype=kv_dtype, fixed_split_pages=fixed,
-                             max_num_pages=max_pages)
+                             max_num_pages=max_pages, row_waves=waves)
     return pkv.Plan(params, kv_indptr=b.kv_indptr, kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
 
 
@@ -95,12 +95,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("waves", [0, 1])
 @pytest.mark.parametrize("layout,page_size,dtype,kv_dtype,n_max,fixed", CASES)
-def test_fused_append_matches_append_then_run(torch, pkv, layout, page_size, dtype, kv_dtype, n_max, fixed):
-    print("case fused append", layout, page_size, dtype, kv_dtype, n_max, fixed, flush=True)
+def test_fused_append_matches_append_then_run(torch, pkv, layout, page_size, dtype, kv_dtype, n_max, fixed, waves):
+    """Row kernel workgroups as the plan picks them and forced to one wave."""
+    print("case fused append", layout, page_size, dtype, kv_dtype, n_max, fixed, waves, flush=True)
     b, append_indptr, k_new, v_new, (k_pois, v_pois), (k_exp, v_exp) = _batch(
         layout=layout, page_size=page_size, dtype=dtype, kv_dtype=kv_dtype, n_max=n_max, seed=n_max + page_size)
-    plan = _plan(pkv, b, kv_dtype, fixed, k_pois.shape[0])
+    plan = _plan(pkv, b, kv_dtype, fixed, k_pois.shape[0], waves)
+    assert plan.info["row_waves"] == waves if waves else plan.info["row_waves"] in (1, 4)
     if fixed:
         assert plan.info["split"] == 1
     q = gu.to_dev(b.q, dtype)

@@ -30,12 +30,13 @@ def pkv(torch):
     return pkv
 
 
-def _plan(pkv, b, fixed, num_cus, max_num_pages):
+def _plan(pkv, b, fixed, num_cus, max_num_pages, waves=0):
     mla = b.mode == "mla"
     params = pkv.plan_params(mode=b.mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads,
                              num_kv_heads=b.num_kv_heads, head_dim_qk=576 if mla else b.head_dim,
                              head_dim_vo=512 if mla else b.head_dim, page_size=b.page_size, causal=b.causal,
-                             dtype=b.dtype, num_cus=num_cus, fixed_split_pages=fixed, max_num_pages=max_num_pages)
+                             dtype=b.dtype, num_cus=num_cus, fixed_split_pages=fixed, max_num_pages=max_num_pages,
+                             row_waves=waves)
     plan = pkv.Plan(params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None, kv_indptr=b.kv_indptr,
                     kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
     info = plan.info
@@ -50,14 +51,15 @@ def _check(o, lse, ro, rl, what):
     print(what, gu.check_guard(got, ro, lse, rl, what), flush=True)
 
 
-@pytest.mark.parametrize("fixed,num_cus", [(LIMIT, 256), (0, 1)])
-def test_decode_chunks_at_the_limit(torch, pkv, fixed, num_cus):
-    """Forced 1024-page chunks, and the planner left to itself with one CU
-    (it then makes the longest chunks it may)."""
-    print("case decode chunk limit", fixed, num_cus, flush=True)
+@pytest.mark.parametrize("fixed,num_cus,waves", [(LIMIT, 256, 0), (0, 1, 0), (LIMIT, 256, 1)])
+def test_decode_chunks_at_the_limit(torch, pkv, fixed, num_cus, waves):
+    """Forced 1024-page chunks (row kernel workgroups of 4 waves and of one),
+    and the planner left to itself with one CU (it then makes the longest
+    chunks it may)."""
+    print("case decode chunk limit", fixed, num_cus, waves, flush=True)
     b = wl.make("decode", poison=True, page_size=1, batch=3, kv_range=(2100, 3100), seed=4101)
     k_dev, v_dev = gu.to_dev(b.k_cache, "bf16"), gu.to_dev(b.v_cache, "bf16")
-    plan = _plan(pkv, b, fixed, num_cus, k_dev.shape[0])
+    plan = _plan(pkv, b, fixed, num_cus, k_dev.shape[0], waves)
     q = gu.to_dev(b.q, "bf16")
     out = gu.empty_like_out(q.shape, "bf16")
     lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")
@@ -136,6 +138,8 @@ def test_many_short_requests(torch, pkv, mode):
     plan = pkv.Plan(params, qo_indptr=b.qo_indptr if mode == "prefill" else None, kv_indptr=b.kv_indptr,
                     kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
     assert plan.info["num_items"] >= 512, plan.info
+    # 2048 short decode requests: the plan picks one-wave row workgroups
+    assert plan.info["row_waves"] == (1 if mode == "decode" else 4), plan.info
     q = gu.to_dev(b.q, "bf16")
     out = gu.empty_like_out(q.shape, "bf16")
     lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")

@@ -438,14 +438,15 @@ ROW_KERNEL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("mode,waves", [("decode", 4), ("decode", 1), ("prefill", 0)])
 @pytest.mark.parametrize("dtype,kv_dtype,dim,group", ROW_KERNEL_CASES)
-def test_every_dtype_dim_and_group(torch, pkv, mode, dtype, kv_dtype, dim, group):
+def test_every_dtype_dim_and_group(torch, pkv, mode, waves, dtype, kv_dtype, dim, group):
     """Every (query dtype, cache dtype, head_dim, GQA group) the library builds,
-    in decode and prefill, on small batches (2 kv heads; HND for prefill):
-    each kernel instantiation against the oracle.  bf16 prefill with
-    head_dim 128 runs the MFMA tile kernel, the rest the row kernel."""
-    print("case kernel", mode, dtype, kv_dtype, dim, group, flush=True)
+    in decode (row kernel workgroups of 4 waves and of one) and prefill, on
+    small batches (2 kv heads; HND for prefill): each kernel instantiation
+    against the oracle.  bf16 prefill with head_dim 128 runs the MFMA tile
+    kernel, the rest the row kernel."""
+    print("case kernel", mode, waves, dtype, kv_dtype, dim, group, flush=True)
     kw = dict(hq=2 * group, hkv=2, dim=dim, dtype=dtype, kv_dtype=kv_dtype, batch=5)
     if mode == "decode":
         b = wl.make("decode", kv_range=(1, 300), pool=128, poison=True, **kw)
@@ -456,9 +457,10 @@ def test_every_dtype_dim_and_group(torch, pkv, mode, dtype, kv_dtype, dim, group
     k_dev, v_dev = to_kv(b.k_cache), to_kv(b.v_cache)
     params = pkv.plan_params(mode=mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads,
                              num_kv_heads=2, head_dim_qk=dim, page_size=b.page_size, causal=b.causal,
-                             dtype=dtype, kv_dtype=kv_dtype, max_num_pages=b.max_num_pages)
+                             dtype=dtype, kv_dtype=kv_dtype, max_num_pages=b.max_num_pages, row_waves=waves)
     plan = pkv.Plan(params, qo_indptr=b.qo_indptr if mode == "prefill" else None, kv_indptr=b.kv_indptr,
                     kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
+    assert plan.info["row_waves"] == (waves or 4)
     q = gu.to_dev(b.q, dtype)
     out = gu.empty_like_out(q.shape, dtype)
     lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")

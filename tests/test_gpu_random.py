@@ -57,8 +57,10 @@ def pkv(torch):
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_batch(torch, pkv, i):
     b, fixed = _case(i)
+    waves = 1 if b.mode == "decode" and i % 2 else 0   # odd decode cases: one-wave row workgroups
     print(f"case random {i}: {b.mode} {b.dtype}/{b.kv_dtype} d{b.head_dim} g{b.num_qo_heads // 2} page {b.page_size} "
-          f"{b.layout} causal={b.causal} fixed={fixed} qo={list(b.qo_lens)} kv={list(b.kv_lens)}", flush=True)
+          f"{b.layout} causal={b.causal} fixed={fixed} waves={waves} qo={list(b.qo_lens)} kv={list(b.kv_lens)}",
+          flush=True)
     fp8 = b.kv_dtype == "fp8"
     to_kv = (lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()) if fp8 else (lambda x: gu.to_dev(x, b.dtype))
     k_dev, v_dev = to_kv(b.k_cache), to_kv(b.v_cache)
@@ -73,9 +75,10 @@ def test_random_batch(torch, pkv, i):
     params = pkv.plan_params(mode=b.mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads, num_kv_heads=2,
                              head_dim_qk=b.head_dim, page_size=b.page_size, causal=b.causal, dtype=b.dtype,
                              kv_dtype=b.kv_dtype, fixed_split_pages=fixed, num_cus=8 if fixed else 0,
-                             max_num_pages=b.max_num_pages)
+                             max_num_pages=b.max_num_pages, row_waves=waves)
     plan = pkv.Plan(params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None, kv_indptr=b.kv_indptr,
                     kv_indices=b.kv_indices, kv_last_page_len=b.kv_last_page_len)
+    assert plan.info["row_waves"] == waves if waves else plan.info["row_waves"] in (1, 4)
     q = gu.to_dev(b.q, b.dtype)
     out = gu.empty_like_out(q.shape, b.dtype)
     lse = torch.full((q.shape[0], b.num_qo_heads), float("nan"), dtype=torch.float32, device="cuda")

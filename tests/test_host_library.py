@@ -607,3 +607,43 @@ def test_noalloc_run_rejects_batches_beyond_its_array():
                              _p32(np.array([3], np.int32)), FAKE_DEVICE_PTR, 0, 0, ctypes.byref(desc),
                              FAKE_DEVICE_PTR, FAKE_DEVICE_PTR, 0, 0, None, ctypes.c_float(0.0), None)
     assert st == _abi.ERR_INVALID_ARG
+
+
+def test_row_waves_choice_and_checks():
+    """Decode plans pick one-wave row workgroups when their items average at
+    most 384 keys and number at least 24 per CU (times the kv heads), else 4
+    waves; an explicit row_waves is used as given.  Other values, one-wave
+    plans outside decode and one-wave fixed-capacity plans are refused."""
+    def info(b, **kw):
+        params = pkv.plan_params(mode=b.mode, batch_size=b.batch_size, num_qo_heads=b.num_qo_heads,
+                                 num_kv_heads=b.num_kv_heads, head_dim_qk=b.head_dim, page_size=b.page_size,
+                                 causal=b.causal, dtype=b.dtype, **kw)
+        return pkv.plan_compute(params, qo_indptr=b.qo_indptr if b.mode == "prefill" else None,
+                                kv_indptr=b.kv_indptr, kv_indices=b.kv_indices,
+                                kv_last_page_len=b.kv_last_page_len)[0]
+    short = wl.make("decode", payload=False, batch=2048, kv_range=(1, 96), seed=4104)   # 2048 items of ~47 keys
+    assert info(short, num_cus=256)["row_waves"] == 1          # 64 (item, head) units per CU
+    assert info(short, num_cus=512)["row_waves"] == 1          # 32 per CU
+    assert info(short, num_cus=1024)["row_waves"] == 4         # 16 per CU
+    assert info(short, num_cus=256, row_waves=4)["row_waves"] == 4
+    dec = wl.make("decode", payload=False)                      # 188 items of ~734 keys
+    assert info(dec, num_cus=256)["row_waves"] == 4
+    assert info(dec, num_cus=256, row_waves=1)["row_waves"] == 1
+    assert info(wl.make("skewed", payload=False), num_cus=256)["row_waves"] == 4
+    assert info(wl.make("prefill", payload=False, scale=0.1), num_cus=256)["row_waves"] == 4
+    with pytest.raises(pkv.PkvError) as e:
+        info(dec, num_cus=256, row_waves=2)
+    assert e.value.status == _abi.ERR_INVALID_ARG
+    with pytest.raises(pkv.PkvError) as e:
+        info(wl.make("prefill", payload=False, scale=0.1), num_cus=256, row_waves=1)
+    assert e.value.status == _abi.ERR_UNSUPPORTED
+    params = pkv.plan_params(mode="decode", batch_size=2, num_qo_heads=4, num_kv_heads=2, head_dim_qk=64,
+                             page_size=4, dtype="f32", num_cus=4, max_num_pages=16, row_waves=1)
+    caps = pkv.graph_caps(max_total_pages=8)
+    _, ws, st = pkv.graph_plan_size(params, caps)
+    staging = np.zeros(st, np.uint8)
+    handle = ctypes.c_void_p()
+    assert pkv.lib().pkv_graph_plan_create(ctypes.byref(params), ctypes.byref(caps), FAKE_DEVICE_PTR, ws,
+                                           ctypes.c_void_p(staging.ctypes.data), st, None,
+                                           ctypes.byref(handle)) == _abi.ERR_UNSUPPORTED
+    assert not handle.value
